@@ -1,0 +1,301 @@
+"""ctypes wrapper of the fp64 CPU oracle (vlb_oracle.c).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only tests/, the smoke check in
+__graft_entry__ and the CPU-baseline leg of bench.py import this module.  The
+oracle shares no code with the HIP path; it reads the same seeded host inputs,
+widened exactly to float64.
+
+Page citations for each step live in vlb_oracle.c and vlb_oracle.h.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vlb_oracle.c")
+_LIB = os.path.join(_HERE, "libvlb_oracle.so")
+
+GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
+SRC_NEWLINE, SRC_SEPARATOR = -1, -2
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "vlb_oracle.h"))
+    ):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-std=c11", "-D_GNU_SOURCE", "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ct.CDLL(build())
+        _declare(_lib)
+    return _lib
+
+
+class use_library:
+    """Context manager: route every call of this module to another build of the
+    oracle (the mutation tests load copies with a planted mistake)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = lib()
+        L = ct.CDLL(self.path)
+        _declare(L)
+        _lib = L
+        return L
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def build_variant(src_text: str, out_dir: str, name: str) -> str:
+    """Compile a modified copy of the oracle source (used only by mutation tests)."""
+    import shutil
+    c = os.path.join(out_dir, name + ".c")
+    with open(c, "w") as f:
+        f.write(src_text)
+    shutil.copy(os.path.join(_HERE, "vlb_oracle.h"), os.path.join(out_dir, "vlb_oracle.h"))
+    so = os.path.join(out_dir, "lib" + name + ".so")
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11",
+                           "-D_GNU_SOURCE", "-o", so, c, "-lm", "-lpthread"])
+    return so
+
+
+class _Spec(ct.Structure):
+    _fields_ = [
+        ("n_views", ct.c_int32),
+        ("grid_h", ct.POINTER(ct.c_int32)),
+        ("grid_w", ct.POINTER(ct.c_int32)),
+        ("C", ct.c_int32), ("k", ct.c_int32), ("hidden", ct.c_int32), ("out_dim", ct.c_int32),
+        ("has_ln", ct.c_int32),
+        ("ln_eps", ct.c_double),
+        ("act", ct.c_int32),
+        ("n_images", ct.c_int32),
+        ("views_per_image", ct.POINTER(ct.c_int32)),
+        ("tiled", ct.c_int32),
+        ("tile_w", ct.POINTER(ct.c_int32)),
+        ("tile_h", ct.POINTER(ct.c_int32)),
+        ("global_tail", ct.c_int32),
+    ]
+
+
+_D = ct.POINTER(ct.c_double)
+_I64 = ct.POINTER(ct.c_int64)
+_U8 = ct.POINTER(ct.c_uint8)
+
+
+def _declare(L):
+    i64 = ct.c_int64
+    L.orc_merged_side.restype = i64
+    L.orc_merged_side.argtypes = [i64, i64]
+    L.orc_view_tokens.restype = i64
+    L.orc_view_tokens.argtypes = [i64, i64, i64]
+    L.orc_total_tokens.restype = i64
+    L.orc_total_tokens.argtypes = [ct.POINTER(_Spec)]
+    L.orc_tiled_placeholders.restype = i64
+    L.orc_tiled_placeholders.argtypes = [i64, i64, i64, i64]
+    L.orc_param_count.restype = i64
+    L.orc_param_count.argtypes = [i64, i64, i64, i64, ct.c_int32]
+    L.orc_layer_norm.restype = None
+    L.orc_layer_norm.argtypes = [_D, i64, ct.c_int32, _D, _D, ct.c_double, _D]
+    L.orc_merge_view.restype = None
+    L.orc_merge_view.argtypes = [_D, ct.c_int32, ct.c_int32, ct.c_int32, ct.c_int32, _D]
+    L.orc_unmerge_view.restype = None
+    L.orc_unmerge_view.argtypes = [_D, ct.c_int32, ct.c_int32, ct.c_int32, ct.c_int32, _D]
+    L.orc_linear.restype = None
+    L.orc_linear.argtypes = [_D, i64, ct.c_int32, _D, _D, ct.c_int32, _D, ct.c_int32]
+    L.orc_gelu_erf.restype = None
+    L.orc_gelu_erf.argtypes = [_D, i64]
+    L.orc_gelu_tanh.restype = None
+    L.orc_gelu_tanh.argtypes = [_D, i64]
+    L.orc_merged_row.restype = None
+    L.orc_merged_row.argtypes = [ct.POINTER(_Spec), _D, _D, _D, i64, _D]
+    L.orc_project_rows.restype = None
+    L.orc_project_rows.argtypes = [ct.POINTER(_Spec), _D, _D, _D, _D, _D, _D, _D, _I64, i64, _D,
+                                   ct.c_int32]
+    L.orc_assemble.restype = i64
+    L.orc_assemble.argtypes = [ct.POINTER(_Spec), _I64, i64]
+    L.orc_scatter.restype = ct.c_int32
+    L.orc_scatter.argtypes = [_I64, i64, _D, _D, _D, _U8, i64, ct.c_int32, _D]
+
+
+def _f64(a) -> np.ndarray:
+    """Exact widening of a host array (numpy or torch CPU, any float dtype) to float64."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: widen in torch (bf16 has no numpy dtype)
+        import torch
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _dp(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+@dataclass
+class Spec:
+    """A bridge problem as the oracle sees it (same meaning as orc_spec)."""
+
+    grids: Sequence[tuple]          # (gh, gw) per view, in storage order
+    C: int
+    k: int
+    hidden: int
+    out_dim: int
+    views_per_image: Sequence[int]
+    has_ln: bool = False
+    ln_eps: float = 1e-6
+    act: int = GELU_ERF
+    tiled: bool = False
+    tiles: Sequence[tuple] = ()     # (tw, th) per image when tiled
+    global_tail: bool = False
+    _keep: list = field(default_factory=list, repr=False)
+
+    def c(self) -> _Spec:
+        gh = np.ascontiguousarray([g[0] for g in self.grids], dtype=np.int32)
+        gw = np.ascontiguousarray([g[1] for g in self.grids], dtype=np.int32)
+        vpi = np.ascontiguousarray(self.views_per_image, dtype=np.int32)
+        tw = np.ascontiguousarray([t[0] for t in self.tiles] or [0], dtype=np.int32)
+        th = np.ascontiguousarray([t[1] for t in self.tiles] or [0], dtype=np.int32)
+        self._keep = [gh, gw, vpi, tw, th]
+        p32 = lambda a: a.ctypes.data_as(ct.POINTER(ct.c_int32))
+        return _Spec(len(self.grids), p32(gh), p32(gw), self.C, self.k, self.hidden,
+                     self.out_dim, int(self.has_ln), float(self.ln_eps), int(self.act),
+                     len(self.views_per_image), p32(vpi), int(self.tiled), p32(tw), p32(th),
+                     int(self.global_tail))
+
+
+def merged_side(g: int, k: int) -> int:
+    return int(lib().orc_merged_side(g, k))
+
+
+def view_tokens(gh: int, gw: int, k: int) -> int:
+    return int(lib().orc_view_tokens(gh, gw, k))
+
+
+def total_tokens(spec: Spec) -> int:
+    s = spec.c()
+    return int(lib().orc_total_tokens(ct.byref(s)))
+
+
+def tiled_placeholders(hp: int, wp: int, tw: int, th: int) -> int:
+    return int(lib().orc_tiled_placeholders(hp, wp, tw, th))
+
+
+def param_count(C: int, k: int, hidden: int, out_dim: int, has_ln: bool) -> int:
+    return int(lib().orc_param_count(C, k, hidden, out_dim, int(has_ln)))
+
+
+def layer_norm(x, gamma, beta, eps: float) -> np.ndarray:
+    x = _f64(x)
+    C = x.shape[-1]
+    out = np.empty_like(x)
+    lib().orc_layer_norm(_dp(x), x.size // C, C, _dp(_f64(gamma)), _dp(_f64(beta)), eps, _dp(out))
+    return out
+
+
+def merge_view(x, k: int) -> np.ndarray:
+    """x: (gh, gw, C) -> (tokens, C*k*k) in the pages' feature order."""
+    x = _f64(x)
+    gh, gw, C = x.shape
+    out = np.empty((view_tokens(gh, gw, k), C * k * k), dtype=np.float64)
+    lib().orc_merge_view(_dp(x), gh, gw, C, k, _dp(out))
+    return out
+
+
+def unmerge_view(m, gh: int, gw: int, C: int, k: int) -> np.ndarray:
+    m = _f64(m)
+    out = np.empty((gh, gw, C), dtype=np.float64)
+    lib().orc_unmerge_view(_dp(m), gh, gw, C, k, _dp(out))
+    return out
+
+
+def linear(x, W, b, nthreads: int = 1) -> np.ndarray:
+    x = _f64(x)
+    W = _f64(W)
+    rows, in_dim = x.shape
+    out_dim = W.shape[0]
+    out = np.empty((rows, out_dim), dtype=np.float64)
+    lib().orc_linear(_dp(x), rows, in_dim, _dp(W), _dp(_f64(b)), out_dim, _dp(out), nthreads)
+    return out
+
+
+def gelu_erf(x) -> np.ndarray:
+    x = _f64(x).copy()
+    lib().orc_gelu_erf(_dp(x), x.size)
+    return x
+
+
+def gelu_tanh(x) -> np.ndarray:
+    x = _f64(x).copy()
+    lib().orc_gelu_tanh(_dp(x), x.size)
+    return x
+
+
+def merged_row(spec: Spec, x, gamma, beta, r: int) -> np.ndarray:
+    s = spec.c()
+    out = np.empty(spec.C * spec.k * spec.k, dtype=np.float64)
+    lib().orc_merged_row(ct.byref(s), _dp(_f64(x)), _dp(_f64(gamma)), _dp(_f64(beta)), r, _dp(out))
+    return out
+
+
+def project_rows(spec: Spec, x, gamma, beta, W1, b1, W2, b2, row_ids=None,
+                 nthreads: int = 0) -> np.ndarray:
+    """fp64 projected rows for the listed token rows (all rows when None)."""
+    s = spec.c()
+    if row_ids is None:
+        row_ids = np.arange(total_tokens(spec), dtype=np.int64)
+    row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    if nthreads <= 0:
+        nthreads = os.cpu_count() or 1
+    out = np.empty((len(row_ids), spec.out_dim), dtype=np.float64)
+    xs = [_f64(a) for a in (x, gamma, beta, W1, b1, W2, b2)]
+    lib().orc_project_rows(ct.byref(s), *[_dp(a) for a in xs], row_ids.ctypes.data_as(_I64),
+                           len(row_ids), _dp(out), nthreads)
+    return out
+
+
+def assemble(spec: Spec) -> np.ndarray:
+    s = spec.c()
+    n = int(lib().orc_assemble(ct.byref(s), None, 0))
+    src = np.empty(max(n, 1), dtype=np.int64)
+    got = int(lib().orc_assemble(ct.byref(s), src.ctypes.data_as(_I64), n))
+    assert got == n
+    return src[:n]
+
+
+def scatter(src, rows, newline, separator, mask, seq):
+    """Returns (status, new_seq); status -1 = placeholder-count mismatch (seq untouched)."""
+    src = np.ascontiguousarray(src, dtype=np.int64)
+    rows = _f64(rows)
+    seq = _f64(seq).copy()
+    S, D = seq.shape
+    mask = np.ascontiguousarray(np.asarray(mask), dtype=np.uint8)
+    nl = _f64(newline) if newline is not None else np.zeros(D)
+    sp = _f64(separator) if separator is not None else np.zeros(D)
+    st = int(lib().orc_scatter(src.ctypes.data_as(_I64), len(src), _dp(rows), _dp(nl), _dp(sp),
+                               mask.ctypes.data_as(_U8), S, D, _dp(seq)))
+    return st, seq

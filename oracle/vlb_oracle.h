@@ -1,0 +1,116 @@
+/*
+ * vlb_oracle.h -- plain fp64 CPU oracle of the vision-to-language bridge.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library.  It shares
+ * no code, header, table or helper with the HIP path in patch_merge_mlp_amd/.
+ *
+ * Every value is a double.  Inputs that were stored in bf16 or fp32 are widened
+ * to double exactly by the caller; the oracle itself never rounds to a narrower
+ * type.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [VL2]  "feat(models): port DeepSeek-VL2 (MoE text + SigLIP/SAM vision)",
+ *          mlxcel issue #533 -- sections "Projector (downsample_mlp_gelu)",
+ *          "Tile-sequence assembly (tile_tag 2D)", "Processor" step 7,
+ *          "Validation and acceptance criteria".
+ *   [V4V]  "DeepSeek-V4-Flash-Vision-BF16" model card -- header paragraph
+ *          (2x2 PatchMerger, 4608 -> 4096, 40,119,040 projector parameters).
+ *   [VOIE] "La voie visuelle" (DeepSeek-V4.1-Flash architecture notes) --
+ *          sections "Le pixel-unshuffle 3x3" and "Le calcul".
+ *   [HYB]  "DeepSeek-VL Hybrid" (KerasFormers docs) -- processor argument
+ *          num_image_tokens = 576.
+ */
+#ifndef VLB_ORACLE_H
+#define VLB_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Activation between the two projector Linears. */
+enum { ORC_GELU_ERF = 0, ORC_GELU_TANH = 1, ORC_ACT_NONE = 2 };
+
+/* Source codes of an assembled slot that is not a projected token row. */
+enum { ORC_SRC_NEWLINE = -1, ORC_SRC_SEPARATOR = -2 };
+
+/* One bridge problem.  Views are stored back to back, each (gh, gw, C)
+ * channels-last; images own consecutive views.  For the tiled layout an image
+ * has 1 + tile_w*tile_h views, the global view first. */
+typedef struct {
+  int32_t n_views;
+  const int32_t *grid_h, *grid_w;   /* [n_views] */
+  int32_t C, k, hidden, out_dim;
+  int32_t has_ln;
+  double ln_eps;
+  int32_t act;                      /* ORC_GELU_ERF / ORC_GELU_TANH / ORC_ACT_NONE */
+  int32_t n_images;
+  const int32_t *views_per_image;   /* [n_images] */
+  int32_t tiled;                    /* 0: tokens in order; 1: 2D tile assembly */
+  const int32_t *tile_w, *tile_h;   /* [n_images], tiled only */
+  int32_t global_tail;              /* tiled only: 1 = [local, sep, global] */
+} orc_spec;
+
+/* ceil(g / k): side of the merged grid after high-end zero padding [VL2 Projector 1-2]. */
+int64_t orc_merged_side(int64_t g, int64_t k);
+/* Projected token rows of one view. */
+int64_t orc_view_tokens(int64_t gh, int64_t gw, int64_t k);
+/* Total projected token rows of the problem (views concatenated in order). */
+int64_t orc_total_tokens(const orc_spec *s);
+/* Placeholder count of one tiled image by the closed formula of [VL2 Processor step 7]. */
+int64_t orc_tiled_placeholders(int64_t hp, int64_t wp, int64_t tw, int64_t th);
+/* Parameter count of LN(C, affine, optional) + Linear(C k^2 -> hidden) + Linear(hidden -> out). */
+int64_t orc_param_count(int64_t C, int64_t k, int64_t hidden, int64_t out_dim, int32_t has_ln);
+
+/* Per-pixel LayerNorm over the C channels of npix pixels (biased variance,
+ * eps inside the square root, affine gamma/beta). */
+void orc_layer_norm(const double *x, int64_t npix, int32_t C, const double *gamma,
+                    const double *beta, double eps, double *out);
+
+/* Pad one (gh, gw, C) view with zeros at the high end to a multiple of k and
+ * apply the k x k space-to-depth: out[t][c*k*k + dy*k + dx], t row-major over
+ * the merged grid [VL2 Projector 1-2].  out has orc_view_tokens() rows of C*k*k. */
+void orc_merge_view(const double *x, int32_t gh, int32_t gw, int32_t C, int32_t k, double *out);
+/* Inverse of orc_merge_view on the unpadded cells (the merge is lossless [VOIE]). */
+void orc_unmerge_view(const double *merged, int32_t gh, int32_t gw, int32_t C, int32_t k,
+                      double *x);
+
+/* out[r][j] = b[j] + sum_i in[r][i] * W[j][i]; W stored (out_dim, in_dim). */
+void orc_linear(const double *in, int64_t rows, int32_t in_dim, const double *W,
+                const double *b, int32_t out_dim, double *out, int32_t nthreads);
+/* In-place activations. */
+void orc_gelu_erf(double *x, int64_t n);
+void orc_gelu_tanh(double *x, int64_t n);
+
+/* Merged (LN -> pad -> space-to-depth) feature row of projected token row r of
+ * the whole problem.  x holds all views; gamma/beta may be NULL when has_ln=0. */
+void orc_merged_row(const orc_spec *s, const double *x, const double *gamma,
+                    const double *beta, int64_t r, double *out);
+
+/* Projected rows (merge -> Linear -> act -> Linear) for the listed token rows.
+ * out is [n_rows][out_dim]. */
+void orc_project_rows(const orc_spec *s, const double *x, const double *gamma,
+                      const double *beta, const double *W1, const double *b1,
+                      const double *W2, const double *b2, const int64_t *row_ids,
+                      int64_t n_rows, double *out, int32_t nthreads);
+
+/* Assembly order of all images [VL2 Tile-sequence assembly].  Writes the
+ * source of every placeholder slot into src (token row >= 0, or
+ * ORC_SRC_NEWLINE / ORC_SRC_SEPARATOR) and returns the slot count P.  src may
+ * be NULL to count only; otherwise it must hold cap entries (returns -1 if
+ * P > cap). */
+int64_t orc_assemble(const orc_spec *s, int64_t *src, int64_t cap);
+
+/* Overwrite seq (S x D) at the mask==1 positions, in order, with the assembled
+ * rows [VL2 Tile-sequence assembly, last paragraph].  rows is [T][D] indexed by
+ * token row.  Returns 0, or -1 without writing anything if the number of
+ * placeholder positions differs from P [VL2 Validation]. */
+int32_t orc_scatter(const int64_t *src, int64_t P, const double *rows, const double *newline,
+                    const double *separator, const uint8_t *mask, int64_t S, int32_t D,
+                    double *seq);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,281 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each pin_* function takes the oracle module and raises AssertionError when the
+oracle disagrees with a value the pages print, a closed form, an invariant, or a
+library routine that computes the same special case.  test_oracle_pins runs them
+on the real oracle; test_oracle_mutants runs them on copies of the oracle with
+one planted mistake each and requires that some pin fails.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            out.append(line.rstrip("\n").split("\t"))
+    return out
+
+
+def _tiled_spec(o, grid, k, tw, th, n_images=1, tail=False, D=1):
+    views = 1 + tw * th
+    return o.Spec(grids=[(grid, grid)] * (views * n_images), C=1, k=k, hidden=1, out_dim=D,
+                  views_per_image=[views] * n_images, tiled=True, tiles=[(tw, th)] * n_images,
+                  global_tail=tail)
+
+
+# --- values the pages print -------------------------------------------------
+
+def pin_page_counts(o):
+    """Token and slot counts worked out on the pages (tests/golden/page_counts.tsv)."""
+    for kind, px, patch, k, tw, th, expected, _src in _rows("page_counts.tsv"):
+        px, patch, k, tw, th, expected = map(int, (px, patch, k, tw, th, expected))
+        g = px // patch  # the tower's patch grid: floor(image_size / patch_size)
+        if kind == "patches":
+            assert g * g == expected
+        elif kind == "tokens":
+            assert o.view_tokens(g, g, k) == expected, (px, patch, k)
+            spec = o.Spec(grids=[(g, g)], C=1, k=k, hidden=1, out_dim=1, views_per_image=[1])
+            assert len(o.assemble(spec)) == expected
+        elif kind == "slots":
+            spec = _tiled_spec(o, g, k, tw, th)
+            assert len(o.assemble(spec)) == expected, (px, patch, tw, th)
+            hp = o.merged_side(g, k)
+            assert o.tiled_placeholders(hp, hp, tw, th) == expected
+        else:
+            raise AssertionError(kind)
+
+
+def pin_param_count(o):
+    """40,119,040 = LN(1152) + Linear(4608->4608) + Linear(4608->4096); the other
+    plausible layouts miss it."""
+    for C, k, hidden, out, has_ln, expected in _rows("projector_params.tsv"):
+        C, k, hidden, out, has_ln, expected = map(int, (C, k, hidden, out, has_ln, expected))
+        assert o.param_count(C, k, hidden, out, bool(has_ln)) == expected
+        assert o.param_count(C, k, hidden, out, not has_ln) != expected
+        assert o.param_count(C * k * k, 1, hidden, out, bool(has_ln)) != expected  # LN over 4608
+
+
+def pin_merged_width(o):
+    """4 x 1152 = 4608 (2x2 PatchMerger) and 9 x 1024 = 9216 (3x3 pixel-unshuffle)."""
+    assert o.merge_view(np.ones((2, 2, 1152)), 2).shape == (1, 4608)
+    assert o.merge_view(np.ones((3, 3, 1024)), 3).shape == (1, 9216)
+
+
+# --- the merge: bijection and the library pixel-unshuffle ------------------
+
+_GRIDS = [(4, 4, 3, 2), (5, 7, 2, 2), (7, 5, 3, 3), (6, 6, 4, 3), (3, 3, 5, 1), (1, 1, 2, 2)]
+
+
+def pin_merge_roundtrip(o):
+    """The merge is lossless: unmerge(merge(x)) == x bit for bit; padded cells are 0."""
+    rng = np.random.default_rng(1)
+    for gh, gw, C, k in _GRIDS:
+        x = rng.standard_normal((gh, gw, C)) + 3.0  # no zeros in the data
+        m = o.merge_view(x, k)
+        hp, wp = -(-gh // k), -(-gw // k)
+        assert m.shape == (hp * wp, C * k * k)
+        assert np.array_equal(o.unmerge_view(m, gh, gw, C, k), x)
+        assert int((m == 0).sum()) == (hp * k * wp * k - gh * gw) * C
+
+
+def _torch_merge(x, k):
+    """The library pixel-unshuffle after high-end zero padding: (gh, gw, C) -> (tokens, C k^2)."""
+    gh, gw, C = x.shape
+    hp, wp = -(-gh // k), -(-gw // k)
+    t = torch.from_numpy(x).permute(2, 0, 1).unsqueeze(0)
+    t = F.pad(t, (0, wp * k - gw, 0, hp * k - gh))
+    u = F.pixel_unshuffle(t, k)  # (1, C k^2, hp, wp), channel = c k^2 + dy k + dx
+    return u[0].permute(1, 2, 0).reshape(hp * wp, C * k * k).numpy()
+
+
+def pin_merge_pixel_unshuffle(o):
+    """Feature order c*k*k + dy*k + dx equals torch's pixel_unshuffle channel order."""
+    rng = np.random.default_rng(2)
+    for gh, gw, C, k in _GRIDS:
+        x = rng.standard_normal((gh, gw, C))
+        assert np.array_equal(o.merge_view(x, k), _torch_merge(x, k)), (gh, gw, C, k)
+
+
+# --- assembly: the page's reshape / transpose / concatenate recipe ----------
+
+def _recipe(hp, wp, tw, th, tail):
+    """The tile-sequence assembly run with torch tensor ops on token ids (D = 1):
+    newline = -1, separator = -2."""
+    n = hp * wp
+    tok = torch.arange((1 + tw * th) * n, dtype=torch.int64).reshape(1 + tw * th, n, 1)
+    g = tok[0].reshape(hp, wp, 1)
+    g = torch.cat([g, torch.full((hp, 1, 1), -1)], dim=1).reshape(hp * (wp + 1), 1)
+    loc = tok[1:].reshape(th, tw, hp, wp, 1).permute(0, 2, 1, 3, 4).reshape(th * hp, tw * wp, 1)
+    loc = torch.cat([loc, torch.full((th * hp, 1, 1), -1)], dim=1)
+    loc = loc.reshape(th * hp * (tw * wp + 1), 1)
+    sep = torch.full((1, 1), -2)
+    parts = [loc, sep, g] if tail else [g, sep, loc]
+    return torch.cat(parts, dim=0).reshape(-1).numpy()
+
+
+def pin_assembly_recipe(o):
+    for hp, tw, th, tail in [(2, 2, 3, False), (3, 1, 1, False), (2, 3, 2, True), (14, 2, 1, False),
+                             (4, 1, 3, False), (1, 2, 2, True)]:
+        k = 2
+        spec = _tiled_spec(o, hp * k - 1, k, tw, th, tail=tail)  # odd grid: padded to hp*k
+        assert o.merged_side(hp * k - 1, k) == hp
+        got = o.assemble(spec)
+        want = _recipe(hp, hp, tw, th, tail)
+        assert np.array_equal(got, want), (hp, tw, th, tail)
+        assert (got == -1).sum() == hp + th * hp and (got == -2).sum() == 1
+
+
+def pin_assembly_images(o):
+    """Images are laid out one after another, each with its own token rows."""
+    spec = _tiled_spec(o, 4, 2, 2, 1, n_images=3)
+    got = o.assemble(spec)
+    one = _recipe(2, 2, 2, 1, False)
+    per = 3 * 4  # three views of 2x2 tokens
+    want = np.concatenate([np.where(one >= 0, one + i * per, one) for i in range(3)])
+    assert np.array_equal(got, want)
+    plain = o.Spec(grids=[(4, 6), (3, 3)], C=1, k=2, hidden=1, out_dim=1, views_per_image=[1, 1])
+    assert np.array_equal(o.assemble(plain), np.arange(6 + 4))
+    assert o.total_tokens(plain) == 10
+
+
+# --- projector arithmetic against the library routines ----------------------
+
+def pin_gelu_values(o):
+    """GELU(x) = x Phi(x) at tabulated normal-CDF points, and GELU(x) - GELU(-x) = x."""
+    for x, phi in _rows("normal_cdf.tsv"):
+        x, phi = float(x), float(phi)
+        got = o.gelu_erf(np.array([x, -x]))
+        assert abs(got[0] - x * phi) < 1e-14
+        assert abs(got[1] - (-x) * (1.0 - phi)) < 1e-14
+    xs = np.linspace(-6, 6, 101)
+    assert np.allclose(o.gelu_erf(xs) - o.gelu_erf(-xs), xs, rtol=0, atol=1e-14)
+    assert o.gelu_erf(np.array([0.0]))[0] == 0.0
+
+
+def pin_gelu_library(o):
+    x = torch.linspace(-8, 8, 1001, dtype=torch.float64)
+    assert np.allclose(o.gelu_erf(x.numpy()), F.gelu(x).numpy(), rtol=0, atol=1e-15)
+    assert np.allclose(o.gelu_tanh(x.numpy()), F.gelu(x, approximate="tanh").numpy(), rtol=0,
+                       atol=1e-15)
+
+
+def pin_linear_library(o):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 13))
+    W = rng.standard_normal((5, 13))
+    b = rng.standard_normal(5)
+    want = F.linear(torch.from_numpy(x), torch.from_numpy(W), torch.from_numpy(b)).numpy()
+    for nt in (1, 3):
+        assert np.allclose(o.linear(x, W, b, nt), want, rtol=1e-13, atol=1e-13)
+
+
+def pin_layer_norm(o):
+    rng = np.random.default_rng(4)
+    C = 48
+    x = rng.standard_normal((9, C)) * 3 + 1
+    g = rng.standard_normal(C)
+    b = rng.standard_normal(C)
+    want = F.layer_norm(torch.from_numpy(x), (C,), torch.from_numpy(g), torch.from_numpy(b),
+                        eps=1e-6).numpy()
+    assert np.allclose(o.layer_norm(x, g, b, 1e-6), want, rtol=1e-12, atol=1e-12)
+    # Invariants with gamma = 1, beta = 0: zero mean, variance var/(var+eps).
+    eps = 0.5
+    y = o.layer_norm(x, np.ones(C), np.zeros(C), eps)
+    var = x.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var / (var + eps), rtol=1e-12)
+
+
+def pin_project_rows_library(o):
+    """The whole projector row by row vs. library routines: layer_norm, pad,
+    pixel_unshuffle, linear, gelu, linear; for both activations and with LN on/off,
+    on views of different sizes (odd ones padded)."""
+    rng = np.random.default_rng(5)
+    C, k, H, O = 6, 2, 10, 7
+    grids = [(3, 5), (4, 4), (5, 3)]
+    x = rng.standard_normal((sum(a * b for a, b in grids), C))
+    g = rng.standard_normal(C)
+    bb = rng.standard_normal(C)
+    W1 = rng.standard_normal((H, C * k * k))
+    b1 = rng.standard_normal(H)
+    W2 = rng.standard_normal((O, H))
+    b2 = rng.standard_normal(O)
+    for has_ln in (False, True):
+        for act in (o.GELU_ERF, o.GELU_TANH, o.ACT_NONE):
+            spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[1, 2],
+                          has_ln=has_ln, ln_eps=1e-6, act=act)
+            merged, p = [], 0
+            for gh, gw in grids:
+                v = torch.from_numpy(x[p:p + gh * gw].reshape(gh, gw, C))
+                p += gh * gw
+                if has_ln:
+                    v = F.layer_norm(v, (C,), torch.from_numpy(g), torch.from_numpy(bb), eps=1e-6)
+                merged.append(_torch_merge(v.numpy(), k))
+            m = torch.from_numpy(np.concatenate(merged))
+            h = F.linear(m, torch.from_numpy(W1), torch.from_numpy(b1))
+            if act == o.GELU_ERF:
+                h = F.gelu(h)
+            elif act == o.GELU_TANH:
+                h = F.gelu(h, approximate="tanh")
+            want = F.linear(h, torch.from_numpy(W2), torch.from_numpy(b2)).numpy()
+            got = o.project_rows(spec, x, g, bb, W1, b1, W2, b2, nthreads=2)
+            assert got.shape == want.shape
+            assert np.allclose(got, want, rtol=1e-12, atol=1e-12), (has_ln, act)
+            sub = np.array([5, 0, len(want) - 1])
+            got_sub = o.project_rows(spec, x, g, bb, W1, b1, W2, b2, row_ids=sub, nthreads=1)
+            assert np.array_equal(got_sub, got[sub])
+
+
+# --- scatter -----------------------------------------------------------------
+
+def pin_scatter(o):
+    """Rows overwrite the placeholder positions in order; everything else is kept;
+    a count mismatch writes nothing."""
+    S, D = 12, 3
+    seq = np.arange(S * D, dtype=np.float64).reshape(S, D) + 1000
+    rows = np.array([[1, 1, 1], [2, 2, 2], [3, 3, 3]], dtype=np.float64)
+    nl = np.full(D, -1.0)
+    sp = np.full(D, -2.0)
+    src = np.array([1, -1, 0, -2, 2])  # token 1, newline, token 0, separator, token 2
+    mask = np.zeros(S, dtype=np.uint8)
+    mask[[2, 3, 7, 8, 11]] = 1
+    st, out = o.scatter(src, rows, nl, sp, mask, seq)
+    assert st == 0
+    want = seq.copy()
+    want[2], want[3], want[7], want[8], want[11] = rows[1], nl, rows[0], sp, rows[2]
+    assert np.array_equal(out, want)
+    for bad in ([2, 3, 7, 8], [0, 2, 3, 7, 8, 11]):
+        m = np.zeros(S, dtype=np.uint8)
+        m[bad] = 1
+        st, out = o.scatter(src, rows, nl, sp, m, seq)
+        assert st == -1 and np.array_equal(out, seq)
+    st, out = o.scatter(np.zeros(0, dtype=np.int64), rows, nl, sp, np.zeros(S, np.uint8), seq)
+    assert st == 0 and np.array_equal(out, seq)
+
+
+ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
+       pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
+       pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter]
+
+
+def failing(o):
+    """Names of the pins that fail (used by the mutation tests)."""
+    bad = []
+    for p in ALL:
+        try:
+            p(o)
+        except Exception:  # noqa: BLE001 - any failure counts
+            bad.append(p.__name__)
+    return bad

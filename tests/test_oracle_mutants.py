@@ -1,0 +1,59 @@
+"""Each planted mistake in a copy of the oracle must make at least one pin fail.
+
+The mistakes are the plausible ones: a wrong index or feature order, a dropped
+term, a wrong sign, a transposed operand, a wrong padding rule, a missing check.
+"""
+import os
+
+import pytest
+
+import pins
+from oracle import oracle as o
+
+SRC = open(os.path.join(os.path.dirname(o.__file__), "vlb_oracle.c")).read()
+
+MUTANTS = {
+    "feature order dx/dy swapped": (
+        "out[t * K1 + (int64_t)c * k * k + dy * k + dx] =",
+        "out[t * K1 + (int64_t)c * k * k + dx * k + dy] ="),
+    "position-major features in the row path": (
+        "out[(int64_t)c * k * k + dy * k + dx] = inside",
+        "out[(int64_t)(dy * k + dx) * C + c] = inside"),
+    "merged side rounds down": ("while (g_pad % k != 0) g_pad++;", "g_pad -= g_pad % k;"),
+    "padding at the low end": ("if (y >= gh || xx >= gw) return 0.0;\n  return x[(y * gw + xx) * C + c];",
+                               "int64_t oy = y - (k_pad_h), ox = xx;\n  (void)ox; if (oy < 0 || y >= gh + 0 || xx >= gw) return 0.0;\n  return x[(oy * gw + xx) * C + c];"),
+    "unbiased variance": ("var /= C;", "var /= (C - 1);"),
+    "eps outside the square root": ("1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    "gamma and beta swapped": ("* inv * gamma[c] + beta[c]", "* inv * beta[c] + gamma[c]"),
+    "bias dropped": ("j->out[r * j->out_dim + o] = acc + (j->b ? j->b[o] : 0.0);",
+                     "j->out[r * j->out_dim + o] = acc;"),
+    "weight transposed": ("acc += a[i] * w[i];",
+                          "acc += a[i] * j->W[(int64_t)i * j->out_dim + o]; (void)w;"),
+    "gelu sign": ("(1.0 + erf(x[i] / sqrt(2.0)))", "(1.0 - erf(x[i] / sqrt(2.0)))"),
+    "gelu scale": ("erf(x[i] / sqrt(2.0))", "erf(x[i] / 2.0)"),
+    "no local transpose": ("base + (1 + i * tw + j) * per_view + y * wp + x",
+                           "base + (1 + i * tw + j) * per_view + x * wp + y"),
+    "newline per local view": ("          n = emit(src, cap, n, base + (1 + i * tw + j) * per_view + y * wp + x);\n      n = emit(src, cap, n, ORC_SRC_NEWLINE);",
+                               "          n = emit(src, cap, n, base + (1 + i * tw + j) * per_view + y * wp + x);\n      n = emit(src, cap, n, ORC_SRC_NEWLINE); if (tw > 1) n = emit(src, cap, n, ORC_SRC_NEWLINE);"),
+    "separator before the global view": (
+        "      n = emit_global(src, cap, n, row, hp, wp);\n      n = emit(src, cap, n, ORC_SRC_SEPARATOR);",
+        "      n = emit(src, cap, n, ORC_SRC_SEPARATOR);\n      n = emit_global(src, cap, n, row, hp, wp);"),
+    "placeholder formula without local newlines": ("(th * hp) * (tw * wp + 1)", "(th * hp) * (tw * wp)"),
+    "scatter in reverse": ("const double *from = src[j] >= 0                  ? rows + src[j] * D",
+                           "j = P - 1 - j; const double *from = src[j] >= 0 ? rows + src[j] * D"),
+    "no count check": ("if (count != P) return -1;", "(void)count;"),
+    "param count without second bias": ("hidden * out_dim + out_dim;", "hidden * out_dim;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    text = SRC.replace(old, new)
+    if "k_pad_h" in new:
+        text = text.replace("static double padded_cell(", "static int k_pad_h = 1;\nstatic double padded_cell(")
+    so = o.build_variant(text, str(tmp_path), "mut")
+    with o.use_library(so):
+        bad = pins.failing(o)
+    assert bad, f"no pin catches: {name}"
