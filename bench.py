@@ -1,0 +1,252 @@
+"""Benchmark of the vision-to-language bridge on one MI355X.
+
+One step = one vlb_bridge_fused call over one batch: LayerNorm (when the
+workload has it), k x k space-to-depth gather fused into the first GEMM,
+Linear + bias + GELU, Linear + bias, and the scatter of every row into its
+placeholder slot (plus newline / separator rows for tiled images).  Inputs,
+the packed W1 and the workspace are resident in HBM before timing starts.
+
+Prints one JSON line.  value = visual tokens (projected rows) per second.
+roofline = the first GEMM (the dominant kernel): algorithmic FLOPs per launch
+over its mean duration from HIP events recorded around each launch on the
+stream it runs on.  cpu_baseline = the fp64 oracle on the host's cores over a
+bounded sample of the same workload's rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector / MFMA) dense
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "visual tokens/sec through merge+projector+scatter"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index (1 = MoonViT-style 2x2 bridge with LayerNorm)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the CPU-baseline sample")
+    ap.add_argument("--hbm-kernels", action="store_true",
+                    help="also time the standalone merge and scatter entry points")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    with open(os.path.join(ROOT, "patch_merge_mlp_amd", "csrc", "vlb_gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per GEMM1 launch from the committed counter summary, if it was taken
+    on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, _, val = line.partition(":")
+            vals[k.strip()] = val.strip()
+    if vals.get("kernel_source_sha") != kernel_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this bridge runs on one GPU; multi-GPU runs are not part of this build "
+              "(see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from patch_merge_mlp_amd import vlbridge as v
+    from patch_merge_mlp_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    w = wl.config(args.config)
+    gen = wl.Generator(w)
+    p = v.projector(v.F32 if w.dtype == "f32" else v.BF16, w.C, w.k, w.hidden, w.out_dim,
+                    has_ln=w.has_ln, ln_eps=w.ln_eps)
+    b = v.Batch(w.grids, w.views_per_image, v.LAYOUT_TILED_2D if w.tiled else v.LAYOUT_PLAIN,
+                w.tiles or None, w.global_tail)
+    T = v.vlb_num_tokens(p, b)
+    P = v.vlb_num_slots(p, b)
+    K1 = w.C * w.k * w.k
+    t = gen.tensors(sum(gh * gw for gh, gw in w.grids), K1, v.vlb_image_slots(p, b))
+    d = lambda x: None if x is None else x.to(dev)
+    weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
+                        d(t["ln_beta"]))
+    br = v.Bridge(p, weights)            # packs W1 once (weight preprocessing, untimed)
+    feats, mask = d(t["features"]), d(t["mask"])
+    nl, sep = d(t["newline"]), d(t["separator"])
+    seq = d(t["seq"])
+    ws = br.workspace(b, seq.shape[0])
+
+    def step():
+        v.vlb_bridge_fused(br.p, b, feats, br.w, nl, sep, mask, seq, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert v.vlb_check(ws) == v.OK
+
+    v.vlb_prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    v.vlb_prof_enable(False)
+    kernels = {}
+    for kid, name in enumerate(v.KERNEL_NAMES):
+        n, ms = v.vlb_prof_read(kid)
+        if n:
+            kernels[name] = {"launches": n, "mean_us": round(1000.0 * ms / n, 2)}
+
+    sec = (t1 - t0) / args.steps
+    flops1 = 2.0 * T * K1 * w.hidden
+    flops2 = 2.0 * T * w.hidden * w.out_dim
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    g1 = kernels["gemm1"]["mean_us"] * 1e-6
+    g2 = kernels["gemm2"]["mean_us"] * 1e-6
+    achieved = flops1 / g1 / 1e12
+    traffic = traffic_from_profiles(w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(T / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) features; random-init weights)",
+        "config": {
+            "workload": w.name, "images": w.n_images, "views": len(w.grids),
+            "grid": list(w.grids[0]), "C": w.C, "k": w.k, "hidden": w.hidden,
+            "out_dim": w.out_dim, "layernorm": w.has_ln, "seq_len": w.seq_len,
+            "visual_tokens": T, "placeholder_slots": P, "layout": "tiled_2d" if w.tiled else "plain",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "gemm1 (space-to-depth gather + Linear1 + bias + GELU)",
+            "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+        },
+        "gemm_tflops": {
+            "gemm1": round(achieved, 1),
+            "gemm2": round(flops2 / g2 / 1e12, 1),
+            "both": round((flops1 + flops2) / (g1 + g2) / 1e12, 1),
+            "step": round((flops1 + flops2) / sec / 1e12, 1),
+        },
+        "kernels": kernels,
+    }
+
+    if args.hbm_kernels:
+        out["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, t, T, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def hbm_kernels(v, torch, w, p, b, t, d, T, K1, steps):
+    """Standalone merge (materialised space-to-depth) and scatter, in GB/s of
+    algorithmic bytes (read + write once)."""
+    es = 2 if w.dtype == "bf16" else 4
+    pnl = v.projector(p.dtype, w.C, w.k, w.hidden, w.out_dim)  # merge without LayerNorm
+    merged = torch.empty(T, K1, dtype=w.torch_dtype, device="cuda")
+    ws = v.workspace(pnl, b, w.seq_len)
+    feats = d(t["features"])
+    rows = torch.randn(T, w.out_dim, device="cuda").to(w.torch_dtype)
+    seq = d(t["seq"])
+    mask = d(t["mask"])
+    nl, sep = d(t["newline"]), d(t["separator"])
+    for _ in range(2):
+        v.vlb_merge_tokens(pnl, b, feats, None, None, merged, ws)
+        v.vlb_scatter_tokens(pnl, b, rows, nl, sep, mask, seq, ws)
+    torch.cuda.synchronize()
+    v.vlb_prof_enable(True)
+    for _ in range(steps):
+        v.vlb_merge_tokens(pnl, b, feats, None, None, merged, ws)
+        v.vlb_scatter_tokens(pnl, b, rows, nl, sep, mask, seq, ws)
+    torch.cuda.synchronize()
+    v.vlb_prof_enable(False)
+    res = {}
+    npix = sum(gh * gw for gh, gw in w.grids)
+    nbytes = {
+        "merge": (npix * w.C + T * K1) * es,
+        "scatter": 2 * T * w.out_dim * es,
+    }
+    for kid, name in ((v.K_MERGE, "merge"), (v.K_SCATTER, "scatter")):
+        n, ms = v.vlb_prof_read(kid)
+        sec = ms / n / 1e3
+        gbs = nbytes[name] / sec / 1e9
+        res[name] = {"mean_us": round(sec * 1e6, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
+                     "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
+def cpu_baseline(w, t, T, target_s):
+    """The oracle (unchanged) on the host cores, over the first rows of the workload;
+    the rate is projected rows per second."""
+    from oracle import oracle as o
+    spec = o.Spec(grids=w.grids, C=w.C, k=w.k, hidden=w.hidden, out_dim=w.out_dim,
+                  views_per_image=w.views_per_image, has_ln=w.has_ln, ln_eps=w.ln_eps,
+                  tiled=w.tiled, tiles=w.tiles, global_tail=w.global_tail)
+    cores = min(os.cpu_count() or 1, 16)
+    args = [t["features"], t["ln_gamma"], t["ln_beta"], t["w1"], t["b1"], t["w2"], t["b2"]]
+    wide = [o._f64(a) for a in args]  # widening is input marshalling, outside the timed part
+    n = cores
+    while True:  # grow the sample until it takes about a second, then scale to the target
+        t0 = time.perf_counter()
+        o.project_rows(spec, *wide, row_ids=list(range(n)), nthreads=cores)
+        dt = time.perf_counter() - t0
+        if dt > 1.0 or n >= T:
+            break
+        n = min(T, n * 4)
+    n = int(min(T, max(n, n * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    o.project_rows(spec, *wide, row_ids=list(range(n)), nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {T} token rows of the same workload through the fp64 oracle "
+                      f"(LayerNorm, merge, Linear, GELU, Linear), {dt:.1f} s on {cores} threads"}
+
+
+if __name__ == "__main__":
+    main()

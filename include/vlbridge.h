@@ -1,0 +1,209 @@
+/*
+ * vlbridge.h -- C ABI of the vision-to-language bridge for AMD Instinct MI355X
+ * (gfx950): k x k space-to-depth merge of a ViT patch grid, two-Linear GELU
+ * projector, and scatter of the projected tokens into a text-embedding
+ * sequence at the image-placeholder positions.
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [VL2]  mlxcel issue #533, "feat(models): port DeepSeek-VL2" -- sections
+ *          "Projector (downsample_mlp_gelu)", "Tile-sequence assembly
+ *          (tile_tag 2D)", "Processor" step 7, "Weight loading and sanitize",
+ *          "Validation and acceptance criteria".
+ *   [V4V]  "DeepSeek-V4-Flash-Vision-BF16" model card, header paragraph
+ *          (2x2 PatchMerger, 4608 -> 4096).
+ *   [VOIE] "La voie visuelle" (DeepSeek-V4.1-Flash), sections "Le chemin d'une
+ *          image" and "Le pixel-unshuffle 3x3".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE memory owned by the caller unless marked (host).  The
+ *    library allocates nothing on the device and keeps no state between calls
+ *    (apart from the optional profiling records below); calls with distinct
+ *    workspaces may run concurrently on different streams.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Work is enqueued asynchronously on it.
+ *  - Every argument and shape is validated on the host before anything is
+ *    enqueued; on error nothing is launched and the status is returned.  No
+ *    HIP call is made before validation has passed.
+ *  - dtype: one type for features, LayerNorm parameters, weights, biases,
+ *    newline/separator vectors, projected rows and the sequence.  VLB_BF16
+ *    computes with fp32 accumulation and keeps the hidden activation in bf16;
+ *    VLB_F32 computes in fp32 throughout.
+ *  - Features: views stored back to back, each (grid_h, grid_w, C) row-major
+ *    channels-last ("(tiles, N, input_dim)" with the token axis unflattened
+ *    row-major, [VL2 Projector 1]).  Images own consecutive views; for the 2D
+ *    tile layout an image's views are [global, local tiles row-major].
+ *  - Token rows: the projected tokens of all views, concatenated in view order,
+ *    each view's tokens row-major over its merged grid [VL2 Projector, Output].
+ *  - Alignment: every device pointer must be 16-byte aligned.
+ *  - Supported shapes: k in {1, 2, 3}; C, hidden and out_dim multiples of 8
+ *    (VLB_BF16 additionally: C and hidden multiples of 64).
+ */
+#ifndef VLBRIDGE_H
+#define VLBRIDGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VLB_OK = 0,
+  VLB_ERR_NULL = 1,        /* a required pointer is NULL */
+  VLB_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  VLB_ERR_DTYPE = 3,       /* unknown dtype */
+  VLB_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  VLB_ERR_WORKSPACE = 5,   /* workspace smaller than vlb_workspace_bytes() */
+  VLB_ERR_MASK_COUNT = 6,  /* placeholder count != assembled slots (device-detected) */
+  VLB_ERR_UNSUPPORTED = 7, /* a valid but unsupported setting */
+  VLB_ERR_HIP = 8          /* a HIP runtime call failed */
+} vlb_status;
+
+typedef enum { VLB_F32 = 0, VLB_BF16 = 1 } vlb_dtype;
+
+/* Activation between the two Linears.  The projector of [VL2 Projector 3] is
+ * Linear -> GELU -> Linear; the exact (erf) GELU is the default, the tanh
+ * approximation and no activation are available as flags. */
+typedef enum { VLB_GELU_ERF = 0, VLB_GELU_TANH = 1, VLB_ACT_NONE = 2 } vlb_act;
+
+/* PLAIN: every image's token rows go to its placeholders in token order
+ * (MoonViT / DeepSeek-ViT style, [V4V], [VOIE]).  TILED_2D: the global view
+ * with one newline per token row, the separator, then the local views as one
+ * mosaic with one newline per mosaic row [VL2 Tile-sequence assembly]. */
+typedef enum { VLB_LAYOUT_PLAIN = 0, VLB_LAYOUT_TILED_2D = 1 } vlb_layout;
+
+/* The projector: LN(C) (optional, per patch, biased variance, eps inside the
+ * square root, affine) -> pad to a multiple of k -> k x k space-to-depth with
+ * feature index c*k*k + dy*k + dx [VL2 Projector 1-2] -> Linear(C*k*k ->
+ * hidden) -> act -> Linear(hidden -> out_dim) [VL2 Projector 3]. */
+typedef struct {
+  int32_t dtype;     /* vlb_dtype */
+  int32_t C;         /* channels of the patch grid */
+  int32_t k;         /* merge factor: 1, 2 or 3 */
+  int32_t hidden;    /* width of the first Linear's output */
+  int32_t out_dim;   /* width of the projected tokens (the text model's width) */
+  int32_t has_ln;    /* 1: LayerNorm over C before the merge */
+  float ln_eps;      /* LayerNorm epsilon */
+  int32_t act;       /* vlb_act */
+  int32_t w1_packed; /* 1: weights.w1 was produced by vlb_pack_weights (VLB_BF16 only) */
+} vlb_projector;
+
+/* Weights in PyTorch Linear layout (out_features, in_features), as stored and
+ * used as-is [VL2 Weight loading]. */
+typedef struct {
+  const void *ln_gamma, *ln_beta; /* [C] each, or NULL when has_ln == 0 */
+  const void *w1;                 /* [hidden][C*k*k]; or the packed form */
+  const void *b1;                 /* [hidden] */
+  const void *w2;                 /* [out_dim][hidden] */
+  const void *b2;                 /* [out_dim] */
+} vlb_weights;
+
+/* Batch description; all arrays are (host) memory read during the call only. */
+typedef struct {
+  int32_t n_views;                 /* >= 0; 0 = text only (the bridge is a no-op) */
+  const int32_t *grid_h, *grid_w;  /* (host) [n_views], each in [1, 32767] */
+  int32_t n_images;                /* images; their views sum to n_views */
+  const int32_t *views_per_image;  /* (host) [n_images] */
+  int32_t layout;                  /* vlb_layout */
+  const int32_t *tile_w, *tile_h;  /* (host) [n_images], TILED_2D only: the [tw, th]
+                                      tile grid, width count first [VL2 Processor 6];
+                                      each image then has 1 + tw*th views of one
+                                      common grid */
+  int32_t global_view_tail;        /* TILED_2D: 0 = [global, sep, local] ("head"),
+                                      1 = [local, sep, global] ("tail") */
+} vlb_batch;
+
+/* ---- sizing (host only, no HIP call) ---------------------------------- */
+
+/* Projected token rows T of the batch, or -(vlb_status) on invalid input. */
+int64_t vlb_num_tokens(const vlb_projector *p, const vlb_batch *b);
+/* Assembled placeholder slots P = T + newlines + separators [VL2 Processor 7],
+ * or -(vlb_status). */
+int64_t vlb_num_slots(const vlb_projector *p, const vlb_batch *b);
+/* Slots of each image, written to (host) out[n_images]; returns the total P or
+ * -(vlb_status). */
+int64_t vlb_image_slots(const vlb_projector *p, const vlb_batch *b, int64_t *out);
+/* Device workspace bytes needed by any entry point below for this batch and a
+ * sequence of seq_len rows (0 when only vlb_merge_project is used); 0 on
+ * invalid input. */
+size_t vlb_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t seq_len);
+
+/* ---- entry points (asynchronous on stream) ---------------------------- */
+
+/* One-time re-layout of W1 [hidden][C*k*k] (feature index c*k*k + p) into the
+ * packed form [hidden][k*k*C] (index p*C + c) that lets the first GEMM read
+ * each patch's channels contiguously.  Only the summation order of the first
+ * Linear changes.  w1_packed must not alias w1.  VLB_BF16 only. */
+vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, void *w1_packed,
+                            void *stream);
+
+/* LN (if enabled) -> pad -> space-to-depth, materialised: merged[T][C*k*k] in
+ * the pages' feature order c*k*k + dy*k + dx [VL2 Projector 1-2], [VOIE
+ * pixel-unshuffle].  ws: workspace of vlb_workspace_bytes(p, b, 0) bytes (used
+ * only when has_ln). */
+vlb_status vlb_merge_tokens(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const void *ln_gamma, const void *ln_beta, void *merged, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* The projector: rows[T][out_dim] = Linear2(act(Linear1(merge(LN(features)))))
+ * [VL2 Projector 1-3]. */
+vlb_status vlb_merge_project(const vlb_projector *p, const vlb_batch *b, const void *features,
+                             const vlb_weights *w, void *rows, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Assembly and scatter [VL2 Tile-sequence assembly]: the assembled rows (token
+ * rows, plus newline/separator for TILED_2D) overwrite seq[seq_len][out_dim]
+ * in place at the positions where mask[seq_len] (uint8) is nonzero, in order;
+ * all other rows of seq are untouched.  newline/separator: [out_dim] each
+ * (TILED_2D; may be NULL for PLAIN).  If the number of nonzero mask entries
+ * differs from P [VL2 Validation], the device writes nothing to seq and
+ * records VLB_ERR_MASK_COUNT, which vlb_check returns.  T == 0 is a no-op. */
+vlb_status vlb_scatter_tokens(const vlb_projector *p, const vlb_batch *b, const void *rows,
+                              const void *newline, const void *separator, const uint8_t *mask,
+                              int64_t seq_len, void *seq, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* vlb_merge_project followed by vlb_scatter_tokens without materialising the
+ * projected rows: the second GEMM writes each row straight to its placeholder
+ * slot.  Same arguments and error behaviour as the two calls. */
+vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const vlb_weights *w, const void *newline, const void *separator,
+                            const uint8_t *mask, int64_t seq_len, void *seq, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Waits for stream and returns the status recorded on the device by the last
+ * vlb_scatter_tokens / vlb_bridge_fused that used this workspace (VLB_OK or
+ * VLB_ERR_MASK_COUNT), or VLB_ERR_HIP. */
+vlb_status vlb_check(void *ws, void *stream);
+
+const char *vlb_status_str(vlb_status s);
+
+/* ---- optional per-kernel timing ---------------------------------------- */
+
+/* Kernel ids for the timing records. */
+enum {
+  VLB_K_PLAN = 0,    /* per-token gather descriptors */
+  VLB_K_SCAN = 1,    /* mask prefix sum -> slot positions */
+  VLB_K_PLACE = 2,   /* assembly map, newline/separator rows */
+  VLB_K_LN = 3,      /* LayerNorm */
+  VLB_K_GEMM1 = 4,   /* merge-gather + Linear1 + bias + activation */
+  VLB_K_GEMM2 = 5,   /* Linear2 + bias + row/slot store */
+  VLB_K_SCATTER = 6, /* standalone row scatter */
+  VLB_K_MERGE = 7,   /* standalone space-to-depth */
+  VLB_K_PACK = 8,    /* W1 re-layout */
+  VLB_K_COUNT = 9
+};
+
+/* While enabled, every launch is bracketed by HIP events recorded on its
+ * stream.  vlb_prof_enable(1) clears earlier records. */
+vlb_status vlb_prof_enable(int32_t on);
+/* Waits for the recorded events and returns, for kernel id kid, the number of
+ * launches and their summed duration in milliseconds. */
+vlb_status vlb_prof_read(int32_t kid, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VLBRIDGE_H */

@@ -1,0 +1,433 @@
+// Data-movement kernels of the bridge: gather descriptors, the placeholder
+// prefix sum, the assembly map (with newline / separator rows), LayerNorm,
+// the standalone row scatter and space-to-depth, and the W1 re-layout.
+//
+// Operations follow mlxcel issue #533 "port DeepSeek-VL2": section
+// "Projector (downsample_mlp_gelu)" steps 1-2 (pad, space-to-depth) and
+// section "Tile-sequence assembly" (newline / separator layout and the in-order
+// overwrite of the placeholder positions).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vlb_common.h"
+#include "vlb_internal.h"
+
+namespace vlb {
+
+namespace {
+
+constexpr int kErrMaskCount = 6;  // VLB_ERR_MASK_COUNT
+
+// ---------------------------------------------------------------------------
+// Gather descriptor of every token row of a chunk of views.
+__global__ void k_plan(PlanChunk c, RowDesc *desc) {
+  const int32_t r = c.tok0[0] + blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= c.tok0[c.n]) return;
+  int lo = 0, hi = c.n - 1;
+  while (lo < hi) {  // last view whose first token is <= r
+    const int mid = (lo + hi + 1) >> 1;
+    if (c.tok0[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int v = lo, k = c.k;
+  const int gh = c.gh[v], gw = c.gw[v];
+  const int wp = (gw + k - 1) / k;
+  const int t = r - c.tok0[v];
+  const int y0 = (t / wp) * k, x0 = (t % wp) * k;
+  uint32_t inside = 0;
+  for (int dy = 0; dy < k; ++dy)
+    for (int dx = 0; dx < k; ++dx)
+      if (y0 + dy < gh && x0 + dx < gw) inside |= 1u << (dy * k + dx);
+  desc[r].pix = c.pix0[v] + y0 * gw + x0;
+  desc[r].geo = gw | static_cast<int32_t>(inside << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Placeholder prefix sum: slot_pos[j] = position of the j-th nonzero mask byte.
+// One workgroup streams the mask in chunks of 16 KiB with a running carry.
+// status[kCountWord] = number of placeholders; status[kStatusWord] = 0 when it
+// equals P, else VLB_ERR_MASK_COUNT.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t *mask, int64_t S, int64_t P,
+                                                      int32_t *slot_pos, int32_t *status) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int32_t carry = 0;
+  for (int64_t base = 0; base < S; base += kScanThreads * 16) {
+    const int64_t off = base + static_cast<int64_t>(tid) * 16;
+    uint8_t b[16];
+    if (off + 16 <= S) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(mask + off);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) b[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xff;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) b[i] = (off + i < S) ? mask[off + i] : 0;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cnt += b[i] != 0;
+    int x = cnt;  // inclusive scan inside the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+      int w = lane < kScanThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kScanThreads / 64; d <<= 1) {
+        const int y = __shfl_up(w, d, 64);
+        if (lane >= d) w += y;
+      }
+      if (lane < kScanThreads / 64) wsum[lane] = w;
+    }
+    __syncthreads();
+    int32_t pos = carry + (x - cnt) + (wid > 0 ? wsum[wid - 1] : 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (b[i]) slot_pos[pos++] = static_cast<int32_t>(off + i);
+    carry += wsum[kScanThreads / 64 - 1];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    status[kCountWord] = carry;
+    status[kStatusWord] = (carry == P) ? 0 : kErrMaskCount;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Plain layout: token row r goes to the r-th placeholder.
+__global__ void k_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
+                              int32_t *dst_row) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= T) return;
+  dst_row[r] = status[kStatusWord] == 0 ? slot_pos[r] : -1;
+}
+
+// 2D tile layout: decode what every assembled slot holds -- a token row, the
+// newline or the separator -- by inverting the assembly order of one image:
+//   global view: h' rows of (w' tokens, newline)
+//   separator
+//   local mosaic: th*h' rows of (tw*w' tokens, newline), mosaic row R and
+//                 column X taken from tile (R / h')*tw + X / w', token
+//                 (R % h')*w' + X % w'
+// ("tail" puts the mosaic first).  One wave per slot; token slots record the
+// destination row, newline / separator slots are copied by the whole wave.
+template <typename T>
+__global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32_t *status,
+                              int32_t *dst_row, const T *newline, const T *separator, T *seq,
+                              int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  const bool ok = status[kStatusWord] == 0;
+  const int end = c.slot0[c.n];
+  for (int64_t jj = c.slot0[0] + wave; jj < end; jj += nwaves) {
+    const int j = static_cast<int>(jj);
+    int lo = 0, hi = c.n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (c.slot0[mid] <= j) lo = mid;
+      else hi = mid - 1;
+    }
+    const int im = lo;
+    const int hp = c.hp[im], wp = c.wp[im], tw = c.tw[im], th = c.th[im];
+    const int G = hp * (wp + 1);             // global block
+    const int L = th * hp * (tw * wp + 1);   // local mosaic block
+    int q = j - c.slot0[im];
+    int row = -1;                            // token row, or -1 newline, -2 separator
+    bool global;
+    if (!c.tail) {
+      global = q < G;
+      if (q == G) row = -2;
+      else if (!global) q -= G + 1;
+    } else {
+      global = q > L;
+      if (q == L) row = -2;
+      else if (global) q -= L + 1;
+    }
+    if (row != -2) {
+      if (global) {
+        const int R = q / (wp + 1), X = q % (wp + 1);
+        row = (X == wp) ? -1 : c.row0[im] + R * wp + X;
+      } else {
+        const int W = tw * wp + 1;
+        const int R = q / W, X = q % W;
+        if (X == tw * wp) {
+          row = -1;
+        } else {
+          const int tile = (R / hp) * tw + X / wp;
+          row = c.row0[im] + (1 + tile) * hp * wp + (R % hp) * wp + (X % wp);
+        }
+      }
+    }
+    if (row >= 0) {
+      if (lane == 0) dst_row[row] = ok ? slot_pos[j] : -1;
+    } else if (ok) {
+      const uint4 *from = reinterpret_cast<const uint4 *>(row == -1 ? newline : separator);
+      uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(slot_pos[j]) * D);
+      const int n16 = D * static_cast<int>(sizeof(T)) / 16;
+      for (int i = lane; i < n16; i += 64) to[i] = from[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm over C per pixel, one wave per pixel: mean, biased variance, eps
+// inside the square root, affine.  Values stay in registers (up to
+// kLnChunks 16-byte chunks per lane).
+constexpr int kLnChunks = 8;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int C, const T *gamma,
+                                                   const T *beta, float eps, T *out) {
+  constexpr int E = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  const int nch = C / E;
+  for (int64_t px = wave; px < npix; px += nwaves) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + px * C);
+    uint4 v[kLnChunks];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLnChunks; ++i) {
+      const int q = lane + 64 * i;
+      if (q < nch) {
+        v[i] = src[q];
+        const T *e = reinterpret_cast<const T *>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < E; ++j) s += Elem<T>::load(e[j]);
+      }
+    }
+    const float mean = wave_sum(s) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLnChunks; ++i) {
+      const int q = lane + 64 * i;
+      if (q < nch) {
+        const T *e = reinterpret_cast<const T *>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const float d = Elem<T>::load(e[j]) - mean;
+          ss += d * d;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+    uint4 *dst = reinterpret_cast<uint4 *>(out + px * C);
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(gamma);
+    const uint4 *b4 = reinterpret_cast<const uint4 *>(beta);
+#pragma unroll
+    for (int i = 0; i < kLnChunks; ++i) {
+      const int q = lane + 64 * i;
+      if (q < nch) {
+        const uint4 gv = g4[q], bv = b4[q];
+        const T *e = reinterpret_cast<const T *>(&v[i]);
+        const T *ge = reinterpret_cast<const T *>(&gv);
+        const T *be = reinterpret_cast<const T *>(&bv);
+        uint4 o;
+        T *oe = reinterpret_cast<T *>(&o);
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+          oe[j] = Elem<T>::store((Elem<T>::load(e[j]) - mean) * rstd * Elem<T>::load(ge[j]) +
+                                 Elem<T>::load(be[j]));
+        dst[q] = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone scatter: row r of rows[T][D] -> seq[dst_row[r]] (skipped if < 0).
+template <typename T>
+__global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, int D,
+                                                 const int32_t *dst_row, T *seq) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  const int n16 = D * static_cast<int>(sizeof(T)) / 16;
+  for (int64_t r = wave; r < Trows; r += nwaves) {
+    const int32_t d = dst_row[r];
+    if (d < 0) continue;
+    const uint4 *from = reinterpret_cast<const uint4 *>(rows + r * D);
+    uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(d) * D);
+    int i = lane;
+    for (; i + 192 < n16; i += 256) {
+      const uint4 a = from[i], b = from[i + 64], cc = from[i + 128], e = from[i + 192];
+      to[i] = a;
+      to[i + 64] = b;
+      to[i + 128] = cc;
+      to[i + 192] = e;
+    }
+    for (; i < n16; i += 64) to[i] = from[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone space-to-depth in the pages' feature order c*k*k + dy*k + dx: one
+// workgroup per token stages the token's k*k pixels ([p][C], zeros for padded
+// cells) in LDS, then writes the interleaved row with 16-byte stores.
+constexpr int kMergeThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kMergeThreads) void k_merge(const T *x, const RowDesc *desc,
+                                                         int64_t Trows, int C, int k, T *merged) {
+  extern __shared__ uint4 merge_lds[];
+  T *tile = reinterpret_cast<T *>(merge_lds);
+  constexpr int E = 16 / sizeof(T);
+  const int kk = k * k;
+  const int nrow = C / E;           // 16-byte chunks per pixel
+  const int K1 = C * kk;
+  for (int64_t r = blockIdx.x; r < Trows; r += gridDim.x) {
+    const RowDesc d = desc[r];
+    const int gw = d.geo & 0xffff;
+    const uint32_t inside = static_cast<uint32_t>(d.geo) >> 16;
+    for (int q = threadIdx.x; q < kk * nrow; q += kMergeThreads) {
+      const int p = q / nrow, cq = q - p * nrow;
+      const int dy = p / k, dx = p - dy * k;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if ((inside >> p) & 1)
+        v = reinterpret_cast<const uint4 *>(
+            x + static_cast<int64_t>(d.pix + dy * gw + dx) * C)[cq];
+      merge_lds[q] = v;
+    }
+    __syncthreads();
+    uint4 *dst = reinterpret_cast<uint4 *>(merged + r * K1);
+    for (int q = threadIdx.x; q < K1 / E; q += kMergeThreads) {
+      uint4 o;
+      T *oe = reinterpret_cast<T *>(&o);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int e = q * E + j;
+        const int c = e / kk, p = e - c * kk;
+        oe[j] = tile[p * C + c];
+      }
+      dst[q] = o;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// W1 re-layout: w1p[n][p*C + c] = w1[n][c*k*k + p].
+__global__ void k_pack(const uint16_t *w1, int64_t hidden, int C, int k, uint16_t *w1p) {
+  const int kk = k * k;
+  const int64_t K1 = static_cast<int64_t>(C) * kk;
+  const int64_t total = hidden * K1;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t n = e / K1, j = e - n * K1;
+    const int64_t p = j / C, c = j - p * C;
+    w1p[e] = w1[n * K1 + c * kk + p];
+  }
+}
+
+int grid_for(int64_t waves_or_items, int per_block, int cap) {
+  int64_t g = (waves_or_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s) {
+  const int64_t n = c.tok0[c.n] - c.tok0[0];
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_plan, dim3(grid_for(n, 256, 1 << 30)), dim3(256), 0, s, c, desc);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
+                       int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, mask, S, P, slot_pos, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
+                              int32_t *dst_row, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_place_plain, dim3(grid_for(T, 256, 1 << 30)), dim3(256), 0, s, T,
+                     slot_pos, status, dst_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
+                              const int32_t *status, int32_t *dst_row, const void *newline,
+                              const void *separator, void *seq, int D, hipStream_t s) {
+  const int64_t n = c.slot0[c.n] - c.slot0[0];
+  if (n <= 0) return hipSuccess;
+  const int grid = grid_for(n, 4, 4096);  // 4 waves per block, one slot per wave per pass
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_place_tiled<float>, dim3(grid), dim3(256), 0, s, c, slot_pos, status,
+                       dst_row, static_cast<const float *>(newline),
+                       static_cast<const float *>(separator), static_cast<float *>(seq), D);
+  else
+    hipLaunchKernelGGL(k_place_tiled<uint16_t>, dim3(grid), dim3(256), 0, s, c, slot_pos, status,
+                       dst_row, static_cast<const uint16_t *>(newline),
+                       static_cast<const uint16_t *>(separator), static_cast<uint16_t *>(seq), D);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const void *gamma,
+                            const void *beta, float eps, void *out, hipStream_t s) {
+  if (npix <= 0) return hipSuccess;
+  const int grid = grid_for(npix, 4, 8192);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_layernorm<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float *>(x), npix, C, static_cast<const float *>(gamma),
+                       static_cast<const float *>(beta), eps, static_cast<float *>(out));
+  else
+    hipLaunchKernelGGL(k_layernorm<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(x), npix, C,
+                       static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
+                       eps, static_cast<uint16_t *>(out));
+  return hipGetLastError();
+}
+
+int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 : 8); }
+
+hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const int32_t *dst_row,
+                          void *seq, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int grid = grid_for(T, 4, 8192);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_scatter<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float *>(rows), T, D, dst_row, static_cast<float *>(seq));
+  else
+    hipLaunchKernelGGL(k_scatter<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(rows), T, D, dst_row,
+                       static_cast<uint16_t *>(seq));
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                        void *merged, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const size_t lds = static_cast<size_t>(C) * k * k * (dtype == 0 ? 4 : 2);
+  const int grid = grid_for(T, 1, 1 << 20);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_merge<float>, dim3(grid), dim3(kMergeThreads), lds, s,
+                       static_cast<const float *>(x), desc, T, C, k, static_cast<float *>(merged));
+  else
+    hipLaunchKernelGGL(k_merge<uint16_t>, dim3(grid), dim3(kMergeThreads), lds, s,
+                       static_cast<const uint16_t *>(x), desc, T, C, k,
+                       static_cast<uint16_t *>(merged));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const void *w1, int64_t hidden, int C, int k, void *w1p, hipStream_t s) {
+  const int64_t total = hidden * C * k * k;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack, dim3(grid_for(total, 256, 65536)), dim3(256), 0, s,
+                     static_cast<const uint16_t *>(w1), hidden, C, k, static_cast<uint16_t *>(w1p));
+  return hipGetLastError();
+}
+
+}  // namespace vlb

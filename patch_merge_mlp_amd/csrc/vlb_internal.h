@@ -1,0 +1,87 @@
+// Internal declarations shared by the host planner (vlb_api.hip) and the HIP
+// kernels (vlb_data.hip, vlb_gemm.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vlb {
+
+// ---- per-token gather descriptor ------------------------------------------
+// pix: index (in pixels, over all views) of the top-left pixel of the token's
+//      k x k block.
+// geo: bits 0..15  the view's grid width (pixel stride of one grid row);
+//      bits 16..24 bit (dy*k + dx) set when that block position lies inside the
+//                  grid (clear = high-end zero padding).
+// A token row past the end of the batch is never read.
+struct RowDesc {
+  int32_t pix;
+  int32_t geo;
+};
+
+// Views handled by one launch of the descriptor kernel (kernel-argument table).
+constexpr int kPlanViews = 64;
+struct PlanChunk {
+  int32_t n;                     // views in this chunk
+  int32_t k;                     // merge factor
+  int32_t tok0[kPlanViews + 1];  // first token row of each view; tok0[n] = end
+  int32_t pix0[kPlanViews];      // first pixel of each view
+  int16_t gh[kPlanViews], gw[kPlanViews];
+};
+
+// Tiled images handled by one launch of the placement kernel.
+constexpr int kPlaceImages = 64;
+struct PlaceChunk {
+  int32_t n;                        // images in this chunk
+  int32_t tail;                     // 1: [local, separator, global]
+  int32_t slot0[kPlaceImages + 1];  // first assembled slot of each image; slot0[n] = end
+  int32_t row0[kPlaceImages];       // first token row of each image (its global view)
+  int16_t hp[kPlaceImages], wp[kPlaceImages];  // merged grid of every view of the image
+  int16_t tw[kPlaceImages], th[kPlaceImages];  // local tile grid, width count first
+};
+
+// Status words at the start of the workspace.
+enum { kStatusWord = 0, kCountWord = 1 };
+
+// ---- GEMM arguments -------------------------------------------------------
+// out[dst(m)][n] = act(sum_k A[m][k] * B[n][k] + bias[n]) for m < M, n < N.
+// A is either row-major [M][K] (lda = K) or gathered through RowDesc from the
+// channels-last patch grid with K ordered position-major (k' = p*C + c).
+struct GemmArgs {
+  const void *A;          // activations, or the (normalised) patch grid
+  const RowDesc *desc;    // gather descriptors (gather mode only)
+  const void *B;          // [N][K] row-major
+  const void *bias;       // [N]
+  void *out;              // output rows
+  const int32_t *dst_row; // nullptr: row m -> out + m*ldo; else dst_row[m] (< 0: skipped)
+  int32_t M, N, K, ldo;
+  int32_t C, k;           // gather mode: channels and merge factor
+  int32_t act;            // vlb_act
+  int32_t tiles_m, tiles_n;
+};
+
+// ---- launchers (return the launch error, hipSuccess otherwise) ------------
+hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
+hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
+                       int32_t *status, hipStream_t s);
+hipError_t launch_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
+                              int32_t *dst_row, hipStream_t s);
+hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
+                              const int32_t *status, int32_t *dst_row, const void *newline,
+                              const void *separator, void *seq, int D, hipStream_t s);
+// Largest C the LayerNorm kernel keeps in registers.
+int layernorm_max_channels(int dtype);
+hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const void *gamma,
+                            const void *beta, float eps, void *out, hipStream_t s);
+hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const int32_t *dst_row,
+                          void *seq, hipStream_t s);
+hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                        void *merged, hipStream_t s);
+hipError_t launch_pack(const void *w1, int64_t hidden, int C, int k, void *w1p, hipStream_t s);
+
+// bf16 MFMA GEMMs.  gemm1: gather-mode A, B = packed W1.  gemm2: row-major A.
+hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s);
+// fp32 GEMMs (FMA).  In gather mode K follows the pages' order c*k*k + p and B
+// is the unpacked W1.
+hipError_t launch_gemm_f32(bool gather, GemmArgs g, hipStream_t s);
+
+}  // namespace vlb

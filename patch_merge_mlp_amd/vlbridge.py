@@ -1,0 +1,337 @@
+"""Python binding of the vlbridge C ABI (include/vlbridge.h).
+
+Argument marshalling only: every step of the bridge runs in the HIP kernels of
+libvlbridge.so.  Tensors supply device pointers, torch's current stream
+supplies the HIP stream.  The functions keep the C names; each raises VlbError
+(with .status) when the library returns an error.  Sizes of the tensors handed
+in are checked here against what the library will read or write.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvlbridge.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
+    ERR_UNSUPPORTED, ERR_HIP = range(9)
+F32, BF16 = 0, 1
+GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
+LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
+K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK = range(9)
+KERNEL_NAMES = ["plan", "scan", "place", "layernorm", "gemm1", "gemm2", "scatter", "merge", "pack"]
+
+
+class VlbError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class vlb_projector(ct.Structure):
+    _fields_ = [("dtype", ct.c_int32), ("C", ct.c_int32), ("k", ct.c_int32),
+                ("hidden", ct.c_int32), ("out_dim", ct.c_int32), ("has_ln", ct.c_int32),
+                ("ln_eps", ct.c_float), ("act", ct.c_int32), ("w1_packed", ct.c_int32)]
+
+
+class vlb_weights(ct.Structure):
+    _fields_ = [("ln_gamma", ct.c_void_p), ("ln_beta", ct.c_void_p), ("w1", ct.c_void_p),
+                ("b1", ct.c_void_p), ("w2", ct.c_void_p), ("b2", ct.c_void_p)]
+
+
+_P32 = ct.POINTER(ct.c_int32)
+
+
+class vlb_batch(ct.Structure):
+    _fields_ = [("n_views", ct.c_int32), ("grid_h", _P32), ("grid_w", _P32),
+                ("n_images", ct.c_int32), ("views_per_image", _P32), ("layout", ct.c_int32),
+                ("tile_w", _P32), ("tile_h", _P32), ("global_view_tail", ct.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"vlbridge HIP library missing at {LIB_PATH}: build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ct.CDLL(LIB_PATH)
+        pp, pb, vp, i64, sz = (ct.POINTER(vlb_projector), ct.POINTER(vlb_batch), ct.c_void_p,
+                               ct.c_int64, ct.c_size_t)
+        st = ct.c_int
+        sigs = {
+            "vlb_num_tokens": (i64, [pp, pb]),
+            "vlb_num_slots": (i64, [pp, pb]),
+            "vlb_image_slots": (i64, [pp, pb, ct.POINTER(ct.c_int64)]),
+            "vlb_workspace_bytes": (sz, [pp, pb, i64]),
+            "vlb_pack_weights": (st, [pp, vp, vp, vp]),
+            "vlb_merge_tokens": (st, [pp, pb, vp, vp, vp, vp, vp, sz, vp]),
+            "vlb_merge_project": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, sz, vp]),
+            "vlb_scatter_tokens": (st, [pp, pb, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
+            "vlb_bridge_fused": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, i64, vp,
+                                      vp, sz, vp]),
+            "vlb_check": (st, [vp, vp]),
+            "vlb_status_str": (ct.c_char_p, [st]),
+            "vlb_prof_enable": (st, [ct.c_int32]),
+            "vlb_prof_read": (st, [ct.c_int32, ct.POINTER(ct.c_int64), ct.POINTER(ct.c_double)]),
+        }
+        for name, (res, args) in sigs.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().vlb_status_str(s).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise VlbError(status, where)
+
+
+def projector(dtype: int, C: int, k: int, hidden: int, out_dim: int, has_ln: bool = False,
+              ln_eps: float = 1e-6, act: int = GELU_ERF, w1_packed: bool = False) -> vlb_projector:
+    return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(w1_packed))
+
+
+class Batch:
+    """Host-side batch description (keeps its int32 arrays alive for the C struct)."""
+
+    def __init__(self, grids: Sequence[tuple], views_per_image: Sequence[int],
+                 layout: int = LAYOUT_PLAIN, tiles: Optional[Sequence[tuple]] = None,
+                 global_view_tail: bool = False):
+        self.grids = [tuple(g) for g in grids]
+        self.views_per_image = list(views_per_image)
+        self.layout = layout
+        self.tiles = list(tiles or [])
+        arr = lambda xs: (ct.c_int32 * max(len(xs), 1))(*xs)
+        self._gh = arr([g[0] for g in self.grids])
+        self._gw = arr([g[1] for g in self.grids])
+        self._vpi = arr(self.views_per_image)
+        self._tw = arr([t[0] for t in self.tiles])
+        self._th = arr([t[1] for t in self.tiles])
+        self.c = vlb_batch(len(self.grids), self._gh, self._gw, len(self.views_per_image),
+                           self._vpi, layout, self._tw, self._th, int(global_view_tail))
+
+
+@dataclass
+class Weights:
+    w1: torch.Tensor
+    b1: torch.Tensor
+    w2: torch.Tensor
+    b2: torch.Tensor
+    ln_gamma: Optional[torch.Tensor] = None
+    ln_beta: Optional[torch.Tensor] = None
+
+    def c(self) -> vlb_weights:
+        return vlb_weights(_ptr(self.ln_gamma), _ptr(self.ln_beta), _ptr(self.w1), _ptr(self.b1),
+                           _ptr(self.w2), _ptr(self.b2))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("vlbridge takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("vlbridge takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _tdtype(p: vlb_projector):
+    return torch.float32 if p.dtype == F32 else torch.bfloat16
+
+
+def _need(t: Optional[torch.Tensor], n: int, dtype, what: str):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() < n:
+        raise ValueError(f"{what}: {t.numel()} elements, need {n}")
+
+
+def _pixels(b: Batch) -> int:
+    return sum(gh * gw for gh, gw in b.grids)
+
+
+# ---- sizing ------------------------------------------------------------------
+
+def vlb_num_tokens(p: vlb_projector, b: Batch) -> int:
+    n = lib().vlb_num_tokens(ct.byref(p), ct.byref(b.c))
+    if n < 0:
+        raise VlbError(-n, "vlb_num_tokens")
+    return n
+
+
+def vlb_num_slots(p: vlb_projector, b: Batch) -> int:
+    n = lib().vlb_num_slots(ct.byref(p), ct.byref(b.c))
+    if n < 0:
+        raise VlbError(-n, "vlb_num_slots")
+    return n
+
+
+def vlb_image_slots(p: vlb_projector, b: Batch) -> list:
+    out = (ct.c_int64 * max(len(b.views_per_image), 1))()
+    n = lib().vlb_image_slots(ct.byref(p), ct.byref(b.c), out)
+    if n < 0:
+        raise VlbError(-n, "vlb_image_slots")
+    return [int(out[i]) for i in range(len(b.views_per_image))]
+
+
+def vlb_workspace_bytes(p: vlb_projector, b: Batch, seq_len: int) -> int:
+    return int(lib().vlb_workspace_bytes(ct.byref(p), ct.byref(b.c), seq_len))
+
+
+def workspace(p: vlb_projector, b: Batch, seq_len: int, device="cuda") -> torch.Tensor:
+    n = vlb_workspace_bytes(p, b, seq_len)
+    if n == 0:
+        raise VlbError(ERR_SHAPE, "vlb_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---- entry points -----------------------------------------------------------
+
+def vlb_pack_weights(p: vlb_projector, w1: torch.Tensor, w1_packed: torch.Tensor, stream=None):
+    n = p.hidden * p.C * p.k * p.k
+    _need(w1, n, _tdtype(p), "w1")
+    _need(w1_packed, n, _tdtype(p), "w1_packed")
+    _check(lib().vlb_pack_weights(ct.byref(p), _ptr(w1), _ptr(w1_packed), _stream(stream)),
+           "vlb_pack_weights")
+
+
+def _check_weights(p, w: Weights):
+    dt = _tdtype(p)
+    _need(w.w1, p.hidden * p.C * p.k * p.k, dt, "w1")
+    _need(w.b1, p.hidden, dt, "b1")
+    _need(w.w2, p.out_dim * p.hidden, dt, "w2")
+    _need(w.b2, p.out_dim, dt, "b2")
+    _need(w.ln_gamma, p.C, dt, "ln_gamma")
+    _need(w.ln_beta, p.C, dt, "ln_beta")
+
+
+def vlb_merge_tokens(p, b: Batch, features, ln_gamma, ln_beta, merged, ws, stream=None):
+    dt = _tdtype(p)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _need(merged, vlb_num_tokens(p, b) * p.C * p.k * p.k, dt, "merged")
+    _need(ln_gamma, p.C, dt, "ln_gamma")
+    _need(ln_beta, p.C, dt, "ln_beta")
+    _check(lib().vlb_merge_tokens(ct.byref(p), ct.byref(b.c), _ptr(features), _ptr(ln_gamma),
+                                  _ptr(ln_beta), _ptr(merged), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "vlb_merge_tokens")
+
+
+def vlb_merge_project(p, b: Batch, features, w: Weights, rows, ws, stream=None):
+    dt = _tdtype(p)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _check_weights(p, w)
+    _need(rows, vlb_num_tokens(p, b) * p.out_dim, dt, "rows")
+    wc = w.c()
+    _check(lib().vlb_merge_project(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                   _ptr(rows), _ptr(ws), ws.numel(), _stream(stream)),
+           "vlb_merge_project")
+
+
+def _check_seq(p, mask, seq):
+    if mask.dtype != torch.uint8:
+        raise ValueError("mask must be uint8")
+    if seq.dim() != 2 or seq.shape[1] != p.out_dim or mask.numel() != seq.shape[0]:
+        raise ValueError("seq must be [seq_len, out_dim] and mask [seq_len]")
+    if seq.dtype != _tdtype(p):
+        raise ValueError(f"seq dtype {seq.dtype}")
+
+
+def vlb_scatter_tokens(p, b: Batch, rows, newline, separator, mask, seq, ws, stream=None):
+    dt = _tdtype(p)
+    _check_seq(p, mask, seq)
+    _need(rows, vlb_num_tokens(p, b) * p.out_dim, dt, "rows")
+    _need(newline, p.out_dim, dt, "newline")
+    _need(separator, p.out_dim, dt, "separator")
+    _check(lib().vlb_scatter_tokens(ct.byref(p), ct.byref(b.c), _ptr(rows), _ptr(newline),
+                                    _ptr(separator), _ptr(mask), seq.shape[0], _ptr(seq),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "vlb_scatter_tokens")
+
+
+def vlb_bridge_fused(p, b: Batch, features, w: Weights, newline, separator, mask, seq, ws,
+                     stream=None):
+    dt = _tdtype(p)
+    _check_seq(p, mask, seq)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _check_weights(p, w)
+    _need(newline, p.out_dim, dt, "newline")
+    _need(separator, p.out_dim, dt, "separator")
+    wc = w.c()
+    _check(lib().vlb_bridge_fused(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                  _ptr(newline), _ptr(separator), _ptr(mask), seq.shape[0],
+                                  _ptr(seq), _ptr(ws), ws.numel(), _stream(stream)),
+           "vlb_bridge_fused")
+
+
+def vlb_check(ws, stream=None) -> int:
+    """Device-recorded status of the last scatter / fused call on this workspace."""
+    return int(lib().vlb_check(_ptr(ws), _stream(stream)))
+
+
+def vlb_prof_enable(on: bool):
+    _check(lib().vlb_prof_enable(int(on)), "vlb_prof_enable")
+
+
+def vlb_prof_read(kid: int):
+    n = ct.c_int64(0)
+    ms = ct.c_double(0.0)
+    _check(lib().vlb_prof_read(kid, ct.byref(n), ct.byref(ms)), "vlb_prof_read")
+    return int(n.value), float(ms.value)
+
+
+class Bridge:
+    """A projector with its weights resident on the device (W1 packed once for bf16),
+    plus a cached workspace."""
+
+    def __init__(self, p: vlb_projector, w: Weights, pack: bool = True):
+        self.w = w
+        if p.dtype == BF16 and pack and not p.w1_packed:
+            w1p = torch.empty_like(w.w1)
+            vlb_pack_weights(p, w.w1, w1p)
+            self.w = Weights(w1p, w.b1, w.w2, w.b2, w.ln_gamma, w.ln_beta)
+            p = vlb_projector.from_buffer_copy(p)
+            p.w1_packed = 1
+        self.p = p
+        self._ws = None
+
+    def workspace(self, b: Batch, seq_len: int = 0) -> torch.Tensor:
+        n = vlb_workspace_bytes(self.p, b, seq_len)
+        if n == 0:
+            raise VlbError(ERR_SHAPE, "vlb_workspace_bytes")
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.w.w2.device)
+        return self._ws
+
+    def project(self, b: Batch, features, rows=None):
+        if rows is None:
+            rows = torch.empty(vlb_num_tokens(self.p, b), self.p.out_dim, dtype=_tdtype(self.p),
+                               device=features.device)
+        vlb_merge_project(self.p, b, features, self.w, rows, self.workspace(b))
+        return rows
+
+    def fused(self, b: Batch, features, newline, separator, mask, seq):
+        ws = self.workspace(b, seq.shape[0])
+        vlb_bridge_fused(self.p, b, features, self.w, newline, separator, mask, seq, ws)
+        return ws

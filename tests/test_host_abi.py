@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads and exports every entry point of
+include/vlbridge.h; the host planner's sizes agree with the oracle; argument
+validation returns its error codes before any HIP call is made."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import common
+from oracle import oracle as o
+from patch_merge_mlp_amd import vlbridge as v
+from patch_merge_mlp_amd import workloads as wl
+
+HEADER = os.path.join(common.__file__.rsplit("/tests/", 1)[0], "include", "vlbridge.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vlb_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 13
+    L = v.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _batches():
+    out = []
+    for i in range(wl.N_CONFIGS):
+        w = wl.config(i)
+        wl.Generator(w)  # draws the ragged grids of the last workload
+        out.append(w)
+    # odd, rectangular, k=1 and tail variants
+    out.append(wl.Workload("odd", 9, "bf16", 64, 3, 64, 64, 100, grids=[(5, 7), (1, 1), (9, 4)],
+                           views_per_image=[2, 1]))
+    out.append(wl.Workload("k1", 9, "bf16", 64, 1, 64, 64, 700, grids=[(24, 24)],
+                           views_per_image=[1]))
+    out.append(wl.Workload("tail", 9, "bf16", 64, 2, 64, 64, 4000, grids=[(27, 27)] * 7 + [(9, 9)] * 3,
+                           views_per_image=[7, 3], tiled=True, tiles=[(3, 2), (1, 2)],
+                           global_tail=True))
+    return out
+
+
+@pytest.mark.parametrize("w", _batches(), ids=lambda w: w.name)
+def test_planner_sizes_match_oracle(w):
+    p, b = common.lib_projector(w), common.lib_batch(w)
+    spec = common.oracle_spec(w)
+    assert v.vlb_num_tokens(p, b) == o.total_tokens(spec)
+    assert v.vlb_num_slots(p, b) == len(o.assemble(spec))
+    assert v.vlb_image_slots(p, b) == common.oracle_spans(w)
+    ws = v.vlb_workspace_bytes(p, b, w.seq_len)
+    assert ws > 0 and ws % 256 == 0
+
+
+def test_config_slot_counts():
+    """The tiled workload: 16 images of 210 + 1 + 42*29 slots; the text-only batch is empty."""
+    w = wl.config(3)
+    p, b = common.lib_projector(w), common.lib_batch(w)
+    assert v.vlb_image_slots(p, b) == [1429] * 16
+    assert v.vlb_num_slots(p, b) == 22864 <= w.seq_len
+    empty = v.Batch([], [])
+    assert v.vlb_num_tokens(p, empty) == 0 and v.vlb_num_slots(p, empty) == 0
+
+
+# ---- validation: error codes, no HIP call --------------------------------------
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def _proj(**kw):
+    base = dict(dtype=v.BF16, C=64, k=2, hidden=128, out_dim=64)
+    base.update(kw)
+    return v.projector(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=4), v.ERR_UNSUPPORTED), (dict(k=0), v.ERR_UNSUPPORTED),
+    (dict(dtype=7), v.ERR_DTYPE), (dict(C=0), v.ERR_SHAPE), (dict(C=12), v.ERR_UNSUPPORTED),
+    (dict(C=72), v.ERR_UNSUPPORTED), (dict(hidden=100), v.ERR_UNSUPPORTED),
+    (dict(act=5), v.ERR_UNSUPPORTED), (dict(has_ln=True, ln_eps=0.0), v.ERR_SHAPE),
+    (dict(dtype=v.F32, w1_packed=True), v.ERR_UNSUPPORTED),
+])
+def test_bad_projector(kw, status):
+    p = _proj(**kw)
+    b = v.Batch([(4, 4)], [1])
+    assert v.lib().vlb_num_tokens(ct.byref(p), ct.byref(b.c)) == -status
+
+
+@pytest.mark.parametrize("batch,status", [
+    (lambda: v.Batch([(0, 4)], [1]), v.ERR_SHAPE),
+    (lambda: v.Batch([(4, 4)], [2]), v.ERR_SHAPE),
+    (lambda: v.Batch([(4, 4), (4, 4)], [1]), v.ERR_SHAPE),
+    (lambda: v.Batch([(4, 4)] * 3, [3], v.LAYOUT_TILED_2D, [(2, 2)]), v.ERR_SHAPE),
+    (lambda: v.Batch([(4, 4), (4, 4), (6, 6)], [3], v.LAYOUT_TILED_2D, [(2, 1)]), v.ERR_SHAPE),
+    (lambda: v.Batch([(4, 4)], [1], layout=5), v.ERR_UNSUPPORTED),
+])
+def test_bad_batch(batch, status):
+    p = _proj()
+    b = batch()
+    assert v.lib().vlb_num_slots(ct.byref(p), ct.byref(b.c)) == -status
+
+
+def test_entry_points_validate_before_launching():
+    L = v.lib()
+    p = _proj()
+    b = v.Batch([(4, 4)], [1])
+    need = v.vlb_workspace_bytes(p, b, 32)
+    need0 = v.vlb_workspace_bytes(p, b, 0)
+    assert 0 < need0 < need
+    w = v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE)
+    # workspace too small
+    assert L.vlb_merge_project(ct.byref(p), ct.byref(b.c), FAKE, ct.byref(w), FAKE, FAKE,
+                               need0 - 1, None) == v.ERR_WORKSPACE
+    assert L.vlb_bridge_fused(ct.byref(p), ct.byref(b.c), FAKE, ct.byref(w), None, None, FAKE, 32,
+                              FAKE, FAKE, need - 1, None) == v.ERR_WORKSPACE
+    # null and misaligned pointers
+    assert L.vlb_merge_project(ct.byref(p), ct.byref(b.c), None, ct.byref(w), FAKE, FAKE, need,
+                               None) == v.ERR_NULL
+    assert L.vlb_merge_project(ct.byref(p), ct.byref(b.c), FAKE + 2, ct.byref(w), FAKE, FAKE, need,
+                               None) == v.ERR_ALIGN
+    wnull = v.vlb_weights(None, None, None, FAKE, FAKE, FAKE)
+    assert L.vlb_merge_project(ct.byref(p), ct.byref(b.c), FAKE, ct.byref(wnull), FAKE, FAKE, need,
+                               None) == v.ERR_NULL
+    pln = _proj(has_ln=True)
+    assert L.vlb_merge_project(ct.byref(pln), ct.byref(b.c), FAKE, ct.byref(w), FAKE, FAKE,
+                               1 << 30, None) == v.ERR_NULL  # LN parameters missing
+    assert L.vlb_scatter_tokens(ct.byref(p), ct.byref(b.c), FAKE, None, None, None, 32, FAKE, FAKE,
+                                need, None) == v.ERR_NULL
+    assert L.vlb_scatter_tokens(ct.byref(p), ct.byref(b.c), FAKE, None, None, FAKE + 1, 32, FAKE,
+                                FAKE, need, None) == v.ERR_ALIGN
+    bt = v.Batch([(4, 4)] * 2, [2], v.LAYOUT_TILED_2D, [(1, 1)])
+    assert L.vlb_scatter_tokens(ct.byref(p), ct.byref(bt.c), FAKE, None, FAKE, FAKE, 64, FAKE, FAKE,
+                                1 << 30, None) == v.ERR_NULL  # tiled needs the newline
+    assert L.vlb_pack_weights(ct.byref(p), FAKE, FAKE, None) == v.ERR_UNSUPPORTED  # aliasing
+    pf = _proj(dtype=v.F32)
+    assert L.vlb_pack_weights(ct.byref(pf), FAKE, FAKE + 16, None) == v.ERR_UNSUPPORTED
+    assert L.vlb_merge_project(None, ct.byref(b.c), FAKE, ct.byref(w), FAKE, FAKE, need,
+                               None) == v.ERR_NULL
+    # text only: a successful no-op
+    e = v.Batch([], [])
+    assert L.vlb_bridge_fused(ct.byref(p), ct.byref(e.c), None, None, None, None, None, 0, None,
+                              None, 0, None) == v.OK
+
+
+def test_status_strings():
+    for s in range(9):
+        assert v.status_str(s)
+    assert "placeholder" in v.status_str(v.ERR_MASK_COUNT)
