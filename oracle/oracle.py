@@ -270,7 +270,7 @@ def project_rows(spec: Spec, x, gamma, beta, W1, b1, W2, b2, row_ids=None,
         row_ids = np.arange(total_tokens(spec), dtype=np.int64)
     row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
     if nthreads <= 0:
-        nthreads = os.cpu_count() or 1
+        nthreads = min(os.cpu_count() or 1, 16)
     out = np.empty((len(row_ids), spec.out_dim), dtype=np.float64)
     xs = [_f64(a) for a in (x, gamma, beta, W1, b1, W2, b2)]
     lib().orc_project_rows(ct.byref(s), *[_dp(a) for a in xs], row_ids.ctypes.data_as(_I64),
