@@ -12,7 +12,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/vlbridge.h"
+#include "vlbridge.h"
 #include "vlb_internal.h"
 
 namespace {
@@ -122,6 +122,11 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   pl->P = slot;
   if (pl->T * std::max<int64_t>(p->hidden, p->out_dim) > kI32Max) return VLB_ERR_SHAPE;
   if (seq_len * p->out_dim > kI32Max) return VLB_ERR_SHAPE;
+  // The GEMMs address their operands with 32-bit byte offsets (buffer loads).
+  if (pl->npix * p->C * pl->es > kI32Max || pl->T * p->hidden * pl->es > kI32Max ||
+      pl->K1 * p->hidden * pl->es > kI32Max ||
+      static_cast<int64_t>(p->hidden) * p->out_dim * pl->es > kI32Max)
+    return VLB_ERR_SHAPE;
 
   size_t off = 0;
   pl->off_status = off;
@@ -230,6 +235,8 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   g1.C = p->C;
   g1.k = p->k;
   g1.act = p->act;
+  g1.a_bytes = static_cast<uint32_t>(pl.npix * p->C * pl.es);
+  g1.b_bytes = static_cast<uint32_t>(pl.K1 * p->hidden * pl.es);
   vlb::GemmArgs g2{};
   g2.A = hbuf;
   g2.B = w->w2;
@@ -241,6 +248,8 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   g2.K = p->hidden;
   g2.ldo = p->out_dim;
   g2.act = VLB_ACT_NONE;
+  g2.a_bytes = static_cast<uint32_t>(pl.T * p->hidden * pl.es);
+  g2.b_bytes = static_cast<uint32_t>(static_cast<int64_t>(p->out_dim) * p->hidden * pl.es);
   if (p->dtype == VLB_BF16) {
     const void *w1p = w->w1;
     if (!p->w1_packed) {

@@ -58,72 +58,96 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-template <bool GATHER>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offset that lies past every buffer (buffers are < 2^31 bytes): a buffer
+// load from it returns zeros, which is how padding and out-of-range rows are
+// filled without branches.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes bytes [16 l, 16 l + 16) after `dst`.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst), 16, off, 0, 0, 0);
+}
+
+template <bool GATHER, int ACT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BN];  // this tile's bias
+  __shared__ int32_t s_dst[BM];                                 // destination row per tile row
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int tm, tn;
   map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const uint16_t *A = static_cast<const uint16_t *>(g.A);
-  const uint16_t *B = static_cast<const uint16_t *>(g.B);
+  // Epilogue operands are fetched now so their latency hides under the K loop.
+  {
+    const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
+    const int c = n0 + tid;
+    s_bias[tid] = c < g.N ? bias[c] : static_cast<uint16_t>(0);
+    const int m = m0 + tid;
+    s_dst[tid] = m >= g.M ? -1 : (g.dst_row ? g.dst_row[m] : m);
+  }
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.A, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(g.B, g.b_bytes);
 
-  // Loader role: chunk lc of rows lr + 32*i (i < 8) of both A and B stages.
-  const int lc = tid & 7, lr = tid >> 3;
-  int32_t a_base[8], a_geo[8], b_base[8];
+  // Loader role: wave `wid` fills rows [64 wid, 64 wid + 64) of both stage
+  // halves, 8 rows (1 KiB) per instruction.  Lane l lands on row 8i + l/8 at
+  // physical chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7).
+  int32_t a_pix[8], a_geo[8];
+  uint32_t a_off[8], b_off[8], c_off[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int m = m0 + lr + 32 * i;
+    const int row = wid * 64 + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    c_off[i] = chunk * 16;
+    const int m = m0 + row, n = n0 + row;
     if (GATHER) {
       RowDesc d = {0, 0};
       if (m < g.M) d = g.desc[m];
-      a_base[i] = d.pix;
-      a_geo[i] = d.geo;  // 0 for rows past M: every position reads as padding
+      a_pix[i] = d.pix;
+      a_geo[i] = d.geo;  // 0 past the last row: every position reads as padding
+      a_off[i] = 0;
     } else {
-      a_base[i] = m < g.M ? m * g.K : -1;
-      a_geo[i] = 0;
+      a_pix[i] = a_geo[i] = 0;
+      a_off[i] = m < g.M ? static_cast<uint32_t>(m) * g.K * 2 + c_off[i] : kOOB;
     }
-    const int n = n0 + lr + 32 * i;
-    b_base[i] = n < g.N ? n * g.K : -1;
+    b_off[i] = n < g.N ? static_cast<uint32_t>(n) * g.K * 2 + c_off[i] : kOOB;
   }
 
-  uint4 ra[8], rb[8];
-  auto gload = [&](int kt) {
+  // Loads of K step kt into `stage`.  Steps at or past the end of K read
+  // zeros (the loop runs an even number of steps and prefetches one more).
+  const int KT = g.K / BK;
+  auto issue = [&](int kt, uint8_t *stage) {
     const int kk = kt * BK;
+    const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
+    uint8_t *sa = stage + wid * 8 * 1024;
+    uint8_t *sb = stage + A_BYTES + wid * 8 * 1024;
+    int p = 0, c0 = 0, dy = 0, dx = 0;
     if (GATHER) {
-      const int p = kk / g.C, c0 = kk - p * g.C;
-      const int dy = p / g.k, dx = p - dy * g.k;
+      p = kk / g.C;
+      c0 = kk - p * g.C;
+      dy = p / g.k;
+      dx = p - dy * g.k;
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      uint32_t ao;
+      if (GATHER) {
         const int gw = a_geo[i] & 0xffff;
-        const bool in = (a_geo[i] >> (16 + p)) & 1;
-        ra[i] = make_uint4(0, 0, 0, 0);
-        if (in)
-          ra[i] = *reinterpret_cast<const uint4 *>(A + (a_base[i] + dy * gw + dx) * g.C + c0 +
-                                                   lc * 8);
+        const uint32_t pad = ((a_geo[i] >> (16 + p)) & 1) ? 0u : kOOB;
+        ao = (static_cast<uint32_t>((a_pix[i] + dy * gw + dx) * g.C + c0) * 2 + c_off[i]) | pad;
+      } else {
+        ao = a_off[i] + kk * 2;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ra[i] = make_uint4(0, 0, 0, 0);
-        if (a_base[i] >= 0)
-          ra[i] = *reinterpret_cast<const uint4 *>(A + a_base[i] + kk + lc * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      rb[i] = make_uint4(0, 0, 0, 0);
-      if (b_base[i] >= 0) rb[i] = *reinterpret_cast<const uint4 *>(B + b_base[i] + kk + lc * 8);
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t *sa = smem + stage * STAGE_BYTES;
-    uint8_t *sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = lr + 32 * i;
-      *reinterpret_cast<uint4 *>(sa + swz(row, lc)) = ra[i];
-      *reinterpret_cast<uint4 *>(sb + swz(row, lc)) = rb[i];
+      load_lds16(rA, sa + i * 1024, ao | dead);
+      load_lds16(rB, sb + i * 1024, (b_off[i] + kk * 2) | dead);
     }
   };
 
@@ -137,57 +161,114 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
 
   const int wm = wid >> 1, wn = wid & 1;
   const int fr = lane & 31, fk = lane >> 5;  // fragment row / k-half of this lane
-  const int KT = g.K / BK;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t *sa = smem + cur * STAGE_BYTES;
-    const uint8_t *sb = sa + A_BYTES;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto rd = [&](const uint8_t *stage, int ks, bf16x8 *fa, bf16x8 *fb) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[4], bfg[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = *reinterpret_cast<const bf16x8 *>(sa + swz(wm * 128 + t * 32 + fr, ks * 2 + fk));
-        bfg[t] = *reinterpret_cast<const bf16x8 *>(sb + swz(wn * 128 + t * 32 + fr, ks * 2 + fk));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * 128 + t * 32 + fr, ks * 2 + fk));
+      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + A_BYTES +
+                                                swz(wn * 128 + t * 32 + fr, ks * 2 + fk));
     }
-    if (kt + 1 < KT) lstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane holds column fr of each 32x32 tile and rows
-  // 8*(q/4) + 4*fk + q%4 (q < 16).
-  const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
-  uint16_t *out = static_cast<uint16_t *>(g.out);
-  float bv[4];
-  int col[4];
+  };
+  auto mma = [&](const bf16x8 *fa, const bf16x8 *fb) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    col[j] = n0 + wn * 128 + j * 32 + fr;
-    bv[j] = col[j] < g.N ? bf2f(bias[col[j]]) : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = m0 + wm * 128 + i * 32 + 8 * (q >> 2) + 4 * fk + (q & 3);
-      if (m >= g.M) continue;
-      const int dst = g.dst_row ? g.dst_row[m] : m;
-      if (dst < 0) continue;
-      uint16_t *orow = out + static_cast<int64_t>(dst) * g.ldo;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (col[j] < g.N) orow[col[j]] = f2bf(activate(acc[i][j][q] + bv[j], g.act));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  // One K step: the next stage's loads are issued first; fragments of step
+  // ks+1 are read while step ks multiplies; the barrier sits before the last
+  // 16 MFMAs so the first fragments of the next stage arrive under them.
+  auto step = [&](int kt, const uint8_t *cur, uint8_t *nxt) {
+    issue(kt + 1, nxt);
+    rd(cur, 1, fa1, fb1);
+    mma(fa0, fb0);
+    rd(cur, 2, fa0, fb0);
+    mma(fa1, fb1);
+    rd(cur, 3, fa1, fb1);
+    mma(fa0, fb0);
+    // Interleave: each fragment read and stage load rides between MFMAs.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global -> LDS load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    __syncthreads();  // next stage landed everywhere; this stage fully read
+    rd(nxt, 0, fa0, fb0);
+    mma(fa1, fb1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  issue(0, smem0);
+  __syncthreads();
+  rd(smem0, 0, fa0, fb0);
+  for (int kt = 0; kt < KT; kt += 2) {  // an odd KT runs one all-zero step
+    step(kt, smem0, smem1);
+    step(kt + 1, smem1, smem0);
+  }
+
+  // Epilogue.  The weight fragment is the MFMA's first operand, so acc[i][j]
+  // holds the transposed product: lane (fr, fk) owns token row
+  // wm*128 + 32 i + fr and features wn*128 + 32 j + 8 a + 4 fk + e in element
+  // 4 a + e (a, e < 4).  Bias and activation are applied in fp32, the tile is
+  // rounded to bf16 and staged in LDS (rows 0..127 in smem0, 128..255 in
+  // smem1; 512-byte rows of 16-byte chunks XOR-swizzled by the row), and then
+  // written out whole rows at a time with 16-byte stores.
+  __syncthreads();  // every fragment read has finished: the stages become the C tile
+  uint8_t *half = wm ? smem1 : smem0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int cl = wn * 128 + j * 32 + 8 * a + 4 * fk;  // 4 consecutive features
+      const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
+      const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
+                          bf2f(bb.y >> 16)};
+      const int chunk = cl >> 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + fr;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][4 * a + e] + b[e]));
+        uint2 v;
+        v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+        v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+        *reinterpret_cast<uint2 *>(half + row * 512 + ((chunk ^ (row & 31)) << 4) + fk * 8) = v;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t *out = static_cast<uint16_t *>(g.out);
+  const int chunk = tid & 31;
+  const int col = n0 + chunk * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint8_t *src = h ? smem1 : smem0;
+#pragma unroll 4
+    for (int s8 = 0; s8 < 16; ++s8) {
+      const int row = (tid >> 5) + 8 * s8;
+      const int dst = s_dst[h * 128 + row];  // -1: past the last row, or not placed
+      if (dst < 0 || col >= g.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4 *>(src + row * 512 + ((chunk ^ (row & 31)) << 4));
+      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
     }
   }
 }
@@ -269,10 +350,16 @@ hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s) {
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   const dim3 grid(g.tiles_m * g.tiles_n);
-  if (gather)
-    hipLaunchKernelGGL(k_gemm_bf16<true>, grid, dim3(NTHREADS), 0, s, g);
+  if (gather && g.act == 0)
+    hipLaunchKernelGGL((k_gemm_bf16<true, 0>), grid, dim3(NTHREADS), 0, s, g);
+  else if (gather && g.act == 1)
+    hipLaunchKernelGGL((k_gemm_bf16<true, 1>), grid, dim3(NTHREADS), 0, s, g);
+  else if (gather)
+    hipLaunchKernelGGL((k_gemm_bf16<true, 2>), grid, dim3(NTHREADS), 0, s, g);
+  else if (g.act == 2)
+    hipLaunchKernelGGL((k_gemm_bf16<false, 2>), grid, dim3(NTHREADS), 0, s, g);
   else
-    hipLaunchKernelGGL(k_gemm_bf16<false>, grid, dim3(NTHREADS), 0, s, g);
+    return hipErrorInvalidValue;  // the second Linear has no activation
   return hipGetLastError();
 }
 

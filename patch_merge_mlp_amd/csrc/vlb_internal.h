@@ -57,6 +57,7 @@ struct GemmArgs {
   int32_t C, k;           // gather mode: channels and merge factor
   int32_t act;            // vlb_act
   int32_t tiles_m, tiles_n;
+  uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31): loads past it read 0
 };
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------

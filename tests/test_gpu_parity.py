@@ -85,7 +85,7 @@ def small_workloads():
                     grids=[(13, 13)] * 10, views_per_image=[7, 3], tiled=True,
                     tiles=[(2, 3), (1, 2)]),
         wl.Workload("small-tiled-tail", 14, "bf16", C=64, k=2, hidden=128, out_dim=64,
-                    seq_len=900, grids=[(27, 27)] * 5, views_per_image=[5], tiled=True,
+                    seq_len=1200, grids=[(27, 27)] * 5, views_per_image=[5], tiled=True,
                     tiles=[(2, 2)], global_tail=True),
         wl.Workload("small-k1", 15, "bf16", C=64, k=1, hidden=128, out_dim=64, seq_len=600,
                     grids=[(24, 24)], views_per_image=[1]),
