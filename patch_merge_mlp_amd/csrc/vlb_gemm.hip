@@ -26,10 +26,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
-constexpr int A_BYTES = BM * BK * 2;
+constexpr int BM = 256, BN = 256, BK = 32, NTHREADS = 256;
+constexpr int NSTAGE = 4;               // LDS stages; three are in flight
+constexpr int A_BYTES = BM * BK * 2;    // 16 KiB
 constexpr int B_BYTES = BN * BK * 2;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 32 KiB
 constexpr int GROUP_M = 8;
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs, so
@@ -51,12 +52,20 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
   tn = in_group / gsz;
 }
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of row `row` inside a stage
-// half: 128-byte rows, chunk XOR-swizzled with bits 1..3 of the row so that 16
-// consecutive rows reading the same logical chunk hit distinct banks.
+// Byte offset of 16-byte chunk `chunk` (0..3) of row `row` inside a stage
+// half: 64-byte rows, the chunk XOR-ed with ((row >> 1) ^ (row >> 3)) & 3 so
+// that any 8 or 16 consecutive rows reading the same logical chunk fall on
+// distinct LDS banks.
+__device__ __forceinline__ int swz_xor(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 64 + ((chunk ^ swz_xor(row)) << 4);
 }
+
+// Barrier for the stage pipeline: this wave's loads are complete except the
+// newest `kInFlight` (the two younger stages) and its LDS reads are done, then
+// the workgroup synchronises.  Written as one asm block so that no memory
+// access is moved across it.
+#define VLB_STAGE_BARRIER() asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -80,6 +89,8 @@ template <bool GATHER, int ACT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[BN];  // this tile's bias
   __shared__ int32_t s_dst[BM];                                 // destination row per tile row
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -98,14 +109,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(g.B, g.b_bytes);
 
   // Loader role: wave `wid` fills rows [64 wid, 64 wid + 64) of both stage
-  // halves, 8 rows (1 KiB) per instruction.  Lane l lands on row 8i + l/8 at
-  // physical chunk l%8, which holds logical chunk (l%8) ^ ((row >> 1) & 7).
-  int32_t a_pix[8], a_geo[8];
-  uint32_t a_off[8], b_off[8], c_off[8];
+  // halves, 16 rows (1 KiB) per instruction.  Lane l lands on row 16i + l/4 at
+  // physical chunk l%4, which holds logical chunk (l%4) ^ swz_xor(row).
+  int32_t a_pix[4], a_geo[4];
+  uint32_t a_off[4], b_off[4], c_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = wid * 64 + 8 * i + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+  for (int i = 0; i < 4; ++i) {
+    const int row = wid * 64 + 16 * i + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz_xor(row);
     c_off[i] = chunk * 16;
     const int m = m0 + row, n = n0 + row;
     if (GATHER) {
@@ -122,13 +133,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   }
 
   // Loads of K step kt into `stage`.  Steps at or past the end of K read
-  // zeros (the loop runs an even number of steps and prefetches one more).
+  // zeros (the loop runs a multiple of NSTAGE steps and prefetches beyond).
   const int KT = g.K / BK;
   auto issue = [&](int kt, uint8_t *stage) {
     const int kk = kt * BK;
     const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
-    uint8_t *sa = stage + wid * 8 * 1024;
-    uint8_t *sb = stage + A_BYTES + wid * 8 * 1024;
+    uint8_t *sa = stage + wid * 4 * 1024;
+    uint8_t *sb = stage + A_BYTES + wid * 4 * 1024;
     int p = 0, c0 = 0, dy = 0, dx = 0;
     if (GATHER) {
       p = kk / g.C;
@@ -137,7 +148,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
       dx = p - dy * g.k;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       uint32_t ao;
       if (GATHER) {
         const int gw = a_geo[i] & 0xffff;
@@ -177,35 +188,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
-  // One K step: the next stage's loads are issued first; fragments of step
-  // ks+1 are read while step ks multiplies; the barrier sits before the last
-  // 16 MFMAs so the first fragments of the next stage arrive under them.
-  auto step = [&](int kt, const uint8_t *cur, uint8_t *nxt) {
-    issue(kt + 1, nxt);
+  // One K step of 32: the loads of step kt+3 are issued into the stage freed
+  // by step kt-1; the second 16-wide slice is read while the first multiplies;
+  // the barrier (step kt+1 landed everywhere, step kt fully read) sits before
+  // the last 16 MFMAs so the next step's first fragments arrive under them.
+  auto step = [&](int kt, const uint8_t *cur, const uint8_t *nxt, uint8_t *fut) {
+    issue(kt + 3, fut);
     rd(cur, 1, fa1, fb1);
     mma(fa0, fb0);
-    rd(cur, 2, fa0, fb0);
-    mma(fa1, fb1);
-    rd(cur, 3, fa1, fb1);
-    mma(fa0, fb0);
-    // Interleave: each fragment read and stage load rides between MFMAs.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global -> LDS load
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global -> LDS load
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-    __syncthreads();  // next stage landed everywhere; this stage fully read
+    VLB_STAGE_BARRIER();
     rd(nxt, 0, fa0, fb0);
     mma(fa1, fb1);
 #pragma unroll
@@ -217,22 +215,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   };
 
   issue(0, smem0);
-  __syncthreads();
+  issue(1, smem1);
+  issue(2, smem2);
+  VLB_STAGE_BARRIER();  // step 0 landed
   rd(smem0, 0, fa0, fb0);
-  for (int kt = 0; kt < KT; kt += 2) {  // an odd KT runs one all-zero step
-    step(kt, smem0, smem1);
-    step(kt + 1, smem1, smem0);
+  for (int kt = 0; kt < KT; kt += NSTAGE) {  // KT rounds up: the extra steps are all-zero
+    step(kt, smem0, smem1, smem3);
+    step(kt + 1, smem1, smem2, smem0);
+    step(kt + 2, smem2, smem3, smem1);
+    step(kt + 3, smem3, smem0, smem2);
   }
 
   // Epilogue.  The weight fragment is the MFMA's first operand, so acc[i][j]
   // holds the transposed product: lane (fr, fk) owns token row
   // wm*128 + 32 i + fr and features wn*128 + 32 j + 8 a + 4 fk + e in element
   // 4 a + e (a, e < 4).  Bias and activation are applied in fp32, the tile is
-  // rounded to bf16 and staged in LDS (rows 0..127 in smem0, 128..255 in
-  // smem1; 512-byte rows of 16-byte chunks XOR-swizzled by the row), and then
-  // written out whole rows at a time with 16-byte stores.
-  __syncthreads();  // every fragment read has finished: the stages become the C tile
-  uint8_t *half = wm ? smem1 : smem0;
+  // rounded to bf16 and staged in LDS (64 rows per stage buffer; 512-byte rows
+  // of 16-byte chunks XOR-swizzled by the row), then written out whole rows at
+  // a time with 16-byte stores.
+  __syncthreads();  // every load and fragment read has finished: the stages become the C tile
+  auto bufs = [&](int b) -> uint8_t * {
+    return b == 0 ? smem0 : b == 1 ? smem1 : b == 2 ? smem2 : smem3;
+  };
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -244,14 +248,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
       const int chunk = cl >> 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = i * 32 + fr;
+        const int row = (i & 1) * 32 + fr;  // inside buffer wm*2 + i/2
         uint16_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][4 * a + e] + b[e]));
         uint2 v;
         v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
         v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-        *reinterpret_cast<uint2 *>(half + row * 512 + ((chunk ^ (row & 31)) << 4) + fk * 8) = v;
+        *reinterpret_cast<uint2 *>(bufs(wm * 2 + (i >> 1)) + row * 512 +
+                                   ((chunk ^ (row & 31)) << 4) + fk * 8) = v;
       }
     }
   }
@@ -260,14 +265,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   const int chunk = tid & 31;
   const int col = n0 + chunk * 8;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint8_t *src = h ? smem1 : smem0;
+  for (int bi = 0; bi < NSTAGE; ++bi) {
 #pragma unroll 4
-    for (int s8 = 0; s8 < 16; ++s8) {
-      const int row = (tid >> 5) + 8 * s8;
-      const int dst = s_dst[h * 128 + row];  // -1: past the last row, or not placed
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int row = (tid >> 5) + 8 * s8;  // inside buffer bi
+      const int dst = s_dst[bi * 64 + row];  // -1: past the last row, or not placed
       if (dst < 0 || col >= g.N) continue;
-      const uint4 v = *reinterpret_cast<const uint4 *>(src + row * 512 + ((chunk ^ (row & 31)) << 4));
+      const uint4 v =
+          *reinterpret_cast<const uint4 *>(bufs(bi) + row * 512 + ((chunk ^ (row & 31)) << 4));
       *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
     }
   }
