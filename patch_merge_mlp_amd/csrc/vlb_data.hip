@@ -17,6 +17,7 @@ namespace vlb {
 namespace {
 
 constexpr int kErrMaskCount = 6;  // VLB_ERR_MASK_COUNT
+constexpr int kLnChunks = 8;      // LayerNorm: most 16-byte chunks a lane holds
 
 // ---------------------------------------------------------------------------
 // Gather descriptor of every token row of a chunk of views.
@@ -179,11 +180,10 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
 
 // ---------------------------------------------------------------------------
 // LayerNorm over C per pixel, one wave per pixel: mean, biased variance, eps
-// inside the square root, affine.  Values stay in registers (up to
-// kLnChunks 16-byte chunks per lane).
-constexpr int kLnChunks = 8;
-
-template <typename T>
+// inside the square root, affine.  The pixel stays in registers: NCH 16-byte
+// chunks per lane (NCH chosen from C at launch, so a lane holds as few
+// registers as the row needs and many waves stay resident).
+template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int C, const T *gamma,
                                                    const T *beta, float eps, T *out) {
   constexpr int E = 16 / sizeof(T);
@@ -191,26 +191,25 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   const int nch = C / E;
+  const uint4 *g4 = reinterpret_cast<const uint4 *>(gamma);
+  const uint4 *b4 = reinterpret_cast<const uint4 *>(beta);
   for (int64_t px = wave; px < npix; px += nwaves) {
     const uint4 *src = reinterpret_cast<const uint4 *>(x + px * C);
-    uint4 v[kLnChunks];
+    uint4 v[NCH];
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kLnChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
-      if (q < nch) {
-        v[i] = src[q];
-        const T *e = reinterpret_cast<const T *>(&v[i]);
+      v[i] = q < nch ? src[q] : make_uint4(0, 0, 0, 0);
+      const T *e = reinterpret_cast<const T *>(&v[i]);
 #pragma unroll
-        for (int j = 0; j < E; ++j) s += Elem<T>::load(e[j]);
-      }
+      for (int j = 0; j < E; ++j) s += Elem<T>::load(e[j]);
     }
     const float mean = wave_sum(s) / C;
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kLnChunks; ++i) {
-      const int q = lane + 64 * i;
-      if (q < nch) {
+    for (int i = 0; i < NCH; ++i) {
+      if (lane + 64 * i < nch) {
         const T *e = reinterpret_cast<const T *>(&v[i]);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -221,10 +220,8 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
     }
     const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
     uint4 *dst = reinterpret_cast<uint4 *>(out + px * C);
-    const uint4 *g4 = reinterpret_cast<const uint4 *>(gamma);
-    const uint4 *b4 = reinterpret_cast<const uint4 *>(beta);
 #pragma unroll
-    for (int i = 0; i < kLnChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
       if (q < nch) {
         const uint4 gv = g4[q], bv = b4[q];
@@ -375,20 +372,35 @@ hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slo
   return hipGetLastError();
 }
 
+template <typename T, int NCH>
+static void ln_launch(const void *x, int64_t npix, int C, const void *gamma, const void *beta,
+                      float eps, void *out, hipStream_t s) {
+  const int grid = grid_for(npix, 4, 16384);
+  hipLaunchKernelGGL((k_layernorm<T, NCH>), dim3(grid), dim3(256), 0, s,
+                     static_cast<const T *>(x), npix, C, static_cast<const T *>(gamma),
+                     static_cast<const T *>(beta), eps, static_cast<T *>(out));
+}
+
+template <typename T>
+static hipError_t ln_dispatch(const void *x, int64_t npix, int C, const void *gamma,
+                              const void *beta, float eps, void *out, hipStream_t s) {
+  const int nch = (C * static_cast<int>(sizeof(T)) / 16 + 63) / 64;  // chunks per lane
+  switch (nch) {
+    case 1: ln_launch<T, 1>(x, npix, C, gamma, beta, eps, out, s); break;
+    case 2: ln_launch<T, 2>(x, npix, C, gamma, beta, eps, out, s); break;
+    case 3: ln_launch<T, 3>(x, npix, C, gamma, beta, eps, out, s); break;
+    case 4: ln_launch<T, 4>(x, npix, C, gamma, beta, eps, out, s); break;
+    case 5: case 6: ln_launch<T, 6>(x, npix, C, gamma, beta, eps, out, s); break;
+    default: ln_launch<T, kLnChunks>(x, npix, C, gamma, beta, eps, out, s); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const void *gamma,
                             const void *beta, float eps, void *out, hipStream_t s) {
   if (npix <= 0) return hipSuccess;
-  const int grid = grid_for(npix, 4, 8192);
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_layernorm<float>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const float *>(x), npix, C, static_cast<const float *>(gamma),
-                       static_cast<const float *>(beta), eps, static_cast<float *>(out));
-  else
-    hipLaunchKernelGGL(k_layernorm<uint16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(x), npix, C,
-                       static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
-                       eps, static_cast<uint16_t *>(out));
-  return hipGetLastError();
+  return dtype == 0 ? ln_dispatch<float>(x, npix, C, gamma, beta, eps, out, s)
+                    : ln_dispatch<uint16_t>(x, npix, C, gamma, beta, eps, out, s);
 }
 
 int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 : 8); }

@@ -26,23 +26,29 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 32, NTHREADS = 256;
-constexpr int NSTAGE = 4;               // LDS stages; three are in flight
-constexpr int A_BYTES = BM * BK * 2;    // 16 KiB
-constexpr int B_BYTES = BN * BK * 2;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 32 KiB
+constexpr int BK = kGemmBK, NTHREADS = 256;
+constexpr int NSTAGE = kGemmStages;  // LDS stages; three are in flight
 constexpr int GROUP_M = 8;
 
-// Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs, so
-// workgroup b runs on XCD b % 8; each XCD is given a contiguous range of
-// logical tiles, and logical tiles are ordered in groups of GROUP_M tile-rows,
-// column by column, so the tiles an XCD runs together share A and B panels in
-// its L2.
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int nblk = tiles_m * tiles_n;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
+// Geometry of a BMT x BMT output tile (BMT = 256 or 128) computed by 4 waves
+// in a 2x2 grid, each wave owning a (BMT/2)^2 block of 32x32 MFMA tiles.
+template <int BMT>
+struct Geo {
+  static constexpr int TI = BMT / 64;          // MFMA tiles per wave per dimension
+  static constexpr int WT = BMT / 2;           // wave tile side
+  static constexpr int LPW = BMT / 64;         // 16-row loads per wave per operand per stage
+  static constexpr int HALF = BMT * BK * 2;    // bytes of one operand in a stage
+  static constexpr int STAGE = 2 * HALF;       // bytes of a stage
+  static constexpr int ROWB = BMT * 2;         // bytes of one bf16 output row
+  static constexpr int CCH = BMT / 8;          // 16-byte chunks per output row
+  static constexpr int RPB = STAGE / ROWB;     // output rows staged per stage buffer (64)
+  static_assert(RPB == 64, "C staging assumes 64 rows per stage buffer");
+};
+
+// Logical tile -> (tile row, tile column): groups of GROUP_M tile-rows, column
+// by column, so tiles that run together share A and B panels in L2.
+__device__ __forceinline__ void tile_coords(int logical, int tiles_m, int tiles_n, int &tm,
+                                            int &tn) {
   const int span = GROUP_M * tiles_n;
   const int group = logical / span;
   const int first_m = group * GROUP_M;
@@ -50,6 +56,14 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
   const int in_group = logical - group * span;
   tm = first_m + in_group % gsz;
   tn = in_group / gsz;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+// b % 8); this gives each XCD a contiguous range of the n logical indices.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = n >> 3, rem = n & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
 // Byte offset of 16-byte chunk `chunk` (0..3) of row `row` inside a stage
@@ -61,11 +75,16 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 64 + ((chunk ^ swz_xor(row)) << 4);
 }
 
-// Barrier for the stage pipeline: this wave's loads are complete except the
-// newest `kInFlight` (the two younger stages) and its LDS reads are done, then
-// the workgroup synchronises.  Written as one asm block so that no memory
-// access is moved across it.
-#define VLB_STAGE_BARRIER() asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// Barrier of the stage pipeline: this wave's loads are complete except those
+// of the two younger stages (16 or 8 loads), its LDS reads are done, then the
+// workgroup synchronises.  One asm block, so no memory access moves across it.
+template <int BMT>
+__device__ __forceinline__ void stage_barrier() {
+  if constexpr (BMT == 256)
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -85,20 +104,98 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst), 16, off, 0, 0, 0);
 }
 
-template <bool GATHER, int ACT>
+// Epilogue of one tile.  The weight fragment is the MFMA's first operand, so
+// acc[i][j] holds the transposed product: lane (fr, fk) of wave (wm, wn) owns
+// token row wm*WT + 32 i + fr and features wn*WT + 32 j + 8 a + 4 fk + e in
+// element 4 a + e (a, e < 4).  Bias and activation are applied in fp32, the
+// tile is rounded to bf16 and staged in the stage buffers (64 rows each; rows
+// of 16-byte chunks XOR-swizzled by the row), then written out whole rows at a
+// time with 16-byte stores to row s_dst[r] (skipped when negative).  The
+// caller has synchronised the workgroup after its last use of the buffers.
+template <int ACT, int BMT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+                                           const GemmArgs &g, int n0, uint8_t *b0, uint8_t *b1,
+                                           uint8_t *b2, uint8_t *b3, const uint16_t *s_bias,
+                                           const int32_t *s_dst) {
+  using G = Geo<BMT>;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int fr = lane & 31, fk = lane >> 5;
+  auto bufs = [&](int b) -> uint8_t * { return b == 0 ? b0 : b == 1 ? b1 : b == 2 ? b2 : b3; };
+#pragma unroll
+  for (int j = 0; j < G::TI; ++j) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int cl = wn * G::WT + j * 32 + 8 * a + 4 * fk;  // 4 consecutive features
+      const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
+      const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
+                          bf2f(bb.y >> 16)};
+      const int chunk = cl >> 3;
+#pragma unroll
+      for (int i = 0; i < G::TI; ++i) {
+        const int r = wm * G::WT + i * 32 + fr;  // tile row
+        const int row = r & 63;                  // inside buffer r / 64
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][4 * a + e] + b[e]));
+        uint2 v;
+        v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+        v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+        *reinterpret_cast<uint2 *>(bufs(r >> 6) + row * G::ROWB +
+                                   ((chunk ^ (row & (G::CCH - 1))) << 4) + fk * 8) = v;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t *out = static_cast<uint16_t *>(g.out);
+  const int chunk = tid % G::CCH;
+  const int col = n0 + chunk * 8;
+  constexpr int RSTEP = NTHREADS / G::CCH;  // rows per pass
+#pragma unroll
+  for (int bi = 0; bi < BMT / 64; ++bi) {
+#pragma unroll 4
+    for (int s8 = 0; s8 < 64 / RSTEP; ++s8) {
+      const int row = tid / G::CCH + RSTEP * s8;  // inside buffer bi
+      const int dst = s_dst[bi * 64 + row];       // -1: past the last row, or not placed
+      if (dst < 0 || col >= g.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4 *>(bufs(bi) + row * G::ROWB +
+                                                       ((chunk ^ (row & (G::CCH - 1))) << 4));
+      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
+    }
+  }
+}
+
+// One launch covers either the whole-tile part of the problem (BMT = 256:
+// tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
+// quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
+// whole 128-grid).
+template <bool GATHER, int ACT, int BMT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem3[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BN];  // this tile's bias
-  __shared__ int32_t s_dst[BM];                                 // destination row per tile row
+  using G = Geo<BMT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BMT];  // this tile's bias
+  __shared__ int32_t s_dst[BMT];                                 // destination row per tile row
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int tm, tn;
-  map_tile(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  if (BMT == 256) {
+    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+  } else if (g.n_full > 0) {
+    const int rem = g.tiles_m * g.tiles_n - g.n_full;
+    const int q = xcd_remap(blockIdx.x, 4 * rem);  // quarters of one 256-tile stay together
+    int bm, bn;
+    tile_coords(g.n_full + (q >> 2), g.tiles_m, g.tiles_n, bm, bn);
+    tm = 2 * bm + ((q >> 1) & 1);
+    tn = 2 * bn + (q & 1);
+  } else {
+    const int tm128 = (g.M + 127) / 128, tn128 = (g.N + 127) / 128;
+    tile_coords(xcd_remap(blockIdx.x, tm128 * tn128), tm128, tn128, tm, tn);
+  }
+  const int m0 = tm * BMT, n0 = tn * BMT;
   // Epilogue operands are fetched now so their latency hides under the K loop.
-  {
+  if (tid < BMT) {
     const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
     const int c = n0 + tid;
     s_bias[tid] = c < g.N ? bias[c] : static_cast<uint16_t>(0);
@@ -108,14 +205,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(g.A, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(g.B, g.b_bytes);
 
-  // Loader role: wave `wid` fills rows [64 wid, 64 wid + 64) of both stage
-  // halves, 16 rows (1 KiB) per instruction.  Lane l lands on row 16i + l/4 at
-  // physical chunk l%4, which holds logical chunk (l%4) ^ swz_xor(row).
-  int32_t a_pix[4], a_geo[4];
-  uint32_t a_off[4], b_off[4], c_off[4];
+  // Loader role: wave `wid` fills rows [wid*BMT/4, (wid+1)*BMT/4) of both
+  // stage halves, 16 rows (1 KiB) per instruction.  Lane l lands on row
+  // 16i + l/4 at physical chunk l%4, which holds logical chunk (l%4) ^ swz_xor(row).
+  int32_t a_pix[G::LPW], a_geo[G::LPW];
+  uint32_t a_off[G::LPW], b_off[G::LPW], c_off[G::LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wid * 64 + 16 * i + (lane >> 2);
+  for (int i = 0; i < G::LPW; ++i) {
+    const int row = wid * (BMT / 4) + 16 * i + (lane >> 2);
     const int chunk = (lane & 3) ^ swz_xor(row);
     c_off[i] = chunk * 16;
     const int m = m0 + row, n = n0 + row;
@@ -132,14 +229,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     b_off[i] = n < g.N ? static_cast<uint32_t>(n) * g.K * 2 + c_off[i] : kOOB;
   }
 
-  // Loads of K step kt into `stage`.  Steps at or past the end of K read
-  // zeros (the loop runs a multiple of NSTAGE steps and prefetches beyond).
+  // Loads of K step kt into `stage`.  Steps at or past the end of K read zeros
+  // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
   const int KT = g.K / BK;
   auto issue = [&](int kt, uint8_t *stage) {
     const int kk = kt * BK;
     const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
-    uint8_t *sa = stage + wid * 4 * 1024;
-    uint8_t *sb = stage + A_BYTES + wid * 4 * 1024;
+    uint8_t *sa = stage + wid * G::LPW * 1024;
+    uint8_t *sb = stage + G::HALF + wid * G::LPW * 1024;
     int p = 0, c0 = 0, dy = 0, dx = 0;
     if (GATHER) {
       p = kk / g.C;
@@ -148,7 +245,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
       dx = p - dy * g.k;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < G::LPW; ++i) {
       uint32_t ao;
       if (GATHER) {
         const int gw = a_geo[i] & 0xffff;
@@ -162,62 +259,63 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[G::TI][G::TI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G::TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < G::TI; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   const int wm = wid >> 1, wn = wid & 1;
   const int fr = lane & 31, fk = lane >> 5;  // fragment row / k-half of this lane
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  bf16x8 fa0[G::TI], fb0[G::TI], fa1[G::TI], fb1[G::TI];
   auto rd = [&](const uint8_t *stage, int ks, bf16x8 *fa, bf16x8 *fb) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * 128 + t * 32 + fr, ks * 2 + fk));
-      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + A_BYTES +
-                                                swz(wn * 128 + t * 32 + fr, ks * 2 + fk));
+    for (int t = 0; t < G::TI; ++t) {
+      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * G::WT + t * 32 + fr, ks * 2 + fk));
+      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + G::HALF +
+                                                swz(wn * G::WT + t * 32 + fr, ks * 2 + fk));
     }
   };
   auto mma = [&](const bf16x8 *fa, const bf16x8 *fb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < G::TI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
   // One K step of 32: the loads of step kt+3 are issued into the stage freed
   // by step kt-1; the second 16-wide slice is read while the first multiplies;
   // the barrier (step kt+1 landed everywhere, step kt fully read) sits before
-  // the last 16 MFMAs so the next step's first fragments arrive under them.
+  // the last MFMAs so the next step's first fragments arrive under them.
+  constexpr int NM = G::TI * G::TI;  // MFMAs per 16-wide K slice
   auto step = [&](int kt, const uint8_t *cur, const uint8_t *nxt, uint8_t *fut) {
     issue(kt + 3, fut);
     rd(cur, 1, fa1, fb1);
     mma(fa0, fb0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 2 * G::TI; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global -> LDS load
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    VLB_STAGE_BARRIER();
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * G::TI, 0);
+    stage_barrier<BMT>();
     rd(nxt, 0, fa0, fb0);
     mma(fa1, fb1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 2 * G::TI; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * G::TI, 0);
   };
 
   issue(0, smem0);
   issue(1, smem1);
   issue(2, smem2);
-  VLB_STAGE_BARRIER();  // step 0 landed
+  stage_barrier<BMT>();  // step 0 landed
   rd(smem0, 0, fa0, fb0);
   for (int kt = 0; kt < KT; kt += NSTAGE) {  // KT rounds up: the extra steps are all-zero
     step(kt, smem0, smem1, smem3);
@@ -225,58 +323,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     step(kt + 2, smem2, smem3, smem1);
     step(kt + 3, smem3, smem0, smem2);
   }
-
-  // Epilogue.  The weight fragment is the MFMA's first operand, so acc[i][j]
-  // holds the transposed product: lane (fr, fk) owns token row
-  // wm*128 + 32 i + fr and features wn*128 + 32 j + 8 a + 4 fk + e in element
-  // 4 a + e (a, e < 4).  Bias and activation are applied in fp32, the tile is
-  // rounded to bf16 and staged in LDS (64 rows per stage buffer; 512-byte rows
-  // of 16-byte chunks XOR-swizzled by the row), then written out whole rows at
-  // a time with 16-byte stores.
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
-  auto bufs = [&](int b) -> uint8_t * {
-    return b == 0 ? smem0 : b == 1 ? smem1 : b == 2 ? smem2 : smem3;
-  };
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int cl = wn * 128 + j * 32 + 8 * a + 4 * fk;  // 4 consecutive features
-      const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
-      const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
-                          bf2f(bb.y >> 16)};
-      const int chunk = cl >> 3;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (i & 1) * 32 + fr;  // inside buffer wm*2 + i/2
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][4 * a + e] + b[e]));
-        uint2 v;
-        v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
-        v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-        *reinterpret_cast<uint2 *>(bufs(wm * 2 + (i >> 1)) + row * 512 +
-                                   ((chunk ^ (row & 31)) << 4) + fk * 8) = v;
-      }
-    }
-  }
-  __syncthreads();
-  uint16_t *out = static_cast<uint16_t *>(g.out);
-  const int chunk = tid & 31;
-  const int col = n0 + chunk * 8;
-#pragma unroll
-  for (int bi = 0; bi < NSTAGE; ++bi) {
-#pragma unroll 4
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const int row = (tid >> 5) + 8 * s8;  // inside buffer bi
-      const int dst = s_dst[bi * 64 + row];  // -1: past the last row, or not placed
-      if (dst < 0 || col >= g.N) continue;
-      const uint4 v =
-          *reinterpret_cast<const uint4 *>(bufs(bi) + row * 512 + ((chunk ^ (row & 31)) << 4));
-      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
-    }
-  }
+  store_tile<ACT, BMT>(acc, g, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
 }
+
+template <bool GATHER, int ACT>
+void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
+  if (blocks256 > 0)
+    hipLaunchKernelGGL((k_gemm_bf16<GATHER, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
+  if (blocks128 > 0)
+    hipLaunchKernelGGL((k_gemm_bf16<GATHER, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const TilePlan tp = tile_plan(g.M, g.N);
+  g.tiles_m = tp.tiles_m;
+  g.tiles_n = tp.tiles_n;
+  g.n_full = tp.n_full;
+  if (!gather && g.act != 2) return hipErrorInvalidValue;  // the second Linear has no activation
+  if (gather && g.act == 0)
+    launch_bf16<true, 0>(g, tp.n_full, tp.blocks128, s);
+  else if (gather && g.act == 1)
+    launch_bf16<true, 1>(g, tp.n_full, tp.blocks128, s);
+  else if (gather)
+    launch_bf16<true, 2>(g, tp.n_full, tp.blocks128, s);
+  else
+    launch_bf16<false, 2>(g, tp.n_full, tp.blocks128, s);
+  return hipGetLastError();
+}
+
+namespace {
 
 // ---------------------------------------------------------------------------
 // fp32 path: 64x64 tile, 16 K per stage, 4x4 outputs per thread, plain FMA.
@@ -349,24 +428,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 }
 
 }  // namespace
-
-hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  g.tiles_m = (g.M + BM - 1) / BM;
-  g.tiles_n = (g.N + BN - 1) / BN;
-  const dim3 grid(g.tiles_m * g.tiles_n);
-  if (gather && g.act == 0)
-    hipLaunchKernelGGL((k_gemm_bf16<true, 0>), grid, dim3(NTHREADS), 0, s, g);
-  else if (gather && g.act == 1)
-    hipLaunchKernelGGL((k_gemm_bf16<true, 1>), grid, dim3(NTHREADS), 0, s, g);
-  else if (gather)
-    hipLaunchKernelGGL((k_gemm_bf16<true, 2>), grid, dim3(NTHREADS), 0, s, g);
-  else if (g.act == 2)
-    hipLaunchKernelGGL((k_gemm_bf16<false, 2>), grid, dim3(NTHREADS), 0, s, g);
-  else
-    return hipErrorInvalidValue;  // the second Linear has no activation
-  return hipGetLastError();
-}
 
 hipError_t launch_gemm_f32(bool gather, GemmArgs g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;

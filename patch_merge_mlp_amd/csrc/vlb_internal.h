@@ -58,7 +58,42 @@ struct GemmArgs {
   int32_t act;            // vlb_act
   int32_t tiles_m, tiles_n;
   uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31): loads past it read 0
+  // bf16 path: tiles [0, n_full) of the 256-grid are computed as 256x256
+  // tiles, the rest as 128x128 tiles (see tile_plan).
+  int32_t n_full;
 };
+
+// Tile plan of the bf16 GEMM.  256x256 tiles keep the MFMAs busiest, but on
+// 256 compute units a last round that is at most half full wastes most of a
+// round; those tiles are computed as four 128x128 tiles each instead, so the
+// last round fills the chip.  Problems with fewer than 128 big tiles use
+// 128x128 tiles throughout.
+constexpr int kGemmBK = 32;         // K per pipeline step
+constexpr int kGemmStages = 4;      // pipeline stages
+constexpr int kPlanCUs = 256;       // compute units of MI355X
+struct TilePlan {
+  int32_t tiles_m, tiles_n;  // 256-grid
+  int32_t n_full;            // 256x256 tiles (one workgroup each)
+  int32_t blocks128;         // 128x128 tiles (one workgroup each)
+};
+inline TilePlan tile_plan(int64_t M, int64_t N) {
+  TilePlan tp{};
+  tp.tiles_m = static_cast<int32_t>((M + 255) / 256);
+  tp.tiles_n = static_cast<int32_t>((N + 255) / 256);
+  const int32_t tiles = tp.tiles_m * tp.tiles_n;
+  const int32_t rem = tiles % kPlanCUs;
+  if (tiles < kPlanCUs / 2) {
+    tp.n_full = 0;
+    tp.blocks128 = static_cast<int32_t>(((M + 127) / 128) * ((N + 127) / 128));
+  } else if (rem > 0 && rem <= kPlanCUs / 2) {
+    tp.n_full = tiles - rem;
+    tp.blocks128 = 4 * rem;
+  } else {
+    tp.n_full = tiles;
+    tp.blocks128 = 0;
+  }
+  return tp;
+}
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------
 hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
