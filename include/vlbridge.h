@@ -87,16 +87,17 @@ typedef struct {
   int32_t has_ln;    /* 1: LayerNorm over C before the merge */
   float ln_eps;      /* LayerNorm epsilon */
   int32_t act;       /* vlb_act */
-  int32_t w1_packed; /* 1: weights.w1 was produced by vlb_pack_weights (VLB_BF16 only) */
+  int32_t packed;    /* 1: weights.w1 / weights.w2 are the packed forms made by
+                        vlb_pack_weights (VLB_BF16 only) */
 } vlb_projector;
 
 /* Weights in PyTorch Linear layout (out_features, in_features), as stored and
  * used as-is [VL2 Weight loading]. */
 typedef struct {
   const void *ln_gamma, *ln_beta; /* [C] each, or NULL when has_ln == 0 */
-  const void *w1;                 /* [hidden][C*k*k]; or the packed form */
+  const void *w1;                 /* [hidden][C*k*k]; or its packed form */
   const void *b1;                 /* [hidden] */
-  const void *w2;                 /* [out_dim][hidden] */
+  const void *w2;                 /* [out_dim][hidden]; or its packed form */
   const void *b2;                 /* [out_dim] */
 } vlb_weights;
 
@@ -132,12 +133,21 @@ size_t vlb_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t s
 
 /* ---- entry points (asynchronous on stream) ---------------------------- */
 
-/* One-time re-layout of W1 [hidden][C*k*k] (feature index c*k*k + p) into the
- * packed form [hidden][k*k*C] (index p*C + c) that lets the first GEMM read
- * each patch's channels contiguously.  Only the summation order of the first
- * Linear changes.  w1_packed must not alias w1.  VLB_BF16 only. */
-vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, void *w1_packed,
-                            void *stream);
+/* Bytes of the packed form of W1 (which = 1) or W2 (which = 2); 0 on invalid
+ * input or for VLB_F32 (which has no packed form). */
+size_t vlb_packed_bytes(const vlb_projector *p, int32_t which);
+
+/* One-time re-layout of the weights into the GEMMs' tile-blocked forms
+ * (VLB_BF16 only).  Packed W is [ceil(N/256)][K/32][256][32]: for every
+ * 256-row block of outputs and every 32-wide K slice, the block's 256 rows of
+ * that slice are one contiguous 16 KiB run (rows past N are zero).  For W1 the
+ * K axis is also reordered position-major (index p*C + c instead of the
+ * pages' c*k*k + p) so a K slice is contiguous channels of one pixel; only the
+ * summation order of the first Linear changes.  w1 [hidden][C*k*k] and w2
+ * [out_dim][hidden] are read; w1_packed / w2_packed (vlb_packed_bytes each)
+ * are written and must not overlap the inputs. */
+vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, const void *w2,
+                            void *w1_packed, void *w2_packed, void *stream);
 
 /* LN (if enabled) -> pad -> space-to-depth, materialised: merged[T][C*k*k] in
  * the pages' feature order c*k*k + dy*k + dx [VL2 Projector 1-2], [VOIE
@@ -192,7 +202,7 @@ enum {
   VLB_K_GEMM2 = 5,   /* Linear2 + bias + row/slot store */
   VLB_K_SCATTER = 6, /* standalone row scatter */
   VLB_K_MERGE = 7,   /* standalone space-to-depth */
-  VLB_K_PACK = 8,    /* W1 re-layout */
+  VLB_K_PACK = 8,    /* weight re-layout */
   VLB_K_COUNT = 9
 };
 

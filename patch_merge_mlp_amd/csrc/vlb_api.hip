@@ -33,7 +33,7 @@ struct Plan {
   std::vector<int32_t> img_view0;      // [n_images]
   // workspace carving (bytes)
   size_t off_status = 0, off_dst = 0, off_desc = 0, off_xn = 0, off_h = 0, off_w1p = 0,
-         off_slot = 0, total = 0;
+         off_w2p = 0, off_slot = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -53,9 +53,12 @@ vlb_status check_projector(const vlb_projector *p) {
   if (p->has_ln != 0 && p->has_ln != 1) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && !(p->ln_eps > 0.f)) return VLB_ERR_SHAPE;
   if (p->has_ln && p->C > vlb::layernorm_max_channels(p->dtype)) return VLB_ERR_UNSUPPORTED;
-  if (p->w1_packed && p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (p->packed && p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
   const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
-  if (K1 * p->hidden > kI32Max || static_cast<int64_t>(p->hidden) * p->out_dim > kI32Max)
+  // 32-bit byte offsets address the weights (bf16: padded and tile-blocked)
+  const int64_t es = p->dtype == VLB_BF16 ? 2 : 4;
+  if (vlb::blocked_elems(p->hidden, K1) * es > kI32Max ||
+      vlb::blocked_elems(p->out_dim, p->hidden) * es > kI32Max)
     return VLB_ERR_SHAPE;
   return VLB_OK;
 }
@@ -123,9 +126,7 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   if (pl->T * std::max<int64_t>(p->hidden, p->out_dim) > kI32Max) return VLB_ERR_SHAPE;
   if (seq_len * p->out_dim > kI32Max) return VLB_ERR_SHAPE;
   // The GEMMs address their operands with 32-bit byte offsets (buffer loads).
-  if (pl->npix * p->C * pl->es > kI32Max || pl->T * p->hidden * pl->es > kI32Max ||
-      pl->K1 * p->hidden * pl->es > kI32Max ||
-      static_cast<int64_t>(p->hidden) * p->out_dim * pl->es > kI32Max)
+  if (pl->npix * p->C * pl->es > kI32Max || vlb::blocked_elems(pl->T, p->hidden) * pl->es > kI32Max)
     return VLB_ERR_SHAPE;
 
   size_t off = 0;
@@ -137,11 +138,17 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   off = align256(off + static_cast<size_t>(pl->T) * sizeof(RowDesc));
   pl->off_xn = off;
   if (p->has_ln) off = align256(off + static_cast<size_t>(pl->npix) * p->C * pl->es);
-  pl->off_h = off;
-  off = align256(off + static_cast<size_t>(pl->T) * p->hidden * pl->es);
-  pl->off_w1p = off;
-  if (p->dtype == VLB_BF16 && !p->w1_packed)
-    off = align256(off + static_cast<size_t>(pl->K1) * p->hidden * pl->es);
+  pl->off_h = off;  // hidden activation: tile-blocked (bf16) or row-major (fp32)
+  if (p->dtype == VLB_BF16)
+    off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, p->hidden)) * pl->es);
+  else
+    off = align256(off + static_cast<size_t>(pl->T) * p->hidden * pl->es);
+  pl->off_w1p = off;  // weights packed per call when they are not pre-packed
+  if (p->dtype == VLB_BF16 && !p->packed) {
+    off = align256(off + static_cast<size_t>(vlb::blocked_elems(p->hidden, pl->K1)) * 2);
+    pl->off_w2p = off;
+    off = align256(off + static_cast<size_t>(vlb::blocked_elems(p->out_dim, p->hidden)) * 2);
+  }
   pl->off_slot = off;
   off = align256(off + static_cast<size_t>(seq_len) * 4);
   pl->total = off;
@@ -251,13 +258,20 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   g2.a_bytes = static_cast<uint32_t>(pl.T * p->hidden * pl.es);
   g2.b_bytes = static_cast<uint32_t>(static_cast<int64_t>(p->out_dim) * p->hidden * pl.es);
   if (p->dtype == VLB_BF16) {
-    const void *w1p = w->w1;
-    if (!p->w1_packed) {
-      void *tmp = ws + pl.off_w1p;
-      VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w->w1, p->hidden, p->C, p->k, tmp, s));
-      w1p = tmp;
+    const void *w1p = w->w1, *w2p = w->w2;
+    if (!p->packed) {
+      VLB_LAUNCH(VLB_K_PACK, s,
+                 vlb::launch_pack(w->w1, p->hidden, pl.K1, p->C, p->k, ws + pl.off_w1p, s));
+      VLB_LAUNCH(VLB_K_PACK, s,
+                 vlb::launch_pack(w->w2, p->out_dim, p->hidden, p->C, 1, ws + pl.off_w2p, s));
+      w1p = ws + pl.off_w1p;
+      w2p = ws + pl.off_w2p;
     }
     g1.B = w1p;
+    g1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->hidden, pl.K1) * 2);
+    g2.B = w2p;
+    g2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->out_dim, p->hidden) * 2);
+    g2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, p->hidden) * 2);
     VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_bf16(true, g1, s));
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(false, g2, s));
   } else {
@@ -356,16 +370,36 @@ size_t vlb_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t s
   return make_plan(p, b, seq_len, &pl) == VLB_OK ? pl.total : 0;
 }
 
-vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, void *w1_packed,
-                            void *stream) {
+size_t vlb_packed_bytes(const vlb_projector *p, int32_t which) {
+  if (check_projector(p) != VLB_OK || p->dtype != VLB_BF16) return 0;
+  const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
+  if (which == 1) return static_cast<size_t>(vlb::blocked_elems(p->hidden, K1)) * 2;
+  if (which == 2) return static_cast<size_t>(vlb::blocked_elems(p->out_dim, p->hidden)) * 2;
+  return 0;
+}
+
+vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, const void *w2,
+                            void *w1_packed, void *w2_packed, void *stream) {
   vlb_status st = check_projector(p);
   if (st != VLB_OK) return st;
   if (p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
-  if (!w1 || !w1_packed) return VLB_ERR_NULL;
-  if (!aligned16(w1) || !aligned16(w1_packed)) return VLB_ERR_ALIGN;
-  if (w1 == w1_packed) return VLB_ERR_UNSUPPORTED;
+  if (!w1 || !w2 || !w1_packed || !w2_packed) return VLB_ERR_NULL;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1_packed) || !aligned16(w2_packed))
+    return VLB_ERR_ALIGN;
+  const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
+  auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
+    const uint8_t *x = static_cast<const uint8_t *>(a), *y = static_cast<const uint8_t *>(b);
+    return x < y + nb && y < x + na;
+  };
+  const size_t n1 = static_cast<size_t>(p->hidden) * K1 * 2, n2 = static_cast<size_t>(p->out_dim) * p->hidden * 2;
+  const size_t m1 = vlb_packed_bytes(p, 1), m2 = vlb_packed_bytes(p, 2);
+  if (overlap(w1_packed, m1, w1, n1) || overlap(w1_packed, m1, w2, n2) ||
+      overlap(w2_packed, m2, w1, n1) || overlap(w2_packed, m2, w2, n2) ||
+      overlap(w1_packed, m1, w2_packed, m2))
+    return VLB_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w1, p->hidden, p->C, p->k, w1_packed, s));
+  VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w1, p->hidden, K1, p->C, p->k, w1_packed, s));
+  VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w2, p->out_dim, p->hidden, p->C, 1, w2_packed, s));
   return VLB_OK;
 }
 

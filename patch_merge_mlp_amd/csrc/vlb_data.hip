@@ -312,16 +312,35 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const T *x, const RowDe
 }
 
 // ---------------------------------------------------------------------------
-// W1 re-layout: w1p[n][p*C + c] = w1[n][c*k*k + p].
-__global__ void k_pack(const uint16_t *w1, int64_t hidden, int C, int k, uint16_t *w1p) {
+// Weight packing into the tile-blocked layout; with k > 1 the K axis of W1 is
+// reordered position-major on the way.  One thread per 16-byte packed chunk.
+__global__ void k_pack(const uint16_t *w, int64_t R, int64_t K, int C, int k, uint16_t *out) {
   const int kk = k * k;
-  const int64_t K1 = static_cast<int64_t>(C) * kk;
-  const int64_t total = hidden * K1;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t n = e / K1, j = e - n * K1;
-    const int64_t p = j / C, c = j - p * C;
-    w1p[e] = w1[n * K1 + c * kk + p];
+  const int64_t KB = K / 32;
+  const int64_t nchunks = (R + 255) / 256 * 256 * K / 8;
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < nchunks;
+       q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = q * 8;                 // packed element index
+    const int64_t cc = e % 32, rr = (e / 32) % 256, blk = e / (32 * 256);
+    const int64_t rb = blk / KB, kb = blk % KB;
+    const int64_t r = rb * 256 + rr;
+    uint16_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t j = kb * 32 + cc + i;    // packed column
+      int64_t src = j;
+      if (kk > 1) {
+        const int64_t p = j / C, c = j - p * C;
+        src = c * kk + p;
+      }
+      v[i] = r < R ? w[r * K + src] : static_cast<uint16_t>(0);
+    }
+    uint4 o;
+    o.x = v[0] | (static_cast<uint32_t>(v[1]) << 16);
+    o.y = v[2] | (static_cast<uint32_t>(v[3]) << 16);
+    o.z = v[4] | (static_cast<uint32_t>(v[5]) << 16);
+    o.w = v[6] | (static_cast<uint32_t>(v[7]) << 16);
+    reinterpret_cast<uint4 *>(out)[q] = o;
   }
 }
 
@@ -434,11 +453,12 @@ hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const void *w1, int64_t hidden, int C, int k, void *w1p, hipStream_t s) {
-  const int64_t total = hidden * C * k * k;
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack, dim3(grid_for(total, 256, 65536)), dim3(256), 0, s,
-                     static_cast<const uint16_t *>(w1), hidden, C, k, static_cast<uint16_t *>(w1p));
+hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *packed,
+                       hipStream_t s) {
+  const int64_t nchunks = blocked_elems(R, K) / 8;
+  if (nchunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack, dim3(grid_for(nchunks, 256, 65536)), dim3(256), 0, s,
+                     static_cast<const uint16_t *>(w), R, K, C, k, static_cast<uint16_t *>(packed));
   return hipGetLastError();
 }
 

@@ -112,11 +112,11 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *ds
 // of 16-byte chunks XOR-swizzled by the row), then written out whole rows at a
 // time with 16-byte stores to row s_dst[r] (skipped when negative).  The
 // caller has synchronised the workgroup after its last use of the buffers.
-template <int ACT, int BMT>
+template <int ACT, int BMT, bool BLOCKED_OUT>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
-                                           const GemmArgs &g, int n0, uint8_t *b0, uint8_t *b1,
-                                           uint8_t *b2, uint8_t *b3, const uint16_t *s_bias,
-                                           const int32_t *s_dst) {
+                                           const GemmArgs &g, int m0, int n0, uint8_t *b0,
+                                           uint8_t *b1, uint8_t *b2, uint8_t *b3,
+                                           const uint16_t *s_bias, const int32_t *s_dst) {
   using G = Geo<BMT>;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -148,6 +148,26 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Geo<BMT>::TI][Geo
   }
   __syncthreads();
   uint16_t *out = static_cast<uint16_t *>(g.out);
+  if constexpr (BLOCKED_OUT) {
+    // Tile-blocked output (the hidden activation): for each 32-wide feature
+    // slice of the tile, rows' 64-byte segments are contiguous, so 4 lanes
+    // write one row segment and a wave 16 rows -- 1 KiB per store.
+    const uint32_t KBo = g.N / 32;
+#pragma unroll 4
+    for (int q = tid; q < BMT * BMT / 8; q += NTHREADS) {
+      const int fs = q / (BMT * 4), rem = q % (BMT * 4);
+      const int row = rem >> 2, c4 = rem & 3;  // tile row, chunk in the slice
+      const int m = m0 + row, f = n0 + fs * 32 + c4 * 8;
+      if (m >= g.M || f >= g.N) continue;
+      const int chunk = fs * 4 + c4, rb = row & 63;
+      const uint4 v = *reinterpret_cast<const uint4 *>(bufs(row >> 6) + rb * G::ROWB +
+                                                       ((chunk ^ (rb & (G::CCH - 1))) << 4));
+      const int64_t e =
+          ((static_cast<int64_t>(m >> 8) * KBo + (f >> 5)) * 256 + (m & 255)) * 32 + (f & 31);
+      *reinterpret_cast<uint4 *>(out + e) = v;
+    }
+    return;
+  }
   const int chunk = tid % G::CCH;
   const int col = n0 + chunk * 8;
   constexpr int RSTEP = NTHREADS / G::CCH;  // rows per pass
@@ -178,7 +198,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[BMT];  // this tile's bias
   __shared__ int32_t s_dst[BMT];                                 // destination row per tile row
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in an SGPR
   int tm, tn;
   if (BMT == 256) {
     tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
@@ -208,6 +229,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   // Loader role: wave `wid` fills rows [wid*BMT/4, (wid+1)*BMT/4) of both
   // stage halves, 16 rows (1 KiB) per instruction.  Lane l lands on row
   // 16i + l/4 at physical chunk l%4, which holds logical chunk (l%4) ^ swz_xor(row).
+  // B (packed weights) and, for Linear2, A (the hidden activation) are
+  // tile-blocked: the 256 rows of a 32-wide K slice of a row block are one
+  // contiguous 16 KiB run, so step kt of row r sits at
+  // ((r/256 * K/32 + kt) * 256 + r%256) * 64 bytes.
+  const uint32_t KB = g.K / BK;
+  auto blocked = [&](int r) {
+    return (static_cast<uint32_t>(r >> 8) * KB * 256 + static_cast<uint32_t>(r & 255)) * 64;
+  };
   int32_t a_pix[G::LPW], a_geo[G::LPW];
   uint32_t a_off[G::LPW], b_off[G::LPW], c_off[G::LPW];
 #pragma unroll
@@ -224,9 +253,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
       a_off[i] = 0;
     } else {
       a_pix[i] = a_geo[i] = 0;
-      a_off[i] = m < g.M ? static_cast<uint32_t>(m) * g.K * 2 + c_off[i] : kOOB;
+      a_off[i] = m < g.M ? blocked(m) + c_off[i] : kOOB;
     }
-    b_off[i] = n < g.N ? static_cast<uint32_t>(n) * g.K * 2 + c_off[i] : kOOB;
+    b_off[i] = n < g.N ? blocked(n) + c_off[i] : kOOB;
   }
 
   // Loads of K step kt into `stage`.  Steps at or past the end of K read zeros
@@ -252,10 +281,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
         const uint32_t pad = ((a_geo[i] >> (16 + p)) & 1) ? 0u : kOOB;
         ao = (static_cast<uint32_t>((a_pix[i] + dy * gw + dx) * g.C + c0) * 2 + c_off[i]) | pad;
       } else {
-        ao = a_off[i] + kk * 2;
+        ao = a_off[i] + kt * (256 * 64);
       }
       load_lds16(rA, sa + i * 1024, ao | dead);
-      load_lds16(rB, sb + i * 1024, (b_off[i] + kk * 2) | dead);
+      load_lds16(rB, sb + i * 1024, (b_off[i] + kt * (256 * 64)) | dead);
     }
   };
 
@@ -324,7 +353,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     step(kt + 3, smem3, smem0, smem2);
   }
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
-  store_tile<ACT, BMT>(acc, g, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  store_tile<ACT, BMT, GATHER>(acc, g, m0, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
 }
 
 template <bool GATHER, int ACT>

@@ -44,8 +44,11 @@ enum { kStatusWord = 0, kCountWord = 1 };
 
 // ---- GEMM arguments -------------------------------------------------------
 // out[dst(m)][n] = act(sum_k A[m][k] * B[n][k] + bias[n]) for m < M, n < N.
-// A is either row-major [M][K] (lda = K) or gathered through RowDesc from the
-// channels-last patch grid with K ordered position-major (k' = p*C + c).
+// bf16 path: B is tile-blocked (packed weights).  Linear1 (gather mode) takes
+// A through RowDesc from the channels-last patch grid with K ordered
+// position-major (k' = p*C + c) and writes its output tile-blocked; Linear2
+// takes that blocked A and writes plain rows to dst(m).  fp32 path: plain
+// row-major A and B, K of W1 in the pages' order.
 struct GemmArgs {
   const void *A;          // activations, or the (normalised) patch grid
   const RowDesc *desc;    // gather descriptors (gather mode only)
@@ -112,7 +115,16 @@ hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const i
                           void *seq, hipStream_t s);
 hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T, int C, int k,
                         void *merged, hipStream_t s);
-hipError_t launch_pack(const void *w1, int64_t hidden, int C, int k, void *w1p, hipStream_t s);
+// Tile-blocked operand layout of the bf16 GEMMs: a [R][K] bf16 matrix is kept
+// as [ceil(R/256)][K/32][256][32], i.e. element (r, c) at
+// ((r/256 * K/32 + c/32) * 256 + r%256) * 32 + c%32, so the 256 rows of one
+// 32-wide K slice of a row block are one contiguous 16 KiB run.  Rows past R
+// are zero (weights) or unused (the hidden activation).
+inline int64_t blocked_elems(int64_t R, int64_t K) { return (R + 255) / 256 * 256 * K; }
+// Packs w [R][K] into the blocked layout.  With k > 1 (W1) the K axis is also
+// reordered position-major: packed column j = p*C + c takes w[r][c*k*k + p].
+hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *packed,
+                       hipStream_t s);
 
 // bf16 MFMA GEMMs.  gemm1: gather-mode A, B = packed W1.  gemm2: row-major A.
 hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s);

@@ -36,7 +36,7 @@ class VlbError(RuntimeError):
 class vlb_projector(ct.Structure):
     _fields_ = [("dtype", ct.c_int32), ("C", ct.c_int32), ("k", ct.c_int32),
                 ("hidden", ct.c_int32), ("out_dim", ct.c_int32), ("has_ln", ct.c_int32),
-                ("ln_eps", ct.c_float), ("act", ct.c_int32), ("w1_packed", ct.c_int32)]
+                ("ln_eps", ct.c_float), ("act", ct.c_int32), ("packed", ct.c_int32)]
 
 
 class vlb_weights(ct.Structure):
@@ -73,7 +73,8 @@ def lib():
             "vlb_num_slots": (i64, [pp, pb]),
             "vlb_image_slots": (i64, [pp, pb, ct.POINTER(ct.c_int64)]),
             "vlb_workspace_bytes": (sz, [pp, pb, i64]),
-            "vlb_pack_weights": (st, [pp, vp, vp, vp]),
+            "vlb_packed_bytes": (sz, [pp, ct.c_int32]),
+            "vlb_pack_weights": (st, [pp, vp, vp, vp, vp, vp]),
             "vlb_merge_tokens": (st, [pp, pb, vp, vp, vp, vp, vp, sz, vp]),
             "vlb_merge_project": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, sz, vp]),
             "vlb_scatter_tokens": (st, [pp, pb, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
@@ -102,8 +103,8 @@ def _check(status: int, where: str):
 
 
 def projector(dtype: int, C: int, k: int, hidden: int, out_dim: int, has_ln: bool = False,
-              ln_eps: float = 1e-6, act: int = GELU_ERF, w1_packed: bool = False) -> vlb_projector:
-    return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(w1_packed))
+              ln_eps: float = 1e-6, act: int = GELU_ERF, packed: bool = False) -> vlb_projector:
+    return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(packed))
 
 
 class Batch:
@@ -210,19 +211,33 @@ def workspace(p: vlb_projector, b: Batch, seq_len: int, device="cuda") -> torch.
 
 # ---- entry points -----------------------------------------------------------
 
-def vlb_pack_weights(p: vlb_projector, w1: torch.Tensor, w1_packed: torch.Tensor, stream=None):
-    n = p.hidden * p.C * p.k * p.k
-    _need(w1, n, _tdtype(p), "w1")
-    _need(w1_packed, n, _tdtype(p), "w1_packed")
-    _check(lib().vlb_pack_weights(ct.byref(p), _ptr(w1), _ptr(w1_packed), _stream(stream)),
-           "vlb_pack_weights")
+def vlb_packed_bytes(p: vlb_projector, which: int) -> int:
+    return int(lib().vlb_packed_bytes(ct.byref(p), which))
+
+
+def vlb_pack_weights(p: vlb_projector, w1: torch.Tensor, w2: torch.Tensor,
+                     w1_packed: torch.Tensor, w2_packed: torch.Tensor, stream=None):
+    dt = _tdtype(p)
+    _need(w1, p.hidden * p.C * p.k * p.k, dt, "w1")
+    _need(w2, p.out_dim * p.hidden, dt, "w2")
+    for t, which, what in ((w1_packed, 1, "w1_packed"), (w2_packed, 2, "w2_packed")):
+        n = vlb_packed_bytes(p, which)
+        if n == 0:
+            raise VlbError(ERR_UNSUPPORTED, "vlb_packed_bytes")
+        _need(t, n // 2, dt, what)
+    _check(lib().vlb_pack_weights(ct.byref(p), _ptr(w1), _ptr(w2), _ptr(w1_packed),
+                                  _ptr(w2_packed), _stream(stream)), "vlb_pack_weights")
 
 
 def _check_weights(p, w: Weights):
     dt = _tdtype(p)
-    _need(w.w1, p.hidden * p.C * p.k * p.k, dt, "w1")
+    if p.packed:
+        _need(w.w1, vlb_packed_bytes(p, 1) // 2, dt, "w1 (packed)")
+        _need(w.w2, vlb_packed_bytes(p, 2) // 2, dt, "w2 (packed)")
+    else:
+        _need(w.w1, p.hidden * p.C * p.k * p.k, dt, "w1")
+        _need(w.w2, p.out_dim * p.hidden, dt, "w2")
     _need(w.b1, p.hidden, dt, "b1")
-    _need(w.w2, p.out_dim * p.hidden, dt, "w2")
     _need(w.b2, p.out_dim, dt, "b2")
     _need(w.ln_gamma, p.C, dt, "ln_gamma")
     _need(w.ln_beta, p.C, dt, "ln_beta")
@@ -302,17 +317,19 @@ def vlb_prof_read(kid: int):
 
 
 class Bridge:
-    """A projector with its weights resident on the device (W1 packed once for bf16),
-    plus a cached workspace."""
+    """A projector with its weights resident on the device (bf16: both weights packed
+    once into the GEMMs' tile-blocked form), plus a cached workspace."""
 
     def __init__(self, p: vlb_projector, w: Weights, pack: bool = True):
         self.w = w
-        if p.dtype == BF16 and pack and not p.w1_packed:
-            w1p = torch.empty_like(w.w1)
-            vlb_pack_weights(p, w.w1, w1p)
-            self.w = Weights(w1p, w.b1, w.w2, w.b2, w.ln_gamma, w.ln_beta)
+        if p.dtype == BF16 and pack and not p.packed:
+            dev = w.w1.device
+            w1p = torch.empty(vlb_packed_bytes(p, 1) // 2, dtype=w.w1.dtype, device=dev)
+            w2p = torch.empty(vlb_packed_bytes(p, 2) // 2, dtype=w.w2.dtype, device=dev)
+            vlb_pack_weights(p, w.w1, w.w2, w1p, w2p)
+            self.w = Weights(w1p, w.b1, w2p, w.b2, w.ln_gamma, w.ln_beta)
             p = vlb_projector.from_buffer_copy(p)
-            p.w1_packed = 1
+            p.packed = 1
         self.p = p
         self._ws = None
 

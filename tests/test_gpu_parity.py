@@ -5,7 +5,7 @@
     Frobenius error <= 1e-2 in bf16, <= 1e-5 in fp32), every other row of the
     sequence bit for bit;
   * the five full-size workloads in the benchmark's launch configuration
-    (packed W1, fused call): sampled rows against the oracle, every text row
+    (packed weights, fused call): sampled rows against the oracle, every text row
     bit for bit, and -- with 0/1 selection weights and no activation -- every
     placeholder slot bit for bit against the oracle's merge, assembly and
     scatter;

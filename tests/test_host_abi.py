@@ -83,7 +83,7 @@ def _proj(**kw):
     (dict(dtype=7), v.ERR_DTYPE), (dict(C=0), v.ERR_SHAPE), (dict(C=12), v.ERR_UNSUPPORTED),
     (dict(C=72), v.ERR_UNSUPPORTED), (dict(hidden=100), v.ERR_UNSUPPORTED),
     (dict(act=5), v.ERR_UNSUPPORTED), (dict(has_ln=True, ln_eps=0.0), v.ERR_SHAPE),
-    (dict(dtype=v.F32, w1_packed=True), v.ERR_UNSUPPORTED),
+    (dict(dtype=v.F32, packed=True), v.ERR_UNSUPPORTED),
 ])
 def test_bad_projector(kw, status):
     p = _proj(**kw)
@@ -136,15 +136,38 @@ def test_entry_points_validate_before_launching():
     bt = v.Batch([(4, 4)] * 2, [2], v.LAYOUT_TILED_2D, [(1, 1)])
     assert L.vlb_scatter_tokens(ct.byref(p), ct.byref(bt.c), FAKE, None, FAKE, FAKE, 64, FAKE, FAKE,
                                 1 << 30, None) == v.ERR_NULL  # tiled needs the newline
-    assert L.vlb_pack_weights(ct.byref(p), FAKE, FAKE, None) == v.ERR_UNSUPPORTED  # aliasing
+    # pack: overlaps between any packed output and any input or the other output
+    G = 1 << 24  # well apart
+    for w1, w2, p1, p2 in [(FAKE, FAKE + G, FAKE, FAKE + 2 * G),          # w1_packed on w1
+                           (FAKE, FAKE + G, FAKE + 2 * G, FAKE + G + 4096),  # w2_packed in w2
+                           (FAKE, FAKE + G, FAKE + G - 4096, FAKE + 2 * G),  # w1_packed runs into w2
+                           (FAKE, FAKE + G, FAKE + 2 * G, FAKE + 2 * G + 16)]:  # outputs overlap
+        assert L.vlb_pack_weights(ct.byref(p), w1, w2, p1, p2, None) == v.ERR_UNSUPPORTED
+    assert L.vlb_pack_weights(ct.byref(p), FAKE, None, FAKE + G, FAKE + 2 * G, None) == v.ERR_NULL
+    assert L.vlb_pack_weights(ct.byref(p), FAKE, FAKE + G, FAKE + 2 * G + 8, FAKE + 3 * G,
+                              None) == v.ERR_ALIGN
     pf = _proj(dtype=v.F32)
-    assert L.vlb_pack_weights(ct.byref(pf), FAKE, FAKE + 16, None) == v.ERR_UNSUPPORTED
+    assert L.vlb_pack_weights(ct.byref(pf), FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G,
+                              None) == v.ERR_UNSUPPORTED
     assert L.vlb_merge_project(None, ct.byref(b.c), FAKE, ct.byref(w), FAKE, FAKE, need,
                                None) == v.ERR_NULL
     # text only: a successful no-op
     e = v.Batch([], [])
     assert L.vlb_bridge_fused(ct.byref(p), ct.byref(e.c), None, None, None, None, None, 0, None,
                               None, 0, None) == v.OK
+
+
+def test_packed_bytes():
+    """Tile-blocked weights: rows padded to a multiple of 256, K unchanged."""
+    p = _proj()  # C=64, k=2 -> K1=256; hidden=128; out_dim=64
+    assert v.vlb_packed_bytes(p, 1) == 256 * 256 * 2
+    assert v.vlb_packed_bytes(p, 2) == 256 * 128 * 2
+    big = _proj(C=1152, hidden=4608, out_dim=4096)
+    assert v.vlb_packed_bytes(big, 1) == 4608 * 4608 * 2
+    assert v.vlb_packed_bytes(big, 2) == 4096 * 4608 * 2
+    assert v.vlb_packed_bytes(p, 0) == 0 and v.vlb_packed_bytes(p, 3) == 0
+    assert v.vlb_packed_bytes(_proj(dtype=v.F32), 1) == 0
+    assert v.vlb_packed_bytes(_proj(k=9), 1) == 0
 
 
 def test_status_strings():
