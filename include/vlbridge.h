@@ -37,7 +37,8 @@
  *    each view's tokens row-major over its merged grid [VL2 Projector, Output].
  *  - Alignment: every device pointer must be 16-byte aligned.
  *  - Supported shapes: k in {1, 2, 3}; C, hidden and out_dim multiples of 8
- *    (VLB_BF16 additionally: C and hidden multiples of 64).
+ *    (VLB_BF16 additionally: C and hidden multiples of 64, C <= 4096); with
+ *    LayerNorm, C <= 2048 for VLB_F32.
  */
 #ifndef VLBRIDGE_H
 #define VLBRIDGE_H

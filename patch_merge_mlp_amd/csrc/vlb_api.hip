@@ -52,7 +52,9 @@ vlb_status check_projector(const vlb_projector *p) {
   if (p->act < VLB_GELU_ERF || p->act > VLB_ACT_NONE) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln != 0 && p->has_ln != 1) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && !(p->ln_eps > 0.f)) return VLB_ERR_SHAPE;
-  if (p->has_ln && p->C > vlb::layernorm_max_channels(p->dtype)) return VLB_ERR_UNSUPPORTED;
+  // LayerNorm holds a pixel in registers; the bf16 merge stages 16 of them in LDS
+  if ((p->has_ln || p->dtype == VLB_BF16) && p->C > vlb::layernorm_max_channels(p->dtype))
+    return VLB_ERR_UNSUPPORTED;
   if (p->packed && p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
   const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
   // 32-bit byte offsets address the weights (bf16: padded and tile-blocked)
@@ -126,7 +128,8 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   if (pl->T * std::max<int64_t>(p->hidden, p->out_dim) > kI32Max) return VLB_ERR_SHAPE;
   if (seq_len * p->out_dim > kI32Max) return VLB_ERR_SHAPE;
   // The GEMMs address their operands with 32-bit byte offsets (buffer loads).
-  if (pl->npix * p->C * pl->es > kI32Max || vlb::blocked_elems(pl->T, p->hidden) * pl->es > kI32Max)
+  if (pl->npix * p->C * pl->es > kI32Max || vlb::blocked_elems(pl->T, p->hidden) * pl->es > kI32Max ||
+      vlb::blocked_elems(pl->T, pl->K1) * pl->es > kI32Max)
     return VLB_ERR_SHAPE;
 
   size_t off = 0;
@@ -136,8 +139,11 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   off = align256(off + static_cast<size_t>(pl->T) * 4);
   pl->off_desc = off;
   off = align256(off + static_cast<size_t>(pl->T) * sizeof(RowDesc));
-  pl->off_xn = off;
-  if (p->has_ln) off = align256(off + static_cast<size_t>(pl->npix) * p->C * pl->es);
+  pl->off_xn = off;  // bf16: merged tokens, tile-blocked; fp32: the normalised grid
+  if (p->dtype == VLB_BF16)
+    off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, pl->K1)) * 2);
+  else if (p->has_ln)
+    off = align256(off + static_cast<size_t>(pl->npix) * p->C * pl->es);
   pl->off_h = off;  // hidden activation: tile-blocked (bf16) or row-major (fp32)
   if (p->dtype == VLB_BF16)
     off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, p->hidden)) * pl->es);
@@ -221,7 +227,14 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   vlb_status st = run_plan(p, b, pl, desc, s);
   if (st != VLB_OK) return st;
   const void *x = features;
-  if (p->has_ln) {
+  if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
+    void *xm = ws + pl.off_xn;
+    VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
+               vlb::launch_merge_blocked(features, desc, pl.T, p->C, p->k,
+                                         p->has_ln ? w->ln_gamma : nullptr,
+                                         p->has_ln ? w->ln_beta : nullptr, p->ln_eps, xm, s));
+    x = xm;
+  } else if (p->has_ln) {
     void *xn = ws + pl.off_xn;
     VLB_LAUNCH(VLB_K_LN, s,
                vlb::launch_layernorm(p->dtype, features, pl.npix, p->C, w->ln_gamma, w->ln_beta,
@@ -271,6 +284,7 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
     g1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->hidden, pl.K1) * 2);
     g2.B = w2p;
     g2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->out_dim, p->hidden) * 2);
+    g1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, pl.K1) * 2);
     g2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, p->hidden) * 2);
     VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_bf16(true, g1, s));
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(false, g2, s));

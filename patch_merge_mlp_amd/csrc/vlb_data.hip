@@ -241,6 +241,115 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 }
 
 // ---------------------------------------------------------------------------
+// Space-to-depth into the first GEMM's tile-blocked operand (bf16), with the
+// LayerNorm fused when LN is set.  Merged row m, position p = dy*k + dx holds
+// pixel (y0 + dy, x0 + dx) of the token's k x k block (zeros where the block
+// hangs over the grid's high edge), at columns p*C .. p*C + C - 1: the K axis
+// is position-major, as in the packed W1.  Element (m, j) of the [T][C*k*k]
+// result sits at ((m/256 * K/32 + j/32) * 256 + m%256) * 32 + j%32.
+// A workgroup takes one item: 16 consecutive tokens at one position.  Each
+// wave loads 4 of the 16 pixels at once (NCH 16-byte chunks per lane per
+// pixel), normalises them and stages the rows in LDS; then, per 32-wide K
+// slice, the 16 rows' 64-byte pieces -- one contiguous KiB of the output --
+// go out as one store instruction of a wave.
+constexpr int kMbRows = 16;                 // tokens per item
+constexpr int kMbPix = kMbRows / 4;         // pixels per wave
+
+template <bool LN, int NCH>
+__global__ __launch_bounds__(256) void k_merge_blocked(const uint16_t *x, const RowDesc *desc,
+                                                       int32_t T, int C, int k,
+                                                       const uint16_t *gamma,
+                                                       const uint16_t *beta, float eps,
+                                                       uint16_t *out) {
+  extern __shared__ uint4 mb_lds[];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int kk = k * k, nch = C / 8;
+  const int rs = nch + 1;  // LDS row stride in 16-byte chunks (odd: rows hit distinct banks)
+  const int64_t KB = static_cast<int64_t>(C) * kk / 32;
+  uint4 gv[LN ? NCH : 1], bv[LN ? NCH : 1];
+  if constexpr (LN) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      gv[i] = q < nch ? reinterpret_cast<const uint4 *>(gamma)[q] : make_uint4(0, 0, 0, 0);
+      bv[i] = q < nch ? reinterpret_cast<const uint4 *>(beta)[q] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const int ngrp = (T + kMbRows - 1) / kMbRows;
+  for (int item = blockIdx.x; item < ngrp * kk; item += gridDim.x) {
+    const int grp = item / kk, p = item - grp * kk;
+    const int dy = p / k, dx = p - dy * k;
+    uint4 v[kMbPix][NCH];
+    bool inside[kMbPix];
+#pragma unroll
+    for (int t = 0; t < kMbPix; ++t) {  // all four pixels' loads in flight together
+      const int m = grp * kMbRows + wid + 4 * t;
+      RowDesc d = {0, 0};
+      if (m < T) d = desc[m];
+      inside[t] = (d.geo >> (16 + p)) & 1;  // false past the last token
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          x + static_cast<int64_t>(d.pix + dy * (d.geo & 0xffff) + dx) * C);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int q = lane + 64 * i;
+        v[t][i] = (inside[t] && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMbPix; ++t) {
+      if (LN && inside[t]) {  // wave-uniform
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[t][i]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
+        }
+        const float mean = wave_sum(sum) / C;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          if (lane + 64 * i < nch) {
+            const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[t][i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float dlt = bf2f(e[j]) - mean;
+              ss += dlt * dlt;
+            }
+          }
+        }
+        const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          uint16_t *e = reinterpret_cast<uint16_t *>(&v[t][i]);
+          const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gv[i]);
+          const uint16_t *be = reinterpret_cast<const uint16_t *>(&bv[i]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            e[j] = f2bf((bf2f(e[j]) - mean) * rstd * bf2f(ge[j]) + bf2f(be[j]));
+        }
+      }
+      uint4 *row = mb_lds + (wid + 4 * t) * rs;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        if (lane + 64 * i < nch) row[lane + 64 * i] = v[t][i];
+    }
+    __syncthreads();
+    // Per K slice: lane -> (row lane/4, chunk lane%4); rows past T are not written.
+    const int r = lane >> 2, c4 = lane & 3;
+    const int m = grp * kMbRows + r;
+    uint16_t *dst = out + (static_cast<int64_t>(m >> 8) * KB * 256 + (m & 255)) * 32 + c4 * 8;
+    const int slices = C / 32, sl0 = p * slices;
+    for (int sl = wid; sl < slices; sl += 4) {
+      const uint4 val = mb_lds[r * rs + sl * 4 + c4];
+      if (m < T)
+        *reinterpret_cast<uint4 *>(dst + static_cast<int64_t>(sl0 + sl) * (256 * 32)) = val;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone scatter: row r of rows[T][D] -> seq[dst_row[r]] (skipped if < 0).
 template <typename T>
 __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, int D,
@@ -423,6 +532,48 @@ hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const
 }
 
 int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 : 8); }
+
+template <bool LN, int NCH>
+static hipError_t mb_launch(const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                            const void *gamma, const void *beta, float eps, void *out,
+                            hipStream_t s) {
+  const int64_t items = (T + kMbRows - 1) / kMbRows * k * k;
+  const size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16;  // <= 131 KiB
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_merge_blocked<LN, NCH>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_merge_blocked<LN, NCH>), dim3(grid_for(items, 1, 1 << 20)), dim3(256), lds,
+                     s, static_cast<const uint16_t *>(x), desc, static_cast<int32_t>(T), C, k,
+                     static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
+                     eps, static_cast<uint16_t *>(out));
+  return hipGetLastError();
+}
+
+template <bool LN>
+static hipError_t mb_dispatch(const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                              const void *gamma, const void *beta, float eps, void *out,
+                              hipStream_t s) {
+  switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane per pixel
+    case 1: return mb_launch<LN, 1>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 2: return mb_launch<LN, 2>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 3: return mb_launch<LN, 3>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 4: return mb_launch<LN, 4>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 5: case 6: return mb_launch<LN, 6>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 7: case 8: return mb_launch<LN, kLnChunks>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_merge_blocked(const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                                const void *gamma, const void *beta, float eps, void *out,
+                                hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  return gamma ? mb_dispatch<true>(x, desc, T, C, k, gamma, beta, eps, out, s)
+               : mb_dispatch<false>(x, desc, T, C, k, nullptr, nullptr, 0.f, out, s);
+}
 
 hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const int32_t *dst_row,
                           void *seq, hipStream_t s) {

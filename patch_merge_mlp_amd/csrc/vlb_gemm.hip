@@ -1,18 +1,19 @@
 // GEMM kernels of the bridge projector: Linear(C*k*k -> hidden) + bias + GELU
-// fed by the space-to-depth gather, and Linear(hidden -> out) + bias whose
-// epilogue writes each row to its destination (a row of the output, or its
-// placeholder slot in the sequence).  mlxcel issue #533 "port DeepSeek-VL2",
-// section "Projector (downsample_mlp_gelu)" steps 1-3.
+// over the merged tokens, and Linear(hidden -> out) + bias whose epilogue
+// writes each row to its destination (a row of the output, or its placeholder
+// slot in the sequence).  mlxcel issue #533 "port DeepSeek-VL2", section
+// "Projector (downsample_mlp_gelu)" steps 1-3.
 //
 // bf16 path (gfx950): 256x256 output tile per 256-thread workgroup, 4 waves in
 // a 2x2 grid, each wave 128x128 from 4x4 v_mfma_f32_32x32x16_bf16 tiles with
-// fp32 accumulation.  K advances 64 per stage through two LDS stages of
-// 64 KiB (A and B, 128-byte rows, 16-byte chunks XOR-swizzled by row); the
-// next stage's global loads are in flight while the current one is consumed.
-// In gather mode the A rows come straight from the channels-last patch grid:
-// with K ordered position-major (k' = p*C + c, the packed W1) every 64-wide K
-// slice is 64 contiguous channels of one pixel, so each row of an A stage is
-// one 128-byte load -- the merged tensor is never materialised.
+// fp32 accumulation; the last, partly filled round of tiles runs as 128x128
+// tiles.  K advances 32 per stage through four LDS stages (A and B halves,
+// 64-byte rows of 16-byte chunks XOR-swizzled by row), filled by
+// direct-to-LDS buffer loads three stages ahead of the MFMAs.  Every operand
+// is tile-blocked ([R/256][K/32][256][32]), so each load instruction of a
+// wave moves one contiguous KiB.  Linear1 takes the merged tokens (K ordered
+// position-major, k' = p*C + c, like the packed W1) and writes the hidden
+// activation tile-blocked; Linear2 reads it and stores plain rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -189,7 +190,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Geo<BMT>::TI][Geo
 // tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
 // quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
 // whole 128-grid).
-template <bool GATHER, int ACT, int BMT>
+template <bool LINEAR1, int ACT, int BMT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   using G = Geo<BMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -229,62 +230,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   // Loader role: wave `wid` fills rows [wid*BMT/4, (wid+1)*BMT/4) of both
   // stage halves, 16 rows (1 KiB) per instruction.  Lane l lands on row
   // 16i + l/4 at physical chunk l%4, which holds logical chunk (l%4) ^ swz_xor(row).
-  // B (packed weights) and, for Linear2, A (the hidden activation) are
-  // tile-blocked: the 256 rows of a 32-wide K slice of a row block are one
-  // contiguous 16 KiB run, so step kt of row r sits at
+  // Both operands are tile-blocked (the 256 rows of a 32-wide K slice of a
+  // row block are one contiguous 16 KiB run), so step kt of row r sits at
   // ((r/256 * K/32 + kt) * 256 + r%256) * 64 bytes.
   const uint32_t KB = g.K / BK;
   auto blocked = [&](int r) {
     return (static_cast<uint32_t>(r >> 8) * KB * 256 + static_cast<uint32_t>(r & 255)) * 64;
   };
-  int32_t a_pix[G::LPW], a_geo[G::LPW];
-  uint32_t a_off[G::LPW], b_off[G::LPW], c_off[G::LPW];
+  uint32_t a_off[G::LPW], b_off[G::LPW];
 #pragma unroll
   for (int i = 0; i < G::LPW; ++i) {
     const int row = wid * (BMT / 4) + 16 * i + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz_xor(row);
-    c_off[i] = chunk * 16;
+    const uint32_t c_off = ((lane & 3) ^ swz_xor(row)) * 16;
     const int m = m0 + row, n = n0 + row;
-    if (GATHER) {
-      RowDesc d = {0, 0};
-      if (m < g.M) d = g.desc[m];
-      a_pix[i] = d.pix;
-      a_geo[i] = d.geo;  // 0 past the last row: every position reads as padding
-      a_off[i] = 0;
-    } else {
-      a_pix[i] = a_geo[i] = 0;
-      a_off[i] = m < g.M ? blocked(m) + c_off[i] : kOOB;
-    }
-    b_off[i] = n < g.N ? blocked(n) + c_off[i] : kOOB;
+    a_off[i] = m < g.M ? blocked(m) + c_off : kOOB;
+    b_off[i] = n < g.N ? blocked(n) + c_off : kOOB;
   }
 
   // Loads of K step kt into `stage`.  Steps at or past the end of K read zeros
   // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
   const int KT = g.K / BK;
   auto issue = [&](int kt, uint8_t *stage) {
-    const int kk = kt * BK;
     const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
+    const uint32_t step_off = kt * (256 * 64);
     uint8_t *sa = stage + wid * G::LPW * 1024;
     uint8_t *sb = stage + G::HALF + wid * G::LPW * 1024;
-    int p = 0, c0 = 0, dy = 0, dx = 0;
-    if (GATHER) {
-      p = kk / g.C;
-      c0 = kk - p * g.C;
-      dy = p / g.k;
-      dx = p - dy * g.k;
-    }
 #pragma unroll
     for (int i = 0; i < G::LPW; ++i) {
-      uint32_t ao;
-      if (GATHER) {
-        const int gw = a_geo[i] & 0xffff;
-        const uint32_t pad = ((a_geo[i] >> (16 + p)) & 1) ? 0u : kOOB;
-        ao = (static_cast<uint32_t>((a_pix[i] + dy * gw + dx) * g.C + c0) * 2 + c_off[i]) | pad;
-      } else {
-        ao = a_off[i] + kt * (256 * 64);
-      }
-      load_lds16(rA, sa + i * 1024, ao | dead);
-      load_lds16(rB, sb + i * 1024, (b_off[i] + kt * (256 * 64)) | dead);
+      load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
+      load_lds16(rB, sb + i * 1024, (b_off[i] + step_off) | dead);
     }
   };
 
@@ -353,31 +327,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     step(kt + 3, smem3, smem0, smem2);
   }
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
-  store_tile<ACT, BMT, GATHER>(acc, g, m0, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  store_tile<ACT, BMT, LINEAR1>(acc, g, m0, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
 }
 
-template <bool GATHER, int ACT>
+template <bool LINEAR1, int ACT>
 void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
   if (blocks256 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<GATHER, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_bf16<LINEAR1, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
   if (blocks128 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<GATHER, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_bf16<LINEAR1, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s) {
+hipError_t launch_gemm_bf16(bool linear1, GemmArgs g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const TilePlan tp = tile_plan(g.M, g.N);
   g.tiles_m = tp.tiles_m;
   g.tiles_n = tp.tiles_n;
   g.n_full = tp.n_full;
-  if (!gather && g.act != 2) return hipErrorInvalidValue;  // the second Linear has no activation
-  if (gather && g.act == 0)
+  if (!linear1 && g.act != 2) return hipErrorInvalidValue;  // the second Linear has no activation
+  if (linear1 && g.act == 0)
     launch_bf16<true, 0>(g, tp.n_full, tp.blocks128, s);
-  else if (gather && g.act == 1)
+  else if (linear1 && g.act == 1)
     launch_bf16<true, 1>(g, tp.n_full, tp.blocks128, s);
-  else if (gather)
+  else if (linear1)
     launch_bf16<true, 2>(g, tp.n_full, tp.blocks128, s);
   else
     launch_bf16<false, 2>(g, tp.n_full, tp.blocks128, s);

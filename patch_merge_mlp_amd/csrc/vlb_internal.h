@@ -44,20 +44,20 @@ enum { kStatusWord = 0, kCountWord = 1 };
 
 // ---- GEMM arguments -------------------------------------------------------
 // out[dst(m)][n] = act(sum_k A[m][k] * B[n][k] + bias[n]) for m < M, n < N.
-// bf16 path: B is tile-blocked (packed weights).  Linear1 (gather mode) takes
-// A through RowDesc from the channels-last patch grid with K ordered
-// position-major (k' = p*C + c) and writes its output tile-blocked; Linear2
-// takes that blocked A and writes plain rows to dst(m).  fp32 path: plain
-// row-major A and B, K of W1 in the pages' order.
+// bf16 path: A and B are tile-blocked (see blocked_elems).  Linear1 takes the
+// merged tokens with K ordered position-major (k' = p*C + c) and the packed
+// W1, and writes its output tile-blocked; Linear2 takes that blocked A and
+// writes plain rows to dst(m).  fp32 path: plain row-major B; Linear1 gathers
+// A through RowDesc from the patch grid with K of W1 in the pages' order.
 struct GemmArgs {
-  const void *A;          // activations, or the (normalised) patch grid
-  const RowDesc *desc;    // gather descriptors (gather mode only)
-  const void *B;          // [N][K] row-major
+  const void *A;          // activations, or the (normalised) patch grid (fp32 gather)
+  const RowDesc *desc;    // gather descriptors (fp32 gather mode only)
+  const void *B;          // weights
   const void *bias;       // [N]
   void *out;              // output rows
   const int32_t *dst_row; // nullptr: row m -> out + m*ldo; else dst_row[m] (< 0: skipped)
   int32_t M, N, K, ldo;
-  int32_t C, k;           // gather mode: channels and merge factor
+  int32_t C, k;           // fp32 gather mode: channels and merge factor
   int32_t act;            // vlb_act
   int32_t tiles_m, tiles_n;
   uint32_t a_bytes, b_bytes;  // extent of A and B in bytes (< 2^31): loads past it read 0
@@ -125,9 +125,16 @@ inline int64_t blocked_elems(int64_t R, int64_t K) { return (R + 255) / 256 * 25
 // reordered position-major: packed column j = p*C + c takes w[r][c*k*k + p].
 hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *packed,
                        hipStream_t s);
+// Space-to-depth of the (bf16) patch grid into the blocked [T][C*k*k] operand
+// of Linear1, K position-major, zeros for cells past the grid; LayerNorm over
+// C applied on the way when gamma is non-null (C <= layernorm_max_channels).
+hipError_t launch_merge_blocked(const void *x, const RowDesc *desc, int64_t T, int C, int k,
+                                const void *gamma, const void *beta, float eps, void *out,
+                                hipStream_t s);
 
-// bf16 MFMA GEMMs.  gemm1: gather-mode A, B = packed W1.  gemm2: row-major A.
-hipError_t launch_gemm_bf16(bool gather, GemmArgs g, hipStream_t s);
+// bf16 MFMA GEMMs on blocked operands.  linear1: act epilogue, blocked output.
+// Otherwise: no activation, plain rows to dst(m).
+hipError_t launch_gemm_bf16(bool linear1, GemmArgs g, hipStream_t s);
 // fp32 GEMMs (FMA).  In gather mode K follows the pages' order c*k*k + p and B
 // is the unpacked W1.
 hipError_t launch_gemm_f32(bool gather, GemmArgs g, hipStream_t s);

@@ -82,6 +82,7 @@ def _proj(**kw):
     (dict(k=4), v.ERR_UNSUPPORTED), (dict(k=0), v.ERR_UNSUPPORTED),
     (dict(dtype=7), v.ERR_DTYPE), (dict(C=0), v.ERR_SHAPE), (dict(C=12), v.ERR_UNSUPPORTED),
     (dict(C=72), v.ERR_UNSUPPORTED), (dict(hidden=100), v.ERR_UNSUPPORTED),
+    (dict(C=4160), v.ERR_UNSUPPORTED), (dict(dtype=v.F32, C=2056, has_ln=True), v.ERR_UNSUPPORTED),
     (dict(act=5), v.ERR_UNSUPPORTED), (dict(has_ln=True, ln_eps=0.0), v.ERR_SHAPE),
     (dict(dtype=v.F32, packed=True), v.ERR_UNSUPPORTED),
 ])
