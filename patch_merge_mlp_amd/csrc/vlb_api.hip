@@ -199,22 +199,26 @@ void prof_end(int idx, hipStream_t s) {
     if (_e != hipSuccess) return VLB_ERR_HIP;         \
   } while (0)
 
+// The planner table of views [v0, v0 + kPlanViews) (clipped to the batch).
+PlanChunk view_chunk(const vlb_projector *p, const vlb_batch *b, const Plan &pl, int v0) {
+  PlanChunk c{};
+  c.n = std::min(vlb::kPlanViews, b->n_views - v0);
+  c.k = p->k;
+  for (int i = 0; i < c.n; ++i) {
+    c.tok0[i] = pl.view_tok0[v0 + i];
+    c.pix0[i] = pl.view_pix0[v0 + i];
+    c.gh[i] = static_cast<int16_t>(b->grid_h[v0 + i]);
+    c.gw[i] = static_cast<int16_t>(b->grid_w[v0 + i]);
+  }
+  c.tok0[c.n] = pl.view_tok0[v0 + c.n];
+  return c;
+}
+
 // Per-token gather descriptors, one launch per kPlanViews views.
 vlb_status run_plan(const vlb_projector *p, const vlb_batch *b, const Plan &pl, RowDesc *desc,
                     hipStream_t s) {
-  for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews) {
-    PlanChunk c{};
-    c.n = std::min(vlb::kPlanViews, b->n_views - v0);
-    c.k = p->k;
-    for (int i = 0; i < c.n; ++i) {
-      c.tok0[i] = pl.view_tok0[v0 + i];
-      c.pix0[i] = pl.view_pix0[v0 + i];
-      c.gh[i] = static_cast<int16_t>(b->grid_h[v0 + i]);
-      c.gw[i] = static_cast<int16_t>(b->grid_w[v0 + i]);
-    }
-    c.tok0[c.n] = pl.view_tok0[v0 + c.n];
-    VLB_LAUNCH(VLB_K_PLAN, s, vlb::launch_plan(c, desc, s));
-  }
+  for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
+    VLB_LAUNCH(VLB_K_PLAN, s, vlb::launch_plan(view_chunk(p, b, pl, v0), desc, s));
   return VLB_OK;
 }
 
@@ -224,22 +228,25 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
                        const void *features, const vlb_weights *w, void *out,
                        const int32_t *dst_row, uint8_t *ws, hipStream_t s) {
   RowDesc *desc = reinterpret_cast<RowDesc *>(ws + pl.off_desc);
-  vlb_status st = run_plan(p, b, pl, desc, s);
-  if (st != VLB_OK) return st;
   const void *x = features;
   if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
     void *xm = ws + pl.off_xn;
-    VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
-               vlb::launch_merge_blocked(features, desc, pl.T, p->C, p->k,
-                                         p->has_ln ? w->ln_gamma : nullptr,
-                                         p->has_ln ? w->ln_beta : nullptr, p->ln_eps, xm, s));
+    for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
+      VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
+                 vlb::launch_merge_blocked(features, view_chunk(p, b, pl, v0), p->C,
+                                           p->has_ln ? w->ln_gamma : nullptr,
+                                           p->has_ln ? w->ln_beta : nullptr, p->ln_eps, xm, s));
     x = xm;
-  } else if (p->has_ln) {
-    void *xn = ws + pl.off_xn;
-    VLB_LAUNCH(VLB_K_LN, s,
-               vlb::launch_layernorm(p->dtype, features, pl.npix, p->C, w->ln_gamma, w->ln_beta,
-                                     p->ln_eps, xn, s));
-    x = xn;
+  } else {
+    vlb_status st = run_plan(p, b, pl, desc, s);
+    if (st != VLB_OK) return st;
+    if (p->has_ln) {
+      void *xn = ws + pl.off_xn;
+      VLB_LAUNCH(VLB_K_LN, s,
+                 vlb::launch_layernorm(p->dtype, features, pl.npix, p->C, w->ln_gamma,
+                                       w->ln_beta, p->ln_eps, xn, s));
+      x = xn;
+    }
   }
   void *hbuf = ws + pl.off_h;
   vlb::GemmArgs g1{};

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "vlb_common.h"
 #include "vlb_internal.h"
 
@@ -247,106 +249,111 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // hangs over the grid's high edge), at columns p*C .. p*C + C - 1: the K axis
 // is position-major, as in the packed W1.  Element (m, j) of the [T][C*k*k]
 // result sits at ((m/256 * K/32 + j/32) * 256 + m%256) * 32 + j%32.
-// A workgroup takes one item: 16 consecutive tokens at one position.  Each
-// wave loads 4 of the 16 pixels at once (NCH 16-byte chunks per lane per
-// pixel), normalises them and stages the rows in LDS; then, per 32-wide K
-// slice, the 16 rows' 64-byte pieces -- one contiguous KiB of the output --
-// go out as one store instruction of a wave.
-constexpr int kMbRows = 16;                 // tokens per item
-constexpr int kMbPix = kMbRows / 4;         // pixels per wave
+//
+// One launch covers the token rows of a chunk of up to 64 views; lane v of
+// every wave keeps view v's table entry, so a row's view is found with one
+// ballot.  A workgroup of 16 waves takes one item: 16 consecutive rows
+// (aligned to 16, so they share a 256-row block) at one position.  Wave r
+// loads row r's pixel (NCH 16-byte chunks per lane), normalises it and stages
+// it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
+// contiguous KiB of the output -- go out as one store instruction of a wave.
+constexpr int kMbRows = 16;  // rows per item = waves per workgroup
 
 template <bool LN, int NCH>
-__global__ __launch_bounds__(256) void k_merge_blocked(const uint16_t *x, const RowDesc *desc,
-                                                       int32_t T, int C, int k,
-                                                       const uint16_t *gamma,
-                                                       const uint16_t *beta, float eps,
-                                                       uint16_t *out) {
+__global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *x, PlanChunk c,
+                                                                int C, const uint16_t *gamma,
+                                                                const uint16_t *beta, float eps,
+                                                                uint16_t *out) {
   extern __shared__ uint4 mb_lds[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int kk = k * k, nch = C / 8;
+  const int k = c.k, kk = k * k, nch = C / 8;
   const int rs = nch + 1;  // LDS row stride in 16-byte chunks (odd: rows hit distinct banks)
   const int64_t KB = static_cast<int64_t>(C) * kk / 32;
-  uint4 gv[LN ? NCH : 1], bv[LN ? NCH : 1];
-  if constexpr (LN) {
+  const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
+  const int g0 = t_begin / kMbRows;
+  const int grp = g0 + blockIdx.x / kk, p = blockIdx.x % kk;
+  const int dy = p / k, dx = p - dy * k;
+
+  // This wave's row and its pixel (wave-uniform): the view is the number of
+  // views starting at or before the row, less one.  Lane l reads view l's
+  // entry with a vector load and the wave picks entry v with a shuffle; the
+  // table is never indexed with the uniform v directly (a scalar load from a
+  // computed kernel-argument address must be dword-aligned at its base, which
+  // the 16-bit entries do not guarantee).
+  const int m = grp * kMbRows + wid;
+  bool inside = false;
+  int64_t off = 0;
+  if (m >= t_begin && m < t_end) {
+    const bool have = lane < c.n;
+    const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
+    const int32_t l_pix0 = have ? c.pix0[lane] : 0;
+    const int32_t l_gh = have ? c.gh[lane] : 0, l_gw = have ? c.gw[lane] : 1;
+    const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
+    const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
+    const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
+    const int wp = (gw + k - 1) / k, t = m - tok0;
+    const int y = (t / wp) * k + dy, xx = (t % wp) * k + dx;
+    inside = y < gh && xx < gw;
+    off = static_cast<int64_t>(pix0 + y * gw + xx) * C;
+  }
+  uint4 v[NCH];
+  const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int q = lane + 64 * i;
+    v[i] = (inside && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
+  }
+  if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
+    }
+    const float mean = wave_sum(sum) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (lane + 64 * i < nch) {
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float dlt = bf2f(e[j]) - mean;
+          ss += dlt * dlt;
+        }
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
-      gv[i] = q < nch ? reinterpret_cast<const uint4 *>(gamma)[q] : make_uint4(0, 0, 0, 0);
-      bv[i] = q < nch ? reinterpret_cast<const uint4 *>(beta)[q] : make_uint4(0, 0, 0, 0);
-    }
-  }
-  const int ngrp = (T + kMbRows - 1) / kMbRows;
-  for (int item = blockIdx.x; item < ngrp * kk; item += gridDim.x) {
-    const int grp = item / kk, p = item - grp * kk;
-    const int dy = p / k, dx = p - dy * k;
-    uint4 v[kMbPix][NCH];
-    bool inside[kMbPix];
+      if (q < nch) {
+        const uint4 gq = reinterpret_cast<const uint4 *>(gamma)[q];
+        const uint4 bq = reinterpret_cast<const uint4 *>(beta)[q];
+        uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
+        const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+        const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
 #pragma unroll
-    for (int t = 0; t < kMbPix; ++t) {  // all four pixels' loads in flight together
-      const int m = grp * kMbRows + wid + 4 * t;
-      RowDesc d = {0, 0};
-      if (m < T) d = desc[m];
-      inside[t] = (d.geo >> (16 + p)) & 1;  // false past the last token
-      const uint4 *src = reinterpret_cast<const uint4 *>(
-          x + static_cast<int64_t>(d.pix + dy * (d.geo & 0xffff) + dx) * C);
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int q = lane + 64 * i;
-        v[t][i] = (inside[t] && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < 8; ++j)
+          e[j] = f2bf((bf2f(e[j]) - mean) * rstd * bf2f(ge[j]) + bf2f(be[j]));
       }
     }
-#pragma unroll
-    for (int t = 0; t < kMbPix; ++t) {
-      if (LN && inside[t]) {  // wave-uniform
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[t][i]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
-        }
-        const float mean = wave_sum(sum) / C;
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          if (lane + 64 * i < nch) {
-            const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[t][i]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float dlt = bf2f(e[j]) - mean;
-              ss += dlt * dlt;
-            }
-          }
-        }
-        const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          uint16_t *e = reinterpret_cast<uint16_t *>(&v[t][i]);
-          const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gv[i]);
-          const uint16_t *be = reinterpret_cast<const uint16_t *>(&bv[i]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            e[j] = f2bf((bf2f(e[j]) - mean) * rstd * bf2f(ge[j]) + bf2f(be[j]));
-        }
-      }
-      uint4 *row = mb_lds + (wid + 4 * t) * rs;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i)
-        if (lane + 64 * i < nch) row[lane + 64 * i] = v[t][i];
-    }
-    __syncthreads();
-    // Per K slice: lane -> (row lane/4, chunk lane%4); rows past T are not written.
-    const int r = lane >> 2, c4 = lane & 3;
-    const int m = grp * kMbRows + r;
-    uint16_t *dst = out + (static_cast<int64_t>(m >> 8) * KB * 256 + (m & 255)) * 32 + c4 * 8;
-    const int slices = C / 32, sl0 = p * slices;
-    for (int sl = wid; sl < slices; sl += 4) {
-      const uint4 val = mb_lds[r * rs + sl * 4 + c4];
-      if (m < T)
-        *reinterpret_cast<uint4 *>(dst + static_cast<int64_t>(sl0 + sl) * (256 * 32)) = val;
-    }
-    __syncthreads();
   }
+  uint4 *row = mb_lds + wid * rs;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+    if (lane + 64 * i < nch) row[lane + 64 * i] = v[i];
+  __syncthreads();
+  // Per K slice: lane -> (row lane/4, chunk lane%4); only this chunk's rows are written.
+  const int r = lane >> 2, c4 = lane & 3;
+  const int mr = grp * kMbRows + r;
+  if (mr < t_begin || mr >= t_end) return;
+  uint16_t *dst = out + (static_cast<int64_t>(mr >> 8) * KB * 256 + (mr & 255)) * 32 + c4 * 8;
+  const int slices = C / 32, sl0 = p * slices;
+  for (int sl = wid; sl < slices; sl += kMbRows)
+    *reinterpret_cast<uint4 *>(dst + static_cast<int64_t>(sl0 + sl) * (256 * 32)) =
+        mb_lds[r * rs + sl * 4 + c4];
 }
 
 // ---------------------------------------------------------------------------
@@ -534,10 +541,10 @@ hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const
 int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 : 8); }
 
 template <bool LN, int NCH>
-static hipError_t mb_launch(const void *x, const RowDesc *desc, int64_t T, int C, int k,
-                            const void *gamma, const void *beta, float eps, void *out,
-                            hipStream_t s) {
-  const int64_t items = (T + kMbRows - 1) / kMbRows * k * k;
+static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void *gamma,
+                            const void *beta, float eps, void *out, hipStream_t s) {
+  const int64_t items =
+      ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k;
   const size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16;  // <= 131 KiB
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(
@@ -545,34 +552,32 @@ static hipError_t mb_launch(const void *x, const RowDesc *desc, int64_t T, int C
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_merge_blocked<LN, NCH>), dim3(grid_for(items, 1, 1 << 20)), dim3(256), lds,
-                     s, static_cast<const uint16_t *>(x), desc, static_cast<int32_t>(T), C, k,
+  hipLaunchKernelGGL((k_merge_blocked<LN, NCH>), dim3(static_cast<uint32_t>(items)),
+                     dim3(64 * kMbRows), lds, s, static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
                      eps, static_cast<uint16_t *>(out));
   return hipGetLastError();
 }
 
 template <bool LN>
-static hipError_t mb_dispatch(const void *x, const RowDesc *desc, int64_t T, int C, int k,
-                              const void *gamma, const void *beta, float eps, void *out,
-                              hipStream_t s) {
+static hipError_t mb_dispatch(const void *x, const PlanChunk &c, int C, const void *gamma,
+                              const void *beta, float eps, void *out, hipStream_t s) {
   switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane per pixel
-    case 1: return mb_launch<LN, 1>(x, desc, T, C, k, gamma, beta, eps, out, s);
-    case 2: return mb_launch<LN, 2>(x, desc, T, C, k, gamma, beta, eps, out, s);
-    case 3: return mb_launch<LN, 3>(x, desc, T, C, k, gamma, beta, eps, out, s);
-    case 4: return mb_launch<LN, 4>(x, desc, T, C, k, gamma, beta, eps, out, s);
-    case 5: case 6: return mb_launch<LN, 6>(x, desc, T, C, k, gamma, beta, eps, out, s);
-    case 7: case 8: return mb_launch<LN, kLnChunks>(x, desc, T, C, k, gamma, beta, eps, out, s);
+    case 1: return mb_launch<LN, 1>(x, c, C, gamma, beta, eps, out, s);
+    case 2: return mb_launch<LN, 2>(x, c, C, gamma, beta, eps, out, s);
+    case 3: return mb_launch<LN, 3>(x, c, C, gamma, beta, eps, out, s);
+    case 4: return mb_launch<LN, 4>(x, c, C, gamma, beta, eps, out, s);
+    case 5: case 6: return mb_launch<LN, 6>(x, c, C, gamma, beta, eps, out, s);
+    case 7: case 8: return mb_launch<LN, kLnChunks>(x, c, C, gamma, beta, eps, out, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_merge_blocked(const void *x, const RowDesc *desc, int64_t T, int C, int k,
-                                const void *gamma, const void *beta, float eps, void *out,
-                                hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  return gamma ? mb_dispatch<true>(x, desc, T, C, k, gamma, beta, eps, out, s)
-               : mb_dispatch<false>(x, desc, T, C, k, nullptr, nullptr, 0.f, out, s);
+hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const void *gamma,
+                                const void *beta, float eps, void *out, hipStream_t s) {
+  if (c.n <= 0 || c.tok0[c.n] <= c.tok0[0]) return hipSuccess;
+  return gamma ? mb_dispatch<true>(x, c, C, gamma, beta, eps, out, s)
+               : mb_dispatch<false>(x, c, C, nullptr, nullptr, 0.f, out, s);
 }
 
 hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const int32_t *dst_row,

@@ -18,7 +18,8 @@ struct RowDesc {
   int32_t geo;
 };
 
-// Views handled by one launch of the descriptor kernel (kernel-argument table).
+// Views handled by one launch of the descriptor or blocked-merge kernel
+// (kernel-argument table; one view per lane of a wave in the latter).
 constexpr int kPlanViews = 64;
 struct PlanChunk {
   int32_t n;                     // views in this chunk
@@ -126,11 +127,11 @@ inline int64_t blocked_elems(int64_t R, int64_t K) { return (R + 255) / 256 * 25
 hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *packed,
                        hipStream_t s);
 // Space-to-depth of the (bf16) patch grid into the blocked [T][C*k*k] operand
-// of Linear1, K position-major, zeros for cells past the grid; LayerNorm over
-// C applied on the way when gamma is non-null (C <= layernorm_max_channels).
-hipError_t launch_merge_blocked(const void *x, const RowDesc *desc, int64_t T, int C, int k,
-                                const void *gamma, const void *beta, float eps, void *out,
-                                hipStream_t s);
+// of Linear1 for the token rows of one chunk of views, K position-major, zeros
+// for cells past the grid; LayerNorm over C applied on the way when gamma is
+// non-null (C <= layernorm_max_channels).
+hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const void *gamma,
+                                const void *beta, float eps, void *out, hipStream_t s);
 
 // bf16 MFMA GEMMs on blocked operands.  linear1: act epilogue, blocked output.
 // Otherwise: no activation, plain rows to dst(m).

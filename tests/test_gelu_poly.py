@@ -1,0 +1,51 @@
+"""The bf16 epilogue's GELU (act_fn<0> in vlb_common.h) against x * Phi(x).
+
+The coefficients are read from the kernel header and the epilogue's float32
+arithmetic is replayed in numpy; scipy's normal CDF is the exact reference.
+Bounds: absolute error <= 1e-6 everywhere on [-12, 12], relative error
+<= 1e-5 wherever |GELU(x)| > 1e-3, and the two asymptotes (x for large x,
+0 for very negative x).
+"""
+import os
+import re
+
+import numpy as np
+from scipy.special import ndtr
+
+HDR = os.path.join(os.path.dirname(__file__), "..", "patch_merge_mlp_amd", "csrc", "vlb_common.h")
+
+
+def _coeffs():
+    src = open(HDR).read()
+    body = src[src.index("if constexpr (ACT == 0)"):src.index("} else if constexpr (ACT == 1)")]
+    clamp = float(re.search(r"fminf\(fabsf\(x\), ([0-9.e+-]+)f\)", body).group(1))
+    top = float(re.search(r"float h = ([0-9.e+-]+)f;", body).group(1))
+    rest = [float(v) for v in re.findall(r"h = fmaf\(h, a, ([0-9.e+-]+)f\);", body)]
+    return clamp, [top] + rest  # highest degree first
+
+
+def _gelu32(x):
+    clamp, c = _coeffs()
+    x = x.astype(np.float32)
+    a = np.minimum(np.abs(x), np.float32(clamp))
+    h = np.full_like(a, np.float32(c[0]))
+    for ck in c[1:]:
+        h = (h * a + np.float32(ck)).astype(np.float32)
+    tail = np.exp2(-h).astype(np.float32)
+    return (np.maximum(x, np.float32(0)) - np.abs(x) * tail).astype(np.float32)
+
+
+def test_gelu_poly_accuracy():
+    clamp, c = _coeffs()
+    assert clamp == 6.0 and len(c) == 8
+    x = np.linspace(-12.0, 12.0, 2400001)
+    y = _gelu32(x).astype(np.float64)
+    ref = x * ndtr(x)
+    err = np.abs(y - ref)
+    assert err.max() <= 1e-6, err.max()
+    big = np.abs(ref) > 1e-3
+    assert (err[big] / np.abs(ref[big])).max() <= 1e-5
+    # asymptotes and the origin
+    assert _gelu32(np.array([0.0]))[0] == 0.0
+    assert np.allclose(_gelu32(np.array([8.0, 30.0, 1e4])), [8.0, 30.0, 1e4], rtol=1e-7)
+    assert np.all(np.abs(_gelu32(np.array([-8.0, -30.0, -1e4]))) <= 1e-7 * np.array([8, 30, 1e4]))
