@@ -1,16 +1,20 @@
 """Benchmark of the vision-to-language bridge on one MI355X.
 
 One step = one vlb_bridge_fused call over one batch: LayerNorm (when the
-workload has it), k x k space-to-depth gather fused into the first GEMM,
-Linear + bias + GELU, Linear + bias, and the scatter of every row into its
-placeholder slot (plus newline / separator rows for tiled images).  Inputs,
-the packed W1 and the workspace are resident in HBM before timing starts.
+workload has it) fused with the k x k space-to-depth into Linear1's
+tile-blocked operand, Linear + bias + GELU, Linear + bias, and the scatter of
+every row into its placeholder slot (plus newline / separator rows for tiled
+images).  Inputs, the packed weights and the workspace are resident in HBM
+before timing starts.
 
 Prints one JSON line.  value = visual tokens (projected rows) per second.
 roofline = the first GEMM (the dominant kernel): algorithmic FLOPs per launch
-over its mean duration from HIP events recorded around each launch on the
-stream it runs on.  cpu_baseline = the fp64 oracle on the host's cores over a
-bounded sample of the same workload's rows.
+over its mean duration from HIP events recorded around each of its launches in
+the timed region, on the stream it runs on (only Linear1 is bracketed there;
+the per-kernel table and Linear2's rate come from a separate untimed pass in
+which every launch is bracketed).
+cpu_baseline = the fp64 oracle on the host's cores over a bounded sample of
+the same workload's rows.
 """
 from __future__ import annotations
 
@@ -107,7 +111,7 @@ def main():
     d = lambda x: None if x is None else x.to(dev)
     weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
                         d(t["ln_beta"]))
-    br = v.Bridge(p, weights)            # packs W1 once (weight preprocessing, untimed)
+    br = v.Bridge(p, weights)            # packs W1 and W2 once (weight preprocessing, untimed)
     feats, mask = d(t["features"]), d(t["mask"])
     nl, sep = d(t["newline"]), d(t["separator"])
     seq = d(t["seq"])
@@ -121,13 +125,23 @@ def main():
     torch.cuda.synchronize()
     assert v.vlb_check(ws) == v.OK
 
-    v.vlb_prof_enable(True)
+    # Timed region: HIP events bracket only the Linear1 launches (on the stream
+    # they run on); every other kernel runs untimed.
+    v.vlb_prof_enable(1 << v.K_GEMM1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    v.vlb_prof_enable(False)
+    n, ms = v.vlb_prof_read(v.K_GEMM1)
+    gemm1_us = 1000.0 * ms / n
+    # Per-kernel breakdown from a separate, untimed pass with every launch timed.
+    v.vlb_prof_enable(True)
+    for _ in range(max(3, args.steps // 4)):
+        step()
+    torch.cuda.synchronize()
     v.vlb_prof_enable(False)
     kernels = {}
     for kid, name in enumerate(v.KERNEL_NAMES):
@@ -139,8 +153,8 @@ def main():
     flops1 = 2.0 * T * K1 * w.hidden
     flops2 = 2.0 * T * w.hidden * w.out_dim
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    g1 = kernels["gemm1"]["mean_us"] * 1e-6
-    g2 = kernels["gemm2"]["mean_us"] * 1e-6
+    g1 = gemm1_us * 1e-6  # from the timed region
+    g2 = kernels["gemm2"]["mean_us"] * 1e-6  # from the profiled pass
     achieved = flops1 / g1 / 1e12
     traffic = traffic_from_profiles(w.name)
     out = {
@@ -164,8 +178,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "Linear1 (space-to-depth gather + GEMM + bias + GELU; 256-tile body and "
-                      "128-tile tail dispatches)",
+            "kernel": "Linear1 (GEMM + bias + GELU on the blocked merged tokens; 256-tile body "
+                      "and 128-tile tail dispatches)",
             "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
         },

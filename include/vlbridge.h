@@ -207,9 +207,11 @@ enum {
   VLB_K_COUNT = 9
 };
 
-/* While enabled, every launch is bracketed by HIP events recorded on its
- * stream.  vlb_prof_enable(1) clears earlier records. */
-vlb_status vlb_prof_enable(int32_t on);
+/* Launch timing.  mask bit kid (1 << VLB_K_*) enables timing of that kernel
+ * id: each such launch is bracketed by HIP events recorded on the stream it
+ * runs on.  A nonzero mask clears earlier records; 0 stops recording; -1
+ * times every kernel. */
+vlb_status vlb_prof_enable(int32_t mask);
 /* Waits for the recorded events and returns, for kernel id kid, the number of
  * launches and their summed duration in milliseconds. */
 vlb_status vlb_prof_read(int32_t kid, int64_t *launches, double *total_ms);

@@ -167,13 +167,13 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+uint32_t g_prof_mask = 0;  // bit kid: time kernel id kid
 std::vector<ProfRec> g_prof;
 size_t g_prof_used = 0;
 
 int prof_begin(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return -1;
+  if (!((g_prof_mask >> kid) & 1u)) return -1;
   if (g_prof_used == g_prof.size()) {
     ProfRec r{kid, nullptr, nullptr};
     if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return -1;
@@ -536,10 +536,10 @@ const char *vlb_status_str(vlb_status s) {
   return "unknown status";
 }
 
-vlb_status vlb_prof_enable(int32_t on) {
+vlb_status vlb_prof_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
-  if (g_prof_on) g_prof_used = 0;
+  g_prof_mask = static_cast<uint32_t>(mask);
+  if (g_prof_mask) g_prof_used = 0;
   return VLB_OK;
 }
 

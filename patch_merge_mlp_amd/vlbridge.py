@@ -305,8 +305,14 @@ def vlb_check(ws, stream=None) -> int:
     return int(lib().vlb_check(_ptr(ws), _stream(stream)))
 
 
-def vlb_prof_enable(on: bool):
-    _check(lib().vlb_prof_enable(int(on)), "vlb_prof_enable")
+def vlb_prof_enable(mask):
+    """True / -1: time every kernel; an int: bit kid times kernel id kid (K_*);
+    False / 0: stop recording."""
+    if mask is True:
+        mask = -1
+    elif mask is False:
+        mask = 0
+    _check(lib().vlb_prof_enable(int(mask)), "vlb_prof_enable")
 
 
 def vlb_prof_read(kid: int):
