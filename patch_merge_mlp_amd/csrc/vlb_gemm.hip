@@ -5,9 +5,10 @@
 // "Projector (downsample_mlp_gelu)" steps 1-3.
 //
 // bf16 path (gfx950): 256x256 output tile per 256-thread workgroup, 4 waves in
-// a 2x2 grid, each wave 128x128 from 4x4 v_mfma_f32_32x32x16_bf16 tiles with
-// fp32 accumulation; the last, partly filled round of tiles runs as 128x128
-// tiles.  K advances 32 per stage through four LDS stages (A and B halves,
+// a 2x2 grid, each wave 128x128 from 8x8 v_mfma_f32_16x16x32_bf16 tiles with
+// fp32 accumulation (the 16x16x32 form draws less power per flop than
+// 32x32x16, so under the board's power cap it sustains a higher clock); the
+// last, partly filled round of tiles runs as 128x128 tiles.  K advances 32 per stage through four LDS stages (A and B halves,
 // 64-byte rows of 16-byte chunks XOR-swizzled by row), filled by
 // direct-to-LDS buffer loads three stages ahead of the MFMAs.  Every operand
 // is tile-blocked ([R/256][K/32][256][32]), so each load instruction of a
@@ -25,17 +26,17 @@ namespace vlb {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = kGemmBK, NTHREADS = 256;
 constexpr int NSTAGE = kGemmStages;  // LDS stages; three are in flight
 constexpr int GROUP_M = 8;
 
 // Geometry of a BMT x BMT output tile (BMT = 256 or 128) computed by 4 waves
-// in a 2x2 grid, each wave owning a (BMT/2)^2 block of 32x32 MFMA tiles.
+// in a 2x2 grid, each wave owning a (BMT/2)^2 block of 16x16 MFMA tiles.
 template <int BMT>
 struct Geo {
-  static constexpr int TI = BMT / 64;          // MFMA tiles per wave per dimension
+  static constexpr int TI = BMT / 32;          // MFMA tiles per wave per dimension
   static constexpr int WT = BMT / 2;           // wave tile side
   static constexpr int LPW = BMT / 64;         // 16-row loads per wave per operand per stage
   static constexpr int HALF = BMT * BK * 2;    // bytes of one operand in a stage
@@ -76,15 +77,17 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 64 + ((chunk ^ swz_xor(row)) << 4);
 }
 
-// Barrier of the stage pipeline: this wave's loads are complete except those
-// of the two younger stages (16 or 8 loads), its LDS reads are done, then the
-// workgroup synchronises.  One asm block, so no memory access moves across it.
+// Barrier of the stage pipeline: this wave's loads are complete except the
+// younger ones -- the next stage's and the first half of the one after
+// (12 loads for 256-tiles, 6 for 128-tiles) -- its LDS reads are done, then
+// the workgroup synchronises.  One asm block, so no memory access moves
+// across it.
 template <int BMT>
 __device__ __forceinline__ void stage_barrier() {
   if constexpr (BMT == 256)
-    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -106,45 +109,43 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *ds
 }
 
 // Epilogue of one tile.  The weight fragment is the MFMA's first operand, so
-// acc[i][j] holds the transposed product: lane (fr, fk) of wave (wm, wn) owns
-// token row wm*WT + 32 i + fr and features wn*WT + 32 j + 8 a + 4 fk + e in
-// element 4 a + e (a, e < 4).  Bias and activation are applied in fp32, the
-// tile is rounded to bf16 and staged in the stage buffers (64 rows each; rows
-// of 16-byte chunks XOR-swizzled by the row), then written out whole rows at a
-// time with 16-byte stores to row s_dst[r] (skipped when negative).  The
-// caller has synchronised the workgroup after its last use of the buffers.
+// acc[i][j] holds the transposed product: lane (fr, fq) = (lane % 16,
+// lane / 16) of wave (wm, wn) owns token row wm*WT + 16 i + fr and features
+// wn*WT + 16 j + 4 fq + e in element e (e < 4).  Bias and activation are
+// applied in fp32, the tile is rounded to bf16 and staged in the stage
+// buffers (64 rows each; rows of 16-byte chunks XOR-swizzled by the row), then
+// written out whole rows at a time with 16-byte stores to row s_dst[r]
+// (skipped when negative), or tile-blocked.  The caller has synchronised the
+// workgroup after its last use of the buffers.
 template <int ACT, int BMT, bool BLOCKED_OUT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
                                            const GemmArgs &g, int m0, int n0, uint8_t *b0,
                                            uint8_t *b1, uint8_t *b2, uint8_t *b3,
                                            const uint16_t *s_bias, const int32_t *s_dst) {
   using G = Geo<BMT>;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  const int fr = lane & 31, fk = lane >> 5;
+  const int fr = lane & 15, fq = lane >> 4;
   auto bufs = [&](int b) -> uint8_t * { return b == 0 ? b0 : b == 1 ? b1 : b == 2 ? b2 : b3; };
 #pragma unroll
   for (int j = 0; j < G::TI; ++j) {
+    const int cl = wn * G::WT + j * 16 + 4 * fq;  // 4 consecutive features
+    const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
+    const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
+                        bf2f(bb.y >> 16)};
+    const int chunk = cl >> 3, half = (cl >> 2) & 1;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int cl = wn * G::WT + j * 32 + 8 * a + 4 * fk;  // 4 consecutive features
-      const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
-      const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
-                          bf2f(bb.y >> 16)};
-      const int chunk = cl >> 3;
+    for (int i = 0; i < G::TI; ++i) {
+      const int r = wm * G::WT + i * 16 + fr;  // tile row
+      const int row = r & 63;                  // inside buffer r / 64
+      uint16_t h[4];
 #pragma unroll
-      for (int i = 0; i < G::TI; ++i) {
-        const int r = wm * G::WT + i * 32 + fr;  // tile row
-        const int row = r & 63;                  // inside buffer r / 64
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][4 * a + e] + b[e]));
-        uint2 v;
-        v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
-        v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-        *reinterpret_cast<uint2 *>(bufs(r >> 6) + row * G::ROWB +
-                                   ((chunk ^ (row & (G::CCH - 1))) << 4) + fk * 8) = v;
-      }
+      for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][e] + b[e]));
+      uint2 v;
+      v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+      v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+      *reinterpret_cast<uint2 *>(bufs(r >> 6) + row * G::ROWB +
+                                 ((chunk ^ (row & (G::CCH - 1))) << 4) + half * 8) = v;
     }
   }
   __syncthreads();
@@ -250,81 +251,112 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   // Loads of K step kt into `stage`.  Steps at or past the end of K read zeros
   // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
   const int KT = g.K / BK;
-  auto issue = [&](int kt, uint8_t *stage) {
+  // Loads of K step kt into `stage` (the first or second half of them when
+  // part is 0 or 1, all when -1).  Steps at or past the end of K read zeros
+  // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
+  auto issue = [&](int kt, uint8_t *stage, int part) {
     const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
     const uint32_t step_off = kt * (256 * 64);
     uint8_t *sa = stage + wid * G::LPW * 1024;
     uint8_t *sb = stage + G::HALF + wid * G::LPW * 1024;
+    const int i0 = part == 1 ? G::LPW / 2 : 0, i1 = part == 0 ? G::LPW / 2 : G::LPW;
 #pragma unroll
-    for (int i = 0; i < G::LPW; ++i) {
+    for (int i = i0; i < i1; ++i) {
       load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
       load_lds16(rB, sb + i * 1024, (b_off[i] + step_off) | dead);
     }
   };
 
-  f32x16 acc[G::TI][G::TI];
+  f32x4 acc[G::TI][G::TI];
 #pragma unroll
   for (int i = 0; i < G::TI; ++i)
 #pragma unroll
     for (int j = 0; j < G::TI; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+      for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.f;
 
   const int wm = wid >> 1, wn = wid & 1;
-  const int fr = lane & 31, fk = lane >> 5;  // fragment row / k-half of this lane
+  const int fr = lane & 15, fq = lane >> 4;  // fragment row / 8-wide K group of this lane
+  // Fragments of one K step (32): TI tiles of 16 rows for each operand; two
+  // sets, so the next step's are read while this step's multiply.
   bf16x8 fa0[G::TI], fb0[G::TI], fa1[G::TI], fb1[G::TI];
-  auto rd = [&](const uint8_t *stage, int ks, bf16x8 *fa, bf16x8 *fb) {
+  auto rd = [&](const uint8_t *stage, bf16x8 *fa, bf16x8 *fb) {
 #pragma unroll
     for (int t = 0; t < G::TI; ++t) {
-      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * G::WT + t * 32 + fr, ks * 2 + fk));
-      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + G::HALF +
-                                                swz(wn * G::WT + t * 32 + fr, ks * 2 + fk));
+      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * G::WT + t * 16 + fr, fq));
+      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + G::HALF + swz(wn * G::WT + t * 16 + fr, fq));
     }
   };
-  auto mma = [&](const bf16x8 *fa, const bf16x8 *fb) {
+  // MFMAs [i0, i1) of the step, i-major (A tile i, B tile j).
+  auto mma = [&](const bf16x8 *fa, const bf16x8 *fb, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < G::TI; ++i)
+    for (int i = i0; i < i1; ++i)
 #pragma unroll
       for (int j = 0; j < G::TI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
-  // One K step of 32: the loads of step kt+3 are issued into the stage freed
-  // by step kt-1; the second 16-wide slice is read while the first multiplies;
-  // the barrier (step kt+1 landed everywhere, step kt fully read) sits before
-  // the last MFMAs so the next step's first fragments arrive under them.
-  constexpr int NM = G::TI * G::TI;  // MFMAs per 16-wide K slice
-  auto step = [&](int kt, const uint8_t *cur, const uint8_t *nxt, uint8_t *fut) {
-    issue(kt + 3, fut);
-    rd(cur, 1, fa1, fb1);
-    mma(fa0, fb0);
+  // One K step of 32 (NM MFMAs): the loads of step kt+3 are issued into the
+  // stage freed by step kt-1; after the first quarter of the MFMAs the barrier
+  // (step kt+1 landed everywhere, step kt's fragments all read) lets the next
+  // step's fragments be read under the remaining MFMAs.
+  constexpr int NM = G::TI * G::TI;
+  constexpr int Q = G::TI / 4;  // A tiles per quarter
+  auto step = [&](const uint8_t *nxt, uint8_t *fut, int kt, const bf16x8 *fa, const bf16x8 *fb,
+                  bf16x8 *na, bf16x8 *nb) {
+    // Nothing moves across a step boundary: left free, the scheduler hoists
+    // later steps' fragment reads and runs out of registers.
+    __builtin_amdgcn_sched_barrier(0);
+    // Half of the step's loads go out with the MFMAs before the barrier, half
+    // with those after it, so the address unit never sees a burst; the next
+    // step's fragment reads are interleaved with the MFMAs after the barrier.
+    issue(kt + 3, fut, 0);
+    mma(fa, fb, 0, Q);
+    if constexpr (BMT == 256) {  // 16 MFMAs, 4 loads
 #pragma unroll
-    for (int i = 0; i < 2 * G::TI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global -> LDS load
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global -> LDS load
+      }
+    } else {  // 4 MFMAs, 2 loads
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * G::TI, 0);
     stage_barrier<BMT>();
-    rd(nxt, 0, fa0, fb0);
-    mma(fa1, fb1);
+    rd(nxt, na, nb);
+    issue(kt + 3, fut, 1);
+    mma(fa, fb, Q, G::TI);
+    if constexpr (BMT == 256) {  // 48 MFMAs, 16 fragment reads, 4 loads
 #pragma unroll
-    for (int i = 0; i < 2 * G::TI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {  // 12 MFMAs, 8 fragment reads, 2 loads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * G::TI, 0);
   };
 
-  issue(0, smem0);
-  issue(1, smem1);
-  issue(2, smem2);
-  stage_barrier<BMT>();  // step 0 landed
-  rd(smem0, 0, fa0, fb0);
+  issue(0, smem0, -1);
+  issue(1, smem1, -1);
+  issue(2, smem2, -1);
+  stage_barrier<BMT>();  // step 0 landed (12 or 6 younger loads may be in flight)
+  rd(smem0, fa0, fb0);
   for (int kt = 0; kt < KT; kt += NSTAGE) {  // KT rounds up: the extra steps are all-zero
-    step(kt, smem0, smem1, smem3);
-    step(kt + 1, smem1, smem2, smem0);
-    step(kt + 2, smem2, smem3, smem1);
-    step(kt + 3, smem3, smem0, smem2);
+    step(smem1, smem3, kt, fa0, fb0, fa1, fb1);
+    step(smem2, smem0, kt + 1, fa1, fb1, fa0, fb0);
+    step(smem3, smem1, kt + 2, fa0, fb0, fa1, fb1);
+    step(smem0, smem2, kt + 3, fa1, fb1, fa0, fb0);
   }
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
   store_tile<ACT, BMT, LINEAR1>(acc, g, m0, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
