@@ -311,11 +311,11 @@ vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
   int32_t *status = reinterpret_cast<int32_t *>(ws + pl.off_status);
   int32_t *slot_pos = reinterpret_cast<int32_t *>(ws + pl.off_slot);
   int32_t *dst_row = reinterpret_cast<int32_t *>(ws + pl.off_dst);
-  VLB_LAUNCH(VLB_K_SCAN, s, vlb::launch_scan(mask, seq_len, pl.P, slot_pos, status, s));
-  if (b->layout == VLB_LAYOUT_PLAIN) {
-    VLB_LAUNCH(VLB_K_PLACE, s, vlb::launch_place_plain(pl.T, slot_pos, status, dst_row, s));
+  if (b->layout == VLB_LAYOUT_PLAIN) {  // token row r -> the r-th placeholder: the scan writes dst_row
+    VLB_LAUNCH(VLB_K_SCAN, s, vlb::launch_scan(mask, seq_len, pl.P, dst_row, status, true, s));
     return VLB_OK;
   }
+  VLB_LAUNCH(VLB_K_SCAN, s, vlb::launch_scan(mask, seq_len, pl.P, slot_pos, status, false, s));
   for (int i0 = 0; i0 < b->n_images; i0 += vlb::kPlaceImages) {
     PlaceChunk c{};
     c.n = std::min(vlb::kPlaceImages, b->n_images - i0);

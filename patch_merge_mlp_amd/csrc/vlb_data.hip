@@ -50,28 +50,61 @@ __global__ void k_plan(PlanChunk c, RowDesc *desc) {
 // One workgroup streams the mask in chunks of 16 KiB with a running carry.
 // status[kCountWord] = number of placeholders; status[kStatusWord] = 0 when it
 // equals P, else VLB_ERR_MASK_COUNT.
+// Plain layout (direct): token row r goes to the r-th placeholder, so the
+// positions are the rows' destinations.  A counting pass runs first and the
+// positions are written to dst_row only when the count matches; otherwise
+// every dst_row entry (P of them) is -1 and nothing is placed.
 constexpr int kScanThreads = 1024;
 
+// Nonzero bytes among the 16 at mask[off] (bounded by S), unpacked into b.
+__device__ __forceinline__ int scan_load(const uint8_t *mask, int64_t S, int64_t off, uint8_t (&b)[16]) {
+  if (off + 16 <= S) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(mask + off);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xff;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[i] = (off + i < S) ? mask[off + i] : 0;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cnt += b[i] != 0;
+  return cnt;
+}
+
 __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t *mask, int64_t S, int64_t P,
-                                                      int32_t *slot_pos, int32_t *status) {
+                                                      int32_t *slot_pos, int32_t *status,
+                                                      bool direct) {
   __shared__ int32_t wsum[kScanThreads / 64];
+  __shared__ int32_t s_total;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (direct) {  // counting pass
+    int cnt = 0;
+    for (int64_t base = 0; base < S; base += kScanThreads * 16) {
+      uint8_t b[16];
+      cnt += scan_load(mask, S, base + static_cast<int64_t>(tid) * 16, b);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+    if (tid == 0) s_total = 0;
+    __syncthreads();
+    if (lane == 0) atomicAdd(&s_total, cnt);
+    __syncthreads();
+    if (s_total != P) {
+      for (int64_t r = tid; r < P; r += kScanThreads) slot_pos[r] = -1;
+      if (tid == 0) {
+        status[kCountWord] = s_total;
+        status[kStatusWord] = kErrMaskCount;
+      }
+      return;
+    }
+  }
   int32_t carry = 0;
   for (int64_t base = 0; base < S; base += kScanThreads * 16) {
     const int64_t off = base + static_cast<int64_t>(tid) * 16;
     uint8_t b[16];
-    if (off + 16 <= S) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(mask + off);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) b[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xff;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) b[i] = (off + i < S) ? mask[off + i] : 0;
-    }
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cnt += b[i] != 0;
+    const int cnt = scan_load(mask, S, off, b);
     int x = cnt;  // inclusive scan inside the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -104,14 +137,6 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t *mask, int6
 }
 
 // ---------------------------------------------------------------------------
-// Plain layout: token row r goes to the r-th placeholder.
-__global__ void k_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
-                              int32_t *dst_row) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (r >= T) return;
-  dst_row[r] = status[kStatusWord] == 0 ? slot_pos[r] : -1;
-}
-
 // 2D tile layout: decode what every assembled slot holds -- a token row, the
 // newline or the separator -- by inverting the assembly order of one image:
 //   global view: h' rows of (w' tokens, newline)
@@ -477,16 +502,9 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s) {
 }
 
 hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
-                       int32_t *status, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, mask, S, P, slot_pos, status);
-  return hipGetLastError();
-}
-
-hipError_t launch_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
-                              int32_t *dst_row, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_place_plain, dim3(grid_for(T, 256, 1 << 30)), dim3(256), 0, s, T,
-                     slot_pos, status, dst_row);
+                       int32_t *status, bool direct, hipStream_t s) {
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, mask, S, P, slot_pos, status,
+                     direct);
   return hipGetLastError();
 }
 

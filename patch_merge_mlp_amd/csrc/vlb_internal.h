@@ -101,10 +101,10 @@ inline TilePlan tile_plan(int64_t M, int64_t N) {
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------
 hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
+// direct (plain layout): slot_pos is dst_row [P] and receives the positions
+// themselves, or -1 everywhere when the placeholder count differs from P.
 hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
-                       int32_t *status, hipStream_t s);
-hipError_t launch_place_plain(int64_t T, const int32_t *slot_pos, const int32_t *status,
-                              int32_t *dst_row, hipStream_t s);
+                       int32_t *status, bool direct, hipStream_t s);
 hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
                               const int32_t *status, int32_t *dst_row, const void *newline,
                               const void *separator, void *seq, int D, hipStream_t s);
