@@ -408,47 +408,52 @@ __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, i
 }
 
 // ---------------------------------------------------------------------------
-// Standalone space-to-depth in the pages' feature order c*k*k + dy*k + dx: one
-// workgroup per token stages the token's k*k pixels ([p][C], zeros for padded
-// cells) in LDS, then writes the interleaved row with 16-byte stores.
-constexpr int kMergeThreads = 256;
-
-template <typename T>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(const T *x, const RowDesc *desc,
-                                                         int64_t Trows, int C, int k, T *merged) {
-  extern __shared__ uint4 merge_lds[];
-  T *tile = reinterpret_cast<T *>(merge_lds);
-  constexpr int E = 16 / sizeof(T);
-  const int kk = k * k;
-  const int nrow = C / E;           // 16-byte chunks per pixel
-  const int K1 = C * kk;
-  for (int64_t r = blockIdx.x; r < Trows; r += gridDim.x) {
+// Standalone space-to-depth in the pages' feature order c*k*k + dy*k + dx.
+// A thread owns one 4-byte unit of a token's channels (two bf16 channels, or
+// one fp32) and all k*k cells: it reads the unit from each cell (consecutive
+// threads read consecutive units of a pixel, so each read instruction is one
+// coalesced run) and writes the k*k interleaved values of its channels as k*k
+// consecutive dwords of the merged row (together the threads of a wave cover
+// one contiguous stretch).  Padded cells read as zero.
+template <typename T, int KK>
+__global__ __launch_bounds__(256) void k_merge(const T *x, const RowDesc *desc, int64_t Trows,
+                                               int C, int k, T *merged) {
+  constexpr int U = 4 / sizeof(T);  // channels per 4-byte unit
+  const int units = C / U;
+  const int64_t total = Trows * units;
+  const uint32_t *x32 = reinterpret_cast<const uint32_t *>(x);
+  uint32_t *m32 = reinterpret_cast<uint32_t *>(merged);
+  for (int64_t w = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; w < total;
+       w += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = w / units;
+    const int u = static_cast<int>(w - r * units);
     const RowDesc d = desc[r];
     const int gw = d.geo & 0xffff;
     const uint32_t inside = static_cast<uint32_t>(d.geo) >> 16;
-    for (int q = threadIdx.x; q < kk * nrow; q += kMergeThreads) {
-      const int p = q / nrow, cq = q - p * nrow;
-      const int dy = p / k, dx = p - dy * k;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if ((inside >> p) & 1)
-        v = reinterpret_cast<const uint4 *>(
-            x + static_cast<int64_t>(d.pix + dy * gw + dx) * C)[cq];
-      merge_lds[q] = v;
-    }
-    __syncthreads();
-    uint4 *dst = reinterpret_cast<uint4 *>(merged + r * K1);
-    for (int q = threadIdx.x; q < K1 / E; q += kMergeThreads) {
-      uint4 o;
-      T *oe = reinterpret_cast<T *>(&o);
+    uint32_t cell[KK];
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const int e = q * E + j;
-        const int c = e / kk, p = e - c * kk;
-        oe[j] = tile[p * C + c];
-      }
-      dst[q] = o;
+    for (int p = 0; p < KK; ++p) {
+      const int dy = p / k, dx = p - dy * k;
+      cell[p] = ((inside >> p) & 1)
+                    ? x32[(static_cast<int64_t>(d.pix + dy * gw + dx) * C) / U + u]
+                    : 0u;
     }
-    __syncthreads();
+    // The unit's run in the merged row: elements (U*u + i) * KK + p, i.e.
+    // KK*U values = KK dwords starting at dword u*KK.
+    uint32_t *dst = m32 + (r * C * KK) / U + static_cast<int64_t>(u) * KK;
+    if constexpr (U == 1) {
+#pragma unroll
+      for (int p = 0; p < KK; ++p) dst[p] = cell[p];
+    } else {
+      // run element e = i*KK + p holds channel half i of cell p; dword j packs
+      // elements 2j (low half) and 2j+1.
+      auto elem = [&](int e) -> uint32_t {
+        const int i = e / KK, p = e - i * KK;
+        return i == 0 ? (cell[p] & 0xffffu) : (cell[p] >> 16);
+      };
+#pragma unroll
+      for (int j = 0; j < KK; ++j) dst[j] = elem(2 * j) | (elem(2 * j + 1) << 16);
+    }
   }
 }
 
@@ -612,18 +617,27 @@ hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const i
   return hipGetLastError();
 }
 
+template <typename T>
+static void merge_launch(const void *x, const RowDesc *desc, int64_t Trows, int C, int k,
+                         void *merged, hipStream_t s) {
+  const int64_t work = Trows * (C / (4 / static_cast<int>(sizeof(T))));
+  const int grid = grid_for(work, 256, 16384);
+  const T *xp = static_cast<const T *>(x);
+  T *mp = static_cast<T *>(merged);
+  switch (k) {
+    case 1: hipLaunchKernelGGL((k_merge<T, 1>), dim3(grid), dim3(256), 0, s, xp, desc, Trows, C, k, mp); break;
+    case 2: hipLaunchKernelGGL((k_merge<T, 4>), dim3(grid), dim3(256), 0, s, xp, desc, Trows, C, k, mp); break;
+    default: hipLaunchKernelGGL((k_merge<T, 9>), dim3(grid), dim3(256), 0, s, xp, desc, Trows, C, k, mp); break;
+  }
+}
+
 hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T, int C, int k,
                         void *merged, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const size_t lds = static_cast<size_t>(C) * k * k * (dtype == 0 ? 4 : 2);
-  const int grid = grid_for(T, 1, 1 << 20);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_merge<float>, dim3(grid), dim3(kMergeThreads), lds, s,
-                       static_cast<const float *>(x), desc, T, C, k, static_cast<float *>(merged));
+    merge_launch<float>(x, desc, T, C, k, merged, s);
   else
-    hipLaunchKernelGGL(k_merge<uint16_t>, dim3(grid), dim3(kMergeThreads), lds, s,
-                       static_cast<const uint16_t *>(x), desc, T, C, k,
-                       static_cast<uint16_t *>(merged));
+    merge_launch<uint16_t>(x, desc, T, C, k, merged, s);
   return hipGetLastError();
 }
 
