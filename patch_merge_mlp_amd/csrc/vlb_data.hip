@@ -383,27 +383,35 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
 
 // ---------------------------------------------------------------------------
 // Standalone scatter: row r of rows[T][D] -> seq[dst_row[r]] (skipped if < 0).
+// One wave per row; the row's data (up to 8 KiB at a time) is loaded together
+// with its destination, so the loads never wait on the index.
 template <typename T>
 __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, int D,
                                                  const int32_t *dst_row, T *seq) {
+  constexpr int V = 8;  // 16-byte chunks per lane per pass
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   const int n16 = D * static_cast<int>(sizeof(T)) / 16;
   for (int64_t r = wave; r < Trows; r += nwaves) {
     const int32_t d = dst_row[r];
-    if (d < 0) continue;
     const uint4 *from = reinterpret_cast<const uint4 *>(rows + r * D);
-    uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(d) * D);
-    int i = lane;
-    for (; i + 192 < n16; i += 256) {
-      const uint4 a = from[i], b = from[i + 64], cc = from[i + 128], e = from[i + 192];
-      to[i] = a;
-      to[i + 64] = b;
-      to[i + 128] = cc;
-      to[i + 192] = e;
+    for (int base = 0; base < n16; base += 64 * V) {
+      uint4 v[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int q = base + lane + 64 * i;
+        v[i] = q < n16 ? from[q] : make_uint4(0, 0, 0, 0);
+      }
+      if (d >= 0) {
+        uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(d) * D);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int q = base + lane + 64 * i;
+          if (q < n16) to[q] = v[i];
+        }
+      }
     }
-    for (; i < n16; i += 64) to[i] = from[i];
   }
 }
 
