@@ -140,6 +140,9 @@ def _declare(L):
     L.orc_assemble.argtypes = [ct.POINTER(_Spec), _I64, i64]
     L.orc_scatter.restype = ct.c_int32
     L.orc_scatter.argtypes = [_I64, i64, _D, _D, _D, _U8, i64, ct.c_int32, _D]
+    L.orc_embed_scatter.restype = ct.c_int32
+    L.orc_embed_scatter.argtypes = [_I64, i64, _D, _D, _D, ct.POINTER(ct.c_int32), i64,
+                                    ct.c_int32, ct.POINTER(ct.c_uint16), _D, i64, ct.c_int32, _D]
 
 
 def _f64(a) -> np.ndarray:
@@ -298,4 +301,34 @@ def scatter(src, rows, newline, separator, mask, seq):
     sp = _f64(separator) if separator is not None else np.zeros(D)
     st = int(lib().orc_scatter(src.ctypes.data_as(_I64), len(src), _dp(rows), _dp(nl), _dp(sp),
                                mask.ctypes.data_as(_U8), S, D, _dp(seq)))
+    return st, seq
+
+
+def embed_scatter(src, rows, newline, separator, ids, image_id, embed, D):
+    """Whole embedded sequence: text positions from the table, image_id positions
+    from the assembled rows in order.  embed: torch bf16 / fp32 / fp64 or numpy
+    [vocab][D] (bf16 is passed as its bit patterns and widened exactly in C).
+    Returns (status, seq [S][D] fp64); status -1 = placeholder-count mismatch,
+    -2 = text id out of range (seq is then all zero, i.e. untouched)."""
+    src = np.ascontiguousarray(src, dtype=np.int64)
+    rows = _f64(rows)
+    ids = np.ascontiguousarray(np.asarray(ids), dtype=np.int32)
+    S = len(ids)
+    nl = _f64(newline) if newline is not None else np.zeros(D)
+    sp = _f64(separator) if separator is not None else np.zeros(D)
+    bits = None
+    e64 = None
+    if hasattr(embed, "detach") and str(embed.dtype) == "torch.bfloat16":
+        import torch
+        bits = np.ascontiguousarray(embed.detach().cpu().contiguous().view(torch.int16).numpy()).view(np.uint16)
+        vocab = bits.shape[0]
+    else:
+        e64 = _f64(embed)
+        vocab = e64.shape[0]
+    seq = np.zeros((S, D), dtype=np.float64)
+    st = int(lib().orc_embed_scatter(
+        src.ctypes.data_as(_I64), len(src), _dp(rows), _dp(nl), _dp(sp),
+        ids.ctypes.data_as(ct.POINTER(ct.c_int32)), S, int(image_id),
+        bits.ctypes.data_as(ct.POINTER(ct.c_uint16)) if bits is not None else None,
+        _dp(e64) if e64 is not None else None, vocab, D, _dp(seq)))
     return st, seq

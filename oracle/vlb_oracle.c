@@ -364,3 +364,40 @@ int32_t orc_scatter(const int64_t *src, int64_t P, const double *rows, const dou
   }
   return 0;
 }
+
+/* bf16 bit pattern -> double (exact: bf16 is the upper half of an fp32). */
+static double bf16_bits(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+int32_t orc_embed_scatter(const int64_t *src, int64_t P, const double *rows,
+                          const double *newline, const double *separator, const int32_t *ids,
+                          int64_t S, int32_t image_id, const uint16_t *e_bf16,
+                          const double *e_f64, int64_t vocab, int32_t D, double *seq) {
+  int64_t n_img = 0;
+  int bad_id = 0;
+  for (int64_t i = 0; i < S; i++) {
+    if (ids[i] == image_id) n_img++;
+    else if (ids[i] < 0 || ids[i] >= vocab) bad_id = 1;
+  }
+  if (n_img != P) return -1;
+  if (bad_id) return -2;
+  int64_t j = 0;
+  for (int64_t i = 0; i < S; i++) {
+    double *to = seq + i * D;
+    if (ids[i] == image_id) {
+      const double *from = src[j] >= 0                  ? rows + src[j] * D
+                           : src[j] == ORC_SRC_NEWLINE ? newline
+                                                        : separator;
+      memcpy(to, from, sizeof(double) * D);
+      j++;
+    } else {
+      const int64_t e = (int64_t)ids[i] * D;
+      for (int32_t d = 0; d < D; d++) to[d] = e_bf16 ? bf16_bits(e_bf16[e + d]) : e_f64[e + d];
+    }
+  }
+  return 0;
+}

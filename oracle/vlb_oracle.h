@@ -110,6 +110,19 @@ int32_t orc_scatter(const int64_t *src, int64_t P, const double *rows, const dou
                     const double *separator, const uint8_t *mask, int64_t S, int32_t D,
                     double *seq);
 
+/* The whole embedded sequence [VL2 Tile-sequence assembly, last paragraph;
+ * language config vocab_size, image_token_index]: position s holds row ids[s]
+ * of the token-embedding table E [vocab][D] unless ids[s] == image_id; the
+ * positions holding image_id take the assembled rows in order (as
+ * orc_scatter).  E is given in its stored form, as bf16 bit patterns (e_bf16)
+ * when that is non-NULL, else as doubles (e_f64); it is widened exactly.
+ * Returns 0; -1 if the number of image_id positions differs from P; else -2
+ * if a text id lies outside [0, vocab).  On error seq is left untouched. */
+int32_t orc_embed_scatter(const int64_t *src, int64_t P, const double *rows,
+                          const double *newline, const double *separator, const int32_t *ids,
+                          int64_t S, int32_t image_id, const uint16_t *e_bf16,
+                          const double *e_f64, int64_t vocab, int32_t D, double *seq);
+
 #ifdef __cplusplus
 }
 #endif

@@ -265,9 +265,47 @@ def pin_scatter(o):
     assert st == 0 and np.array_equal(out, seq)
 
 
+def pin_embed_scatter(o):
+    """The embedded sequence equals torch's embedding lookup with the assembled rows
+    placed by masked_scatter at the image-token positions (the page's "overwrite the
+    token embeddings at exactly the positions holding image_token_index, in order");
+    a placeholder-count mismatch or an out-of-range text id writes nothing."""
+    g = torch.Generator().manual_seed(7)
+    S, D, vocab, img = 20, 5, 11, 9
+    E = torch.randn(vocab, D, generator=g, dtype=torch.float64)
+    rows = torch.randn(4, D, generator=g, dtype=torch.float64)
+    nl = torch.full((D,), -1.0, dtype=torch.float64)
+    sp = torch.full((D,), -2.0, dtype=torch.float64)
+    src = np.array([2, -1, 0, -2, 3, 1])  # assembled slots: token 2, newline, token 0, sep, 3, 1
+    ids = torch.tensor([1, 0, img, img, 4, img, 10, 2, img, img, 3, 7, img, 5, 6, 8, 0, 10, 1, 2],
+                       dtype=torch.int32)
+    A = torch.stack([rows[s] if s >= 0 else (nl if s == -1 else sp) for s in src])
+    mask = ids == img
+    want = F.embedding(torch.where(mask, torch.zeros_like(ids), ids).long(), E)
+    want = want.masked_scatter(mask[:, None].expand(S, D), A)
+    st, got = o.embed_scatter(src, rows, nl, sp, ids, img, E, D)
+    assert st == 0 and np.array_equal(got, want.numpy())
+    # bf16 table: widened exactly
+    Eb = E.to(torch.bfloat16)
+    st, got = o.embed_scatter(src, rows, nl, sp, ids, img, Eb, D)
+    want_b = F.embedding(torch.where(mask, torch.zeros_like(ids), ids).long(), Eb.double())
+    want_b = want_b.masked_scatter(mask[:, None].expand(S, D), A)
+    assert st == 0 and np.array_equal(got, want_b.numpy())
+    # errors: one placeholder too many / too few, then a text id past the vocabulary
+    for pos, val, code in ((0, img, -1), (2, 4, -1), (6, vocab, -2), (7, -3, -2)):
+        bad = ids.clone()
+        bad[pos] = val
+        st, got = o.embed_scatter(src, rows, nl, sp, bad, img, E, D)
+        assert st == code and not got.any(), (pos, val, st)
+    # text only: every row comes from the table
+    st, got = o.embed_scatter(np.zeros(0, np.int64), rows, nl, sp, ids[~mask], img, E, D)
+    assert st == 0 and np.array_equal(got, F.embedding(ids[~mask].long(), E).numpy())
+
+
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
-       pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter]
+       pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
+       pin_embed_scatter]
 
 
 def failing(o):

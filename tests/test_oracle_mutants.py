@@ -39,10 +39,21 @@ MUTANTS = {
         "      n = emit_global(src, cap, n, row, hp, wp);\n      n = emit(src, cap, n, ORC_SRC_SEPARATOR);",
         "      n = emit(src, cap, n, ORC_SRC_SEPARATOR);\n      n = emit_global(src, cap, n, row, hp, wp);"),
     "placeholder formula without local newlines": ("(th * hp) * (tw * wp + 1)", "(th * hp) * (tw * wp)"),
-    "scatter in reverse": ("const double *from = src[j] >= 0                  ? rows + src[j] * D",
-                           "j = P - 1 - j; const double *from = src[j] >= 0 ? rows + src[j] * D"),
+    "scatter in reverse": ("    if (!mask[i]) continue;\n    const double *from = src[j] >= 0                  ? rows + src[j] * D",
+                           "    if (!mask[i]) continue;\n    j = P - 1 - j; const double *from = src[j] >= 0 ? rows + src[j] * D"),
     "no count check": ("if (count != P) return -1;", "(void)count;"),
     "param count without second bias": ("hidden * out_dim + out_dim;", "hidden * out_dim;"),
+    "embedding row off by one": ("const int64_t e = (int64_t)ids[i] * D;",
+                                 "const int64_t e = (int64_t)(ids[i] > 0 ? ids[i] - 1 : 0) * D;"),
+    "embedding keeps text positions at zero": (
+        "for (int32_t d = 0; d < D; d++) to[d] = e_bf16 ? bf16_bits(e_bf16[e + d]) : e_f64[e + d];",
+        "for (int32_t d = 0; d < D; d++) to[d] = 0.0 * e;"),
+    "embedding without the id range check": ("if (bad_id) return -2;", "(void)bad_id;"),
+    "embedding without the count check": ("if (n_img != P) return -1;", "(void)n_img;"),
+    "embedding places visual rows in reverse": (
+        "      const double *from = src[j] >= 0                  ? rows + src[j] * D\n                           : src[j] == ORC_SRC_NEWLINE ? newline",
+        "      const int64_t jj = P - 1 - j;\n      const double *from = src[jj] >= 0                 ? rows + src[jj] * D\n                           : src[jj] == ORC_SRC_NEWLINE ? newline"),
+    "bf16 table widened as the low half": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
 }
 
 
