@@ -59,7 +59,8 @@ typedef enum {
   VLB_ERR_WORKSPACE = 5,   /* workspace smaller than vlb_workspace_bytes() */
   VLB_ERR_MASK_COUNT = 6,  /* placeholder count != assembled slots (device-detected) */
   VLB_ERR_UNSUPPORTED = 7, /* a valid but unsupported setting */
-  VLB_ERR_HIP = 8          /* a HIP runtime call failed */
+  VLB_ERR_HIP = 8,         /* a HIP runtime call failed */
+  VLB_ERR_TOKEN_ID = 9     /* a text token id outside [0, vocab) (device-detected) */
 } vlb_status;
 
 typedef enum { VLB_F32 = 0, VLB_BF16 = 1 } vlb_dtype;
@@ -184,6 +185,25 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
                             const uint8_t *mask, int64_t seq_len, void *seq, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* The whole embedded sequence in one call [VL2 Tile-sequence assembly, last
+ * paragraph; VL2 language config: vocab_size 102400, image_token_index
+ * 100015]: every position s of seq [seq_len][out_dim] whose id is not
+ * image_token_id receives row ids[s] of the token-embedding table embed
+ * [vocab][out_dim]; the positions holding image_token_id receive the
+ * projected visual rows (and newline / separator rows), in order, exactly as
+ * vlb_bridge_fused places them.  Every row of seq is written.
+ *   ids: int32 [seq_len] (device).  embed: dtype, row-major.
+ *   Device-detected errors (reported by vlb_check; nothing is written): the
+ *   number of image_token_id positions differs from vlb_num_slots
+ *   (VLB_ERR_MASK_COUNT), else a text id lies outside [0, vocab)
+ *   (VLB_ERR_TOKEN_ID).  A batch without images (n_views = 0) writes the
+ *   text embeddings only.  Workspace: vlb_workspace_bytes(p, b, seq_len). */
+vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const vlb_weights *w, const void *newline, const void *separator,
+                            const int32_t *ids, int32_t image_token_id, const void *embed,
+                            int64_t vocab, int64_t seq_len, void *seq, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* Waits for stream and returns the status recorded on the device by the last
  * vlb_scatter_tokens / vlb_bridge_fused that used this workspace (VLB_OK or
  * VLB_ERR_MASK_COUNT), or VLB_ERR_HIP. */
@@ -204,7 +224,8 @@ enum {
   VLB_K_SCATTER = 6, /* standalone row scatter */
   VLB_K_MERGE = 7,   /* standalone space-to-depth */
   VLB_K_PACK = 8,    /* weight re-layout */
-  VLB_K_COUNT = 9
+  VLB_K_EMBED = 9,   /* token-embedding rows */
+  VLB_K_COUNT = 10
 };
 
 /* Launch timing.  mask bit kid (1 << VLB_K_*) enables timing of that kernel

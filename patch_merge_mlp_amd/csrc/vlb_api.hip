@@ -305,17 +305,30 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
 
 // Prefix sum of the mask and the assembly map -> dst_row; newline / separator
 // rows are written to their slots here.
+// Where the placeholders are: a uint8 mask, or token ids equal to image_id
+// (the other ids must lie in [0, vocab)).
+struct PlaceSrc {
+  const uint8_t *mask;
+  const int32_t *ids;
+  int32_t image_id;
+  int64_t vocab;
+};
+
 vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
-                     const void *newline, const void *separator, const uint8_t *mask,
+                     const void *newline, const void *separator, const PlaceSrc &src,
                      int64_t seq_len, void *seq, uint8_t *ws, hipStream_t s) {
   int32_t *status = reinterpret_cast<int32_t *>(ws + pl.off_status);
   int32_t *slot_pos = reinterpret_cast<int32_t *>(ws + pl.off_slot);
   int32_t *dst_row = reinterpret_cast<int32_t *>(ws + pl.off_dst);
   if (b->layout == VLB_LAYOUT_PLAIN) {  // token row r -> the r-th placeholder: the scan writes dst_row
-    VLB_LAUNCH(VLB_K_SCAN, s, vlb::launch_scan(mask, seq_len, pl.P, dst_row, status, true, s));
+    VLB_LAUNCH(VLB_K_SCAN, s,
+               vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, dst_row,
+                                status, true, s));
     return VLB_OK;
   }
-  VLB_LAUNCH(VLB_K_SCAN, s, vlb::launch_scan(mask, seq_len, pl.P, slot_pos, status, false, s));
+  VLB_LAUNCH(VLB_K_SCAN, s,
+             vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, slot_pos,
+                              status, false, s));
   for (int i0 = 0; i0 < b->n_images; i0 += vlb::kPlaceImages) {
     PlaceChunk c{};
     c.n = std::min(vlb::kPlaceImages, b->n_images - i0);
@@ -483,7 +496,7 @@ vlb_status vlb_scatter_tokens(const vlb_projector *p, const vlb_batch *b, const 
   if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  st = run_place(p, b, pl, newline, separator, mask, seq_len, seq, w8, s);
+  st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8, s);
   if (st != VLB_OK) return st;
   VLB_LAUNCH(VLB_K_SCATTER, s,
              vlb::launch_scatter(p->dtype, rows, pl.T, p->out_dim,
@@ -506,8 +519,43 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  st = run_place(p, b, pl, newline, separator, mask, seq_len, seq, w8, s);
+  st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8, s);
   if (st != VLB_OK) return st;
+  return run_project(p, b, pl, features, w, seq,
+                     reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s);
+}
+
+vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const vlb_weights *w, const void *newline, const void *separator,
+                            const int32_t *ids, int32_t image_token_id, const void *embed,
+                            int64_t vocab, int64_t seq_len, void *seq, void *ws, size_t ws_bytes,
+                            void *stream) {
+  Plan pl;
+  vlb_status st = make_plan(p, b, seq_len, &pl);
+  if (st != VLB_OK) return st;
+  if (!ids || !embed || !seq || !ws) return VLB_ERR_NULL;
+  if (!aligned16(ids) || !aligned16(embed) || !aligned16(seq) || !aligned16(ws))
+    return VLB_ERR_ALIGN;
+  if (seq_len < 1 || vocab < 1 || vocab > kI32Max) return VLB_ERR_SHAPE;
+  if (pl.T > 0) {
+    if ((st = check_weights(p, w)) != VLB_OK) return st;
+    if (!features) return VLB_ERR_NULL;
+    if (!aligned16(features)) return VLB_ERR_ALIGN;
+    if (b->layout == VLB_LAYOUT_TILED_2D) {
+      if (!newline || !separator) return VLB_ERR_NULL;
+      if (!aligned16(newline) || !aligned16(separator)) return VLB_ERR_ALIGN;
+    }
+  }
+  if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  st = run_place(p, b, pl, newline, separator, PlaceSrc{nullptr, ids, image_token_id, vocab},
+                 seq_len, seq, w8, s);
+  if (st != VLB_OK) return st;
+  VLB_LAUNCH(VLB_K_EMBED, s,
+             vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
+                                    reinterpret_cast<const int32_t *>(w8 + pl.off_status), seq, s));
+  if (pl.T == 0) return VLB_OK;
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s);
 }
@@ -532,6 +580,7 @@ const char *vlb_status_str(vlb_status s) {
     case VLB_ERR_MASK_COUNT: return "placeholder count differs from assembled slots";
     case VLB_ERR_UNSUPPORTED: return "unsupported setting";
     case VLB_ERR_HIP: return "HIP runtime error";
+    case VLB_ERR_TOKEN_ID: return "text token id outside the vocabulary";
   }
   return "unknown status";
 }

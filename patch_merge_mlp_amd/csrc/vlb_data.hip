@@ -46,65 +46,106 @@ __global__ void k_plan(PlanChunk c, RowDesc *desc) {
 }
 
 // ---------------------------------------------------------------------------
-// Placeholder prefix sum: slot_pos[j] = position of the j-th nonzero mask byte.
-// One workgroup streams the mask in chunks of 16 KiB with a running carry.
-// status[kCountWord] = number of placeholders; status[kStatusWord] = 0 when it
-// equals P, else VLB_ERR_MASK_COUNT.
+// Placeholder prefix sum: slot_pos[j] = position of the j-th placeholder.
+// The placeholders are the nonzero bytes of a mask, or (token-id form) the
+// positions whose id equals the image token; in the id form every other id
+// must lie in [0, vocab).  One workgroup streams the sequence in chunks of
+// 16K positions with a running carry.  status[kCountWord] = number of
+// placeholders; status[kStatusWord] = 0, VLB_ERR_MASK_COUNT when the count
+// differs from P, else VLB_ERR_TOKEN_ID when a text id is out of range.
 // Plain layout (direct): token row r goes to the r-th placeholder, so the
-// positions are the rows' destinations.  A counting pass runs first and the
-// positions are written to dst_row only when the count matches; otherwise
+// positions are the rows' destinations.  A checking pass runs first and the
+// positions are written to dst_row only when everything is valid; otherwise
 // every dst_row entry (P of them) is -1 and nothing is placed.
 constexpr int kScanThreads = 1024;
+constexpr int kErrTokenId = 9;  // VLB_ERR_TOKEN_ID
 
-// Nonzero bytes among the 16 at mask[off] (bounded by S), unpacked into b.
-__device__ __forceinline__ int scan_load(const uint8_t *mask, int64_t S, int64_t off, uint8_t (&b)[16]) {
-  if (off + 16 <= S) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(mask + off);
+struct ScanSrc {
+  const uint8_t *mask;  // mask form, or
+  const int32_t *ids;   // token-id form
+  int32_t image_id;
+  int64_t vocab;
+};
+
+// Placeholder flags of the 16 positions at off (bounded by S) into b; returns
+// their count and adds the out-of-range text ids to bad.
+__device__ __forceinline__ int scan_load(const ScanSrc &src, int64_t S, int64_t off,
+                                         uint8_t (&b)[16], int &bad) {
+  if (src.ids) {
+    int32_t id[16];
+    if (off + 16 <= S) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = reinterpret_cast<const uint4 *>(src.ids + off)[q];
+        id[4 * q] = static_cast<int32_t>(v.x);
+        id[4 * q + 1] = static_cast<int32_t>(v.y);
+        id[4 * q + 2] = static_cast<int32_t>(v.z);
+        id[4 * q + 3] = static_cast<int32_t>(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) id[i] = (off + i < S) ? src.ids[off + i] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool live = off + i < S;
+      b[i] = live && id[i] == src.image_id;
+      bad += live && !b[i] && (id[i] < 0 || id[i] >= src.vocab);
+    }
+  } else if (off + 16 <= S) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(src.mask + off);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) b[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xff;
+    for (int i = 0; i < 16; ++i) b[i] = ((w[i >> 2] >> (8 * (i & 3))) & 0xff) != 0;
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) b[i] = (off + i < S) ? mask[off + i] : 0;
+    for (int i = 0; i < 16; ++i) b[i] = (off + i < S) ? src.mask[off + i] != 0 : 0;
   }
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cnt += b[i] != 0;
+  for (int i = 0; i < 16; ++i) cnt += b[i];
   return cnt;
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t *mask, int64_t S, int64_t P,
+__device__ __forceinline__ int block_sum(int v, int32_t *shared_slot) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if (threadIdx.x == 0) *shared_slot = 0;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) atomicAdd(shared_slot, v);
+  __syncthreads();
+  return *shared_slot;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(ScanSrc src, int64_t S, int64_t P,
                                                       int32_t *slot_pos, int32_t *status,
                                                       bool direct) {
   __shared__ int32_t wsum[kScanThreads / 64];
-  __shared__ int32_t s_total;
+  __shared__ int32_t s_total, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (direct) {  // counting pass
-    int cnt = 0;
+  if (direct) {  // checking pass
+    int cnt = 0, bad = 0;
     for (int64_t base = 0; base < S; base += kScanThreads * 16) {
       uint8_t b[16];
-      cnt += scan_load(mask, S, base + static_cast<int64_t>(tid) * 16, b);
+      cnt += scan_load(src, S, base + static_cast<int64_t>(tid) * 16, b, bad);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
-    if (tid == 0) s_total = 0;
-    __syncthreads();
-    if (lane == 0) atomicAdd(&s_total, cnt);
-    __syncthreads();
-    if (s_total != P) {
+    const int total = block_sum(cnt, &s_total);
+    const int nbad = block_sum(bad, &s_bad);
+    if (total != P || nbad != 0) {
       for (int64_t r = tid; r < P; r += kScanThreads) slot_pos[r] = -1;
       if (tid == 0) {
-        status[kCountWord] = s_total;
-        status[kStatusWord] = kErrMaskCount;
+        status[kCountWord] = total;
+        status[kStatusWord] = total != P ? kErrMaskCount : kErrTokenId;
       }
       return;
     }
   }
   int32_t carry = 0;
+  int bad = 0;
   for (int64_t base = 0; base < S; base += kScanThreads * 16) {
     const int64_t off = base + static_cast<int64_t>(tid) * 16;
     uint8_t b[16];
-    const int cnt = scan_load(mask, S, off, b);
+    const int cnt = scan_load(src, S, off, b, bad);
     int x = cnt;  // inclusive scan inside the wave
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -126,13 +167,36 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const uint8_t *mask, int6
     int32_t pos = carry + (x - cnt) + (wid > 0 ? wsum[wid - 1] : 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (b[i]) slot_pos[pos++] = static_cast<int32_t>(off + i);
+      if (b[i] && pos < P) slot_pos[pos++] = static_cast<int32_t>(off + i);
     carry += wsum[kScanThreads / 64 - 1];
     __syncthreads();
   }
+  const int nbad = block_sum(bad, &s_bad);
   if (tid == 0) {
     status[kCountWord] = carry;
-    status[kStatusWord] = (carry == P) ? 0 : kErrMaskCount;
+    status[kStatusWord] = carry != P ? kErrMaskCount : (nbad ? kErrTokenId : 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token-embedding rows: seq[s] = embed[ids[s]] for every position whose id is
+// not the image token, nothing when the scan reported an error.  One wave per
+// position, 16-byte copies.
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed_rows(const int32_t *ids, int64_t S, int32_t image_id,
+                                                    const T *embed, int D, const int32_t *status,
+                                                    T *seq) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  if (status[kStatusWord] != 0) return;
+  const int n16 = D * static_cast<int>(sizeof(T)) / 16;
+  for (int64_t s = wave; s < S; s += nwaves) {
+    const int32_t id = ids[s];
+    if (id == image_id) continue;
+    const uint4 *from = reinterpret_cast<const uint4 *>(embed + static_cast<int64_t>(id) * D);
+    uint4 *to = reinterpret_cast<uint4 *>(seq + s * D);
+    for (int q = lane; q < n16; q += 64) to[q] = from[q];
   }
 }
 
@@ -514,10 +578,27 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
-                       int32_t *status, bool direct, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, mask, S, P, slot_pos, status,
+hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
+                       int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
+                       hipStream_t s) {
+  const ScanSrc src{mask, ids, image_id, vocab};
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, src, S, P, slot_pos, status,
                      direct);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
+                             const void *embed, int D, const int32_t *status, void *seq,
+                             hipStream_t s) {
+  if (S <= 0) return hipSuccess;
+  const int grid = grid_for(S, 4, 16384);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_embed_rows<float>, dim3(grid), dim3(256), 0, s, ids, S, image_id,
+                       static_cast<const float *>(embed), D, status, static_cast<float *>(seq));
+  else
+    hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(grid), dim3(256), 0, s, ids, S, image_id,
+                       static_cast<const uint16_t *>(embed), D, status,
+                       static_cast<uint16_t *>(seq));
   return hipGetLastError();
 }
 

@@ -101,10 +101,17 @@ inline TilePlan tile_plan(int64_t M, int64_t N) {
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------
 hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
+// Placeholder scan over a uint8 mask (ids == nullptr) or over token ids
+// (placeholder = image_id; other ids must lie in [0, vocab)).
 // direct (plain layout): slot_pos is dst_row [P] and receives the positions
-// themselves, or -1 everywhere when the placeholder count differs from P.
-hipError_t launch_scan(const uint8_t *mask, int64_t S, int64_t P, int32_t *slot_pos,
-                       int32_t *status, bool direct, hipStream_t s);
+// themselves, or -1 everywhere when the input is invalid.
+hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
+                       int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
+                       hipStream_t s);
+// seq[s] = embed[ids[s]] where ids[s] != image_id (nothing if the scan failed).
+hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
+                             const void *embed, int D, const int32_t *status, void *seq,
+                             hipStream_t s);
 hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
                               const int32_t *status, int32_t *dst_row, const void *newline,
                               const void *separator, void *seq, int D, hipStream_t s);

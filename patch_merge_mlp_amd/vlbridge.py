@@ -19,12 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvlbridge.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
-    ERR_UNSUPPORTED, ERR_HIP = range(9)
+    ERR_UNSUPPORTED, ERR_HIP, ERR_TOKEN_ID = range(10)
 F32, BF16 = 0, 1
 GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
-K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK = range(9)
-KERNEL_NAMES = ["plan", "scan", "place", "layernorm", "gemm1", "gemm2", "scatter", "merge", "pack"]
+K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK, K_EMBED = range(10)
+KERNEL_NAMES = ["plan", "scan", "place", "layernorm", "gemm1", "gemm2", "scatter", "merge", "pack",
+                "embed"]
 
 
 class VlbError(RuntimeError):
@@ -80,6 +81,8 @@ def lib():
             "vlb_scatter_tokens": (st, [pp, pb, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
             "vlb_bridge_fused": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, i64, vp,
                                       vp, sz, vp]),
+            "vlb_bridge_embed": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, ct.c_int32,
+                                      vp, i64, i64, vp, vp, sz, vp]),
             "vlb_check": (st, [vp, vp]),
             "vlb_status_str": (ct.c_char_p, [st]),
             "vlb_prof_enable": (st, [ct.c_int32]),
@@ -298,6 +301,30 @@ def vlb_bridge_fused(p, b: Batch, features, w: Weights, newline, separator, mask
                                   _ptr(newline), _ptr(separator), _ptr(mask), seq.shape[0],
                                   _ptr(seq), _ptr(ws), ws.numel(), _stream(stream)),
            "vlb_bridge_fused")
+
+
+def vlb_bridge_embed(p, b: Batch, features, w: Weights, newline, separator, ids, image_token_id,
+                     embed, seq, ws, stream=None):
+    """Every row of seq: text positions from the embedding table, image-token
+    positions from the bridge (see vlb_bridge_embed in the header)."""
+    dt = _tdtype(p)
+    if ids.dtype != torch.int32 or ids.dim() != 1:
+        raise ValueError("ids must be int32 [seq_len]")
+    if seq.dim() != 2 or seq.shape[1] != p.out_dim or seq.shape[0] != ids.numel():
+        raise ValueError("seq must be [seq_len, out_dim]")
+    if seq.dtype != dt or embed.dtype != dt or embed.dim() != 2 or embed.shape[1] != p.out_dim:
+        raise ValueError("seq / embed dtype or shape")
+    T = vlb_num_tokens(p, b)
+    if T > 0:
+        _need(features, _pixels(b) * p.C, dt, "features")
+        _check_weights(p, w)
+        _need(newline, p.out_dim, dt, "newline")
+        _need(separator, p.out_dim, dt, "separator")
+    wc = w.c() if w is not None else vlb_weights()
+    _check(lib().vlb_bridge_embed(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                  _ptr(newline), _ptr(separator), _ptr(ids), int(image_token_id),
+                                  _ptr(embed), embed.shape[0], seq.shape[0], _ptr(seq), _ptr(ws),
+                                  ws.numel(), _stream(stream)), "vlb_bridge_embed")
 
 
 def vlb_check(ws, stream=None) -> int:

@@ -15,6 +15,13 @@ Value distributions:
   Linear weights: std fan_in**-0.5; biases: std 0.1 (variance 0.01)
   LayerNorm gamma = 1 + 0.1 N(0,1), beta = 0.1 N(0,1)
 bf16 workloads draw in float32 and round to bf16 (round-to-nearest-even).
+
+Token ids for the embedded-sequence entry point come from a second generator
+(seed 1000 + workload seed, so the draws above are unchanged): the
+token-embedding table [VOCAB][out_dim] ~ N(0, 1), then the text ids, uniform
+over [0, VOCAB) without the image token; placeholder positions hold
+IMAGE_TOKEN_ID.  VOCAB and IMAGE_TOKEN_ID are the VL2 language config's
+vocab_size and image_token_index.
 """
 from __future__ import annotations
 
@@ -22,6 +29,10 @@ from dataclasses import dataclass, field
 from typing import Callable, List, Optional, Sequence, Tuple
 
 import torch
+
+
+VOCAB = 102400           # VL2 language config vocab_size
+IMAGE_TOKEN_ID = 100015  # VL2 image_token_index
 
 
 @dataclass
@@ -147,6 +158,18 @@ class Generator:
             out["newline"] = out["separator"] = None
         out["seq"] = self._randn((w.seq_len, w.out_dim)).to(dt)
         return out
+
+
+def token_inputs(w: Workload, mask: torch.Tensor, vocab: int = VOCAB,
+                 image_token_id: int = IMAGE_TOKEN_ID) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(ids int32 [seq_len], embedding table [vocab][out_dim] in the workload dtype):
+    image_token_id at the mask's positions, uniform text ids elsewhere."""
+    g = torch.Generator("cpu").manual_seed(1000 + w.seed)
+    table = torch.randn((vocab, w.out_dim), generator=g, dtype=torch.float32).to(w.torch_dtype)
+    ids = torch.randint(0, vocab - 1, (w.seq_len,), generator=g, dtype=torch.int64)
+    ids = torch.where(ids >= image_token_id, ids + 1, ids)  # skip the image token
+    ids = torch.where(mask.bool(), torch.full_like(ids, image_token_id), ids)
+    return ids.to(torch.int32), table
 
 
 def make(w: Workload, span_fn: Callable[[Workload], Sequence[int]],

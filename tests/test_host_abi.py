@@ -158,6 +158,38 @@ def test_entry_points_validate_before_launching():
                               None, 0, None) == v.OK
 
 
+def test_embed_validates_before_launching():
+    """vlb_bridge_embed: the same checks as the fused call plus the token ids and the
+    embedding table; text-only batches need no projector inputs."""
+    L = v.lib()
+    p = _proj()
+    b = v.Batch([(4, 4)], [1])
+    need = v.vlb_workspace_bytes(p, b, 32)
+    w = v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE)
+    V = 1000
+
+    def call(b=b, feats=FAKE, w=w, ids=FAKE, embed=FAKE, vocab=V, S=32, seq=FAKE, ws=FAKE,
+             ws_bytes=need):
+        return L.vlb_bridge_embed(ct.byref(p), ct.byref(b.c), feats, ct.byref(w) if w else None,
+                                  None, None, ids, 5, embed, vocab, S, seq, ws, ws_bytes, None)
+
+    assert call(ids=None) == v.ERR_NULL
+    assert call(embed=None) == v.ERR_NULL
+    assert call(ids=FAKE + 4) == v.ERR_ALIGN
+    assert call(embed=FAKE + 8) == v.ERR_ALIGN
+    assert call(vocab=0) == v.ERR_SHAPE
+    assert call(vocab=1 << 31) == v.ERR_SHAPE
+    assert call(S=0) == v.ERR_SHAPE
+    assert call(feats=None) == v.ERR_NULL
+    assert call(w=v.vlb_weights(None, None, None, FAKE, FAKE, FAKE)) == v.ERR_NULL
+    assert call(ws_bytes=need - 1) == v.ERR_WORKSPACE
+    # text only: features and weights may be null, the workspace still holds the status
+    e = v.Batch([], [])
+    need_e = v.vlb_workspace_bytes(p, e, 32)
+    assert need_e > 0
+    assert call(b=e, feats=None, w=None, ws_bytes=need_e - 1) == v.ERR_WORKSPACE
+
+
 def test_packed_bytes():
     """Tile-blocked weights: rows padded to a multiple of 256, K unchanged."""
     p = _proj()  # C=64, k=2 -> K1=256; hidden=128; out_dim=64
@@ -172,6 +204,6 @@ def test_packed_bytes():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert v.status_str(s)
     assert "placeholder" in v.status_str(v.ERR_MASK_COUNT)
