@@ -143,6 +143,14 @@ def _declare(L):
     L.orc_embed_scatter.restype = ct.c_int32
     L.orc_embed_scatter.argtypes = [_I64, i64, _D, _D, _D, ct.POINTER(ct.c_int32), i64,
                                     ct.c_int32, ct.POINTER(ct.c_uint16), _D, i64, ct.c_int32, _D]
+    L.orc_scatter_backward.restype = ct.c_int32
+    L.orc_scatter_backward.argtypes = [_I64, i64, _U8, i64, ct.c_int32, _D, i64, _D, _D, _D]
+    L.orc_project_backward.restype = None
+    L.orc_project_backward.argtypes = [ct.POINTER(_Spec)] + [_D] * 14
+    L.orc_hidden_unit_grads.restype = None
+    L.orc_hidden_unit_grads.argtypes = [ct.POINTER(_Spec)] + [_D] * 7 + [ct.c_int32, _D, _D, _D]
+    L.orc_pixel_grad.restype = None
+    L.orc_pixel_grad.argtypes = [ct.POINTER(_Spec)] + [_D] * 7 + [ct.c_int32] * 3 + [_D]
 
 
 def _f64(a) -> np.ndarray:
@@ -332,3 +340,62 @@ def embed_scatter(src, rows, newline, separator, ids, image_id, embed, D):
         bits.ctypes.data_as(ct.POINTER(ct.c_uint16)) if bits is not None else None,
         _dp(e64) if e64 is not None else None, vocab, D, _dp(seq)))
     return st, seq
+
+
+# ---- backward --------------------------------------------------------------
+
+def scatter_backward(src, mask, dseq, T):
+    """Gradient of scatter: (status, drows [T][D], dnewline [D], dseparator [D]);
+    status -1 = placeholder-count mismatch (outputs zero)."""
+    src = np.ascontiguousarray(src, dtype=np.int64)
+    dseq = _f64(dseq)
+    S, D = dseq.shape
+    mask = np.ascontiguousarray(np.asarray(mask), dtype=np.uint8)
+    drows = np.zeros((T, D))
+    dnl = np.zeros(D)
+    dsp = np.zeros(D)
+    st = int(lib().orc_scatter_backward(src.ctypes.data_as(_I64), len(src),
+                                        mask.ctypes.data_as(_U8), S, D, _dp(dseq), T,
+                                        _dp(drows), _dp(dnl), _dp(dsp)))
+    return st, drows, dnl, dsp
+
+
+def project_backward(spec: Spec, x, gamma, beta, W1, b1, W2, dY) -> dict:
+    """All projector gradients for the output-row gradient dY [T][out_dim]:
+    dict with dx [n_pixels][C], dw1, db1, dw2, db2 and (LayerNorm) dgamma, dbeta."""
+    s = spec.c()
+    x = _f64(x)
+    K1 = spec.C * spec.k * spec.k
+    out = {"dx": np.zeros_like(x), "dw1": np.zeros((spec.hidden, K1)),
+           "db1": np.zeros(spec.hidden), "dw2": np.zeros((spec.out_dim, spec.hidden)),
+           "db2": np.zeros(spec.out_dim), "dgamma": np.zeros(spec.C), "dbeta": np.zeros(spec.C)}
+    ins = [x] + [_f64(a) for a in (gamma, beta, W1, b1, W2, dY)]
+    lib().orc_project_backward(ct.byref(s), *[_dp(a) for a in ins],
+                               *[_dp(out[n]) for n in ("dx", "dw1", "db1", "dw2", "db2",
+                                                       "dgamma", "dbeta")])
+    if not spec.has_ln:
+        del out["dgamma"], out["dbeta"]
+    return out
+
+
+def hidden_unit_grads(spec: Spec, x, gamma, beta, W1, b1, W2, dY, h: int):
+    """(row h of dW1, db1[h], column h of dW2)."""
+    s = spec.c()
+    K1 = spec.C * spec.k * spec.k
+    dw1 = np.zeros(K1)
+    db1 = np.zeros(1)
+    dw2 = np.zeros(spec.out_dim)
+    ins = [_f64(a) for a in (x, gamma, beta, W1, b1, W2, dY)]
+    lib().orc_hidden_unit_grads(ct.byref(s), *[_dp(a) for a in ins], int(h), _dp(dw1), _dp(db1),
+                                _dp(dw2))
+    return dw1, float(db1[0]), dw2
+
+
+def pixel_grad(spec: Spec, x, gamma, beta, W1, b1, W2, dY, view: int, y: int, xx: int):
+    """Feature gradient [C] of pixel (y, xx) of view `view`."""
+    s = spec.c()
+    out = np.zeros(spec.C)
+    ins = [_f64(a) for a in (x, gamma, beta, W1, b1, W2, dY)]
+    lib().orc_pixel_grad(ct.byref(s), *[_dp(a) for a in ins], int(view), int(y), int(xx),
+                         _dp(out))
+    return out

@@ -401,3 +401,234 @@ int32_t orc_embed_scatter(const int64_t *src, int64_t P, const double *rows,
   }
   return 0;
 }
+
+/* ---- backward --------------------------------------------------------- */
+/*
+ * The projector is the trained part of the bridge: [V4V header] trains only its
+ * parameters (the LayerNorm, both Linears) with tower and text model frozen,
+ * and [VOIE "Pendant le pré-entraînement du squelette"] keeps the projector
+ * (and the tower's final norm, whose gradient is the one reaching the features)
+ * trainable.  The gradients below are the chain rule taken through the forward
+ * steps in reverse: scatter, Linear2, activation, Linear1, space-to-depth,
+ * LayerNorm.
+ */
+
+/* d/dz of the activation. erf form: Phi(z) + z phi(z). tanh form: the
+ * derivative of 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3). */
+static double act_slope(int32_t act, double z) {
+  if (act == ORC_GELU_ERF)
+    return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * M_PI);
+  if (act == ORC_GELU_TANH) {
+    const double a = sqrt(2.0 / M_PI);
+    const double t = tanh(a * (z + 0.044715 * z * z * z));
+    return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * a * (1.0 + 3.0 * 0.044715 * z * z);
+  }
+  return 1.0;
+}
+
+static double act_value(int32_t act, double z) {
+  if (act == ORC_GELU_ERF) orc_gelu_erf(&z, 1);
+  else if (act == ORC_GELU_TANH) orc_gelu_tanh(&z, 1);
+  return z;
+}
+
+int32_t orc_scatter_backward(const int64_t *src, int64_t P, const uint8_t *mask, int64_t S,
+                             int32_t D, const double *dseq, int64_t T, double *drows,
+                             double *dnewline, double *dseparator) {
+  int64_t count = 0;
+  for (int64_t i = 0; i < S; i++) count += mask[i] != 0;
+  if (count != P) return -1;
+  memset(drows, 0, sizeof(double) * T * D);
+  memset(dnewline, 0, sizeof(double) * D);
+  memset(dseparator, 0, sizeof(double) * D);
+  int64_t j = 0;
+  for (int64_t i = 0; i < S; i++) {
+    if (!mask[i]) continue;
+    const double *g = dseq + i * D;
+    if (src[j] >= 0) {
+      memcpy(drows + src[j] * D, g, sizeof(double) * D);
+    } else {
+      double *to = src[j] == ORC_SRC_NEWLINE ? dnewline : dseparator;
+      for (int32_t d = 0; d < D; d++) to[d] += g[d];
+    }
+    j++;
+  }
+  return 0;
+}
+
+/* Backward of the LayerNorm of one pixel: x its C inputs, dn the gradient of
+ * its normalised output.  With xh = (x - mean) * r, r = 1 / sqrt(var + eps)
+ * and n = gamma * xh + beta:
+ *   dgamma += dn * xh,  dbeta += dn,
+ *   dx = r * (g - mean(g) - xh * mean(g * xh)),  g = gamma * dn. */
+static void ln_backward_pixel(const double *x, const double *dn, int32_t C, const double *gamma,
+                              double eps, double *dx, double *dgamma, double *dbeta) {
+  double mean = 0.0;
+  for (int32_t c = 0; c < C; c++) mean += x[c];
+  mean /= C;
+  double var = 0.0;
+  for (int32_t c = 0; c < C; c++) var += (x[c] - mean) * (x[c] - mean);
+  var /= C;
+  const double r = 1.0 / sqrt(var + eps);
+  double mg = 0.0, mgx = 0.0;
+  for (int32_t c = 0; c < C; c++) {
+    const double xh = (x[c] - mean) * r, g = gamma[c] * dn[c];
+    if (dgamma) dgamma[c] += dn[c] * xh;
+    if (dbeta) dbeta[c] += dn[c];
+    mg += g;
+    mgx += g * xh;
+  }
+  mg /= C;
+  mgx /= C;
+  for (int32_t c = 0; c < C; c++) {
+    const double xh = (x[c] - mean) * r;
+    dx[c] = r * (gamma[c] * dn[c] - mg - xh * mgx);
+  }
+}
+
+/* First pixel of view v and the first token row of view v. */
+static void view_bases(const orc_spec *s, int32_t v, int64_t *pix, int64_t *row) {
+  *pix = 0;
+  *row = 0;
+  for (int32_t q = 0; q < v; q++) {
+    *pix += (int64_t)s->grid_h[q] * s->grid_w[q];
+    *row += orc_view_tokens(s->grid_h[q], s->grid_w[q], s->k);
+  }
+}
+
+void orc_project_backward(const orc_spec *s, const double *x, const double *gamma,
+                          const double *beta, const double *W1, const double *b1,
+                          const double *W2, const double *dY, double *dx, double *dW1,
+                          double *db1, double *dW2, double *db2, double *dgamma,
+                          double *dbeta) {
+  const int32_t C = s->C, k = s->k, H = s->hidden, O = s->out_dim;
+  const int64_t K1 = (int64_t)C * k * k;
+  int64_t npix = 0;
+  for (int32_t v = 0; v < s->n_views; v++) npix += (int64_t)s->grid_h[v] * s->grid_w[v];
+  memset(dW1, 0, sizeof(double) * H * K1);
+  memset(db1, 0, sizeof(double) * H);
+  memset(dW2, 0, sizeof(double) * O * H);
+  memset(db2, 0, sizeof(double) * O);
+  if (s->has_ln) {
+    memset(dgamma, 0, sizeof(double) * C);
+    memset(dbeta, 0, sizeof(double) * C);
+  }
+  double *m = (double *)malloc(sizeof(double) * K1);
+  double *z = (double *)malloc(sizeof(double) * H);
+  double *dz = (double *)malloc(sizeof(double) * H);
+  double *dm = (double *)malloc(sizeof(double) * K1);
+  double *dn = (double *)calloc((size_t)npix * C, sizeof(double)); /* d(LN output) per pixel */
+  int64_t r = 0, pix = 0;
+  for (int32_t v = 0; v < s->n_views; v++) {
+    const int32_t gh = s->grid_h[v], gw = s->grid_w[v];
+    const int64_t wp = orc_merged_side(gw, k), nt = orc_view_tokens(gh, gw, k);
+    for (int64_t t = 0; t < nt; t++, r++) {
+      const double *dy = dY + r * O;
+      /* forward of the row: merged features, Linear1 pre-activation */
+      orc_merged_row(s, x, gamma, beta, r, m);
+      orc_linear(m, 1, (int32_t)K1, W1, b1, H, z, 1);
+      /* Linear2: y = W2 a + b2 */
+      for (int32_t o = 0; o < O; o++) db2[o] += dy[o];
+      for (int32_t o = 0; o < O; o++)
+        for (int32_t h = 0; h < H; h++) dW2[(int64_t)o * H + h] += dy[o] * act_value(s->act, z[h]);
+      /* activation, then Linear1: z = W1 m + b1 */
+      for (int32_t h = 0; h < H; h++) {
+        double da = 0.0;
+        for (int32_t o = 0; o < O; o++) da += dy[o] * W2[(int64_t)o * H + h];
+        dz[h] = da * act_slope(s->act, z[h]);
+        db1[h] += dz[h];
+        for (int64_t i = 0; i < K1; i++) dW1[h * K1 + i] += dz[h] * m[i];
+      }
+      for (int64_t i = 0; i < K1; i++) {
+        double acc = 0.0;
+        for (int32_t h = 0; h < H; h++) acc += dz[h] * W1[h * K1 + i];
+        dm[i] = acc;
+      }
+      /* space-to-depth, reversed: feature c*k*k + dy*k + dx of token (ty, tx)
+       * came from cell (ty*k + dy, tx*k + dx); padded cells take no gradient */
+      const int64_t ty = t / wp, tx = t % wp;
+      for (int32_t ddy = 0; ddy < k; ddy++)
+        for (int32_t ddx = 0; ddx < k; ddx++) {
+          const int64_t y = ty * k + ddy, xx = tx * k + ddx;
+          if (y >= gh || xx >= gw) continue;
+          for (int32_t c = 0; c < C; c++)
+            dn[(pix + y * gw + xx) * C + c] = dm[(int64_t)c * k * k + ddy * k + ddx];
+        }
+    }
+    pix += (int64_t)gh * gw;
+  }
+  /* LayerNorm, reversed (or the identity without it) */
+  for (int64_t p = 0; p < npix; p++) {
+    if (s->has_ln)
+      ln_backward_pixel(x + p * C, dn + p * C, C, gamma, s->ln_eps, dx + p * C, dgamma, dbeta);
+    else
+      memcpy(dx + p * C, dn + p * C, sizeof(double) * C);
+  }
+  free(m);
+  free(z);
+  free(dz);
+  free(dm);
+  free(dn);
+}
+
+void orc_hidden_unit_grads(const orc_spec *s, const double *x, const double *gamma,
+                           const double *beta, const double *W1, const double *b1,
+                           const double *W2, const double *dY, int32_t h, double *dW1_row,
+                           double *db1_h, double *dW2_col) {
+  const int32_t C = s->C, k = s->k, H = s->hidden, O = s->out_dim;
+  const int64_t K1 = (int64_t)C * k * k, T = orc_total_tokens(s);
+  double *m = (double *)malloc(sizeof(double) * K1);
+  memset(dW1_row, 0, sizeof(double) * K1);
+  memset(dW2_col, 0, sizeof(double) * O);
+  *db1_h = 0.0;
+  for (int64_t r = 0; r < T; r++) {
+    const double *dy = dY + r * O;
+    orc_merged_row(s, x, gamma, beta, r, m);
+    double z = 0.0;
+    for (int64_t i = 0; i < K1; i++) z += m[i] * W1[(int64_t)h * K1 + i];
+    z += b1[h];
+    const double a = act_value(s->act, z);
+    double da = 0.0;
+    for (int32_t o = 0; o < O; o++) {
+      dW2_col[o] += dy[o] * a;
+      da += dy[o] * W2[(int64_t)o * H + h];
+    }
+    const double dz = da * act_slope(s->act, z);
+    *db1_h += dz;
+    for (int64_t i = 0; i < K1; i++) dW1_row[i] += dz * m[i];
+  }
+  free(m);
+}
+
+void orc_pixel_grad(const orc_spec *s, const double *x, const double *gamma, const double *beta,
+                    const double *W1, const double *b1, const double *W2, const double *dY,
+                    int32_t v, int32_t y, int32_t xx, double *dx_out) {
+  const int32_t C = s->C, k = s->k, H = s->hidden, O = s->out_dim;
+  const int64_t K1 = (int64_t)C * k * k;
+  int64_t pix0, row0;
+  view_bases(s, v, &pix0, &row0);
+  const int32_t gw = s->grid_w[v];
+  const int64_t r = row0 + (y / k) * orc_merged_side(gw, k) + xx / k;
+  const int32_t p = (y % k) * k + xx % k;
+  double *m = (double *)malloc(sizeof(double) * K1);
+  double *z = (double *)malloc(sizeof(double) * H);
+  double *dn = (double *)malloc(sizeof(double) * C);
+  orc_merged_row(s, x, gamma, beta, r, m);
+  orc_linear(m, 1, (int32_t)K1, W1, b1, H, z, 1);
+  const double *dy = dY + r * O;
+  for (int32_t c = 0; c < C; c++) dn[c] = 0.0;
+  for (int32_t h = 0; h < H; h++) {
+    double da = 0.0;
+    for (int32_t o = 0; o < O; o++) da += dy[o] * W2[(int64_t)o * H + h];
+    const double dz = da * act_slope(s->act, z[h]);
+    for (int32_t c = 0; c < C; c++) dn[c] += dz * W1[(int64_t)h * K1 + (int64_t)c * k * k + p];
+  }
+  const double *px = x + (pix0 + (int64_t)y * gw + xx) * C;
+  if (s->has_ln)
+    ln_backward_pixel(px, dn, C, gamma, s->ln_eps, dx_out, NULL, NULL);
+  else
+    memcpy(dx_out, dn, sizeof(double) * C);
+  free(m);
+  free(z);
+  free(dn);
+}

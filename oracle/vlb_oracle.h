@@ -123,6 +123,40 @@ int32_t orc_embed_scatter(const int64_t *src, int64_t P, const double *rows,
                           int64_t S, int32_t image_id, const uint16_t *e_bf16,
                           const double *e_f64, int64_t vocab, int32_t D, double *seq);
 
+/* ---- backward (training the projector [V4V header]; [VOIE] "Pendant le
+ * pré-entraînement du squelette") ------------------------------------------- */
+
+/* Gradient of orc_scatter: given dseq (S x D), the gradient of each scattered
+ * token row (drows [T][D]; each row sits in exactly one slot) and of the
+ * newline and separator vectors (summed over every slot that holds them).
+ * Returns 0, or -1 (nothing written) on a placeholder-count mismatch. */
+int32_t orc_scatter_backward(const int64_t *src, int64_t P, const uint8_t *mask, int64_t S,
+                             int32_t D, const double *dseq, int64_t T, double *drows,
+                             double *dnewline, double *dseparator);
+
+/* Gradients of the projector for the gradient dY [T][out_dim] of its output
+ * rows: dx [n_pixels][C] (of the features), dW1 [hidden][C*k*k] (pages' feature
+ * order), db1 [hidden], dW2 [out_dim][hidden], db2 [out_dim], and with the
+ * LayerNorm dgamma, dbeta [C] (untouched, may be NULL, without it).  Padded
+ * cells take no gradient. */
+void orc_project_backward(const orc_spec *s, const double *x, const double *gamma,
+                          const double *beta, const double *W1, const double *b1,
+                          const double *W2, const double *dY, double *dx, double *dW1,
+                          double *db1, double *dW2, double *db2, double *dgamma,
+                          double *dbeta);
+
+/* The same gradients restricted to hidden unit h: row h of dW1, db1[h] and
+ * column h of dW2 (dW2_col [out_dim]). */
+void orc_hidden_unit_grads(const orc_spec *s, const double *x, const double *gamma,
+                           const double *beta, const double *W1, const double *b1,
+                           const double *W2, const double *dY, int32_t h, double *dW1_row,
+                           double *db1_h, double *dW2_col);
+
+/* The feature gradient of one pixel (view v, row y, column xx): dx_out [C]. */
+void orc_pixel_grad(const orc_spec *s, const double *x, const double *gamma, const double *beta,
+                    const double *W1, const double *b1, const double *W2, const double *dY,
+                    int32_t v, int32_t y, int32_t xx, double *dx_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -302,10 +302,144 @@ def pin_embed_scatter(o):
     assert st == 0 and np.array_equal(got, F.embedding(ids[~mask].long(), E).numpy())
 
 
+
+# --- backward ------------------------------------------------------------------
+
+def _torch_projector(x, g, bb, W1, b1, W2, b2, grids, C, k, has_ln, act, eps):
+    """The projector forward composed from library routines (differentiable)."""
+    merged, p = [], 0
+    for gh, gw in grids:
+        v = x[p:p + gh * gw].reshape(gh, gw, C)
+        p += gh * gw
+        if has_ln:
+            v = F.layer_norm(v, (C,), g, bb, eps=eps)
+        hp, wp = -(-gh // k), -(-gw // k)
+        t = F.pad(v.permute(2, 0, 1).unsqueeze(0), (0, wp * k - gw, 0, hp * k - gh))
+        merged.append(F.pixel_unshuffle(t, k)[0].permute(1, 2, 0).reshape(hp * wp, C * k * k))
+    h = F.linear(torch.cat(merged), W1, b1)
+    if act == 0:
+        h = F.gelu(h)
+    elif act == 1:
+        h = F.gelu(h, approximate="tanh")
+    return F.linear(h, W2, b2)
+
+
+def _bwd_problem(seed, C=5, k=2, H=9, O=7, grids=((3, 5), (4, 4), (5, 3))):
+    rng = np.random.default_rng(seed)
+    P = sum(a * b for a, b in grids)
+    T = sum((-(-a // k)) * (-(-b // k)) for a, b in grids)
+    d = dict(x=rng.standard_normal((P, C)) * 2 + 0.5, g=1 + 0.5 * rng.standard_normal(C),
+             bb=rng.standard_normal(C), W1=rng.standard_normal((H, C * k * k)),
+             b1=rng.standard_normal(H), W2=rng.standard_normal((O, H)), b2=rng.standard_normal(O),
+             dY=rng.standard_normal((T, O)))
+    return d, list(grids), C, k, H, O
+
+
+def pin_project_backward_autograd(o):
+    """Every projector gradient equals torch autograd (fp64) through the library
+    forward, for each activation, with the LayerNorm on and off, on padded views."""
+    d, grids, C, k, H, O = _bwd_problem(11)
+    for has_ln in (False, True):
+        for act in (o.GELU_ERF, o.GELU_TANH, o.ACT_NONE):
+            eps = 0.3  # large enough that its place in the formula matters
+            spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[3],
+                          has_ln=has_ln, ln_eps=eps, act=act)
+            ts = {n: torch.from_numpy(d[n]).requires_grad_(True)
+                  for n in ("x", "g", "bb", "W1", "b1", "W2", "b2")}
+            y = _torch_projector(ts["x"], ts["g"], ts["bb"], ts["W1"], ts["b1"], ts["W2"], ts["b2"],
+                                 grids, C, k, has_ln, act, eps)
+            (y * torch.from_numpy(d["dY"])).sum().backward()
+            got = o.project_backward(spec, d["x"], d["g"], d["bb"], d["W1"], d["b1"], d["W2"],
+                                     d["dY"])
+            pairs = [("dx", "x"), ("dw1", "W1"), ("db1", "b1"), ("dw2", "W2"), ("db2", "b2")]
+            if has_ln:
+                pairs += [("dgamma", "g"), ("dbeta", "bb")]
+            for mine, theirs in pairs:
+                assert np.allclose(got[mine], ts[theirs].grad.numpy(), rtol=1e-10, atol=1e-11), \
+                    (has_ln, act, mine)
+
+
+def pin_project_backward_fd(o):
+    """Central finite differences of the (pinned) forward: L = sum(dY * Y)."""
+    d, grids, C, k, H, O = _bwd_problem(12, C=3, H=5, O=4, grids=((3, 3), (2, 5)))
+    spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[2], has_ln=True,
+                  ln_eps=0.2, act=o.GELU_ERF)
+    got = o.project_backward(spec, d["x"], d["g"], d["bb"], d["W1"], d["b1"], d["W2"], d["dY"])
+    names = {"x": "dx", "g": "dgamma", "bb": "dbeta", "W1": "dw1", "b1": "db1", "W2": "dw2",
+             "b2": "db2"}
+    rng = np.random.default_rng(3)
+
+    def loss(dd):
+        y = o.project_rows(spec, dd["x"], dd["g"], dd["bb"], dd["W1"], dd["b1"], dd["W2"],
+                           dd["b2"], nthreads=1)
+        return float((y * d["dY"]).sum())
+
+    h = 1e-5
+    for n, gname in names.items():
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, s)) for s in d[n].shape)
+            plus = {kk: v.copy() for kk, v in d.items()}
+            minus = {kk: v.copy() for kk, v in d.items()}
+            plus[n][idx] += h
+            minus[n][idx] -= h
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            assert abs(fd - got[gname][idx]) <= 1e-6 * max(1.0, abs(fd)), (n, idx, fd,
+                                                                             got[gname][idx])
+
+
+def pin_backward_samples(o):
+    """The sampled forms (one hidden unit; one pixel) equal the full gradients."""
+    d, grids, C, k, H, O = _bwd_problem(13, C=4, k=3, H=6, O=5, grids=((4, 5), (3, 3)))
+    for has_ln, act in ((True, o.GELU_ERF), (False, o.GELU_TANH)):
+        spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[1, 1],
+                      has_ln=has_ln, ln_eps=1e-6, act=act)
+        args = (d["x"], d["g"], d["bb"], d["W1"], d["b1"], d["W2"], d["dY"])
+        full = o.project_backward(spec, *args)
+        for h in range(H):
+            dw1, db1, dw2 = o.hidden_unit_grads(spec, *args, h)
+            assert np.allclose(dw1, full["dw1"][h], rtol=1e-12, atol=1e-13)
+            assert np.isclose(db1, full["db1"][h], rtol=1e-12, atol=1e-13)
+            assert np.allclose(dw2, full["dw2"][:, h], rtol=1e-12, atol=1e-13)
+        p = 0
+        for v, (gh, gw) in enumerate(grids):
+            for y in range(gh):
+                for xx in range(gw):
+                    got = o.pixel_grad(spec, *args, v, y, xx)
+                    assert np.allclose(got, full["dx"][p + y * gw + xx], rtol=1e-12, atol=1e-13)
+            p += gh * gw
+
+
+def pin_scatter_backward(o):
+    """The scatter's gradient equals autograd through masked_scatter of the
+    assembled rows (newline and separator rows summed over their slots); a
+    count mismatch is reported."""
+    g = torch.Generator().manual_seed(5)
+    S, D, T = 14, 3, 4
+    src = np.array([2, -1, 0, -2, 3, -1, 1])
+    mask = np.zeros(S, dtype=np.uint8)
+    mask[[1, 2, 5, 6, 7, 10, 13]] = 1
+    rows = torch.randn(T, D, generator=g, dtype=torch.float64, requires_grad=True)
+    nl = torch.randn(D, generator=g, dtype=torch.float64, requires_grad=True)
+    sp = torch.randn(D, generator=g, dtype=torch.float64, requires_grad=True)
+    seq0 = torch.randn(S, D, generator=g, dtype=torch.float64)
+    G = torch.randn(S, D, generator=g, dtype=torch.float64)
+    A = torch.stack([rows[s] if s >= 0 else (nl if s == -1 else sp) for s in src])
+    m = torch.from_numpy(mask).bool()[:, None].expand(S, D)
+    (seq0.masked_scatter(m, A) * G).sum().backward()
+    st, drows, dnl, dsp = o.scatter_backward(src, mask, G, T)
+    assert st == 0
+    assert np.allclose(drows, rows.grad.numpy(), rtol=1e-14, atol=0)
+    assert np.allclose(dnl, nl.grad.numpy(), rtol=1e-14, atol=1e-15)
+    assert np.allclose(dsp, sp.grad.numpy(), rtol=1e-14, atol=1e-15)
+    bad = mask.copy()
+    bad[0] = 1
+    assert o.scatter_backward(src, bad, G, T)[0] == -1
+
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
        pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
-       pin_embed_scatter]
+       pin_embed_scatter, pin_project_backward_autograd, pin_project_backward_fd,
+       pin_backward_samples, pin_scatter_backward]
 
 
 def failing(o):

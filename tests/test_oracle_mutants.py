@@ -22,8 +22,9 @@ MUTANTS = {
     "merged side rounds down": ("while (g_pad % k != 0) g_pad++;", "g_pad -= g_pad % k;"),
     "padding at the low end": ("if (y >= gh || xx >= gw) return 0.0;\n  return x[(y * gw + xx) * C + c];",
                                "int64_t oy = y - (k_pad_h), ox = xx;\n  (void)ox; if (oy < 0 || y >= gh + 0 || xx >= gw) return 0.0;\n  return x[(oy * gw + xx) * C + c];"),
-    "unbiased variance": ("var /= C;", "var /= (C - 1);"),
-    "eps outside the square root": ("1.0 / sqrt(var + eps)", "1.0 / (sqrt(var) + eps)"),
+    "unbiased variance": ("var /= C;\n    double inv", "var /= (C - 1);\n    double inv"),
+    "eps outside the square root": ("double inv = 1.0 / sqrt(var + eps)",
+                                    "double inv = 1.0 / (sqrt(var) + eps)"),
     "gamma and beta swapped": ("* inv * gamma[c] + beta[c]", "* inv * beta[c] + gamma[c]"),
     "bias dropped": ("j->out[r * j->out_dim + o] = acc + (j->b ? j->b[o] : 0.0);",
                      "j->out[r * j->out_dim + o] = acc;"),
@@ -41,7 +42,8 @@ MUTANTS = {
     "placeholder formula without local newlines": ("(th * hp) * (tw * wp + 1)", "(th * hp) * (tw * wp)"),
     "scatter in reverse": ("    if (!mask[i]) continue;\n    const double *from = src[j] >= 0                  ? rows + src[j] * D",
                            "    if (!mask[i]) continue;\n    j = P - 1 - j; const double *from = src[j] >= 0 ? rows + src[j] * D"),
-    "no count check": ("if (count != P) return -1;", "(void)count;"),
+    "no count check": ("if (count != P) return -1;\n  int64_t j = 0;",
+                       "(void)count;\n  int64_t j = 0;"),
     "param count without second bias": ("hidden * out_dim + out_dim;", "hidden * out_dim;"),
     "embedding row off by one": ("const int64_t e = (int64_t)ids[i] * D;",
                                  "const int64_t e = (int64_t)(ids[i] > 0 ? ids[i] - 1 : 0) * D;"),
@@ -54,6 +56,48 @@ MUTANTS = {
         "      const double *from = src[j] >= 0                  ? rows + src[j] * D\n                           : src[j] == ORC_SRC_NEWLINE ? newline",
         "      const int64_t jj = P - 1 - j;\n      const double *from = src[jj] >= 0                 ? rows + src[jj] * D\n                           : src[jj] == ORC_SRC_NEWLINE ? newline"),
     "bf16 table widened as the low half": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
+    # backward
+    "gelu slope without the z*phi term": (
+        "return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * M_PI);",
+        "return 0.5 * (1.0 + erf(z / sqrt(2.0)));"),
+    "tanh slope without the inner derivative": (
+        "* a * (1.0 + 3.0 * 0.044715 * z * z);", "* a;"),
+    "dW2 from the pre-activation": ("dW2[(int64_t)o * H + h] += dy[o] * act_value(s->act, z[h]);",
+                                    "dW2[(int64_t)o * H + h] += dy[o] * z[h];"),
+    "dW2 transposed": ("dW2[(int64_t)o * H + h] += dy[o] * act_value(s->act, z[h]);",
+                       "dW2[(int64_t)h * O + o] += dy[o] * act_value(s->act, z[h]);"),
+    "db2 dropped": ("for (int32_t o = 0; o < O; o++) db2[o] += dy[o];",
+                    "for (int32_t o = 0; o < O; o++) db2[o] += 0.0 * dy[o];"),
+    "activation gradient without the slope": ("dz[h] = da * act_slope(s->act, z[h]);",
+                                              "dz[h] = da;"),
+    "dA through W2 transposed": (
+        "        for (int32_t o = 0; o < O; o++) da += dy[o] * W2[(int64_t)o * H + h];\n        dz[h]",
+        "        for (int32_t o = 0; o < O; o++) da += dy[o] * W2[(int64_t)h * O + o];\n        dz[h]"),
+    "dW1 row and column swapped": ("for (int64_t i = 0; i < K1; i++) dW1[h * K1 + i] += dz[h] * m[i];",
+                                   "for (int64_t i = 0; i < K1; i++) dW1[i * H + h] += dz[h] * m[i];"),
+    "db1 before the slope": ("db1[h] += dz[h];", "db1[h] += dz[h] / act_slope(s->act, z[h]);"),
+    "dm through W1 with the wrong stride": ("for (int32_t h = 0; h < H; h++) acc += dz[h] * W1[h * K1 + i];",
+                                            "for (int32_t h = 0; h < H; h++) acc += dz[h] * W1[h * K1 + (i + 1) % K1];"),
+    "unmerge dx/dy swapped": ("= dm[(int64_t)c * k * k + ddy * k + ddx];",
+                              "= dm[(int64_t)c * k * k + ddx * k + ddy];"),
+    "LN backward without mean(g)": ("dx[c] = r * (gamma[c] * dn[c] - mg - xh * mgx);",
+                                    "dx[c] = r * (gamma[c] * dn[c] - xh * mgx);"),
+    "LN backward without the xh term": ("dx[c] = r * (gamma[c] * dn[c] - mg - xh * mgx);",
+                                        "dx[c] = r * (gamma[c] * dn[c] - mg);"),
+    "LN backward ignores gamma": ("const double xh = (x[c] - mean) * r, g = gamma[c] * dn[c];",
+                                  "const double xh = (x[c] - mean) * r, g = dn[c];"),
+    "LN backward eps outside the root": ("const double r = 1.0 / sqrt(var + eps);",
+                                         "const double r = 1.0 / (sqrt(var) + eps);"),
+    "dgamma and dbeta swapped": ("if (dgamma) dgamma[c] += dn[c] * xh;\n    if (dbeta) dbeta[c] += dn[c];",
+                                 "if (dgamma) dgamma[c] += dn[c];\n    if (dbeta) dbeta[c] += dn[c] * xh;"),
+    "scatter backward keeps the last newline only": ("for (int32_t d = 0; d < D; d++) to[d] += g[d];",
+                                                     "for (int32_t d = 0; d < D; d++) to[d] = g[d];"),
+    "scatter backward without the count check": ("if (count != P) return -1;\n  memset(drows",
+                                                 "(void)count;\n  memset(drows"),
+    "sampled unit misses the bias": ("    z += b1[h];\n    const double a = act_value(s->act, z);",
+                                     "    const double a = act_value(s->act, z);"),
+    "sampled pixel at the transposed block position": ("const int32_t p = (y % k) * k + xx % k;",
+                                                       "const int32_t p = (xx % k) * k + y % k;"),
 }
 
 
