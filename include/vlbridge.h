@@ -204,9 +204,70 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
                             int64_t vocab, int64_t seq_len, void *seq, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* ---- training the projector (VLB_BF16) -------------------------------- */
+/*
+ * The projector is the trained part of the bridge: [V4V header] trains only
+ * its parameters (tower and text model frozen), and [VOIE "Pendant le
+ * pré-entraînement du squelette"] keeps it trainable while the tower is
+ * frozen.  A training step calls vlb_bridge_fused_train (the forward, keeping
+ * what the backward needs in `saved`) and then vlb_bridge_backward with the
+ * gradient of the loss with respect to the sequence.  The gradients are the
+ * chain rule through [VL2 Projector 1-3] and [VL2 Tile-sequence assembly].
+ */
+
+/* Bytes of the saved-activation buffer of a batch (the merged tokens and the
+ * first Linear's pre-activation, in the GEMMs' tile-blocked layouts; the
+ * contents are opaque); 0 on invalid input or for VLB_F32. */
+size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b);
+
+/* Device workspace bytes of vlb_bridge_backward for this batch and sequence
+ * length; 0 on invalid input or an unsupported setting (see below). */
+size_t vlb_backward_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t seq_len);
+
+/* vlb_bridge_fused (same arguments, errors and sequence values), and the
+ * activations the backward needs written to saved (vlb_saved_bytes bytes,
+ * which must not overlap any other argument).  VLB_BF16 only (VLB_F32:
+ * VLB_ERR_UNSUPPORTED). */
+vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
+                                  const void *features, const vlb_weights *w,
+                                  const void *newline, const void *separator,
+                                  const uint8_t *mask, int64_t seq_len, void *seq, void *saved,
+                                  size_t saved_bytes, void *ws, size_t ws_bytes, void *stream);
+
+/* Gradient outputs of vlb_bridge_backward: fp32 unless marked, each written
+ * whole (not accumulated into). */
+typedef struct {
+  void *d_features;               /* [n_pixels][C] in the projector dtype; NULL: skipped */
+  float *d_w1;                    /* [hidden][C*k*k], the pages' feature order */
+  float *d_b1;                    /* [hidden] */
+  float *d_w2;                    /* [out_dim][hidden] */
+  float *d_b2;                    /* [out_dim] */
+  float *d_ln_gamma, *d_ln_beta;  /* [C]; has_ln only (ignored otherwise) */
+  float *d_newline, *d_separator; /* [out_dim]; TILED_2D only (ignored otherwise) */
+} vlb_grads;
+
+/* Backward of the bridge.  dseq [seq_len][out_dim] (dtype) is the gradient of
+ * the loss with respect to the sequence vlb_bridge_fused_train wrote; its rows
+ * at text positions (mask == 0) are not read.  features, w, mask and saved
+ * must be those of that forward call (features and w->ln_gamma are read only
+ * with the LayerNorm; w->w1 and w->w2 unpacked, p->packed == 0; biases and
+ * ln_beta are not read).  Every token row's gradient is the dseq row of its
+ * slot; the newline and separator gradients sum the rows of all their slots;
+ * padded merge cells take no gradient.
+ * Unsupported (VLB_ERR_UNSUPPORTED): VLB_F32, p->packed, has_ln with
+ * C > 2048.  Device-detected placeholder-count mismatch: nothing is written
+ * and vlb_check(ws) returns VLB_ERR_MASK_COUNT.  With no token rows
+ * (n_views = 0) every gradient is set to zero and the mask is not read.
+ * Workspace: vlb_backward_workspace_bytes(p, b, seq_len). */
+vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const void *features,
+                               const vlb_weights *w, const uint8_t *mask, int64_t seq_len,
+                               const void *dseq, const void *saved, size_t saved_bytes,
+                               const vlb_grads *g, void *ws, size_t ws_bytes, void *stream);
+
 /* Waits for stream and returns the status recorded on the device by the last
- * vlb_scatter_tokens / vlb_bridge_fused that used this workspace (VLB_OK or
- * VLB_ERR_MASK_COUNT), or VLB_ERR_HIP. */
+ * vlb_scatter_tokens / vlb_bridge_fused / vlb_bridge_fused_train /
+ * vlb_bridge_embed / vlb_bridge_backward that used this workspace (VLB_OK,
+ * VLB_ERR_MASK_COUNT or VLB_ERR_TOKEN_ID), or VLB_ERR_HIP. */
 vlb_status vlb_check(void *ws, void *stream);
 
 const char *vlb_status_str(vlb_status s);
@@ -225,7 +286,14 @@ enum {
   VLB_K_MERGE = 7,   /* standalone space-to-depth */
   VLB_K_PACK = 8,    /* weight re-layout */
   VLB_K_EMBED = 9,   /* token-embedding rows */
-  VLB_K_COUNT = 10
+  VLB_K_BWD_PACK = 10,    /* backward: gradient gather and operand transposes */
+  VLB_K_BWD_DW2 = 11,     /* backward: dW2 = dY^T act(Z1) */
+  VLB_K_BWD_DA1 = 12,     /* backward: dA1 = dY W2 */
+  VLB_K_BWD_DW1 = 13,     /* backward: dW1 = dZ1^T Xm */
+  VLB_K_BWD_DX = 14,      /* backward: dXm = dZ1 W1 */
+  VLB_K_BWD_UNMERGE = 15, /* backward: unmerge + LayerNorm backward */
+  VLB_K_BWD_SUM = 16,     /* backward: bias / LayerNorm / newline sums */
+  VLB_K_COUNT = 17
 };
 
 /* Launch timing.  mask bit kid (1 << VLB_K_*) enables timing of that kernel

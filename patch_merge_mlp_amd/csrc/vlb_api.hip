@@ -42,6 +42,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 vlb_status check_projector(const vlb_projector *p) {
   if (!p) return VLB_ERR_NULL;
   if (p->dtype != VLB_F32 && p->dtype != VLB_BF16) return VLB_ERR_DTYPE;
@@ -161,6 +166,93 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   return VLB_OK;
 }
 
+// Saved activations of a training forward (bf16): the merged tokens (Linear1's
+// operand) and Linear1's pre-activation, both tile-blocked.
+struct SavedLayout {
+  size_t off_xm = 0, off_z1 = 0, total = 0;
+};
+
+SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
+  SavedLayout L;
+  size_t off = 0;
+  L.off_xm = off;
+  off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, pl.K1)) * 2);
+  L.off_z1 = off;
+  off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, p->hidden)) * 2);
+  L.total = off;
+  return L;
+}
+
+// Workspace of the backward (bf16).  Tk = T and Op = out_dim rounded up to 32.
+struct BwdLayout {
+  int64_t Tk = 0, Op = 0, NL = 0;  // NL: newline slots of the batch
+  size_t off_status = 0, off_dst = 0, off_slot = 0, off_nl = 0, off_sep = 0, off_dy = 0,
+         off_dyt = 0, off_a1t = 0, off_w2t = 0, off_da1 = 0, off_dz1 = 0, off_dz1t = 0,
+         off_xmt = 0, off_w1t = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
+         off_pnl = 0, off_psep = 0, total = 0;
+  std::vector<int> ln_grid;  // unmerge workgroups per chunk of views
+  int64_t ln_rows = 0;       // their sum: rows of each LayerNorm partial
+};
+
+vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
+                      int64_t seq_len, BwdLayout *L) {
+  if (p->dtype != VLB_BF16 || p->packed) return VLB_ERR_UNSUPPORTED;
+  if (p->has_ln && p->C > vlb::kBwdMaxChannels) return VLB_ERR_UNSUPPORTED;
+  const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1;
+  L->Tk = (T + 31) / 32 * 32;
+  L->Op = (O + 31) / 32 * 32;
+  L->NL = 0;
+  if (b->layout == VLB_LAYOUT_TILED_2D)
+    for (int im = 0; im < b->n_images; ++im) {
+      const int v = pl.img_view0[im];
+      L->NL += ceil_div(b->grid_h[v], p->k) * (1 + b->tile_h[im]);
+    }
+  // 32-bit byte extents of the GEMM operands
+  const int64_t Tk = L->Tk, Op = L->Op;
+  for (const int64_t e : {vlb::blocked_elems(T, Op), vlb::blocked_elems(O, Tk),
+                          vlb::blocked_elems(H, Tk), vlb::blocked_elems(H, Op),
+                          vlb::blocked_elems(K1, Tk), vlb::blocked_elems(K1, H),
+                          vlb::blocked_elems(T, H)})
+    if (e * 2 > kI32Max) return VLB_ERR_SHAPE;
+  L->ln_grid.clear();
+  L->ln_rows = 0;
+  for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews) {
+    const int v1 = std::min(b->n_views, v0 + vlb::kPlanViews);
+    const int g = vlb::bwd_unmerge_grid(
+        static_cast<int64_t>(pl.view_tok0[v1] - pl.view_tok0[v0]) * p->k * p->k);
+    L->ln_grid.push_back(g);
+    L->ln_rows += g;
+  }
+  auto take = [](size_t &off, size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  size_t off = 0;
+  L->off_status = take(off, 16);
+  L->off_dst = take(off, static_cast<size_t>(T) * 4);
+  L->off_slot = take(off, static_cast<size_t>(seq_len) * 4);
+  L->off_nl = take(off, static_cast<size_t>(L->NL) * 4);
+  L->off_sep = take(off, static_cast<size_t>(b->n_images) * 4);
+  L->off_dy = take(off, static_cast<size_t>(vlb::blocked_elems(T, Op)) * 2);
+  L->off_dyt = take(off, static_cast<size_t>(vlb::blocked_elems(O, Tk)) * 2);
+  L->off_a1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
+  L->off_w2t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Op)) * 2);
+  L->off_da1 = take(off, static_cast<size_t>(vlb::blocked_elems(T, H)) * 2);
+  L->off_dz1 = take(off, static_cast<size_t>(vlb::blocked_elems(T, H)) * 2);
+  L->off_dz1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
+  L->off_xmt = take(off, static_cast<size_t>(vlb::blocked_elems(K1, Tk)) * 2);
+  L->off_w1t = take(off, static_cast<size_t>(vlb::blocked_elems(K1, H)) * 2);
+  L->off_dxm = take(off, static_cast<size_t>(T) * K1 * 2);
+  L->off_pb2 = take(off, static_cast<size_t>(Tk / 32) * O * 4);
+  L->off_pb1 = take(off, static_cast<size_t>(Tk / 32) * H * 4);
+  L->off_pln = take(off, static_cast<size_t>(2 * L->ln_rows) * p->C * 4);
+  L->off_pnl = take(off, static_cast<size_t>(ceil_div(L->NL, 64)) * O * 4);
+  L->off_psep = take(off, static_cast<size_t>(ceil_div(b->n_images, 64)) * O * 4);
+  L->total = off;
+  return VLB_OK;
+}
+
 // ---- optional per-kernel timing ---------------------------------------------
 struct ProfRec {
   int kid;
@@ -224,13 +316,17 @@ vlb_status run_plan(const vlb_projector *p, const vlb_batch *b, const Plan &pl, 
 
 // LN (optional) + both GEMMs.  dst_row == nullptr: rows[m] = projected row m;
 // otherwise row m goes to out + dst_row[m] * out_dim.
+// saved (bf16 training forward, else null): the merged tokens and Linear1's
+// pre-activation are kept there (saved_layout).
 vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                        const void *features, const vlb_weights *w, void *out,
-                       const int32_t *dst_row, uint8_t *ws, hipStream_t s) {
+                       const int32_t *dst_row, uint8_t *ws, hipStream_t s,
+                       uint8_t *saved = nullptr) {
   RowDesc *desc = reinterpret_cast<RowDesc *>(ws + pl.off_desc);
   const void *x = features;
+  const SavedLayout sl = saved ? saved_layout(p, pl) : SavedLayout{};
   if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
-    void *xm = ws + pl.off_xn;
+    void *xm = saved ? saved + sl.off_xm : ws + pl.off_xn;
     for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
       VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
                  vlb::launch_merge_blocked(features, view_chunk(p, b, pl, v0), p->C,
@@ -293,8 +389,10 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
     g2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->out_dim, p->hidden) * 2);
     g1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, pl.K1) * 2);
     g2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, p->hidden) * 2);
-    VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_bf16(true, g1, s));
-    VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(false, g2, s));
+    g1.out2 = saved ? saved + sl.off_z1 : nullptr;
+    VLB_LAUNCH(VLB_K_GEMM1, s,
+               vlb::launch_gemm_bf16(saved ? vlb::kGemmBlockedSave : vlb::kGemmBlocked, g1, s));
+    VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(vlb::kGemmRows, g2, s));
   } else {
     g1.B = w->w1;
     VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_f32(true, g1, s));
@@ -523,6 +621,233 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   if (st != VLB_OK) return st;
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s);
+}
+
+size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
+  Plan pl;
+  if (make_plan(p, b, 0, &pl) != VLB_OK || p->dtype != VLB_BF16) return 0;
+  return saved_layout(p, pl).total;
+}
+
+size_t vlb_backward_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t seq_len) {
+  Plan pl;
+  BwdLayout L;
+  if (make_plan(p, b, seq_len, &pl) != VLB_OK || bwd_layout(p, b, pl, seq_len, &L) != VLB_OK)
+    return 0;
+  return L.total;
+}
+
+vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
+                                  const void *features, const vlb_weights *w,
+                                  const void *newline, const void *separator,
+                                  const uint8_t *mask, int64_t seq_len, void *seq, void *saved,
+                                  size_t saved_bytes, void *ws, size_t ws_bytes, void *stream) {
+  Plan pl;
+  vlb_status st = make_plan(p, b, seq_len, &pl);
+  if (st != VLB_OK) return st;
+  if (p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (pl.T == 0) return VLB_OK;
+  if ((st = check_weights(p, w)) != VLB_OK) return st;
+  if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;
+  if (!features || !ws || !saved) return VLB_ERR_NULL;
+  if (!aligned16(features) || !aligned16(ws) || !aligned16(saved)) return VLB_ERR_ALIGN;
+  if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
+  const size_t need = saved_layout(p, pl).total;
+  if (saved_bytes < need) return VLB_ERR_WORKSPACE;
+  const size_t seq_bytes = static_cast<size_t>(seq_len) * p->out_dim * pl.es;
+  if (overlaps(saved, need, ws, pl.total) || overlaps(saved, need, seq, seq_bytes))
+    return VLB_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8, s);
+  if (st != VLB_OK) return st;
+  return run_project(p, b, pl, features, w, seq,
+                     reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s,
+                     static_cast<uint8_t *>(saved));
+}
+
+vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const void *features,
+                               const vlb_weights *w, const uint8_t *mask, int64_t seq_len,
+                               const void *dseq, const void *saved, size_t saved_bytes,
+                               const vlb_grads *g, void *ws, size_t ws_bytes, void *stream) {
+  Plan pl;
+  vlb_status st = make_plan(p, b, seq_len, &pl);
+  if (st != VLB_OK) return st;
+  BwdLayout L;
+  if ((st = bwd_layout(p, b, pl, seq_len, &L)) != VLB_OK) return st;
+  const bool ln = p->has_ln != 0, tiled = b->layout == VLB_LAYOUT_TILED_2D;
+  if (!g || !w || !mask || !dseq || !saved || !ws) return VLB_ERR_NULL;
+  if (!g->d_w1 || !g->d_b1 || !g->d_w2 || !g->d_b2 || !w->w1 || !w->w2) return VLB_ERR_NULL;
+  if (ln && (!g->d_ln_gamma || !g->d_ln_beta || !w->ln_gamma)) return VLB_ERR_NULL;
+  if (ln && pl.T > 0 && !features) return VLB_ERR_NULL;
+  if (tiled && (!g->d_newline || !g->d_separator)) return VLB_ERR_NULL;
+  const void *ptrs[] = {mask, dseq, saved, ws, g->d_w1, g->d_b1, g->d_w2, g->d_b2, w->w1, w->w2,
+                        g->d_features, features, w->ln_gamma, g->d_ln_gamma, g->d_ln_beta,
+                        g->d_newline, g->d_separator};
+  for (const void *q : ptrs)
+    if (!aligned16(q)) return VLB_ERR_ALIGN;
+  if (seq_len < 1) return VLB_ERR_SHAPE;
+  if (ws_bytes < L.total) return VLB_ERR_WORKSPACE;
+  if (saved_bytes < saved_layout(p, pl).total) return VLB_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1, C = p->C;
+  if (T == 0) {  // no token rows: every gradient is zero
+    auto zero = [&](void *q, size_t bytes) {
+      return q == nullptr || hipMemsetAsync(q, 0, bytes, s) == hipSuccess;
+    };
+    const bool ok = zero(g->d_w1, H * K1 * 4) && zero(g->d_b1, H * 4) &&
+                    zero(g->d_w2, O * H * 4) && zero(g->d_b2, O * 4) &&
+                    (!ln || (zero(g->d_ln_gamma, C * 4) && zero(g->d_ln_beta, C * 4))) &&
+                    (!tiled || (zero(g->d_newline, O * 4) && zero(g->d_separator, O * 4))) &&
+                    zero(g->d_features, static_cast<size_t>(pl.npix) * C * 2);
+    return ok ? VLB_OK : VLB_ERR_HIP;
+  }
+  uint8_t *w8 = static_cast<uint8_t *>(ws);
+  const uint8_t *sv = static_cast<const uint8_t *>(saved);
+  const SavedLayout sl = saved_layout(p, pl);
+  int32_t *status = reinterpret_cast<int32_t *>(w8 + L.off_status);
+  int32_t *dst_row = reinterpret_cast<int32_t *>(w8 + L.off_dst);
+  int32_t *slot_pos = reinterpret_cast<int32_t *>(w8 + L.off_slot);
+  int32_t *nl_pos = reinterpret_cast<int32_t *>(w8 + L.off_nl);
+  int32_t *sep_pos = reinterpret_cast<int32_t *>(w8 + L.off_sep);
+  const int32_t Tk = static_cast<int32_t>(L.Tk), Op = static_cast<int32_t>(L.Op);
+  const int32_t Ti = static_cast<int32_t>(T), Hi = static_cast<int32_t>(H),
+                Oi = static_cast<int32_t>(O), K1i = static_cast<int32_t>(K1);
+
+  // 1. slot of every token row (and of every newline / separator)
+  if (!tiled) {
+    VLB_LAUNCH(VLB_K_SCAN, s,
+               vlb::launch_scan(mask, nullptr, 0, 0, seq_len, pl.P, dst_row, status, true, s));
+  } else {
+    VLB_LAUNCH(VLB_K_SCAN, s,
+               vlb::launch_scan(mask, nullptr, 0, 0, seq_len, pl.P, slot_pos, status, false, s));
+    int32_t nl0 = 0;
+    for (int i0 = 0; i0 < b->n_images; i0 += vlb::kPlaceImages) {
+      PlaceChunk c{};
+      c.n = std::min(vlb::kPlaceImages, b->n_images - i0);
+      c.tail = b->global_view_tail;
+      c.img0 = i0;
+      for (int i = 0; i < c.n; ++i) {
+        const int im = i0 + i, v = pl.img_view0[im];
+        c.slot0[i] = pl.img_slot0[im];
+        c.row0[i] = pl.img_row0[im];
+        c.hp[i] = static_cast<int16_t>(ceil_div(b->grid_h[v], p->k));
+        c.wp[i] = static_cast<int16_t>(ceil_div(b->grid_w[v], p->k));
+        c.tw[i] = static_cast<int16_t>(b->tile_w[im]);
+        c.th[i] = static_cast<int16_t>(b->tile_h[im]);
+        c.nl0[i] = nl0;
+        nl0 += c.hp[i] * (1 + c.th[i]);
+      }
+      c.slot0[c.n] = pl.img_slot0[i0 + c.n];
+      VLB_LAUNCH(VLB_K_PLACE, s,
+                 vlb::launch_place_tiled_record(c, slot_pos, status, dst_row, nl_pos, sep_pos, s));
+    }
+  }
+  // 2. dY, its transpose, db2
+  float *pb2 = reinterpret_cast<float *>(w8 + L.off_pb2);
+  VLB_LAUNCH(VLB_K_BWD_PACK, s,
+             vlb::launch_bwd_gather_dy(dseq, dst_row, Ti, Oi, Op, Tk, w8 + L.off_dy,
+                                       w8 + L.off_dyt, pb2, s));
+  VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pb2, Tk / 32, Oi, g->d_b2, status, s));
+  // 3. dW2 = dY^T act(Z1)
+  VLB_LAUNCH(VLB_K_BWD_PACK, s,
+             vlb::launch_bwd_act_t(p->act, sv + sl.off_z1, Ti, Hi, Tk, w8 + L.off_a1t, s));
+  vlb::GemmArgs gw2{};
+  gw2.A = w8 + L.off_dyt;
+  gw2.B = w8 + L.off_a1t;
+  gw2.out = g->d_w2;
+  gw2.status = status;
+  gw2.M = Oi;
+  gw2.N = Hi;
+  gw2.K = Tk;
+  gw2.ldo = Hi;
+  gw2.act = VLB_ACT_NONE;
+  gw2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(O, Tk) * 2);
+  gw2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+  VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw2, s));
+  // 4. dA1 = dY W2, then dZ1 = dA1 * act'(Z1) and db1
+  VLB_LAUNCH(VLB_K_BWD_PACK, s,
+             vlb::launch_bwd_weight_t(w->w2, Oi, Hi, p->C, 1, Op, w8 + L.off_w2t, s));
+  vlb::GemmArgs ga{};
+  ga.A = w8 + L.off_dy;
+  ga.B = w8 + L.off_w2t;
+  ga.out = w8 + L.off_da1;
+  ga.M = Ti;
+  ga.N = Hi;
+  ga.K = Op;
+  ga.ldo = Hi;
+  ga.act = VLB_ACT_NONE;
+  ga.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, Op) * 2);
+  ga.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Op) * 2);
+  VLB_LAUNCH(VLB_K_BWD_DA1, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, ga, s));
+  float *pb1 = reinterpret_cast<float *>(w8 + L.off_pb1);
+  VLB_LAUNCH(VLB_K_BWD_PACK, s,
+             vlb::launch_bwd_dact(p->act, w8 + L.off_da1, sv + sl.off_z1, Ti, Hi, Tk,
+                                  w8 + L.off_dz1, w8 + L.off_dz1t, pb1, s));
+  VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pb1, Tk / 32, Hi, g->d_b1, status, s));
+  // 5. dW1 = dZ1^T Xm (columns in the pages' order)
+  VLB_LAUNCH(VLB_K_BWD_PACK, s,
+             vlb::launch_bwd_xm_t(sv + sl.off_xm, Ti, p->C, p->k, Tk, w8 + L.off_xmt, s));
+  vlb::GemmArgs gw1{};
+  gw1.A = w8 + L.off_dz1t;
+  gw1.B = w8 + L.off_xmt;
+  gw1.out = g->d_w1;
+  gw1.status = status;
+  gw1.M = Hi;
+  gw1.N = K1i;
+  gw1.K = Tk;
+  gw1.ldo = K1i;
+  gw1.act = VLB_ACT_NONE;
+  gw1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+  gw1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(K1, Tk) * 2);
+  VLB_LAUNCH(VLB_K_BWD_DW1, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw1, s));
+  // 6. dXm = dZ1 W1 (K position-major), unmerge, LayerNorm backward
+  if (ln || g->d_features) {
+    VLB_LAUNCH(VLB_K_BWD_PACK, s,
+               vlb::launch_bwd_weight_t(w->w1, Hi, K1i, p->C, p->k, Hi, w8 + L.off_w1t, s));
+    vlb::GemmArgs gx{};
+    gx.A = w8 + L.off_dz1;
+    gx.B = w8 + L.off_w1t;
+    gx.out = w8 + L.off_dxm;
+    gx.M = Ti;
+    gx.N = K1i;
+    gx.K = Hi;
+    gx.ldo = K1i;
+    gx.act = VLB_ACT_NONE;
+    gx.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, H) * 2);
+    gx.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(K1, H) * 2);
+    VLB_LAUNCH(VLB_K_BWD_DX, s, vlb::launch_gemm_bf16(vlb::kGemmRows, gx, s));
+    float *pg = reinterpret_cast<float *>(w8 + L.off_pln);
+    float *pbeta = pg + L.ln_rows * C;
+    int64_t row = 0;
+    for (int v0 = 0, ci = 0; v0 < b->n_views; v0 += vlb::kPlanViews, ++ci) {
+      const int grid = L.ln_grid[ci];
+      VLB_LAUNCH(VLB_K_BWD_UNMERGE, s,
+                 vlb::launch_bwd_unmerge(w8 + L.off_dxm, features, view_chunk(p, b, pl, v0),
+                                         p->C, ln ? w->ln_gamma : nullptr, p->ln_eps,
+                                         g->d_features, pg + row * C, pbeta + row * C, status,
+                                         grid, s));
+      row += grid;
+    }
+    if (ln) {
+      const int32_t R = static_cast<int32_t>(L.ln_rows);
+      VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pg, R, p->C, g->d_ln_gamma, status, s));
+      VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pbeta, R, p->C, g->d_ln_beta, status, s));
+    }
+  }
+  // 7. newline and separator: sums over their slots
+  if (tiled) {
+    float *pnl = reinterpret_cast<float *>(w8 + L.off_pnl);
+    float *psep = reinterpret_cast<float *>(w8 + L.off_psep);
+    const int32_t NL = static_cast<int32_t>(L.NL);
+    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(dseq, nl_pos, NL, Oi, pnl, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s,
+               vlb::launch_colsum(pnl, (NL + 63) / 64, Oi, g->d_newline, status, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(dseq, sep_pos, b->n_images, Oi, psep, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s,
+               vlb::launch_colsum(psep, (b->n_images + 63) / 64, Oi, g->d_separator, status, s));
+  }
+  return VLB_OK;
 }
 
 vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const void *features,

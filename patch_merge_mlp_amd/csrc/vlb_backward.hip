@@ -1,0 +1,510 @@
+// Kernels of the projector's backward pass (bf16), besides the GEMMs.
+//
+// The projector is the bridge's trained part ("DeepSeek-V4-Flash-Vision-BF16"
+// model card, header: only its parameters are trained, tower and text model
+// frozen; "La voie visuelle", "Pendant le pré-entraînement du squelette": the
+// projector stays trainable).  Its gradients are the chain rule through the
+// forward of mlxcel issue #533 "port DeepSeek-VL2", "Projector
+// (downsample_mlp_gelu)" steps 1-3 and "Tile-sequence assembly":
+//   dY = gradient rows gathered from the sequence's placeholder slots
+//   dW2 = dY^T act(Z1), db2 = sum dY, dA1 = dY W2
+//   dZ1 = dA1 * act'(Z1), db1 = sum dZ1, dW1 = dZ1^T Xm, dXm = dZ1 W1
+//   dXm unmerged to pixels, then through the LayerNorm.
+//
+// The four products run on the MFMA GEMM, which contracts over the 32-wide K
+// slices of two tile-blocked operands (element (r, c) of [R][K] at
+// ((r/256 * K/32 + c/32) * 256 + r%256) * 32 + c%32).  The kernels here build
+// those operands: a workgroup takes 32 consecutive rows t (one K slice of the
+// transposed operand) and 256 columns, stages them in LDS, and writes each
+// column's 32 values as one contiguous 64-byte piece of the transposed
+// operand -- 256 such pieces are one 16 KiB run.  Rows past T are zero, so the
+// padded part of every contraction over T adds nothing.  Column sums (the
+// bias gradients) are written per 32-row slice and reduced in a fixed order,
+// so every gradient is deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vlb_common.h"
+#include "vlb_internal.h"
+
+namespace vlb {
+
+namespace {
+
+constexpr int kTR = 32;            // rows t per workgroup (one K slice)
+constexpr int kTC = 256;           // columns per workgroup
+constexpr int kPitch = kTC + 8;    // LDS row pitch in bf16 (16-byte aligned rows)
+
+__device__ __forceinline__ int64_t blk(int64_t r, int64_t c, int64_t K) {
+  return ((r >> 8) * (K >> 5) + (c >> 5)) * 8192 + (r & 255) * 32 + (c & 31);
+}
+
+// d/dz of act_fn<ACT>, in fp32.
+//   erf form: Phi(z) + z phi(z), with Phi from the same tail polynomial as
+//   the forward (Phi(-a) = 2^(-h(a))) and phi(z) = exp(-z^2/2) / sqrt(2 pi);
+//   tanh form: 0.5 (1 + th) + 0.5 z (1 - th^2) sqrt(2/pi) (1 + 3 * 0.044715 z^2).
+template <int ACT>
+__device__ __forceinline__ float act_slope(float z) {
+  if constexpr (ACT == 0) {
+    const float a = fminf(fabsf(z), 6.0f);
+    float h = 1.83484644e-06f;
+    h = fmaf(h, a, -6.15989775e-05f);
+    h = fmaf(h, a, 0.000930530019f);
+    h = fmaf(h, a, -0.00850791018f);
+    h = fmaf(h, a, 0.0539601035f);
+    h = fmaf(h, a, 0.458464354f);
+    h = fmaf(h, a, 1.15125108f);
+    h = fmaf(h, a, 0.999995291f);
+    const float tail = __builtin_amdgcn_exp2f(-h);  // Phi(-|z|)
+    const float cdf = z >= 0.f ? 1.0f - tail : tail;
+    const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z);
+    return fmaf(z, pdf, cdf);
+  } else if constexpr (ACT == 1) {
+    const float k0 = 0.79788456080286536f;
+    const float u = k0 * (z + 0.044715f * z * z * z);
+    const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2f(2.0f * 1.4426950408889634f * u) + 1.0f);
+    return 0.5f * (1.0f + th) + 0.5f * z * (1.0f - th * th) * k0 * (1.0f + 3.0f * 0.044715f * z * z);
+  } else {
+    return 1.0f;
+  }
+}
+
+// Column r of the staged 32 x 256 tile as one 64-byte piece of the
+// transposed operand.
+__device__ __forceinline__ void store_column(const uint16_t *tile, int r, uint16_t *dst) {
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    w[i] = tile[(2 * i) * kPitch + r] | (static_cast<uint32_t>(tile[(2 * i + 1) * kPitch + r]) << 16);
+  uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
+__device__ __forceinline__ float col_sum(const uint16_t *tile, int r) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kTR; ++i) s += bf2f(tile[i * kPitch + r]);
+  return s;
+}
+
+// Gradient rows of the token rows: dY[t] = G[dst_row[t]] (zero for t >= T or
+// an unplaced row).  Writes dY tile-blocked [T][Op] (K = Op, zero past O),
+// its transpose [O][Tk], and per-slice column sums part[t/32][o].
+__global__ __launch_bounds__(256) void k_bwd_gather_dy(const uint16_t *G, const int32_t *dst_row,
+                                                       int32_t T, int32_t O, int32_t Op,
+                                                       int32_t Tk, uint16_t *dy, uint16_t *dyt,
+                                                       float *part) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
+    const int row = q >> 5, ch = q & 31;
+    const int t = t0 + row, o = n0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < T && o < O) {
+      const int32_t d = dst_row[t];
+      if (d >= 0) v = *reinterpret_cast<const uint4 *>(G + static_cast<int64_t>(d) * O + o);
+    }
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
+  }
+  __syncthreads();
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {  // dY: 8 slices of 32 rows x 64 bytes
+    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int o = n0 + sl * 32 + c4 * 8;
+    if (o < Op)
+      *reinterpret_cast<uint4 *>(dy + blk(t0 + row, o, Op)) =
+          *reinterpret_cast<const uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8);
+  }
+  const int o = n0 + tid;
+  if (o < O) {
+    store_column(tile, tid, dyt + blk(o, t0, Tk));
+    part[static_cast<int64_t>(blockIdx.x) * O + o] = col_sum(tile, tid);
+  }
+}
+
+// act(Z1)^T: Z1 tile-blocked [T][H] (rows past T unused) -> [H][Tk].
+template <int ACT>
+__global__ __launch_bounds__(256) void k_bwd_act_t(const uint16_t *z1, int32_t T, int32_t H,
+                                                   int32_t Tk, uint16_t *a1t) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
+    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < T && h < H) {
+      v = *reinterpret_cast<const uint4 *>(z1 + blk(t, h, H));
+      uint16_t *e = reinterpret_cast<uint16_t *>(&v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = f2bf(act_fn<ACT>(bf2f(e[i])));
+    }
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
+  }
+  __syncthreads();
+  const int h = n0 + tid;
+  if (h < H) store_column(tile, tid, a1t + blk(h, t0, Tk));
+}
+
+// dZ1 = dA1 * act'(Z1) (both tile-blocked [T][H]): dZ1 tile-blocked, its
+// transpose [H][Tk], and per-slice column sums of the rounded values (the
+// values dW1 and dXm are computed from).
+template <int ACT>
+__global__ __launch_bounds__(256) void k_bwd_dact(const uint16_t *da1, const uint16_t *z1,
+                                                  int32_t T, int32_t H, int32_t Tk, uint16_t *dz1,
+                                                  uint16_t *dz1t, float *part) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
+    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < T && h < H) {
+      const int64_t e = blk(t, h, H);
+      const uint4 a = *reinterpret_cast<const uint4 *>(da1 + e);
+      const uint4 z = *reinterpret_cast<const uint4 *>(z1 + e);
+      const uint16_t *ae = reinterpret_cast<const uint16_t *>(&a);
+      const uint16_t *ze = reinterpret_cast<const uint16_t *>(&z);
+      uint16_t *ve = reinterpret_cast<uint16_t *>(&v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ve[i] = f2bf(bf2f(ae[i]) * act_slope<ACT>(bf2f(ze[i])));
+      *reinterpret_cast<uint4 *>(dz1 + e) = v;
+    }
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
+  }
+  __syncthreads();
+  const int h = n0 + tid;
+  if (h < H) {
+    store_column(tile, tid, dz1t + blk(h, t0, Tk));
+    part[static_cast<int64_t>(blockIdx.x) * H + h] = col_sum(tile, tid);
+  }
+}
+
+// Xm (tile-blocked [T][K1], K position-major j = p*C + c) -> its transpose
+// with rows in the pages' feature order c*k*k + p: [K1][Tk].
+__global__ __launch_bounds__(256) void k_bwd_xm_t(const uint16_t *xm, int32_t T, int32_t K1,
+                                                  int32_t C, int32_t kk, int32_t Tk,
+                                                  uint16_t *xmt) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
+    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int t = t0 + row, j = n0 + sl * 32 + c4 * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < T && j < K1) v = *reinterpret_cast<const uint4 *>(xm + blk(t, j, K1));
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
+  }
+  __syncthreads();
+  const int j = n0 + tid;
+  if (j < K1) store_column(tile, tid, xmt + blk(static_cast<int64_t>(j % C) * kk + j / C, t0, Tk));
+}
+
+// Transpose of a row-major weight W [R][Cs] into the tile-blocked [Cs][Rk]
+// (Rk = R rounded up to 32, zeros past R).  kk > 1 (W1, columns in the pages'
+// order c*k*k + p): output row of column i is the position-major p*C + c.
+__global__ __launch_bounds__(256) void k_bwd_weight_t(const uint16_t *w, int32_t R, int32_t Cs,
+                                                      int32_t C, int32_t kk, int32_t Rk,
+                                                      uint16_t *out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
+  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
+    const int row = q >> 5, ch = q & 31;
+    const int r = r0 + row, i = n0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && i < Cs) v = *reinterpret_cast<const uint4 *>(w + static_cast<int64_t>(r) * Cs + i);
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
+  }
+  __syncthreads();
+  const int i = n0 + tid;
+  if (i < Cs) {
+    const int64_t orow = kk > 1 ? static_cast<int64_t>(i % kk) * C + i / kk : i;
+    store_column(tile, tid, out + blk(orow, r0, Rk));
+  }
+}
+
+// Feature gradient of the pixels of one chunk of views (see PlanChunk), one
+// wave per (token row, block position): the pixel's slice dn = dXm[m][p*C ..
+// p*C + C) (row-major, K position-major) goes back through the LayerNorm,
+//   xh = (x - mean) * rstd, g = gamma * dn,
+//   dx = rstd * (g - mean(g) - xh * mean(g * xh)),
+// recomputing mean and rstd from the pixel as the forward did; without the
+// LayerNorm dx = dn.  Positions in the padding are skipped.  Each workgroup
+// adds its pixels' dn * xh and dn into one row of part_g / part_b (waves in
+// order), so the parameter gradients come out the same on every run.  Nothing
+// is written when the placeholder scan failed.
+template <bool LN, int NCH>
+__global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const uint16_t *x,
+                                                     PlanChunk c, int C, const uint16_t *gamma,
+                                                     float eps, uint16_t *dx, float *part_g,
+                                                     float *part_b, const int32_t *status) {
+  if (status[kStatusWord] != 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = c.k, kk = k * k, nch = C / 8;
+  const int64_t K1 = static_cast<int64_t>(C) * kk;
+  const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
+  const int64_t items = static_cast<int64_t>(t_end - t_begin) * kk;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const bool have = lane < c.n;
+  const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
+  const int32_t l_pix0 = have ? c.pix0[lane] : 0;
+  const int32_t l_gh = have ? c.gh[lane] : 0, l_gw = have ? c.gw[lane] : 1;
+  float ag[NCH][8], ab[NCH][8];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 4 + wid; it < items; it += nw) {
+    const int m = t_begin + static_cast<int>(it / kk), p = static_cast<int>(it % kk);
+    const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
+    const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
+    const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
+    const int wp = (gw + k - 1) / k, t = m - tok0;
+    const int y = (t / wp) * k + p / k, xx = (t % wp) * k + p % k;
+    if (y >= gh || xx >= gw) continue;  // padding: no pixel
+    const int64_t pix = pix0 + static_cast<int64_t>(y) * gw + xx;
+    const uint4 *dsrc = reinterpret_cast<const uint4 *>(dxm + m * K1 + static_cast<int64_t>(p) * C);
+    uint4 dv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      dv[i] = q < nch ? dsrc[q] : make_uint4(0, 0, 0, 0);
+    }
+    uint4 *ddst = dx ? reinterpret_cast<uint4 *>(dx + pix * C) : nullptr;
+    if (!LN) {
+      if (ddst) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+          if (lane + 64 * i < nch) ddst[lane + 64 * i] = dv[i];
+      }
+      continue;
+    }
+    const uint4 *xs = reinterpret_cast<const uint4 *>(x + pix * C);
+    float xf[NCH][8], gf[NCH][8];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      const uint4 xv = q < nch ? xs[q] : make_uint4(0, 0, 0, 0);
+      const uint16_t *e = reinterpret_cast<const uint16_t *>(&xv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xf[i][j] = bf2f(e[j]);
+        sum += xf[i][j];
+      }
+    }
+    const float mean = wave_sum(sum) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nch)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d = xf[i][j] - mean;
+          ss += d * d;
+        }
+    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      const uint4 gq = q < nch ? reinterpret_cast<const uint4 *>(gamma)[q] : make_uint4(0, 0, 0, 0);
+      const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+      const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float xh = (xf[i][j] - mean) * rstd, dn = bf2f(de[j]);
+        xf[i][j] = xh;
+        gf[i][j] = bf2f(ge[j]) * dn;
+        ag[i][j] += dn * xh;
+        ab[i][j] += dn;
+        sg += gf[i][j];
+        sgx += gf[i][j] * xh;
+      }
+    }
+    const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+    if (ddst) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int q = lane + 64 * i;
+        if (q < nch) {
+          uint4 o;
+          uint16_t *oe = reinterpret_cast<uint16_t *>(&o);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) oe[j] = f2bf(rstd * (gf[i][j] - mg - xf[i][j] * mgx));
+          ddst[q] = o;
+        }
+      }
+    }
+  }
+  if (!LN) return;
+  // Workgroup sum of the waves' accumulators, wave 0 first, then one row each.
+  extern __shared__ float red[];  // [2][C]
+  for (int w = 0; w < 4; ++w) {
+    if (wid == w) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int q = lane + 64 * i;
+        if (q < nch)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int ch = q * 8 + j;
+            red[ch] = (w == 0 ? 0.f : red[ch]) + ag[i][j];
+            red[C + ch] = (w == 0 ? 0.f : red[C + ch]) + ab[i][j];
+          }
+      }
+    }
+    __syncthreads();
+  }
+  for (int ch = threadIdx.x; ch < C; ch += 256) {
+    part_g[static_cast<int64_t>(blockIdx.x) * C + ch] = red[ch];
+    part_b[static_cast<int64_t>(blockIdx.x) * C + ch] = red[C + ch];
+  }
+}
+
+// out[n] = sum over r in order of part[r][n] (nothing when the scan failed).
+__global__ __launch_bounds__(256) void k_colsum(const float *part, int32_t R, int32_t N,
+                                                float *out, const int32_t *status) {
+  if (status[kStatusWord] != 0) return;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int r = 0; r < R; ++r) s += part[static_cast<int64_t>(r) * N + n];
+  out[n] = s;
+}
+
+// part[b][o] = sum of G[pos[i]][o] over list entries i of block b (64 each;
+// negative positions add nothing).
+__global__ __launch_bounds__(256) void k_rows_sum(const uint16_t *G, const int32_t *pos,
+                                                  int32_t n, int32_t O, float *part) {
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= O) return;
+  const int i0 = blockIdx.y * 64, i1 = min(n, i0 + 64);
+  float s = 0.f;
+  for (int i = i0; i < i1; ++i) {
+    const int32_t p = pos[i];
+    if (p >= 0) s += bf2f(G[static_cast<int64_t>(p) * O + o]);
+  }
+  part[static_cast<int64_t>(blockIdx.y) * O + o] = s;
+}
+
+template <bool LN, int NCH>
+hipError_t unmerge_launch(const void *dxm, const void *x, const PlanChunk &c, int C,
+                          const void *gamma, float eps, void *dx, float *part_g, float *part_b,
+                          const int32_t *status, int grid, hipStream_t s) {
+  const size_t lds = LN ? static_cast<size_t>(2) * C * sizeof(float) : 0;
+  hipLaunchKernelGGL((k_bwd_unmerge<LN, NCH>), dim3(grid), dim3(256), lds, s,
+                     static_cast<const uint16_t *>(dxm), static_cast<const uint16_t *>(x), c, C,
+                     static_cast<const uint16_t *>(gamma), eps, static_cast<uint16_t *>(dx),
+                     part_g, part_b, status);
+  return hipGetLastError();
+}
+
+template <bool LN>
+hipError_t unmerge_dispatch(const void *dxm, const void *x, const PlanChunk &c, int C,
+                            const void *gamma, float eps, void *dx, float *part_g, float *part_b,
+                            const int32_t *status, int grid, hipStream_t s) {
+  switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane
+    case 1: return unmerge_launch<LN, 1>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+    case 2: return unmerge_launch<LN, 2>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+    case 3: return unmerge_launch<LN, 3>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+    case 4: return unmerge_launch<LN, 4>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+    default: return hipErrorInvalidValue;  // C > kBwdMaxChannels
+  }
+}
+
+}  // namespace
+
+int bwd_unmerge_grid(int64_t items) {
+  const int64_t g = (items + 15) / 16;  // about 4 items per wave
+  return static_cast<int>(g < 1 ? 1 : (g > kBwdUnmergeGrid ? kBwdUnmergeGrid : g));
+}
+
+hipError_t launch_bwd_gather_dy(const void *G, const int32_t *dst_row, int32_t T, int32_t O,
+                                int32_t Op, int32_t Tk, void *dy, void *dyt, float *part,
+                                hipStream_t s) {
+  if (Tk <= 0) return hipSuccess;
+  const dim3 grid(Tk / kTR, (Op + kTC - 1) / kTC);
+  hipLaunchKernelGGL(k_bwd_gather_dy, grid, dim3(256), 0, s, static_cast<const uint16_t *>(G),
+                     dst_row, T, O, Op, Tk, static_cast<uint16_t *>(dy),
+                     static_cast<uint16_t *>(dyt), part);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_act_t(int act, const void *z1, int32_t T, int32_t H, int32_t Tk, void *a1t,
+                            hipStream_t s) {
+  if (Tk <= 0) return hipSuccess;
+  const dim3 grid(Tk / kTR, (H + kTC - 1) / kTC);
+  const uint16_t *zz = static_cast<const uint16_t *>(z1);
+  uint16_t *o = static_cast<uint16_t *>(a1t);
+  if (act == 0)
+    hipLaunchKernelGGL(k_bwd_act_t<0>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
+  else if (act == 1)
+    hipLaunchKernelGGL(k_bwd_act_t<1>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
+  else
+    hipLaunchKernelGGL(k_bwd_act_t<2>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dact(int act, const void *da1, const void *z1, int32_t T, int32_t H,
+                           int32_t Tk, void *dz1, void *dz1t, float *part, hipStream_t s) {
+  if (Tk <= 0) return hipSuccess;
+  const dim3 grid(Tk / kTR, (H + kTC - 1) / kTC);
+  const uint16_t *a = static_cast<const uint16_t *>(da1), *z = static_cast<const uint16_t *>(z1);
+  uint16_t *d = static_cast<uint16_t *>(dz1), *dt = static_cast<uint16_t *>(dz1t);
+  if (act == 0)
+    hipLaunchKernelGGL(k_bwd_dact<0>, grid, dim3(256), 0, s, a, z, T, H, Tk, d, dt, part);
+  else if (act == 1)
+    hipLaunchKernelGGL(k_bwd_dact<1>, grid, dim3(256), 0, s, a, z, T, H, Tk, d, dt, part);
+  else
+    hipLaunchKernelGGL(k_bwd_dact<2>, grid, dim3(256), 0, s, a, z, T, H, Tk, d, dt, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_xm_t(const void *xm, int32_t T, int32_t C, int32_t k, int32_t Tk, void *xmt,
+                           hipStream_t s) {
+  if (Tk <= 0) return hipSuccess;
+  const int32_t K1 = C * k * k;
+  const dim3 grid(Tk / kTR, (K1 + kTC - 1) / kTC);
+  hipLaunchKernelGGL(k_bwd_xm_t, grid, dim3(256), 0, s, static_cast<const uint16_t *>(xm), T, K1,
+                     C, k * k, Tk, static_cast<uint16_t *>(xmt));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_weight_t(const void *w, int32_t R, int32_t Cs, int32_t C, int32_t k,
+                               int32_t Rk, void *out, hipStream_t s) {
+  const dim3 grid(Rk / kTR, (Cs + kTC - 1) / kTC);
+  hipLaunchKernelGGL(k_bwd_weight_t, grid, dim3(256), 0, s, static_cast<const uint16_t *>(w), R,
+                     Cs, C, k * k, Rk, static_cast<uint16_t *>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_unmerge(const void *dxm, const void *x, const PlanChunk &c, int C,
+                              const void *gamma, float eps, void *dx, float *part_g,
+                              float *part_b, const int32_t *status, int grid, hipStream_t s) {
+  if (c.tok0[c.n] <= c.tok0[0]) return hipSuccess;
+  return gamma ? unmerge_dispatch<true>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status,
+                                        grid, s)
+               : unmerge_dispatch<false>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status,
+                                         grid, s);
+}
+
+hipError_t launch_colsum(const float *part, int32_t R, int32_t N, float *out,
+                         const int32_t *status, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_colsum, dim3((N + 255) / 256), dim3(256), 0, s, part, R, N, out, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_sum(const void *G, const int32_t *pos, int32_t n, int32_t O, float *part,
+                           hipStream_t s) {
+  if (n <= 0 || O <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rows_sum, dim3((O + 255) / 256, (n + 63) / 64), dim3(256), 0, s,
+                     static_cast<const uint16_t *>(G), pos, n, O, part);
+  return hipGetLastError();
+}
+
+}  // namespace vlb

@@ -210,10 +210,15 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t *ids, int64_t 
 //                 (R % h')*w' + X % w'
 // ("tail" puts the mosaic first).  One wave per slot; token slots record the
 // destination row, newline / separator slots are copied by the whole wave.
-template <typename T>
+//
+// REC (gradients): the sequence is not written; the sequence position of each
+// newline slot goes to nl_pos[nl0 + ordinal] -- ordinal counting the image's
+// newlines in assembly order (global rows, then mosaic rows; reversed with
+// "tail") -- and that of the separator to sep_pos[img0 + image].
+template <typename T, bool REC>
 __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32_t *status,
                               int32_t *dst_row, const T *newline, const T *separator, T *seq,
-                              int D) {
+                              int D, int32_t *nl_pos, int32_t *sep_pos) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
@@ -233,6 +238,7 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
     const int L = th * hp * (tw * wp + 1);   // local mosaic block
     int q = j - c.slot0[im];
     int row = -1;                            // token row, or -1 newline, -2 separator
+    int nl_ord = 0;                          // newline ordinal inside the image
     bool global;
     if (!c.tail) {
       global = q < G;
@@ -247,9 +253,11 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
       if (global) {
         const int R = q / (wp + 1), X = q % (wp + 1);
         row = (X == wp) ? -1 : c.row0[im] + R * wp + X;
+        nl_ord = (c.tail ? th * hp : 0) + R;
       } else {
         const int W = tw * wp + 1;
         const int R = q / W, X = q % W;
+        nl_ord = (c.tail ? 0 : hp) + R;
         if (X == tw * wp) {
           row = -1;
         } else {
@@ -260,6 +268,12 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
     }
     if (row >= 0) {
       if (lane == 0) dst_row[row] = ok ? slot_pos[j] : -1;
+    } else if (REC) {
+      if (lane == 0) {
+        const int32_t pos = ok ? slot_pos[j] : -1;
+        if (row == -1) nl_pos[c.nl0[im] + nl_ord] = pos;
+        else sep_pos[c.img0 + im] = pos;
+      }
     } else if (ok) {
       const uint4 *from = reinterpret_cast<const uint4 *>(row == -1 ? newline : separator);
       uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(slot_pos[j]) * D);
@@ -609,13 +623,26 @@ hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slo
   if (n <= 0) return hipSuccess;
   const int grid = grid_for(n, 4, 4096);  // 4 waves per block, one slot per wave per pass
   if (dtype == 0)
-    hipLaunchKernelGGL(k_place_tiled<float>, dim3(grid), dim3(256), 0, s, c, slot_pos, status,
-                       dst_row, static_cast<const float *>(newline),
-                       static_cast<const float *>(separator), static_cast<float *>(seq), D);
+    hipLaunchKernelGGL((k_place_tiled<float, false>), dim3(grid), dim3(256), 0, s, c, slot_pos,
+                       status, dst_row, static_cast<const float *>(newline),
+                       static_cast<const float *>(separator), static_cast<float *>(seq), D,
+                       nullptr, nullptr);
   else
-    hipLaunchKernelGGL(k_place_tiled<uint16_t>, dim3(grid), dim3(256), 0, s, c, slot_pos, status,
-                       dst_row, static_cast<const uint16_t *>(newline),
-                       static_cast<const uint16_t *>(separator), static_cast<uint16_t *>(seq), D);
+    hipLaunchKernelGGL((k_place_tiled<uint16_t, false>), dim3(grid), dim3(256), 0, s, c,
+                       slot_pos, status, dst_row, static_cast<const uint16_t *>(newline),
+                       static_cast<const uint16_t *>(separator), static_cast<uint16_t *>(seq), D,
+                       nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_place_tiled_record(const PlaceChunk &c, const int32_t *slot_pos,
+                                     const int32_t *status, int32_t *dst_row, int32_t *nl_pos,
+                                     int32_t *sep_pos, hipStream_t s) {
+  const int64_t n = c.slot0[c.n] - c.slot0[0];
+  if (n <= 0) return hipSuccess;
+  const int grid = grid_for(n, 4, 4096);
+  hipLaunchKernelGGL((k_place_tiled<uint16_t, true>), dim3(grid), dim3(256), 0, s, c, slot_pos,
+                     status, dst_row, nullptr, nullptr, nullptr, 0, nl_pos, sep_pos);
   return hipGetLastError();
 }
 

@@ -108,25 +108,27 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t *ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst), 16, off, 0, 0, 0);
 }
 
+// Stage buffer i of four (a select, never an indexed private array).
+__device__ __forceinline__ uint8_t *pick(uint8_t *const (&b)[4], int i) {
+  return i == 0 ? b[0] : i == 1 ? b[1] : i == 2 ? b[2] : b[3];
+}
+
 // Epilogue of one tile.  The weight fragment is the MFMA's first operand, so
 // acc[i][j] holds the transposed product: lane (fr, fq) = (lane % 16,
 // lane / 16) of wave (wm, wn) owns token row wm*WT + 16 i + fr and features
-// wn*WT + 16 j + 4 fq + e in element e (e < 4).  Bias and activation are
-// applied in fp32, the tile is rounded to bf16 and staged in the stage
-// buffers (64 rows each; rows of 16-byte chunks XOR-swizzled by the row), then
-// written out whole rows at a time with 16-byte stores to row s_dst[r]
-// (skipped when negative), or tile-blocked.  The caller has synchronised the
+// wn*WT + 16 j + 4 fq + e in element e (e < 4).
+//
+// stage_tile: bias (and the activation when ACT_ON) applied in fp32, the tile
+// rounded to bf16 and staged in the stage buffers (64 rows each; rows of
+// 16-byte chunks XOR-swizzled by the row).  The caller has synchronised the
 // workgroup after its last use of the buffers.
-template <int ACT, int BMT, bool BLOCKED_OUT>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
-                                           const GemmArgs &g, int m0, int n0, uint8_t *b0,
-                                           uint8_t *b1, uint8_t *b2, uint8_t *b3,
-                                           const uint16_t *s_bias, const int32_t *s_dst) {
+template <int ACT, int BMT, bool ACT_ON>
+__device__ __forceinline__ void stage_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+                                           uint8_t *const (&bufs)[4], const uint16_t *s_bias) {
   using G = Geo<BMT>;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int fr = lane & 15, fq = lane >> 4;
-  auto bufs = [&](int b) -> uint8_t * { return b == 0 ? b0 : b == 1 ? b1 : b == 2 ? b2 : b3; };
 #pragma unroll
   for (int j = 0; j < G::TI; ++j) {
     const int cl = wn * G::WT + j * 16 + 4 * fq;  // 4 consecutive features
@@ -140,36 +142,51 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
       const int row = r & 63;                  // inside buffer r / 64
       uint16_t h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = f2bf(act_fn<ACT>(acc[i][j][e] + b[e]));
+      for (int e = 0; e < 4; ++e) {
+        const float v = acc[i][j][e] + b[e];
+        h[e] = f2bf(ACT_ON ? act_fn<ACT>(v) : v);
+      }
       uint2 v;
       v.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
       v.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
-      *reinterpret_cast<uint2 *>(bufs(r >> 6) + row * G::ROWB +
+      *reinterpret_cast<uint2 *>(pick(bufs, r >> 6) + row * G::ROWB +
                                  ((chunk ^ (row & (G::CCH - 1))) << 4) + half * 8) = v;
     }
   }
-  __syncthreads();
-  uint16_t *out = static_cast<uint16_t *>(g.out);
-  if constexpr (BLOCKED_OUT) {
-    // Tile-blocked output (the hidden activation): for each 32-wide feature
-    // slice of the tile, rows' 64-byte segments are contiguous, so 4 lanes
-    // write one row segment and a wave 16 rows -- 1 KiB per store.
-    const uint32_t KBo = g.N / 32;
+}
+
+// Tile-blocked output of a staged tile: for each 32-wide feature slice of the
+// tile, rows' 64-byte segments are contiguous, so 4 lanes write one row
+// segment and a wave 16 rows -- 1 KiB per store.
+template <int BMT>
+__device__ __forceinline__ void write_blocked(uint8_t *const (&bufs)[4], const GemmArgs &g, int m0,
+                                              int n0, uint16_t *out) {
+  using G = Geo<BMT>;
+  const int tid = threadIdx.x;
+  const uint32_t KBo = g.N / 32;
 #pragma unroll 4
-    for (int q = tid; q < BMT * BMT / 8; q += NTHREADS) {
-      const int fs = q / (BMT * 4), rem = q % (BMT * 4);
-      const int row = rem >> 2, c4 = rem & 3;  // tile row, chunk in the slice
-      const int m = m0 + row, f = n0 + fs * 32 + c4 * 8;
-      if (m >= g.M || f >= g.N) continue;
-      const int chunk = fs * 4 + c4, rb = row & 63;
-      const uint4 v = *reinterpret_cast<const uint4 *>(bufs(row >> 6) + rb * G::ROWB +
-                                                       ((chunk ^ (rb & (G::CCH - 1))) << 4));
-      const int64_t e =
-          ((static_cast<int64_t>(m >> 8) * KBo + (f >> 5)) * 256 + (m & 255)) * 32 + (f & 31);
-      *reinterpret_cast<uint4 *>(out + e) = v;
-    }
-    return;
+  for (int q = tid; q < BMT * BMT / 8; q += NTHREADS) {
+    const int fs = q / (BMT * 4), rem = q % (BMT * 4);
+    const int row = rem >> 2, c4 = rem & 3;  // tile row, chunk in the slice
+    const int m = m0 + row, f = n0 + fs * 32 + c4 * 8;
+    if (m >= g.M || f >= g.N) continue;
+    const int chunk = fs * 4 + c4, rb = row & 63;
+    const uint4 v = *reinterpret_cast<const uint4 *>(pick(bufs, row >> 6) + rb * G::ROWB +
+                                                     ((chunk ^ (rb & (G::CCH - 1))) << 4));
+    const int64_t e =
+        ((static_cast<int64_t>(m >> 8) * KBo + (f >> 5)) * 256 + (m & 255)) * 32 + (f & 31);
+    *reinterpret_cast<uint4 *>(out + e) = v;
   }
+}
+
+// Whole rows of a staged tile with 16-byte stores to row s_dst[r] (skipped
+// when negative).
+template <int BMT>
+__device__ __forceinline__ void write_rows(uint8_t *const (&bufs)[4], const GemmArgs &g, int n0,
+                                           const int32_t *s_dst) {
+  using G = Geo<BMT>;
+  const int tid = threadIdx.x;
+  uint16_t *out = static_cast<uint16_t *>(g.out);
   const int chunk = tid % G::CCH;
   const int col = n0 + chunk * 8;
   constexpr int RSTEP = NTHREADS / G::CCH;  // rows per pass
@@ -180,10 +197,58 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
       const int row = tid / G::CCH + RSTEP * s8;  // inside buffer bi
       const int dst = s_dst[bi * 64 + row];       // -1: past the last row, or not placed
       if (dst < 0 || col >= g.N) continue;
-      const uint4 v = *reinterpret_cast<const uint4 *>(bufs(bi) + row * G::ROWB +
+      const uint4 v = *reinterpret_cast<const uint4 *>(pick(bufs, bi) + row * G::ROWB +
                                                        ((chunk ^ (row & (G::CCH - 1))) << 4));
       *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
     }
+  }
+}
+
+// fp32 rows straight from the accumulators: each lane stores its 4
+// consecutive features of a row as one 16-byte store (a wave covers 16 rows x
+// 64 bytes per store instruction).  No bias.
+template <int BMT>
+__device__ __forceinline__ void write_f32(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+                                          const GemmArgs &g, int m0, int n0) {
+  using G = Geo<BMT>;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int fr = lane & 15, fq = lane >> 4;
+  float *out = static_cast<float *>(g.out);
+#pragma unroll
+  for (int j = 0; j < G::TI; ++j) {
+    const int n = n0 + wn * G::WT + j * 16 + 4 * fq;
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i) {
+      const int m = m0 + wm * G::WT + i * 16 + fr;
+      if (m < g.M && n < g.N)
+        *reinterpret_cast<f32x4 *>(out + static_cast<int64_t>(m) * g.ldo + n) = acc[i][j];
+    }
+  }
+}
+
+// The epilogue of each mode (see GemmMode).
+template <int MODE, int ACT, int BMT>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+                                           const GemmArgs &g, int m0, int n0,
+                                           uint8_t *const (&bufs)[4], const uint16_t *s_bias,
+                                           const int32_t *s_dst) {
+  if constexpr (MODE == kGemmF32) {
+    write_f32<BMT>(acc, g, m0, n0);
+  } else if constexpr (MODE == kGemmRows) {
+    stage_tile<ACT, BMT, false>(acc, bufs, s_bias);
+    __syncthreads();
+    write_rows<BMT>(bufs, g, n0, s_dst);
+  } else {
+    if constexpr (MODE == kGemmBlockedSave) {  // pre-activation first
+      stage_tile<ACT, BMT, false>(acc, bufs, s_bias);
+      __syncthreads();
+      write_blocked<BMT>(bufs, g, m0, n0, static_cast<uint16_t *>(g.out2));
+      __syncthreads();
+    }
+    stage_tile<ACT, BMT, true>(acc, bufs, s_bias);
+    __syncthreads();
+    write_blocked<BMT>(bufs, g, m0, n0, static_cast<uint16_t *>(g.out));
   }
 }
 
@@ -191,7 +256,7 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 // tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
 // quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
 // whole 128-grid).
-template <bool LINEAR1, int ACT, int BMT>
+template <int MODE, int ACT, int BMT>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   using G = Geo<BMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -217,11 +282,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     tile_coords(xcd_remap(blockIdx.x, tm128 * tn128), tm128, tn128, tm, tn);
   }
   const int m0 = tm * BMT, n0 = tn * BMT;
+  // A gradient GEMM writes nothing when the placeholder scan failed.
+  if (MODE == kGemmF32 && g.status && g.status[kStatusWord] != 0) return;
   // Epilogue operands are fetched now so their latency hides under the K loop.
   if (tid < BMT) {
     const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
     const int c = n0 + tid;
-    s_bias[tid] = c < g.N ? bias[c] : static_cast<uint16_t>(0);
+    s_bias[tid] = (bias && c < g.N) ? bias[c] : static_cast<uint16_t>(0);
     const int m = m0 + tid;
     s_dst[tid] = m >= g.M ? -1 : (g.dst_row ? g.dst_row[m] : m);
   }
@@ -359,34 +426,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     step(smem0, smem2, kt + 3, fa1, fb1, fa0, fb0);
   }
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
-  store_tile<ACT, BMT, LINEAR1>(acc, g, m0, n0, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  uint8_t *const bufs[4] = {smem0, smem1, smem2, smem3};
+  store_tile<MODE, ACT, BMT>(acc, g, m0, n0, bufs, s_bias, s_dst);
 }
 
-template <bool LINEAR1, int ACT>
+template <int MODE, int ACT>
 void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
   if (blocks256 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<LINEAR1, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
   if (blocks128 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<LINEAR1, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+}
+
+template <int MODE>
+void launch_act(const GemmArgs &g, const TilePlan &tp, hipStream_t s) {
+  if (g.act == 0)
+    launch_bf16<MODE, 0>(g, tp.n_full, tp.blocks128, s);
+  else if (g.act == 1)
+    launch_bf16<MODE, 1>(g, tp.n_full, tp.blocks128, s);
+  else
+    launch_bf16<MODE, 2>(g, tp.n_full, tp.blocks128, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(bool linear1, GemmArgs g, hipStream_t s) {
+hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % BK != 0) return hipErrorInvalidValue;
   const TilePlan tp = tile_plan(g.M, g.N);
   g.tiles_m = tp.tiles_m;
   g.tiles_n = tp.tiles_n;
   g.n_full = tp.n_full;
-  if (!linear1 && g.act != 2) return hipErrorInvalidValue;  // the second Linear has no activation
-  if (linear1 && g.act == 0)
-    launch_bf16<true, 0>(g, tp.n_full, tp.blocks128, s);
-  else if (linear1 && g.act == 1)
-    launch_bf16<true, 1>(g, tp.n_full, tp.blocks128, s);
-  else if (linear1)
-    launch_bf16<true, 2>(g, tp.n_full, tp.blocks128, s);
-  else
-    launch_bf16<false, 2>(g, tp.n_full, tp.blocks128, s);
+  switch (mode) {
+    case kGemmBlocked: launch_act<kGemmBlocked>(g, tp, s); break;
+    case kGemmBlockedSave:
+      if (!g.out2) return hipErrorInvalidValue;
+      launch_act<kGemmBlockedSave>(g, tp, s);
+      break;
+    case kGemmRows:  // no activation
+      if (g.act != 2) return hipErrorInvalidValue;
+      launch_bf16<kGemmRows, 2>(g, tp.n_full, tp.blocks128, s);
+      break;
+    case kGemmF32:  // no bias, no activation
+      if (g.act != 2 || g.N % 4 || g.ldo % 4) return hipErrorInvalidValue;
+      launch_bf16<kGemmF32, 2>(g, tp.n_full, tp.blocks128, s);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

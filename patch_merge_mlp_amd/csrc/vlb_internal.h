@@ -38,6 +38,10 @@ struct PlaceChunk {
   int32_t row0[kPlaceImages];       // first token row of each image (its global view)
   int16_t hp[kPlaceImages], wp[kPlaceImages];  // merged grid of every view of the image
   int16_t tw[kPlaceImages], th[kPlaceImages];  // local tile grid, width count first
+  // Recording mode (gradients): newline slots of image i go to list entries
+  // nl0[i] + ordinal (ordinal in assembly order), its separator to entry img0 + i.
+  int32_t nl0[kPlaceImages];
+  int32_t img0;
 };
 
 // Status words at the start of the workspace.
@@ -65,6 +69,16 @@ struct GemmArgs {
   // bf16 path: tiles [0, n_full) of the 256-grid are computed as 256x256
   // tiles, the rest as 128x128 tiles (see tile_plan).
   int32_t n_full;
+  void *out2;              // kGemmBlockedSave: the pre-activation, tile-blocked like out
+  const int32_t *status;   // kGemmF32: nothing is written when status[0] != 0 (may be null)
+};
+
+// Epilogues of the bf16 GEMM.
+enum GemmMode {
+  kGemmBlocked = 0,      // bias + activation, bf16 tile-blocked output (Linear1)
+  kGemmRows = 1,         // bias, bf16 rows to dst(m) (Linear2)
+  kGemmF32 = 2,          // fp32 rows out + m*ldo, no bias (weight gradients)
+  kGemmBlockedSave = 3,  // kGemmBlocked, and bias without activation to out2 as well
 };
 
 // Tile plan of the bf16 GEMM.  256x256 tiles keep the MFMAs busiest, but on
@@ -115,6 +129,12 @@ hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t i
 hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
                               const int32_t *status, int32_t *dst_row, const void *newline,
                               const void *separator, void *seq, int D, hipStream_t s);
+// The same decode without writing the sequence: dst_row as above, and the
+// sequence positions of the newline and separator slots into nl_pos / sep_pos
+// (see PlaceChunk::nl0, img0).
+hipError_t launch_place_tiled_record(const PlaceChunk &c, const int32_t *slot_pos,
+                                     const int32_t *status, int32_t *dst_row, int32_t *nl_pos,
+                                     int32_t *sep_pos, hipStream_t s);
 // Largest C the LayerNorm kernel keeps in registers.
 int layernorm_max_channels(int dtype);
 hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const void *gamma,
@@ -140,11 +160,49 @@ hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *
 hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const void *gamma,
                                 const void *beta, float eps, void *out, hipStream_t s);
 
-// bf16 MFMA GEMMs on blocked operands.  linear1: act epilogue, blocked output.
-// Otherwise: no activation, plain rows to dst(m).
-hipError_t launch_gemm_bf16(bool linear1, GemmArgs g, hipStream_t s);
+// bf16 MFMA GEMMs on blocked operands (K a multiple of 32), epilogue by mode
+// (GemmMode).  A null bias counts as zero.
+hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s);
 // fp32 GEMMs (FMA).  In gather mode K follows the pages' order c*k*k + p and B
 // is the unpacked W1.
 hipError_t launch_gemm_f32(bool gather, GemmArgs g, hipStream_t s);
+
+// ---- projector backward (bf16; see vlb_backward.hip) ------------------------
+// T: token rows; Tk = T rounded up to 32 (the K extent of every contraction
+// over tokens); Op = out_dim rounded up to 32.  Tile-blocked operands as above.
+constexpr int kBwdMaxChannels = 2048;  // the LayerNorm backward keeps a pixel in registers
+constexpr int kBwdUnmergeGrid = 512;   // most workgroups of one unmerge launch
+int bwd_unmerge_grid(int64_t items);   // workgroups for items (token row, position) pairs
+// dY rows gathered from G [S][O] at dst_row (zero where negative) -> dY [T][Op],
+// dY^T [O][Tk], part [Tk/32][O] (column sums per 32-row slice).
+hipError_t launch_bwd_gather_dy(const void *G, const int32_t *dst_row, int32_t T, int32_t O,
+                                int32_t Op, int32_t Tk, void *dy, void *dyt, float *part,
+                                hipStream_t s);
+// act(Z1)^T [H][Tk] from the blocked pre-activation Z1 [T][H].
+hipError_t launch_bwd_act_t(int act, const void *z1, int32_t T, int32_t H, int32_t Tk, void *a1t,
+                            hipStream_t s);
+// dZ1 = dA1 * act'(Z1) -> dZ1 [T][H], dZ1^T [H][Tk], part [Tk/32][H].
+hipError_t launch_bwd_dact(int act, const void *da1, const void *z1, int32_t T, int32_t H,
+                           int32_t Tk, void *dz1, void *dz1t, float *part, hipStream_t s);
+// Merged tokens Xm [T][C*k*k] (K position-major) -> Xm^T [C*k*k][Tk], rows in
+// the pages' feature order.
+hipError_t launch_bwd_xm_t(const void *xm, int32_t T, int32_t C, int32_t k, int32_t Tk, void *xmt,
+                           hipStream_t s);
+// Row-major W [R][Cs] -> blocked W^T [Cs][Rk] (zeros past R); k > 1: W is
+// W1 and output rows are position-major.
+hipError_t launch_bwd_weight_t(const void *w, int32_t R, int32_t Cs, int32_t C, int32_t k,
+                               int32_t Rk, void *out, hipStream_t s);
+// Feature gradient of one chunk of views from dXm (row-major [T][C*k*k], K
+// position-major) through the LayerNorm (gamma non-null) or not; grid rows of
+// part_g / part_b ([grid][C]) take the per-workgroup dgamma / dbeta sums.
+hipError_t launch_bwd_unmerge(const void *dxm, const void *x, const PlanChunk &c, int C,
+                              const void *gamma, float eps, void *dx, float *part_g,
+                              float *part_b, const int32_t *status, int grid, hipStream_t s);
+// out[n] = sum_r part[r][n], rows in order; nothing when status[0] != 0.
+hipError_t launch_colsum(const float *part, int32_t R, int32_t N, float *out,
+                         const int32_t *status, hipStream_t s);
+// part[ceil(n/64)][O]: sums of G rows pos[i] (negative: none), 64 entries per row.
+hipError_t launch_rows_sum(const void *G, const int32_t *pos, int32_t n, int32_t O, float *part,
+                           hipStream_t s);
 
 }  // namespace vlb

@@ -23,9 +23,11 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
 F32, BF16 = 0, 1
 GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
-K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK, K_EMBED = range(10)
+K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK, K_EMBED, \
+    K_BWD_PACK, K_BWD_DW2, K_BWD_DA1, K_BWD_DW1, K_BWD_DX, K_BWD_UNMERGE, K_BWD_SUM = range(17)
 KERNEL_NAMES = ["plan", "scan", "place", "layernorm", "gemm1", "gemm2", "scatter", "merge", "pack",
-                "embed"]
+                "embed", "bwd_pack", "bwd_dw2", "bwd_da1", "bwd_dw1", "bwd_dx", "bwd_unmerge",
+                "bwd_sum"]
 
 
 class VlbError(RuntimeError):
@@ -46,6 +48,13 @@ class vlb_weights(ct.Structure):
 
 
 _P32 = ct.POINTER(ct.c_int32)
+
+
+class vlb_grads(ct.Structure):
+    _fields_ = [("d_features", ct.c_void_p), ("d_w1", ct.c_void_p), ("d_b1", ct.c_void_p),
+                ("d_w2", ct.c_void_p), ("d_b2", ct.c_void_p), ("d_ln_gamma", ct.c_void_p),
+                ("d_ln_beta", ct.c_void_p), ("d_newline", ct.c_void_p),
+                ("d_separator", ct.c_void_p)]
 
 
 class vlb_batch(ct.Structure):
@@ -83,6 +92,12 @@ def lib():
                                       vp, sz, vp]),
             "vlb_bridge_embed": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, ct.c_int32,
                                       vp, i64, i64, vp, vp, sz, vp]),
+            "vlb_saved_bytes": (sz, [pp, pb]),
+            "vlb_backward_workspace_bytes": (sz, [pp, pb, i64]),
+            "vlb_bridge_fused_train": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, i64,
+                                            vp, vp, sz, vp, sz, vp]),
+            "vlb_bridge_backward": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, i64, vp, vp, sz,
+                                         ct.POINTER(vlb_grads), vp, sz, vp]),
             "vlb_check": (st, [vp, vp]),
             "vlb_status_str": (ct.c_char_p, [st]),
             "vlb_prof_enable": (st, [ct.c_int32]),
@@ -325,6 +340,94 @@ def vlb_bridge_embed(p, b: Batch, features, w: Weights, newline, separator, ids,
                                   _ptr(newline), _ptr(separator), _ptr(ids), int(image_token_id),
                                   _ptr(embed), embed.shape[0], seq.shape[0], _ptr(seq), _ptr(ws),
                                   ws.numel(), _stream(stream)), "vlb_bridge_embed")
+
+
+# ---- training --------------------------------------------------------------
+
+def vlb_saved_bytes(p: vlb_projector, b: Batch) -> int:
+    return int(lib().vlb_saved_bytes(ct.byref(p), ct.byref(b.c)))
+
+
+def vlb_backward_workspace_bytes(p: vlb_projector, b: Batch, seq_len: int) -> int:
+    return int(lib().vlb_backward_workspace_bytes(ct.byref(p), ct.byref(b.c), seq_len))
+
+
+def vlb_bridge_fused_train(p, b: Batch, features, w: Weights, newline, separator, mask, seq,
+                           saved, ws, stream=None):
+    dt = _tdtype(p)
+    _check_seq(p, mask, seq)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _check_weights(p, w)
+    _need(newline, p.out_dim, dt, "newline")
+    _need(separator, p.out_dim, dt, "separator")
+    if saved.dtype != torch.uint8:
+        raise ValueError("saved must be a uint8 buffer")
+    wc = w.c()
+    _check(lib().vlb_bridge_fused_train(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                        _ptr(newline), _ptr(separator), _ptr(mask), seq.shape[0],
+                                        _ptr(seq), _ptr(saved), saved.numel(), _ptr(ws),
+                                        ws.numel(), _stream(stream)), "vlb_bridge_fused_train")
+
+
+@dataclass
+class Grads:
+    """Gradient outputs (fp32 except d_features, in the projector dtype)."""
+    d_w1: torch.Tensor
+    d_b1: torch.Tensor
+    d_w2: torch.Tensor
+    d_b2: torch.Tensor
+    d_features: Optional[torch.Tensor] = None
+    d_ln_gamma: Optional[torch.Tensor] = None
+    d_ln_beta: Optional[torch.Tensor] = None
+    d_newline: Optional[torch.Tensor] = None
+    d_separator: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def empty(p: vlb_projector, b: Batch, features=True, device="cuda") -> "Grads":
+        f32 = dict(dtype=torch.float32, device=device)
+        K1 = p.C * p.k * p.k
+        g = Grads(torch.empty(p.hidden, K1, **f32), torch.empty(p.hidden, **f32),
+                  torch.empty(p.out_dim, p.hidden, **f32), torch.empty(p.out_dim, **f32))
+        if features:
+            g.d_features = torch.empty(_pixels(b), p.C, dtype=_tdtype(p), device=device)
+        if p.has_ln:
+            g.d_ln_gamma = torch.empty(p.C, **f32)
+            g.d_ln_beta = torch.empty(p.C, **f32)
+        if b.layout == LAYOUT_TILED_2D:
+            g.d_newline = torch.empty(p.out_dim, **f32)
+            g.d_separator = torch.empty(p.out_dim, **f32)
+        return g
+
+    def c(self) -> vlb_grads:
+        return vlb_grads(_ptr(self.d_features), _ptr(self.d_w1), _ptr(self.d_b1), _ptr(self.d_w2),
+                         _ptr(self.d_b2), _ptr(self.d_ln_gamma), _ptr(self.d_ln_beta),
+                         _ptr(self.d_newline), _ptr(self.d_separator))
+
+
+def vlb_bridge_backward(p, b: Batch, features, w: Weights, mask, dseq, saved, g: Grads, ws,
+                        stream=None):
+    dt = _tdtype(p)
+    _check_seq(p, mask, dseq)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _need(w.w1, p.hidden * p.C * p.k * p.k, dt, "w1")
+    _need(w.w2, p.out_dim * p.hidden, dt, "w2")
+    _need(w.ln_gamma, p.C, dt, "ln_gamma")
+    f32 = torch.float32
+    _need(g.d_w1, p.hidden * p.C * p.k * p.k, f32, "d_w1")
+    _need(g.d_b1, p.hidden, f32, "d_b1")
+    _need(g.d_w2, p.out_dim * p.hidden, f32, "d_w2")
+    _need(g.d_b2, p.out_dim, f32, "d_b2")
+    _need(g.d_features, _pixels(b) * p.C, dt, "d_features")
+    for t, n, what in ((g.d_ln_gamma, p.C, "d_ln_gamma"), (g.d_ln_beta, p.C, "d_ln_beta"),
+                       (g.d_newline, p.out_dim, "d_newline"),
+                       (g.d_separator, p.out_dim, "d_separator")):
+        _need(t, n, f32, what)
+    wc = w.c()
+    gc = g.c()
+    _check(lib().vlb_bridge_backward(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                     _ptr(mask), dseq.shape[0], _ptr(dseq), _ptr(saved),
+                                     saved.numel(), ct.byref(gc), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "vlb_bridge_backward")
 
 
 def vlb_check(ws, stream=None) -> int:

@@ -22,6 +22,9 @@ token-embedding table [VOCAB][out_dim] ~ N(0, 1), then the text ids, uniform
 over [0, VOCAB) without the image token; placeholder positions hold
 IMAGE_TOKEN_ID.  VOCAB and IMAGE_TOKEN_ID are the VL2 language config's
 vocab_size and image_token_index.
+
+The gradient of a training loss with respect to the sequence (seq_grad) comes
+from a third generator (seed 2000 + workload seed): N(0, 1) per element.
 """
 from __future__ import annotations
 
@@ -170,6 +173,14 @@ def token_inputs(w: Workload, mask: torch.Tensor, vocab: int = VOCAB,
     ids = torch.where(ids >= image_token_id, ids + 1, ids)  # skip the image token
     ids = torch.where(mask.bool(), torch.full_like(ids, image_token_id), ids)
     return ids.to(torch.int32), table
+
+
+def seq_grad(w: Workload) -> torch.Tensor:
+    """Gradient of a loss with respect to the embedded sequence, [seq_len][out_dim]
+    in the workload dtype: N(0, 1) from a generator seeded 2000 + the workload seed
+    (the other draws are unchanged)."""
+    g = torch.Generator("cpu").manual_seed(2000 + w.seed)
+    return torch.randn((w.seq_len, w.out_dim), generator=g, dtype=torch.float32).to(w.torch_dtype)
 
 
 def make(w: Workload, span_fn: Callable[[Workload], Sequence[int]],

@@ -431,9 +431,10 @@ def pin_scatter_backward(o):
     assert np.allclose(drows, rows.grad.numpy(), rtol=1e-14, atol=0)
     assert np.allclose(dnl, nl.grad.numpy(), rtol=1e-14, atol=1e-15)
     assert np.allclose(dsp, sp.grad.numpy(), rtol=1e-14, atol=1e-15)
-    bad = mask.copy()
-    bad[0] = 1
-    assert o.scatter_backward(src, bad, G, T)[0] == -1
+    for pos, val in ((0, 1), (5, 0)):  # one placeholder too many, one too few
+        bad = mask.copy()
+        bad[pos] = val
+        assert o.scatter_backward(src, bad, G, T)[0] == -1
 
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,

@@ -190,6 +190,61 @@ def test_embed_validates_before_launching():
     assert call(b=e, feats=None, w=None, ws_bytes=need_e - 1) == v.ERR_WORKSPACE
 
 
+def test_training_entry_points_validate():
+    """vlb_saved_bytes / vlb_backward_workspace_bytes sizes; the training forward and
+    the backward reject fp32, packed weights (backward), missing or misaligned
+    pointers and small buffers before launching anything."""
+    L = v.lib()
+    p = _proj(has_ln=True)
+    b = v.Batch([(4, 4)], [1])
+    T = v.vlb_num_tokens(p, b)
+    K1 = p.C * p.k * p.k
+    assert v.vlb_saved_bytes(p, b) == 256 * K1 * 2 + 256 * p.hidden * 2
+    assert v.vlb_saved_bytes(_proj(dtype=v.F32), b) == 0
+    need = v.vlb_backward_workspace_bytes(p, b, 32)
+    assert need > 0
+    assert v.vlb_backward_workspace_bytes(_proj(dtype=v.F32), b, 32) == 0
+    assert v.vlb_backward_workspace_bytes(_proj(packed=True), b, 32) == 0
+    assert v.vlb_backward_workspace_bytes(_proj(has_ln=True, C=2112), b, 32) == 0
+    w = v.vlb_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    fneed = v.vlb_workspace_bytes(p, b, 32)
+    sneed = v.vlb_saved_bytes(p, b)
+    G = 1 << 26
+
+    def train(saved=FAKE + 2 * G, saved_bytes=sneed, proj=p, ws_bytes=fneed):
+        return L.vlb_bridge_fused_train(ct.byref(proj), ct.byref(b.c), FAKE, ct.byref(w), None,
+                                        None, FAKE, 32, FAKE + G, saved, saved_bytes, FAKE + 3 * G,
+                                        ws_bytes, None)
+    assert train(proj=_proj(dtype=v.F32)) == v.ERR_UNSUPPORTED
+    assert train(saved=None) == v.ERR_NULL
+    assert train(saved=FAKE + 2 * G + 8) == v.ERR_ALIGN
+    assert train(saved_bytes=sneed - 1) == v.ERR_WORKSPACE
+    assert train(ws_bytes=fneed - 1) == v.ERR_WORKSPACE
+    assert train(saved=FAKE + G) == v.ERR_UNSUPPORTED  # saved overlaps the sequence
+
+    grads = v.vlb_grads(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+
+    def bwd(proj=p, g=grads, wts=w, feats=FAKE, ws_bytes=need, saved_bytes=sneed, S=32):
+        return L.vlb_bridge_backward(ct.byref(proj), ct.byref(b.c), feats, ct.byref(wts), FAKE, S,
+                                     FAKE, FAKE, saved_bytes, ct.byref(g) if g else None, FAKE,
+                                     ws_bytes, None)
+    assert bwd(proj=_proj(dtype=v.F32)) == v.ERR_UNSUPPORTED
+    assert bwd(proj=_proj(has_ln=True, packed=True)) == v.ERR_UNSUPPORTED
+    assert bwd(g=None) == v.ERR_NULL
+    assert bwd(g=v.vlb_grads(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)) == v.ERR_NULL
+    assert bwd(g=v.vlb_grads(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None)) == v.ERR_NULL
+    assert bwd(g=v.vlb_grads(FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)) == v.ERR_ALIGN
+    assert bwd(wts=v.vlb_weights(None, FAKE, FAKE, FAKE, FAKE, FAKE)) == v.ERR_NULL  # LN gamma
+    assert bwd(feats=None) == v.ERR_NULL  # the LayerNorm backward reads the features
+    assert bwd(ws_bytes=need - 1) == v.ERR_WORKSPACE
+    assert bwd(saved_bytes=sneed - 1) == v.ERR_WORKSPACE
+    assert bwd(S=0) == v.ERR_SHAPE
+    bt = v.Batch([(4, 4)] * 2, [2], v.LAYOUT_TILED_2D, [(1, 1)])
+    assert L.vlb_bridge_backward(ct.byref(p), ct.byref(bt.c), FAKE, ct.byref(w), FAKE, 64, FAKE,
+                                 FAKE, 1 << 30, ct.byref(grads), FAKE, 1 << 30,
+                                 None) == v.ERR_NULL  # tiled: newline / separator gradients
+
+
 def test_packed_bytes():
     """Tile-blocked weights: rows padded to a multiple of 256, K unchanged."""
     p = _proj()  # C=64, k=2 -> K1=256; hidden=128; out_dim=64

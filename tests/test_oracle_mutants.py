@@ -42,8 +42,10 @@ MUTANTS = {
     "placeholder formula without local newlines": ("(th * hp) * (tw * wp + 1)", "(th * hp) * (tw * wp)"),
     "scatter in reverse": ("    if (!mask[i]) continue;\n    const double *from = src[j] >= 0                  ? rows + src[j] * D",
                            "    if (!mask[i]) continue;\n    j = P - 1 - j; const double *from = src[j] >= 0 ? rows + src[j] * D"),
-    "no count check": ("if (count != P) return -1;\n  int64_t j = 0;",
-                       "(void)count;\n  int64_t j = 0;"),
+    # count-check mutants keep rejecting too many placeholders: with more
+    # placeholders than slots the mutated code would read past the slot list
+    "count check misses too few placeholders": ("if (count != P) return -1;\n  int64_t j = 0;",
+                                                "if (count > P) return -1;\n  int64_t j = 0;"),
     "param count without second bias": ("hidden * out_dim + out_dim;", "hidden * out_dim;"),
     "embedding row off by one": ("const int64_t e = (int64_t)ids[i] * D;",
                                  "const int64_t e = (int64_t)(ids[i] > 0 ? ids[i] - 1 : 0) * D;"),
@@ -51,7 +53,8 @@ MUTANTS = {
         "for (int32_t d = 0; d < D; d++) to[d] = e_bf16 ? bf16_bits(e_bf16[e + d]) : e_f64[e + d];",
         "for (int32_t d = 0; d < D; d++) to[d] = 0.0 * e;"),
     "embedding without the id range check": ("if (bad_id) return -2;", "(void)bad_id;"),
-    "embedding without the count check": ("if (n_img != P) return -1;", "(void)n_img;"),
+    "embedding count check misses too few": ("if (n_img != P) return -1;",
+                                             "if (n_img > P) return -1;"),
     "embedding places visual rows in reverse": (
         "      const double *from = src[j] >= 0                  ? rows + src[j] * D\n                           : src[j] == ORC_SRC_NEWLINE ? newline",
         "      const int64_t jj = P - 1 - j;\n      const double *from = src[jj] >= 0                 ? rows + src[jj] * D\n                           : src[jj] == ORC_SRC_NEWLINE ? newline"),
@@ -92,8 +95,8 @@ MUTANTS = {
                                  "if (dgamma) dgamma[c] += dn[c];\n    if (dbeta) dbeta[c] += dn[c] * xh;"),
     "scatter backward keeps the last newline only": ("for (int32_t d = 0; d < D; d++) to[d] += g[d];",
                                                      "for (int32_t d = 0; d < D; d++) to[d] = g[d];"),
-    "scatter backward without the count check": ("if (count != P) return -1;\n  memset(drows",
-                                                 "(void)count;\n  memset(drows"),
+    "scatter backward count check misses too few": ("if (count != P) return -1;\n  memset(drows",
+                                                    "if (count > P) return -1;\n  memset(drows"),
     "sampled unit misses the bias": ("    z += b1[h];\n    const double a = act_value(s->act, z);",
                                      "    const double a = act_value(s->act, z);"),
     "sampled pixel at the transposed block position": ("const int32_t p = (y % k) * k + xx % k;",
