@@ -46,6 +46,8 @@ def parse():
                     help="target duration of the CPU-baseline sample")
     ap.add_argument("--no-hbm-kernels", action="store_true",
                     help="skip timing the standalone merge and scatter entry points")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip timing the training step (forward + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -195,6 +197,9 @@ def main():
     if not args.no_hbm_kernels:
         out["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
 
+    if not args.no_train and w.dtype == "bf16":
+        out["train_step"] = train_step(v, torch, wl, w, p, b, t, d, T, K1, args.steps)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, T, args.cpu_seconds)
     print(json.dumps(out))
@@ -235,6 +240,69 @@ def hbm_kernels(v, torch, w, p, b, t, d, T, K1, steps):
         res[name] = {"mean_us": round(sec * 1e6, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
                      "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
     return res
+
+
+def train_step(v, torch, wl, w, p, b, t, d, T, K1, steps):
+    """One training step of the projector: vlb_bridge_fused_train (weights packed
+    in the call, as they change every step) then vlb_bridge_backward for a seeded
+    sequence gradient.  Wall time over `steps` steps, then a separate pass with
+    every launch timed for the per-kernel table and the backward GEMMs' rates."""
+    weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
+                        d(t["ln_beta"]))
+    feats, mask = d(t["features"]), d(t["mask"])
+    nl, sep = d(t["newline"]), d(t["separator"])
+    seq = d(t["seq"])
+    dseq = d(wl.seq_grad(w))
+    S = seq.shape[0]
+    fws = torch.empty(v.vlb_workspace_bytes(p, b, S), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(v.vlb_saved_bytes(p, b), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(v.vlb_backward_workspace_bytes(p, b, S), dtype=torch.uint8, device="cuda")
+    g = v.Grads.empty(p, b)
+
+    def one():
+        v.vlb_bridge_fused_train(p, b, feats, weights, nl, sep, mask, seq, saved, fws)
+        v.vlb_bridge_backward(p, b, feats, weights, mask, dseq, saved, g, bws)
+
+    for _ in range(2):
+        one()
+    torch.cuda.synchronize()
+    assert v.vlb_check(bws) == v.OK
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    v.vlb_prof_enable(True)
+    for _ in range(max(3, steps // 4)):
+        one()
+    torch.cuda.synchronize()
+    v.vlb_prof_enable(False)
+    kernels = {}
+    for kid, name in enumerate(v.KERNEL_NAMES):
+        n, ms = v.vlb_prof_read(kid)
+        if n:
+            kernels[name] = {"launches": n, "mean_us": round(1000.0 * ms / n, 2)}
+    reps = max(3, steps // 4)
+    H, O = w.hidden, w.out_dim
+    f_out = 2.0 * T * H * O   # Linear2-shaped products: dW2, dA1
+    f_in = 2.0 * T * H * K1   # Linear1-shaped products: dW1, dXm
+    rate = {}
+    for name, fl in (("bwd_dw2", f_out), ("bwd_da1", f_out), ("bwd_dw1", f_in), ("bwd_dx", f_in)):
+        if name in kernels:
+            us = kernels[name]["mean_us"] * kernels[name]["launches"] / reps
+            rate[name] = round(fl / (us * 1e-6) / 1e12, 1)
+    fwd_fl = f_in + f_out
+    step_fl = 3 * fwd_fl  # forward + four backward products
+    return {
+        "ms_per_step": round(sec * 1e3, 4),
+        "tokens_per_s": round(T / sec, 1),
+        "flop_per_step": step_fl,
+        "tflops_step": round(step_fl / sec / 1e12, 1),
+        "gemm_tflops": rate,
+        "kernels": kernels,
+        "note": "forward (training form: weights packed per call, Z1 and merged tokens kept) "
+                "+ backward; kernel means from a separate pass with every launch timed",
+    }
 
 
 def cpu_baseline(w, t, T, target_s):

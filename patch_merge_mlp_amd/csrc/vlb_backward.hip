@@ -365,15 +365,28 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
   }
 }
 
-// out[n] = sum over r in order of part[r][n] (nothing when the scan failed).
+// out[n] = sum over r of part[r][n] (nothing when the scan failed).  A
+// workgroup takes 32 columns; row group g (of 8) sums rows g, g + 8, ... in
+// order, then the 8 group sums are added in order: the same result every run.
 __global__ __launch_bounds__(256) void k_colsum(const float *part, int32_t R, int32_t N,
                                                 float *out, const int32_t *status) {
+  __shared__ float red[8][33];
   if (status[kStatusWord] != 0) return;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float s = 0.f;
-  for (int r = 0; r < R; ++r) s += part[static_cast<int64_t>(r) * N + n];
-  out[n] = s;
+  const int c = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  const int n = blockIdx.x * 32 + c;
+  float acc = 0.f;
+  if (n < N) {
+#pragma unroll 4
+    for (int r = rg; r < R; r += 8) acc += part[static_cast<int64_t>(r) * N + n];
+  }
+  red[rg][c] = acc;
+  __syncthreads();
+  if (rg == 0 && n < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += red[i][c];
+    out[n] = t;
+  }
 }
 
 // part[b][o] = sum of G[pos[i]][o] over list entries i of block b (64 each;
@@ -495,7 +508,7 @@ hipError_t launch_bwd_unmerge(const void *dxm, const void *x, const PlanChunk &c
 hipError_t launch_colsum(const float *part, int32_t R, int32_t N, float *out,
                          const int32_t *status, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_colsum, dim3((N + 255) / 256), dim3(256), 0, s, part, R, N, out, status);
+  hipLaunchKernelGGL(k_colsum, dim3((N + 31) / 32), dim3(256), 0, s, part, R, N, out, status);
   return hipGetLastError();
 }
 

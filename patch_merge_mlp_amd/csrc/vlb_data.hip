@@ -544,35 +544,38 @@ __global__ __launch_bounds__(256) void k_merge(const T *x, const RowDesc *desc, 
 }
 
 // ---------------------------------------------------------------------------
-// Weight packing into the tile-blocked layout; with k > 1 the K axis of W1 is
-// reordered position-major on the way.  One thread per 16-byte packed chunk.
-__global__ void k_pack(const uint16_t *w, int64_t R, int64_t K, int C, int k, uint16_t *out) {
-  const int kk = k * k;
-  const int64_t KB = K / 32;
-  const int64_t nchunks = (R + 255) / 256 * 256 * K / 8;
-  for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < nchunks;
-       q += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t e = q * 8;                 // packed element index
-    const int64_t cc = e % 32, rr = (e / 32) % 256, blk = e / (32 * 256);
-    const int64_t rb = blk / KB, kb = blk % KB;
-    const int64_t r = rb * 256 + rr;
-    uint16_t v[8];
+// Weight packing into the tile-blocked layout; with kk = k*k > 1 the K axis of
+// W1 is reordered position-major on the way (packed column p*Cc + c takes
+// source column c*kk + p, Cc = K / kk channels).  A workgroup takes 64 rows
+// and 32 channels: it reads the rows' 32*kk source columns (contiguous) into
+// LDS, then for each position p writes the 64 rows' 64-byte pieces of packed
+// K slice (p*Cc + c0) / 32 -- one contiguous 4 KiB run.  Rows past R are zero.
+__global__ __launch_bounds__(256) void k_pack(const uint16_t *w, int64_t R, int64_t K, int kk,
+                                              uint16_t *out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t pk[];  // [64][32*kk + 8]
+  const int Cc = static_cast<int>(K / kk);
+  const int pitch = 32 * kk + 8, nch = 4 * kk;  // row pitch; 16-byte chunks per row
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int c0 = blockIdx.y * 32;
+  for (int q = threadIdx.x; q < 64 * nch; q += 256) {
+    const int row = q / nch, ch = q - row * nch;
+    const int64_t r = r0 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R) v = *reinterpret_cast<const uint4 *>(w + r * K + static_cast<int64_t>(c0) * kk + ch * 8);
+    *reinterpret_cast<uint4 *>(pk + row * pitch + ch * 8) = v;
+  }
+  __syncthreads();
+  const int row = threadIdx.x >> 2, c4 = threadIdx.x & 3;
+  const int64_t r = r0 + row, KB = K / 32;
+  for (int p = 0; p < kk; ++p) {
+    uint32_t h[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t j = kb * 32 + cc + i;    // packed column
-      int64_t src = j;
-      if (kk > 1) {
-        const int64_t p = j / C, c = j - p * C;
-        src = c * kk + p;
-      }
-      v[i] = r < R ? w[r * K + src] : static_cast<uint16_t>(0);
-    }
-    uint4 o;
-    o.x = v[0] | (static_cast<uint32_t>(v[1]) << 16);
-    o.y = v[2] | (static_cast<uint32_t>(v[3]) << 16);
-    o.z = v[4] | (static_cast<uint32_t>(v[5]) << 16);
-    o.w = v[6] | (static_cast<uint32_t>(v[7]) << 16);
-    reinterpret_cast<uint4 *>(out)[q] = o;
+    for (int i = 0; i < 4; ++i)
+      h[i] = pk[row * pitch + (c4 * 8 + 2 * i) * kk + p] |
+             (static_cast<uint32_t>(pk[row * pitch + (c4 * 8 + 2 * i + 1) * kk + p]) << 16);
+    const int64_t j = static_cast<int64_t>(p) * Cc + c0;  // packed K slice start
+    const int64_t e = (((r >> 8) * KB + (j >> 5)) * 256 + (r & 255)) * 32 + c4 * 8;
+    *reinterpret_cast<uint4 *>(out + e) = make_uint4(h[0], h[1], h[2], h[3]);
   }
 }
 
@@ -759,10 +762,14 @@ hipError_t launch_merge(int dtype, const void *x, const RowDesc *desc, int64_t T
 
 hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *packed,
                        hipStream_t s) {
-  const int64_t nchunks = blocked_elems(R, K) / 8;
-  if (nchunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack, dim3(grid_for(nchunks, 256, 65536)), dim3(256), 0, s,
-                     static_cast<const uint16_t *>(w), R, K, C, k, static_cast<uint16_t *>(packed));
+  const int kk = k * k;
+  if (R <= 0 || K <= 0) return hipSuccess;
+  if (K % (32 * kk) != 0 || (kk > 1 && K != static_cast<int64_t>(C) * kk))
+    return hipErrorInvalidValue;  // 32-channel tiles of whole positions
+  const dim3 grid(static_cast<uint32_t>((R + 255) / 256 * 4), static_cast<uint32_t>(K / kk / 32));
+  const size_t lds = static_cast<size_t>(64) * (32 * kk + 8) * 2;
+  hipLaunchKernelGGL(k_pack, grid, dim3(256), lds, s, static_cast<const uint16_t *>(w), R, K, kk,
+                     static_cast<uint16_t *>(packed));
   return hipGetLastError();
 }
 
