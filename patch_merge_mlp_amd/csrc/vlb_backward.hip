@@ -236,8 +236,10 @@ __global__ __launch_bounds__(256) void k_bwd_weight_t(const uint16_t *w, int32_t
 // adds its pixels' dn * xh and dn into one row of part_g / part_b (waves in
 // order), so the parameter gradients come out the same on every run.  Nothing
 // is written when the placeholder scan failed.
+constexpr int kUmWaves = 4;  // waves per workgroup of the unmerge kernel
+
 template <bool LN, int NCH>
-__global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const uint16_t *x,
+__global__ __launch_bounds__(64 * kUmWaves) void k_bwd_unmerge(const uint16_t *dxm, const uint16_t *x,
                                                      PlanChunk c, int C, const uint16_t *gamma,
                                                      float eps, uint16_t *dx, float *part_g,
                                                      float *part_b, const int32_t *status) {
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
   const int64_t K1 = static_cast<int64_t>(C) * kk;
   const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
   const int64_t items = static_cast<int64_t>(t_end - t_begin) * kk;
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kUmWaves;
   const bool have = lane < c.n;
   const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
   const int32_t l_pix0 = have ? c.pix0[lane] : 0;
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
   for (int i = 0; i < NCH; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 4 + wid; it < items; it += nw) {
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kUmWaves + wid; it < items; it += nw) {
     const int m = t_begin + static_cast<int>(it / kk), p = static_cast<int>(it % kk);
     const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
     const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
@@ -283,7 +285,8 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
       continue;
     }
     const uint4 *xs = reinterpret_cast<const uint4 *>(x + pix * C);
-    float xf[NCH][8], gf[NCH][8];
+    const uint4 *g4 = reinterpret_cast<const uint4 *>(gamma);
+    float xf[NCH][8];
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -311,18 +314,18 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
-      const uint4 gq = q < nch ? reinterpret_cast<const uint4 *>(gamma)[q] : make_uint4(0, 0, 0, 0);
+      const uint4 gq = q < nch ? g4[q] : make_uint4(0, 0, 0, 0);
       const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
       const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float xh = (xf[i][j] - mean) * rstd, dn = bf2f(de[j]);
+        const float gv = bf2f(ge[j]) * dn;
         xf[i][j] = xh;
-        gf[i][j] = bf2f(ge[j]) * dn;
         ag[i][j] += dn * xh;
         ab[i][j] += dn;
-        sg += gf[i][j];
-        sgx += gf[i][j] * xh;
+        sg += gv;
+        sgx += gv * xh;
       }
     }
     const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
@@ -331,10 +334,14 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
       for (int i = 0; i < NCH; ++i) {
         const int q = lane + 64 * i;
         if (q < nch) {
+          const uint4 gq = g4[q];
+          const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+          const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
           uint4 o;
           uint16_t *oe = reinterpret_cast<uint16_t *>(&o);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) oe[j] = f2bf(rstd * (gf[i][j] - mg - xf[i][j] * mgx));
+          for (int j = 0; j < 8; ++j)
+            oe[j] = f2bf(rstd * (bf2f(ge[j]) * bf2f(de[j]) - mg - xf[i][j] * mgx));
           ddst[q] = o;
         }
       }
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
   if (!LN) return;
   // Workgroup sum of the waves' accumulators, wave 0 first, then one row each.
   extern __shared__ float red[];  // [2][C]
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kUmWaves; ++w) {
     if (wid == w) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(256) void k_bwd_unmerge(const uint16_t *dxm, const 
     }
     __syncthreads();
   }
-  for (int ch = threadIdx.x; ch < C; ch += 256) {
+  for (int ch = threadIdx.x; ch < C; ch += 64 * kUmWaves) {
     part_g[static_cast<int64_t>(blockIdx.x) * C + ch] = red[ch];
     part_b[static_cast<int64_t>(blockIdx.x) * C + ch] = red[C + ch];
   }
@@ -409,7 +416,7 @@ hipError_t unmerge_launch(const void *dxm, const void *x, const PlanChunk &c, in
                           const void *gamma, float eps, void *dx, float *part_g, float *part_b,
                           const int32_t *status, int grid, hipStream_t s) {
   const size_t lds = LN ? static_cast<size_t>(2) * C * sizeof(float) : 0;
-  hipLaunchKernelGGL((k_bwd_unmerge<LN, NCH>), dim3(grid), dim3(256), lds, s,
+  hipLaunchKernelGGL((k_bwd_unmerge<LN, NCH>), dim3(grid), dim3(64 * kUmWaves), lds, s,
                      static_cast<const uint16_t *>(dxm), static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), eps, static_cast<uint16_t *>(dx),
                      part_g, part_b, status);
@@ -432,7 +439,7 @@ hipError_t unmerge_dispatch(const void *dxm, const void *x, const PlanChunk &c, 
 }  // namespace
 
 int bwd_unmerge_grid(int64_t items) {
-  const int64_t g = (items + 15) / 16;  // about 4 items per wave
+  const int64_t g = (items + 4 * kUmWaves - 1) / (4 * kUmWaves);  // about 4 items per wave
   return static_cast<int>(g < 1 ? 1 : (g > kBwdUnmergeGrid ? kBwdUnmergeGrid : g));
 }
 

@@ -171,7 +171,7 @@ hipError_t launch_gemm_f32(bool gather, GemmArgs g, hipStream_t s);
 // T: token rows; Tk = T rounded up to 32 (the K extent of every contraction
 // over tokens); Op = out_dim rounded up to 32.  Tile-blocked operands as above.
 constexpr int kBwdMaxChannels = 2048;  // the LayerNorm backward keeps a pixel in registers
-constexpr int kBwdUnmergeGrid = 512;   // most workgroups of one unmerge launch
+constexpr int kBwdUnmergeGrid = 768;   // most workgroups of one unmerge launch (3 per CU)
 int bwd_unmerge_grid(int64_t items);   // workgroups for items (token row, position) pairs
 // dY rows gathered from G [S][O] at dst_row (zero where negative) -> dY [T][Op],
 // dY^T [O][Tk], part [Tk/32][O] (column sums per 32-row slice).
