@@ -99,6 +99,7 @@ class _Spec(ct.Structure):
         ("tile_w", ct.POINTER(ct.c_int32)),
         ("tile_h", ct.POINTER(ct.c_int32)),
         ("global_tail", ct.c_int32),
+        ("n_mid", ct.c_int32),
     ]
 
 
@@ -136,6 +137,9 @@ def _declare(L):
     L.orc_project_rows.restype = None
     L.orc_project_rows.argtypes = [ct.POINTER(_Spec), _D, _D, _D, _D, _D, _D, _D, _I64, i64, _D,
                                    ct.c_int32]
+    L.orc_project_rows_deep.restype = None
+    L.orc_project_rows_deep.argtypes = [ct.POINTER(_Spec), _D, _D, _D, _D, _D, _D, _D, _D, _D,
+                                        _I64, i64, _D, ct.c_int32]
     L.orc_assemble.restype = i64
     L.orc_assemble.argtypes = [ct.POINTER(_Spec), _I64, i64]
     L.orc_scatter.restype = ct.c_int32
@@ -183,6 +187,7 @@ class Spec:
     tiled: bool = False
     tiles: Sequence[tuple] = ()     # (tw, th) per image when tiled
     global_tail: bool = False
+    depth: int = 2                  # Linears in the projector (>= 2)
     _keep: list = field(default_factory=list, repr=False)
 
     def c(self) -> _Spec:
@@ -196,7 +201,7 @@ class Spec:
         return _Spec(len(self.grids), p32(gh), p32(gw), self.C, self.k, self.hidden,
                      self.out_dim, int(self.has_ln), float(self.ln_eps), int(self.act),
                      len(self.views_per_image), p32(vpi), int(self.tiled), p32(tw), p32(th),
-                     int(self.global_tail))
+                     int(self.global_tail), int(self.depth) - 2)
 
 
 def merged_side(g: int, k: int) -> int:
@@ -286,6 +291,30 @@ def project_rows(spec: Spec, x, gamma, beta, W1, b1, W2, b2, row_ids=None,
     xs = [_f64(a) for a in (x, gamma, beta, W1, b1, W2, b2)]
     lib().orc_project_rows(ct.byref(s), *[_dp(a) for a in xs], row_ids.ctypes.data_as(_I64),
                            len(row_ids), _dp(out), nthreads)
+    return out
+
+
+def project_rows_deep(spec: Spec, x, gamma, beta, W1, b1, W_mid, b_mid, W2, b2, row_ids=None,
+                      nthreads: int = 0) -> np.ndarray:
+    """project_rows for depth = spec.depth: W_mid [depth-2][hidden][hidden], b_mid
+    [depth-2][hidden] (sequences of per-layer arrays are stacked)."""
+    s = spec.c()
+    n_mid = spec.depth - 2
+    H = spec.hidden
+    wm = np.ascontiguousarray(np.stack([_f64(a) for a in W_mid]) if n_mid else np.zeros((1, H, H)))
+    bm = np.ascontiguousarray(np.stack([_f64(a) for a in b_mid]) if n_mid else np.zeros((1, H)))
+    assert wm.shape[1:] == (H, H) and (n_mid == 0 or len(wm) == n_mid)
+    if row_ids is None:
+        row_ids = np.arange(total_tokens(spec), dtype=np.int64)
+    row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    if nthreads <= 0:
+        nthreads = min(os.cpu_count() or 1, 16)
+    out = np.empty((len(row_ids), spec.out_dim), dtype=np.float64)
+    xs = [_f64(a) for a in (x, gamma, beta, W1, b1)]
+    ys = [_f64(a) for a in (W2, b2)]
+    lib().orc_project_rows_deep(ct.byref(s), *[_dp(a) for a in xs], _dp(wm), _dp(bm),
+                                *[_dp(a) for a in ys], row_ids.ctypes.data_as(_I64), len(row_ids),
+                                _dp(out), nthreads)
     return out
 
 

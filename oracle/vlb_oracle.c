@@ -229,27 +229,40 @@ void orc_merged_row(const orc_spec *s, const double *x, const double *gamma,
 
 typedef struct {
   const orc_spec *s;
-  const double *x, *gamma, *beta, *W1, *b1, *W2, *b2;
+  const double *x, *gamma, *beta, *W1, *b1, *W_mid, *b_mid, *W2, *b2;
   const int64_t *row_ids;
   double *out;
   int64_t i0, i1;
 } project_job;
 
+static void apply_act(int32_t act, double *h, int64_t n) {
+  if (act == ORC_GELU_ERF) orc_gelu_erf(h, n);
+  else if (act == ORC_GELU_TANH) orc_gelu_tanh(h, n);
+}
+
 static void project_range(const project_job *j) {
   const orc_spec *s = j->s;
   int32_t K1 = s->C * s->k * s->k;
+  const int32_t H = s->hidden;
   double *m = (double *)malloc(sizeof(double) * K1);
-  double *h = (double *)malloc(sizeof(double) * s->hidden);
+  double *h = (double *)malloc(sizeof(double) * H);
+  double *h2 = (double *)malloc(sizeof(double) * H);
   for (int64_t i = j->i0; i < j->i1; i++) {
     orc_merged_row(s, j->x, j->gamma, j->beta, j->row_ids[i], m);
-    /* [VL2 Projector 3]: Linear -> GELU -> Linear. */
-    orc_linear(m, 1, K1, j->W1, j->b1, s->hidden, h, 1);
-    if (s->act == ORC_GELU_ERF) orc_gelu_erf(h, s->hidden);
-    else if (s->act == ORC_GELU_TANH) orc_gelu_tanh(h, s->hidden);
-    orc_linear(h, 1, s->hidden, j->W2, j->b2, s->out_dim, j->out + i * s->out_dim, 1);
+    /* [VL2 Projector 3]: Linear -> GELU -> Linear, with (GELU -> Linear(hidden ->
+     * hidden)) pairs in the middle when the depth is above 2. */
+    orc_linear(m, 1, K1, j->W1, j->b1, H, h, 1);
+    for (int32_t q = 0; q < s->n_mid; q++) {
+      apply_act(s->act, h, H);
+      orc_linear(h, 1, H, j->W_mid + (int64_t)q * H * H, j->b_mid + (int64_t)q * H, H, h2, 1);
+      memcpy(h, h2, sizeof(double) * H);
+    }
+    apply_act(s->act, h, H);
+    orc_linear(h, 1, H, j->W2, j->b2, s->out_dim, j->out + i * s->out_dim, 1);
   }
   free(m);
   free(h);
+  free(h2);
 }
 
 static void *project_thread(void *arg) {
@@ -261,13 +274,24 @@ void orc_project_rows(const orc_spec *s, const double *x, const double *gamma,
                       const double *beta, const double *W1, const double *b1,
                       const double *W2, const double *b2, const int64_t *row_ids,
                       int64_t n_rows, double *out, int32_t nthreads) {
+  orc_spec s2 = *s;
+  s2.n_mid = 0;
+  orc_project_rows_deep(&s2, x, gamma, beta, W1, b1, NULL, NULL, W2, b2, row_ids, n_rows, out,
+                        nthreads);
+}
+
+void orc_project_rows_deep(const orc_spec *s, const double *x, const double *gamma,
+                           const double *beta, const double *W1, const double *b1,
+                           const double *W_mid, const double *b_mid, const double *W2,
+                           const double *b2, const int64_t *row_ids, int64_t n_rows, double *out,
+                           int32_t nthreads) {
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (nthreads > n_rows) nthreads = n_rows > 0 ? (int32_t)n_rows : 1;
   project_job jobs[256];
   pthread_t th[256];
   for (int32_t t = 0; t < nthreads; t++) {
-    project_job j = {s, x, gamma, beta, W1, b1, W2, b2, row_ids, out,
+    project_job j = {s, x, gamma, beta, W1, b1, W_mid, b_mid, W2, b2, row_ids, out,
                      n_rows * t / nthreads, n_rows * (t + 1) / nthreads};
     jobs[t] = j;
   }

@@ -50,6 +50,8 @@ typedef struct {
   int32_t tiled;                    /* 0: tokens in order; 1: 2D tile assembly */
   const int32_t *tile_w, *tile_h;   /* [n_images], tiled only */
   int32_t global_tail;              /* tiled only: 1 = [local, sep, global] */
+  int32_t n_mid;                    /* hidden -> hidden Linears between the two (depth - 2);
+                                       their weights go to orc_project_rows_deep */
 } orc_spec;
 
 /* ceil(g / k): side of the merged grid after high-end zero padding [VL2 Projector 1-2]. */
@@ -95,6 +97,16 @@ void orc_project_rows(const orc_spec *s, const double *x, const double *gamma,
                       const double *W2, const double *b2, const int64_t *row_ids,
                       int64_t n_rows, double *out, int32_t nthreads);
 
+/* The same for a projector of depth 2 + n_mid [VL2 Projector 3: with depth > 2
+ * further act + Linear(hidden -> hidden) pairs sit between the two]: merge ->
+ * Linear1 -> (act -> Linear_mid[i]) for each i -> act -> Linear2.  W_mid is
+ * [n_mid][hidden][hidden] (each stored (out, in)), b_mid [n_mid][hidden]. */
+void orc_project_rows_deep(const orc_spec *s, const double *x, const double *gamma,
+                           const double *beta, const double *W1, const double *b1,
+                           const double *W_mid, const double *b_mid, const double *W2,
+                           const double *b2, const int64_t *row_ids, int64_t n_rows, double *out,
+                           int32_t nthreads);
+
 /* Assembly order of all images [VL2 Tile-sequence assembly].  Writes the
  * source of every placeholder slot into src (token row >= 0, or
  * ORC_SRC_NEWLINE / ORC_SRC_SEPARATOR) and returns the slot count P.  src may
@@ -133,6 +145,8 @@ int32_t orc_embed_scatter(const int64_t *src, int64_t P, const double *rows,
 int32_t orc_scatter_backward(const int64_t *src, int64_t P, const uint8_t *mask, int64_t S,
                              int32_t D, const double *dseq, int64_t T, double *drows,
                              double *dnewline, double *dseparator);
+
+/* The backward functions below take a projector of depth 2 (s->n_mid == 0). */
 
 /* Gradients of the projector for the gradient dY [T][out_dim] of its output
  * rows: dx [n_pixels][C] (of the features), dW1 [hidden][C*k*k] (pages' feature

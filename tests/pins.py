@@ -238,6 +238,49 @@ def pin_project_rows_library(o):
             assert np.array_equal(got_sub, got[sub])
 
 
+def pin_project_rows_deep_library(o):
+    """Depth 3 and 4 ([VL2] Projector 3: extra activation + Linear(hidden -> hidden)
+    pairs in the middle) vs library routines; depth 2 equals project_rows."""
+    rng = np.random.default_rng(6)
+    C, k, H, O = 4, 2, 9, 6
+    grids = [(3, 3), (4, 2)]
+    x = rng.standard_normal((sum(a * b for a, b in grids), C))
+    g = rng.standard_normal(C)
+    bb = rng.standard_normal(C)
+    W1 = rng.standard_normal((H, C * k * k))
+    b1 = rng.standard_normal(H)
+    Wm = [rng.standard_normal((H, H)) / 3 for _ in range(2)]
+    bm = [rng.standard_normal(H) for _ in range(2)]
+    W2 = rng.standard_normal((O, H))
+    b2 = rng.standard_normal(O)
+    T = lambda a: torch.from_numpy(a)
+    for has_ln in (False, True):
+        for act in (o.GELU_ERF, o.GELU_TANH, o.ACT_NONE):
+            merged, p = [], 0
+            for gh, gw in grids:
+                v = T(x[p:p + gh * gw].reshape(gh, gw, C))
+                p += gh * gw
+                if has_ln:
+                    v = F.layer_norm(v, (C,), T(g), T(bb), eps=1e-6)
+                merged.append(_torch_merge(v.numpy(), k))
+            m = T(np.concatenate(merged))
+            actf = {o.GELU_ERF: F.gelu, o.GELU_TANH: lambda z: F.gelu(z, approximate="tanh"),
+                    o.ACT_NONE: lambda z: z}[act]
+            for depth in (2, 3, 4):
+                h = F.linear(m, T(W1), T(b1))
+                for q in range(depth - 2):
+                    h = F.linear(actf(h), T(Wm[q]), T(bm[q]))
+                want = F.linear(actf(h), T(W2), T(b2)).numpy()
+                spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[2],
+                              has_ln=has_ln, ln_eps=1e-6, act=act, depth=depth)
+                got = o.project_rows_deep(spec, x, g, bb, W1, b1, Wm[:depth - 2], bm[:depth - 2],
+                                          W2, b2, nthreads=2)
+                assert np.allclose(got, want, rtol=1e-12, atol=1e-12), (has_ln, act, depth)
+                if depth == 2:
+                    assert np.array_equal(got, o.project_rows(spec, x, g, bb, W1, b1, W2, b2,
+                                                              nthreads=2))
+
+
 # --- scatter -----------------------------------------------------------------
 
 def pin_scatter(o):
@@ -439,7 +482,7 @@ def pin_scatter_backward(o):
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
        pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
-       pin_embed_scatter, pin_project_backward_autograd, pin_project_backward_fd,
+       pin_embed_scatter, pin_project_rows_deep_library, pin_project_backward_autograd, pin_project_backward_fd,
        pin_backward_samples, pin_scatter_backward]
 
 

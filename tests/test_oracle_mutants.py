@@ -59,6 +59,10 @@ MUTANTS = {
         "      const double *from = src[j] >= 0                  ? rows + src[j] * D\n                           : src[j] == ORC_SRC_NEWLINE ? newline",
         "      const int64_t jj = P - 1 - j;\n      const double *from = src[jj] >= 0                 ? rows + src[jj] * D\n                           : src[jj] == ORC_SRC_NEWLINE ? newline"),
     "bf16 table widened as the low half": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
+    "middle Linear without its activation": ("    for (int32_t q = 0; q < s->n_mid; q++) {\n      apply_act(s->act, h, H);",
+                                             "    for (int32_t q = 0; q < s->n_mid; q++) {\n      (void)0;"),
+    "middle Linears in reverse order": ("orc_linear(h, 1, H, j->W_mid + (int64_t)q * H * H, j->b_mid + (int64_t)q * H, H, h2, 1);",
+                                        "orc_linear(h, 1, H, j->W_mid + (int64_t)(s->n_mid - 1 - q) * H * H, j->b_mid + (int64_t)(s->n_mid - 1 - q) * H, H, h2, 1);"),
     # backward
     "gelu slope without the z*phi term": (
         "return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * M_PI);",
