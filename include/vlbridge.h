@@ -79,7 +79,10 @@ typedef enum { VLB_LAYOUT_PLAIN = 0, VLB_LAYOUT_TILED_2D = 1 } vlb_layout;
 /* The projector: LN(C) (optional, per patch, biased variance, eps inside the
  * square root, affine) -> pad to a multiple of k -> k x k space-to-depth with
  * feature index c*k*k + dy*k + dx [VL2 Projector 1-2] -> Linear(C*k*k ->
- * hidden) -> act -> Linear(hidden -> out_dim) [VL2 Projector 3]. */
+ * hidden) -> act -> Linear(hidden -> out_dim) [VL2 Projector 3].  With depth
+ * d > 2 (the projector config's "depth", d Linears in all), d - 2 further
+ * (act -> Linear(hidden -> hidden)) pairs sit between the two [VL2 Projector
+ * 3]. */
 typedef struct {
   int32_t dtype;     /* vlb_dtype */
   int32_t C;         /* channels of the patch grid */
@@ -90,7 +93,9 @@ typedef struct {
   float ln_eps;      /* LayerNorm epsilon */
   int32_t act;       /* vlb_act */
   int32_t packed;    /* 1: weights.w1 / weights.w2 are the packed forms made by
-                        vlb_pack_weights (VLB_BF16 only) */
+                        vlb_pack_weights, and weights.w_mid[i] those made by
+                        vlb_pack_mid (VLB_BF16 only) */
+  int32_t depth;     /* Linears in the projector: 2..16; 0 is read as 2 */
 } vlb_projector;
 
 /* Weights in PyTorch Linear layout (out_features, in_features), as stored and
@@ -101,6 +106,9 @@ typedef struct {
   const void *b1;                 /* [hidden] */
   const void *w2;                 /* [out_dim][hidden]; or its packed form */
   const void *b2;                 /* [out_dim] */
+  const void *const *w_mid;       /* (host) [depth - 2] device pointers, each [hidden][hidden]
+                                     (or its packed form), in order; NULL when depth <= 2 */
+  const void *const *b_mid;       /* (host) [depth - 2] device pointers, each [hidden] */
 } vlb_weights;
 
 /* Batch description; all arrays are (host) memory read during the call only. */
@@ -135,8 +143,9 @@ size_t vlb_workspace_bytes(const vlb_projector *p, const vlb_batch *b, int64_t s
 
 /* ---- entry points (asynchronous on stream) ---------------------------- */
 
-/* Bytes of the packed form of W1 (which = 1) or W2 (which = 2); 0 on invalid
- * input or for VLB_F32 (which has no packed form). */
+/* Bytes of the packed form of W1 (which = 1), W2 (which = 2) or one middle
+ * weight (which = 3); 0 on invalid input or for VLB_F32 (which has no packed
+ * form). */
 size_t vlb_packed_bytes(const vlb_projector *p, int32_t which);
 
 /* One-time re-layout of the weights into the GEMMs' tile-blocked forms
@@ -150,6 +159,11 @@ size_t vlb_packed_bytes(const vlb_projector *p, int32_t which);
  * are written and must not overlap the inputs. */
 vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, const void *w2,
                             void *w1_packed, void *w2_packed, void *stream);
+
+/* The same re-layout for one middle weight [hidden][hidden] of a projector of
+ * depth > 2 (no reordering, like W2); w_packed holds vlb_packed_bytes(p, 3)
+ * bytes and must not overlap w. */
+vlb_status vlb_pack_mid(const vlb_projector *p, const void *w, void *w_packed, void *stream);
 
 /* LN (if enabled) -> pad -> space-to-depth, materialised: merged[T][C*k*k] in
  * the pages' feature order c*k*k + dy*k + dx [VL2 Projector 1-2], [VOIE
@@ -217,7 +231,7 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
 
 /* Bytes of the saved-activation buffer of a batch (the merged tokens and the
  * first Linear's pre-activation, in the GEMMs' tile-blocked layouts; the
- * contents are opaque); 0 on invalid input or for VLB_F32. */
+ * contents are opaque); 0 on invalid input, for VLB_F32 or for depth > 2. */
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b);
 
 /* Device workspace bytes of vlb_bridge_backward for this batch and sequence
@@ -226,8 +240,8 @@ size_t vlb_backward_workspace_bytes(const vlb_projector *p, const vlb_batch *b, 
 
 /* vlb_bridge_fused (same arguments, errors and sequence values), and the
  * activations the backward needs written to saved (vlb_saved_bytes bytes,
- * which must not overlap any other argument).  VLB_BF16 only (VLB_F32:
- * VLB_ERR_UNSUPPORTED). */
+ * which must not overlap any other argument).  VLB_BF16 and depth 2 only
+ * (otherwise VLB_ERR_UNSUPPORTED). */
 vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
                                   const void *features, const vlb_weights *w,
                                   const void *newline, const void *separator,
@@ -254,8 +268,8 @@ typedef struct {
  * ln_beta are not read).  Every token row's gradient is the dseq row of its
  * slot; the newline and separator gradients sum the rows of all their slots;
  * padded merge cells take no gradient.
- * Unsupported (VLB_ERR_UNSUPPORTED): VLB_F32, p->packed, has_ln with
- * C > 2048.  Device-detected placeholder-count mismatch: nothing is written
+ * Unsupported (VLB_ERR_UNSUPPORTED): VLB_F32, p->packed, depth > 2, has_ln
+ * with C > 2048.  Device-detected placeholder-count mismatch: nothing is written
  * and vlb_check(ws) returns VLB_ERR_MASK_COUNT.  With no token rows
  * (n_views = 0) every gradient is set to zero and the mask is not read.
  * Workspace: vlb_backward_workspace_bytes(p, b, seq_len). */
@@ -293,7 +307,8 @@ enum {
   VLB_K_BWD_DX = 14,      /* backward: dXm = dZ1 W1 */
   VLB_K_BWD_UNMERGE = 15, /* backward: unmerge + LayerNorm backward */
   VLB_K_BWD_SUM = 16,     /* backward: bias / LayerNorm / newline sums */
-  VLB_K_COUNT = 17
+  VLB_K_GEMM_MID = 17,    /* middle Linears (depth > 2) */
+  VLB_K_COUNT = 18
 };
 
 /* Launch timing.  mask bit kid (1 << VLB_K_*) enables timing of that kernel

@@ -32,9 +32,14 @@ struct Plan {
   std::vector<int32_t> img_row0;       // [n_images]
   std::vector<int32_t> img_view0;      // [n_images]
   // workspace carving (bytes)
-  size_t off_status = 0, off_dst = 0, off_desc = 0, off_xn = 0, off_h = 0, off_w1p = 0,
-         off_w2p = 0, off_slot = 0, total = 0;
+  size_t off_status = 0, off_dst = 0, off_desc = 0, off_xn = 0, off_h = 0, off_h2 = 0,
+         off_w1p = 0, off_w2p = 0, off_wmp = 0, off_slot = 0, total = 0;
 };
+
+constexpr int kMaxDepth = 16;
+
+// Linears in the projector (the depth field; 0 means the pages' default 2).
+int proj_depth(const vlb_projector *p) { return p->depth == 0 ? 2 : p->depth; }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -61,6 +66,8 @@ vlb_status check_projector(const vlb_projector *p) {
   if ((p->has_ln || p->dtype == VLB_BF16) && p->C > vlb::layernorm_max_channels(p->dtype))
     return VLB_ERR_UNSUPPORTED;
   if (p->packed && p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (p->depth < 0 || p->depth == 1) return VLB_ERR_SHAPE;
+  if (p->depth > kMaxDepth) return VLB_ERR_UNSUPPORTED;
   const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
   // 32-bit byte offsets address the weights (bf16: padded and tile-blocked)
   const int64_t es = p->dtype == VLB_BF16 ? 2 : 4;
@@ -149,16 +156,23 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
     off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, pl->K1)) * 2);
   else if (p->has_ln)
     off = align256(off + static_cast<size_t>(pl->npix) * p->C * pl->es);
-  pl->off_h = off;  // hidden activation: tile-blocked (bf16) or row-major (fp32)
-  if (p->dtype == VLB_BF16)
-    off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, p->hidden)) * pl->es);
-  else
-    off = align256(off + static_cast<size_t>(pl->T) * p->hidden * pl->es);
+  // hidden activation: tile-blocked (bf16) or row-major (fp32); a second
+  // buffer for the middle Linears (depth > 2) to alternate with
+  const size_t hbytes = p->dtype == VLB_BF16
+                            ? static_cast<size_t>(vlb::blocked_elems(pl->T, p->hidden)) * 2
+                            : static_cast<size_t>(pl->T) * p->hidden * pl->es;
+  pl->off_h = off;
+  off = align256(off + hbytes);
+  pl->off_h2 = off;
+  if (proj_depth(p) > 2) off = align256(off + hbytes);
   pl->off_w1p = off;  // weights packed per call when they are not pre-packed
   if (p->dtype == VLB_BF16 && !p->packed) {
     off = align256(off + static_cast<size_t>(vlb::blocked_elems(p->hidden, pl->K1)) * 2);
     pl->off_w2p = off;
     off = align256(off + static_cast<size_t>(vlb::blocked_elems(p->out_dim, p->hidden)) * 2);
+    pl->off_wmp = off;  // one middle weight at a time
+    if (proj_depth(p) > 2)
+      off = align256(off + static_cast<size_t>(vlb::blocked_elems(p->hidden, p->hidden)) * 2);
   }
   pl->off_slot = off;
   off = align256(off + static_cast<size_t>(seq_len) * 4);
@@ -196,7 +210,7 @@ struct BwdLayout {
 
 vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                       int64_t seq_len, BwdLayout *L) {
-  if (p->dtype != VLB_BF16 || p->packed) return VLB_ERR_UNSUPPORTED;
+  if (p->dtype != VLB_BF16 || p->packed || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && p->C > vlb::kBwdMaxChannels) return VLB_ERR_UNSUPPORTED;
   const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1;
   L->Tk = (T + 31) / 32 * 32;
@@ -392,10 +406,47 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
     g1.out2 = saved ? saved + sl.off_z1 : nullptr;
     VLB_LAUNCH(VLB_K_GEMM1, s,
                vlb::launch_gemm_bf16(saved ? vlb::kGemmBlockedSave : vlb::kGemmBlocked, g1, s));
+    // middle Linears: act(H W^T + b), blocked in and out, alternating buffers
+    for (int q = 0; q + 2 < proj_depth(p); ++q) {
+      const void *wm = w->w_mid[q];
+      if (!p->packed) {
+        VLB_LAUNCH(VLB_K_PACK, s,
+                   vlb::launch_pack(wm, p->hidden, p->hidden, p->C, 1, ws + pl.off_wmp, s));
+        wm = ws + pl.off_wmp;
+      }
+      vlb::GemmArgs gm{};
+      gm.A = g2.A;
+      gm.B = wm;
+      gm.bias = w->b_mid[q];
+      gm.out = g2.A == ws + pl.off_h ? ws + pl.off_h2 : ws + pl.off_h;
+      gm.M = static_cast<int32_t>(pl.T);
+      gm.N = p->hidden;
+      gm.K = p->hidden;
+      gm.ldo = p->hidden;
+      gm.act = p->act;
+      gm.a_bytes = g2.a_bytes;
+      gm.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->hidden, p->hidden) * 2);
+      VLB_LAUNCH(VLB_K_GEMM_MID, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, gm, s));
+      g2.A = gm.out;
+    }
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(vlb::kGemmRows, g2, s));
   } else {
     g1.B = w->w1;
     VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_f32(true, g1, s));
+    for (int q = 0; q + 2 < proj_depth(p); ++q) {
+      vlb::GemmArgs gm{};
+      gm.A = g2.A;
+      gm.B = w->w_mid[q];
+      gm.bias = w->b_mid[q];
+      gm.out = g2.A == ws + pl.off_h ? ws + pl.off_h2 : ws + pl.off_h;
+      gm.M = static_cast<int32_t>(pl.T);
+      gm.N = p->hidden;
+      gm.K = p->hidden;
+      gm.ldo = p->hidden;
+      gm.act = p->act;
+      VLB_LAUNCH(VLB_K_GEMM_MID, s, vlb::launch_gemm_f32(false, gm, s));
+      g2.A = gm.out;
+    }
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_f32(false, g2, s));
   }
   return VLB_OK;
@@ -455,6 +506,13 @@ vlb_status check_weights(const vlb_projector *p, const vlb_weights *w) {
   if (!aligned16(w->w1) || !aligned16(w->b1) || !aligned16(w->w2) || !aligned16(w->b2))
     return VLB_ERR_ALIGN;
   if (p->has_ln && (!aligned16(w->ln_gamma) || !aligned16(w->ln_beta))) return VLB_ERR_ALIGN;
+  if (proj_depth(p) > 2) {
+    if (!w->w_mid || !w->b_mid) return VLB_ERR_NULL;
+    for (int q = 0; q + 2 < proj_depth(p); ++q) {
+      if (!w->w_mid[q] || !w->b_mid[q]) return VLB_ERR_NULL;
+      if (!aligned16(w->w_mid[q]) || !aligned16(w->b_mid[q])) return VLB_ERR_ALIGN;
+    }
+  }
   return VLB_OK;
 }
 
@@ -507,7 +565,21 @@ size_t vlb_packed_bytes(const vlb_projector *p, int32_t which) {
   const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
   if (which == 1) return static_cast<size_t>(vlb::blocked_elems(p->hidden, K1)) * 2;
   if (which == 2) return static_cast<size_t>(vlb::blocked_elems(p->out_dim, p->hidden)) * 2;
+  if (which == 3) return static_cast<size_t>(vlb::blocked_elems(p->hidden, p->hidden)) * 2;
   return 0;
+}
+
+vlb_status vlb_pack_mid(const vlb_projector *p, const void *w, void *w_packed, void *stream) {
+  vlb_status st = check_projector(p);
+  if (st != VLB_OK) return st;
+  if (p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (!w || !w_packed) return VLB_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_packed)) return VLB_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(p->hidden) * p->hidden * 2;
+  if (overlaps(w_packed, vlb_packed_bytes(p, 3), w, n)) return VLB_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w, p->hidden, p->hidden, p->C, 1, w_packed, s));
+  return VLB_OK;
 }
 
 vlb_status vlb_pack_weights(const vlb_projector *p, const void *w1, const void *w2,
@@ -625,7 +697,7 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
   Plan pl;
-  if (make_plan(p, b, 0, &pl) != VLB_OK || p->dtype != VLB_BF16) return 0;
+  if (make_plan(p, b, 0, &pl) != VLB_OK || p->dtype != VLB_BF16 || proj_depth(p) > 2) return 0;
   return saved_layout(p, pl).total;
 }
 
@@ -645,7 +717,7 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
   Plan pl;
   vlb_status st = make_plan(p, b, seq_len, &pl);
   if (st != VLB_OK) return st;
-  if (p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (p->dtype != VLB_BF16 || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (pl.T == 0) return VLB_OK;
   if ((st = check_weights(p, w)) != VLB_OK) return st;
   if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;

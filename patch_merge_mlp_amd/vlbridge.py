@@ -24,10 +24,11 @@ F32, BF16 = 0, 1
 GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
 K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK, K_EMBED, \
-    K_BWD_PACK, K_BWD_DW2, K_BWD_DA1, K_BWD_DW1, K_BWD_DX, K_BWD_UNMERGE, K_BWD_SUM = range(17)
+    K_BWD_PACK, K_BWD_DW2, K_BWD_DA1, K_BWD_DW1, K_BWD_DX, K_BWD_UNMERGE, K_BWD_SUM, \
+    K_GEMM_MID = range(18)
 KERNEL_NAMES = ["plan", "scan", "place", "layernorm", "gemm1", "gemm2", "scatter", "merge", "pack",
                 "embed", "bwd_pack", "bwd_dw2", "bwd_da1", "bwd_dw1", "bwd_dx", "bwd_unmerge",
-                "bwd_sum"]
+                "bwd_sum", "gemm_mid"]
 
 
 class VlbError(RuntimeError):
@@ -39,12 +40,14 @@ class VlbError(RuntimeError):
 class vlb_projector(ct.Structure):
     _fields_ = [("dtype", ct.c_int32), ("C", ct.c_int32), ("k", ct.c_int32),
                 ("hidden", ct.c_int32), ("out_dim", ct.c_int32), ("has_ln", ct.c_int32),
-                ("ln_eps", ct.c_float), ("act", ct.c_int32), ("packed", ct.c_int32)]
+                ("ln_eps", ct.c_float), ("act", ct.c_int32), ("packed", ct.c_int32),
+                ("depth", ct.c_int32)]
 
 
 class vlb_weights(ct.Structure):
     _fields_ = [("ln_gamma", ct.c_void_p), ("ln_beta", ct.c_void_p), ("w1", ct.c_void_p),
-                ("b1", ct.c_void_p), ("w2", ct.c_void_p), ("b2", ct.c_void_p)]
+                ("b1", ct.c_void_p), ("w2", ct.c_void_p), ("b2", ct.c_void_p),
+                ("w_mid", ct.POINTER(ct.c_void_p)), ("b_mid", ct.POINTER(ct.c_void_p))]
 
 
 _P32 = ct.POINTER(ct.c_int32)
@@ -85,6 +88,7 @@ def lib():
             "vlb_workspace_bytes": (sz, [pp, pb, i64]),
             "vlb_packed_bytes": (sz, [pp, ct.c_int32]),
             "vlb_pack_weights": (st, [pp, vp, vp, vp, vp, vp]),
+            "vlb_pack_mid": (st, [pp, vp, vp, vp]),
             "vlb_merge_tokens": (st, [pp, pb, vp, vp, vp, vp, vp, sz, vp]),
             "vlb_merge_project": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, sz, vp]),
             "vlb_scatter_tokens": (st, [pp, pb, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
@@ -121,8 +125,14 @@ def _check(status: int, where: str):
 
 
 def projector(dtype: int, C: int, k: int, hidden: int, out_dim: int, has_ln: bool = False,
-              ln_eps: float = 1e-6, act: int = GELU_ERF, packed: bool = False) -> vlb_projector:
-    return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(packed))
+              ln_eps: float = 1e-6, act: int = GELU_ERF, packed: bool = False,
+              depth: int = 2) -> vlb_projector:
+    return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(packed),
+                         depth)
+
+
+def _depth(p: vlb_projector) -> int:
+    return 2 if p.depth == 0 else p.depth
 
 
 class Batch:
@@ -153,10 +163,19 @@ class Weights:
     b2: torch.Tensor
     ln_gamma: Optional[torch.Tensor] = None
     ln_beta: Optional[torch.Tensor] = None
+    w_mid: Sequence[torch.Tensor] = ()   # depth > 2: [hidden][hidden] each (or packed forms)
+    b_mid: Sequence[torch.Tensor] = ()   # [hidden] each
 
     def c(self) -> vlb_weights:
-        return vlb_weights(_ptr(self.ln_gamma), _ptr(self.ln_beta), _ptr(self.w1), _ptr(self.b1),
-                           _ptr(self.w2), _ptr(self.b2))
+        # the pointer arrays live on the returned struct (kept with it)
+        wm = (ct.c_void_p * max(len(self.w_mid), 1))(*[_ptr(t) for t in self.w_mid])
+        bm = (ct.c_void_p * max(len(self.b_mid), 1))(*[_ptr(t) for t in self.b_mid])
+        c = vlb_weights(_ptr(self.ln_gamma), _ptr(self.ln_beta), _ptr(self.w1), _ptr(self.b1),
+                        _ptr(self.w2), _ptr(self.b2),
+                        ct.cast(wm, ct.POINTER(ct.c_void_p)) if self.w_mid else None,
+                        ct.cast(bm, ct.POINTER(ct.c_void_p)) if self.b_mid else None)
+        c._keep = (wm, bm)
+        return c
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -247,6 +266,14 @@ def vlb_pack_weights(p: vlb_projector, w1: torch.Tensor, w2: torch.Tensor,
                                   _ptr(w2_packed), _stream(stream)), "vlb_pack_weights")
 
 
+def vlb_pack_mid(p: vlb_projector, w: torch.Tensor, w_packed: torch.Tensor, stream=None):
+    dt = _tdtype(p)
+    _need(w, p.hidden * p.hidden, dt, "w_mid")
+    _need(w_packed, vlb_packed_bytes(p, 3) // 2, dt, "w_mid_packed")
+    _check(lib().vlb_pack_mid(ct.byref(p), _ptr(w), _ptr(w_packed), _stream(stream)),
+           "vlb_pack_mid")
+
+
 def _check_weights(p, w: Weights):
     dt = _tdtype(p)
     if p.packed:
@@ -259,6 +286,13 @@ def _check_weights(p, w: Weights):
     _need(w.b2, p.out_dim, dt, "b2")
     _need(w.ln_gamma, p.C, dt, "ln_gamma")
     _need(w.ln_beta, p.C, dt, "ln_beta")
+    n_mid = _depth(p) - 2
+    if len(w.w_mid) != n_mid or len(w.b_mid) != n_mid:
+        raise ValueError(f"depth {_depth(p)} needs {n_mid} middle weights and biases")
+    for q in range(n_mid):
+        _need(w.w_mid[q], vlb_packed_bytes(p, 3) // 2 if p.packed else p.hidden * p.hidden, dt,
+              f"w_mid[{q}]")
+        _need(w.b_mid[q], p.hidden, dt, f"b_mid[{q}]")
 
 
 def vlb_merge_tokens(p, b: Batch, features, ln_gamma, ln_beta, merged, ws, stream=None):
@@ -463,7 +497,12 @@ class Bridge:
             w1p = torch.empty(vlb_packed_bytes(p, 1) // 2, dtype=w.w1.dtype, device=dev)
             w2p = torch.empty(vlb_packed_bytes(p, 2) // 2, dtype=w.w2.dtype, device=dev)
             vlb_pack_weights(p, w.w1, w.w2, w1p, w2p)
-            self.w = Weights(w1p, w.b1, w2p, w.b2, w.ln_gamma, w.ln_beta)
+            mids = []
+            for wm in w.w_mid:
+                t = torch.empty(vlb_packed_bytes(p, 3) // 2, dtype=wm.dtype, device=dev)
+                vlb_pack_mid(p, wm, t)
+                mids.append(t)
+            self.w = Weights(w1p, w.b1, w2p, w.b2, w.ln_gamma, w.ln_beta, mids, list(w.b_mid))
             p = vlb_projector.from_buffer_copy(p)
             p.packed = 1
         self.p = p

@@ -24,7 +24,9 @@ IMAGE_TOKEN_ID.  VOCAB and IMAGE_TOKEN_ID are the VL2 language config's
 vocab_size and image_token_index.
 
 The gradient of a training loss with respect to the sequence (seq_grad) comes
-from a third generator (seed 2000 + workload seed): N(0, 1) per element.
+from a third generator (seed 2000 + workload seed): N(0, 1) per element.  The middle
+Linears of a deeper projector (mid_weights) come from a fourth (seed 3000 +
+workload seed), with the Linear weight and bias distributions above.
 """
 from __future__ import annotations
 
@@ -173,6 +175,19 @@ def token_inputs(w: Workload, mask: torch.Tensor, vocab: int = VOCAB,
     ids = torch.where(ids >= image_token_id, ids + 1, ids)  # skip the image token
     ids = torch.where(mask.bool(), torch.full_like(ids, image_token_id), ids)
     return ids.to(torch.int32), table
+
+
+def mid_weights(w: Workload, depth: int):
+    """Middle Linears of a depth > 2 projector, [(W [hidden][hidden], b [hidden])] * (depth - 2)
+    in the workload dtype: W ~ N(0, 1/hidden), b ~ N(0, 0.01), from a generator seeded
+    3000 + the workload seed (the other draws are unchanged)."""
+    g = torch.Generator("cpu").manual_seed(3000 + w.seed)
+    out = []
+    for _ in range(depth - 2):
+        W = torch.randn((w.hidden, w.hidden), generator=g, dtype=torch.float32) * w.hidden ** -0.5
+        b = torch.randn((w.hidden,), generator=g, dtype=torch.float32) * 0.1
+        out.append((W.to(w.torch_dtype), b.to(w.torch_dtype)))
+    return out
 
 
 def seq_grad(w: Workload) -> torch.Tensor:

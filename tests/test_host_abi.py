@@ -245,6 +245,37 @@ def test_training_entry_points_validate():
                                  None) == v.ERR_NULL  # tiled: newline / separator gradients
 
 
+def test_depth_validation():
+    """depth: 0 reads as 2, 1 is a shape error, above 16 unsupported; depth > 2 needs
+    the middle weights, a larger workspace, and has no training entry points."""
+    L = v.lib()
+    b = v.Batch([(4, 4)], [1])
+    assert v.vlb_num_tokens(_proj(depth=0), b) == v.vlb_num_tokens(_proj(), b) == 4
+    assert v.lib().vlb_num_tokens(ct.byref(_proj(depth=1)), ct.byref(b.c)) == -v.ERR_SHAPE
+    assert v.lib().vlb_num_tokens(ct.byref(_proj(depth=17)), ct.byref(b.c)) == -v.ERR_UNSUPPORTED
+    assert v.vlb_num_tokens(_proj(depth=16), b) == 4
+    p3 = _proj(depth=3)
+    n2, n3 = v.vlb_workspace_bytes(_proj(), b, 32), v.vlb_workspace_bytes(p3, b, 32)
+    # a second hidden buffer (256 x 128 bf16) and one packed middle weight (256 x 128)
+    assert n3 - n2 == 2 * 256 * 128 * 2
+    assert v.vlb_saved_bytes(p3, b) == 0 and v.vlb_backward_workspace_bytes(p3, b, 32) == 0
+
+    def fused(w, proj=p3):
+        return L.vlb_bridge_fused(ct.byref(proj), ct.byref(b.c), FAKE, ct.byref(w), None, None,
+                                  FAKE, 32, FAKE + (1 << 26), FAKE + (2 << 26), n3, None)
+    arr = lambda *xs: ct.cast((ct.c_void_p * len(xs))(*xs), ct.POINTER(ct.c_void_p))
+    w_none = v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert fused(w_none) == v.ERR_NULL
+    assert fused(v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE, arr(None), arr(FAKE))) == v.ERR_NULL
+    assert fused(v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE, arr(FAKE + 2), arr(FAKE))) == v.ERR_ALIGN
+    assert L.vlb_bridge_fused_train(ct.byref(p3), ct.byref(b.c), FAKE, ct.byref(w_none), None,
+                                    None, FAKE, 32, FAKE, FAKE, 1 << 30, FAKE, 1 << 30,
+                                    None) == v.ERR_UNSUPPORTED
+    assert L.vlb_pack_mid(ct.byref(p3), FAKE, FAKE + 1024, None) == v.ERR_UNSUPPORTED  # overlap
+    assert L.vlb_pack_mid(ct.byref(_proj(dtype=v.F32)), FAKE, FAKE + (1 << 26), None) == v.ERR_UNSUPPORTED
+    assert L.vlb_pack_mid(ct.byref(p3), None, FAKE, None) == v.ERR_NULL
+
+
 def test_packed_bytes():
     """Tile-blocked weights: rows padded to a multiple of 256, K unchanged."""
     p = _proj()  # C=64, k=2 -> K1=256; hidden=128; out_dim=64
@@ -253,7 +284,8 @@ def test_packed_bytes():
     big = _proj(C=1152, hidden=4608, out_dim=4096)
     assert v.vlb_packed_bytes(big, 1) == 4608 * 4608 * 2
     assert v.vlb_packed_bytes(big, 2) == 4096 * 4608 * 2
-    assert v.vlb_packed_bytes(p, 0) == 0 and v.vlb_packed_bytes(p, 3) == 0
+    assert v.vlb_packed_bytes(p, 3) == 256 * 128 * 2  # a middle weight [hidden][hidden]
+    assert v.vlb_packed_bytes(p, 0) == 0 and v.vlb_packed_bytes(p, 4) == 0
     assert v.vlb_packed_bytes(_proj(dtype=v.F32), 1) == 0
     assert v.vlb_packed_bytes(_proj(k=9), 1) == 0
 
