@@ -479,11 +479,88 @@ def pin_scatter_backward(o):
         bad[pos] = val
         assert o.scatter_backward(src, bad, G, T)[0] == -1
 
+
+# --- processor (tile planning, placeholder expansion) -------------------------
+
+def pin_processor_page_examples(o, pr=None):
+    """[VL2] Processor step 7's worked counts through the planner: a 384 px tower
+    with patch 14 gives 421 slots for a 1x1 grid and 617 for a 2x1 grid; patch
+    16 gives 313 for 1x1.  Step 2 picks 1x1 for a square image (equal effective
+    area, less waste) and the 2x1 candidate for a 2:1 image."""
+    if pr is None:
+        from oracle import processor as pr
+    cands = [(384, 384), (768, 384), (384, 768)]
+    plan = pr.plan_request([(384, 384), (800, 400)], cands, 14, 2)
+    assert plan[0]["best"] == (384, 384) and plan[0]["tiles"] == (1, 1) and plan[0]["slots"] == 421
+    assert plan[1]["best"] == (768, 384) and plan[1]["tiles"] == (2, 1) and plan[1]["slots"] == 617
+    assert pr.plan_request([(640, 480)], [(384, 384)], 16, 2)[0]["slots"] == 313
+    assert pr.merged_side(384, 14, 2) == 14 and pr.merged_side(384, 16, 2) == 12
+
+
+def pin_processor_best_fit(o, pr=None):
+    """Step 2 on hand-worked cases: the largest effective area wins even when it
+    wastes more; the effective area is capped at the image's own area (no credit
+    for upscaling); equal effective areas go to the smaller waste; full ties to
+    the first candidate; floors are taken per side."""
+    if pr is None:
+        from oracle import processor as pr
+    # 1000 x 500: (768, 384) fits 768 x 384 = 294912 (waste 0); (1152, 768) fits
+    # 1152 x 576 = 663552 but is capped at 500000 (waste 384736); the larger area wins
+    assert pr.best_resolution(1000, 500, [(768, 384), (1152, 768)]) == (1152, 768)
+    # 300 x 200 upscales into both; both capped at 60000; (384, 384) wastes less
+    assert pr.best_resolution(300, 200, [(768, 768), (384, 384)]) == (384, 384)
+    # full tie: same size twice -> the first listed
+    assert pr.best_resolution(500, 500, [(384, 768), (768, 384)]) == (384, 768)
+    # 1000 x 300 into (384, 384): scale = min(0.384, 1.28) = 0.384;
+    # floor(1000 * 0.384) = 384, floor(300 * 0.384) = floor(115.2) = 115
+    sc = min(384 / 1000, 384 / 300)
+    assert math.floor(1000 * sc) * math.floor(300 * sc) == 384 * 115
+    assert pr.best_resolution(1000, 300, [(384, 384), (768, 384)]) == (768, 384)
+    # fp64 as the page computes it: 737 x 738 into (384, 768) scales by 384/737, and
+    # 737 * (384/737) evaluates to 383.99999999999994, so that side floors to 383:
+    # 383 * floor(384.52...) = 147072; into (384, 384) (scale 384/738) the sides are
+    # 383.47... and 384.00000000000006: 383 * 384 = 147072 as well.  Equal effective
+    # areas, and (384, 384) wastes 384 against 147840.  (Flooring the product
+    # instead would give 147656 against 147256 and pick (384, 768).)
+    assert 737 * (384 / 737) == 383.99999999999994 and 738 * (384 / 738) == 384.00000000000006
+    assert pr.best_resolution(737, 738, [(384, 768), (384, 384)]) == (384, 384)
+
+
+def pin_processor_crop_rule(o, pr=None):
+    """Step 1: at most two images are cropped; with three every image is 1x1."""
+    if pr is None:
+        from oracle import processor as pr
+    cands = [(384, 384), (768, 384), (1152, 384)]
+    two = pr.plan_request([(1200, 400), (1200, 400)], cands, 14, 2)
+    assert [p["tiles"] for p in two] == [(3, 1), (3, 1)]
+    three = pr.plan_request([(1200, 400)] * 3, cands, 14, 2)
+    assert [p["tiles"] for p in three] == [(1, 1)] * 3 and [p["slots"] for p in three] == [421] * 3
+
+
+def pin_processor_expand(o, pr=None):
+    """Step 7: BOS first, each image token replaced by its image's count, in order;
+    a prompt whose image tokens do not match the images is rejected."""
+    if pr is None:
+        from oracle import processor as pr
+    img, bos = 9, 1
+    got = pr.expand_prompt([5, img, 6, 7, img], img, [3, 2], bos)
+    assert got == [1, 5, 9, 9, 9, 6, 7, 9, 9]
+    for bad in ([5, 6], [img, img, img]):
+        try:
+            pr.expand_prompt(bad, img, [3, 2], bos)
+        except ValueError:
+            continue
+        raise AssertionError("mismatched image tokens accepted")
+
+
+PROCESSOR_PINS = [pin_processor_page_examples, pin_processor_best_fit, pin_processor_crop_rule,
+                  pin_processor_expand]
+
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
        pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
        pin_embed_scatter, pin_project_rows_deep_library, pin_project_backward_autograd, pin_project_backward_fd,
-       pin_backward_samples, pin_scatter_backward]
+       pin_backward_samples, pin_scatter_backward] + PROCESSOR_PINS
 
 
 def failing(o):

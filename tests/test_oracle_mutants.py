@@ -119,3 +119,47 @@ def test_mutant_is_caught(name, tmp_path):
     with o.use_library(so):
         bad = pins.failing(o)
     assert bad, f"no pin catches: {name}"
+
+
+# ---- the processor oracle (pure Python): planted mistakes, caught by its pins ----
+PR_SRC = open(os.path.join(os.path.dirname(o.__file__), "processor.py")).read()
+
+PR_MUTANTS = {
+    "scale as max": ("        scale = min(W / w0, H / h0)\n", "        scale = max(W / w0, H / h0)\n"),
+    "effective not capped": ("eff = min(math.floor(w0 * scale) * math.floor(h0 * scale), w0 * h0)",
+                             "eff = math.floor(w0 * scale) * math.floor(h0 * scale)"),
+    "floor of the product": ("eff = min(math.floor(w0 * scale) * math.floor(h0 * scale), w0 * h0)",
+                             "eff = min(math.floor(w0 * scale * h0 * scale), w0 * h0)"),
+    "waste tie-break reversed": ("(eff == best_eff and waste < best_waste)",
+                                 "(eff == best_eff and waste > best_waste)"),
+    "last of full ties": ("(eff == best_eff and waste < best_waste)",
+                          "(eff == best_eff and waste <= best_waste)"),
+    "crop for three images": ("MAX_CROP_IMAGES = 2", "MAX_CROP_IMAGES = 3"),
+    "tiles height first": ("tw, th = best[0] // image_size, best[1] // image_size",
+                           "th, tw = best[0] // image_size, best[1] // image_size"),
+    "merged side rounds down": ("return -(-(image_size // patch_size) // downsample)",
+                                "return (image_size // patch_size) // downsample"),
+    "no BOS": ("out, i = [bos_id], 0", "out, i = [], 0"),
+    "one image token per image": ("out.extend([image_token_id] * slots[i])",
+                                  "out.extend([image_token_id] * 1)"),
+    "counts in reverse": ("out.extend([image_token_id] * slots[i])",
+                          "out.extend([image_token_id] * slots[len(slots) - 1 - i])"),
+    "no prompt check": ("    if sum(1 for t in ids if t == image_token_id) != len(slots):\n        raise ValueError",
+                        "    if False:\n        raise ValueError"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PR_MUTANTS))
+def test_processor_mutant_is_caught(name):
+    import types
+    old, new = PR_MUTANTS[name]
+    assert PR_SRC.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    mod = types.ModuleType("processor_mutant")
+    exec(compile(PR_SRC.replace(old, new), "processor_mutant", "exec"), mod.__dict__)
+    bad = []
+    for p in pins.PROCESSOR_PINS:
+        try:
+            p(o, mod)
+        except Exception:  # noqa: BLE001 - any failure counts
+            bad.append(p.__name__)
+    assert bad, f"no pin catches: {name}"
