@@ -286,6 +286,48 @@ vlb_status vlb_check(void *ws, void *stream);
 
 const char *vlb_status_str(vlb_status s);
 
+/* ---- request planning (host only, no HIP call) -------------------------- */
+/*
+ * The processor steps that decide the batch [VL2 Processor]: step 1 (crop
+ * only when a request has at most 2 images), step 2 (best-fit candidate
+ * resolution), step 6 (the [tw, th] tile grid, width count first) and step 7
+ * (placeholder count and expansion of the prompt).  A planned image has
+ * 1 + tw*th views of floor(image_size / patch_size)^2 patches each.
+ */
+typedef struct {
+  const int32_t *candidates; /* (host) [n_candidates][2] (W, H) in pixels, whole multiples of
+                                image_size = candidates[0][0] */
+  int32_t n_candidates;
+  int32_t patch_size;        /* the tower's patch size */
+  int32_t downsample;        /* the projector's merge factor k */
+} vlb_processor;
+
+/* [VL2 Processor step 2] for an image of w0 x h0 pixels: per candidate,
+ * scale = min(W / w0, H / h0) and effective = min(floor(w0 * scale) *
+ * floor(h0 * scale), w0 * h0) in IEEE double; the largest effective area
+ * wins, then the smallest W * H - effective, then the first listed.  best:
+ * (host) int32[2] = (W, H).  Errors: VLB_ERR_NULL, VLB_ERR_SHAPE (sizes < 1,
+ * candidates not whole tiles, image_size < patch_size). */
+vlb_status vlb_select_resolution(const vlb_processor *pc, int32_t w0, int32_t h0, int32_t *best);
+
+/* [VL2 Processor steps 1, 2, 6, 7] for the n_images images of one request,
+ * sizes (host) [n_images][2] = (w0, h0): cropping only when n_images <= 2
+ * (otherwise every image is 1 x 1); tiles (host, out) [n_images][2] =
+ * [tw, th]; slots (host, out) [n_images] = h'(w'+1) + 1 + (th h')(tw w' + 1)
+ * with h' = w' = ceil(floor(image_size / patch_size) / downsample), the
+ * image's placeholder count (vlb_image_slots of the planned batch). */
+vlb_status vlb_plan_request(const vlb_processor *pc, int32_t n_images, const int32_t *sizes,
+                            int32_t *tiles, int64_t *slots);
+
+/* [VL2 Processor step 7] placeholder expansion of a prompt holding one
+ * image_token_id per image: out (host) = bos_id, then ids with its i-th
+ * image_token_id replaced by slots[i] copies of it.  Returns the length
+ * (with out == NULL: the length only), or -VLB_ERR_SHAPE when the prompt's
+ * image tokens differ from n_images or the length exceeds cap, -VLB_ERR_NULL. */
+int64_t vlb_expand_prompt(const int32_t *ids, int64_t n_ids, int32_t image_token_id,
+                          int32_t bos_id, const int64_t *slots, int32_t n_images, int32_t *out,
+                          int64_t cap);
+
 /* ---- optional per-kernel timing ---------------------------------------- */
 
 /* Kernel ids for the timing records. */

@@ -66,6 +66,11 @@ class vlb_batch(ct.Structure):
                 ("tile_w", _P32), ("tile_h", _P32), ("global_view_tail", ct.c_int32)]
 
 
+class vlb_processor(ct.Structure):
+    _fields_ = [("candidates", _P32), ("n_candidates", ct.c_int32), ("patch_size", ct.c_int32),
+                ("downsample", ct.c_int32)]
+
+
 _lib = None
 
 
@@ -102,6 +107,12 @@ def lib():
                                             vp, vp, sz, vp, sz, vp]),
             "vlb_bridge_backward": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, i64, vp, vp, sz,
                                          ct.POINTER(vlb_grads), vp, sz, vp]),
+            "vlb_select_resolution": (st, [ct.POINTER(vlb_processor), ct.c_int32, ct.c_int32,
+                                           _P32]),
+            "vlb_plan_request": (st, [ct.POINTER(vlb_processor), ct.c_int32, _P32, _P32,
+                                      ct.POINTER(ct.c_int64)]),
+            "vlb_expand_prompt": (i64, [_P32, i64, ct.c_int32, ct.c_int32, ct.POINTER(ct.c_int64),
+                                        ct.c_int32, _P32, i64]),
             "vlb_check": (st, [vp, vp]),
             "vlb_status_str": (ct.c_char_p, [st]),
             "vlb_prof_enable": (st, [ct.c_int32]),
@@ -462,6 +473,69 @@ def vlb_bridge_backward(p, b: Batch, features, w: Weights, mask, dseq, saved, g:
                                      _ptr(mask), dseq.shape[0], _ptr(dseq), _ptr(saved),
                                      saved.numel(), ct.byref(gc), _ptr(ws), ws.numel(),
                                      _stream(stream)), "vlb_bridge_backward")
+
+
+# ---- request planning (host) ---------------------------------------------------
+
+class Processor:
+    """Candidate resolutions [(W, H)], patch size and merge factor of a tiled
+    (VL2-style) processor; keeps the C arrays alive."""
+
+    def __init__(self, candidates: Sequence[tuple], patch_size: int, downsample: int):
+        self.candidates = [tuple(c) for c in candidates]
+        flat = [x for c in self.candidates for x in c]
+        self._arr = (ct.c_int32 * max(len(flat), 1))(*flat)
+        self.c = vlb_processor(self._arr, len(self.candidates), patch_size, downsample)
+        self.image_size = self.candidates[0][0] if self.candidates else 0
+        self.patch_size = patch_size
+
+    @property
+    def grid(self) -> int:
+        """Patches per side of every view."""
+        return self.image_size // self.patch_size
+
+
+def vlb_select_resolution(pc: Processor, w0: int, h0: int) -> tuple:
+    best = (ct.c_int32 * 2)()
+    _check(lib().vlb_select_resolution(ct.byref(pc.c), w0, h0, best), "vlb_select_resolution")
+    return int(best[0]), int(best[1])
+
+
+def vlb_plan_request(pc: Processor, sizes: Sequence[tuple]):
+    """[(tw, th)] and [slots] for the images (w0, h0) of one request."""
+    n = len(sizes)
+    flat = (ct.c_int32 * max(2 * n, 1))(*[x for s_ in sizes for x in s_])
+    tiles = (ct.c_int32 * max(2 * n, 1))()
+    slots = (ct.c_int64 * max(n, 1))()
+    _check(lib().vlb_plan_request(ct.byref(pc.c), n, flat, tiles, slots), "vlb_plan_request")
+    return [(int(tiles[2 * i]), int(tiles[2 * i + 1])) for i in range(n)], \
+        [int(slots[i]) for i in range(n)]
+
+
+def vlb_expand_prompt(ids: Sequence[int], image_token_id: int, bos_id: int,
+                      slots: Sequence[int]) -> list:
+    n = len(ids)
+    a = (ct.c_int32 * max(n, 1))(*ids)
+    sl = (ct.c_int64 * max(len(slots), 1))(*slots)
+    m = int(lib().vlb_expand_prompt(a, n, image_token_id, bos_id, sl, len(slots), None, 0))
+    if m < 0:
+        raise VlbError(-m, "vlb_expand_prompt")
+    out = (ct.c_int32 * m)()
+    got = int(lib().vlb_expand_prompt(a, n, image_token_id, bos_id, sl, len(slots), out, m))
+    if got != m:
+        raise VlbError(-got if got < 0 else ERR_SHAPE, "vlb_expand_prompt")
+    return list(out)
+
+
+def batch_for_request(pc: Processor, tiles: Sequence[tuple], global_view_tail: bool = False) -> Batch:
+    """The 2D-tiled batch of planned images: image i has 1 + tw*th views of
+    grid x grid patches, the global view first."""
+    g = pc.grid
+    grids, vpi = [], []
+    for tw, th in tiles:
+        vpi.append(1 + tw * th)
+        grids += [(g, g)] * (1 + tw * th)
+    return Batch(grids, vpi, LAYOUT_TILED_2D, list(tiles), global_view_tail)
 
 
 def vlb_check(ws, stream=None) -> int:

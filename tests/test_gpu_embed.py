@@ -120,3 +120,36 @@ def test_embed_text_only():
     st, ref = o.embed_scatter(np.zeros(0, np.int64), np.zeros((0, w.out_dim)), None, None, ids,
                               IMG, table, w.out_dim)
     assert st == 0 and np.array_equal(seq.cpu().double().numpy(), ref)
+
+
+def test_planned_request_end_to_end():
+    """Processor planning -> prompt expansion -> tiled batch -> the embedded
+    sequence, against the oracle's planner and embedded sequence."""
+    from oracle import processor as pr
+    cands = [(56, 56), (112, 56), (56, 112), (112, 112), (168, 56)]
+    pc = v.Processor(cands, 14, 2)
+    sizes = [(130, 47), (60, 61)]
+    tiles, slots = v.vlb_plan_request(pc, sizes)
+    assert [p["tiles"] for p in pr.plan_request(sizes, cands, 14, 2)] == tiles
+    b = v.batch_for_request(pc, tiles)
+    grids, vpi = b.grids, b.views_per_image
+    w = wl.Workload("planned-2img", 31, "bf16", C=64, k=2, hidden=128, out_dim=64,
+                    seq_len=sum(slots) + 40, grids=grids, views_per_image=vpi, tiled=True,
+                    tiles=tiles)
+    t = common.draw(w)
+    _, table = wl.token_inputs(w, t["mask"])
+    g = torch.Generator().manual_seed(5)
+    text = torch.randint(0, IMG, (39,), generator=g).tolist()
+    prompt = text[:10] + [IMG] + text[10:25] + [IMG] + text[25:]
+    ids = torch.tensor(v.vlb_expand_prompt(prompt, IMG, 1, slots), dtype=torch.int32)
+    assert ids.tolist() == pr.expand_prompt(prompt, IMG, slots, 1) and len(ids) == w.seq_len
+    st, out = run_embed(w, t, ids, table)
+    assert st == v.OK
+    rows = o.project_rows(common.oracle_spec(w), t["features"], t["ln_gamma"], t["ln_beta"],
+                          t["w1"], t["b1"], t["w2"], t["b2"])
+    st_ref, ref = oracle_embed(w, t, ids, table, rows)
+    assert st_ref == 0
+    text_pos = (ids != IMG).numpy()
+    got = out.double().numpy()
+    assert np.array_equal(got[text_pos], ref[text_pos])
+    assert common.rel_frob(got[~text_pos], ref[~text_pos]) <= TOL["bf16"]
