@@ -46,6 +46,8 @@ def parse():
                     help="target duration of the CPU-baseline sample")
     ap.add_argument("--no-hbm-kernels", action="store_true",
                     help="skip timing the standalone merge and scatter entry points")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip sampling the GFX clock under load (amd-smi, after the timed region)")
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing the training step (forward + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -114,6 +116,16 @@ def main():
     weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
                         d(t["ln_beta"]))
     br = v.Bridge(p, weights)            # packs W1 and W2 once (weight preprocessing, untimed)
+    pack_us = None
+    if br.p.packed:  # the one-time packing, timed again once the code is loaded
+        w1p, w2p = torch.empty_like(br.w.w1), torch.empty_like(br.w.w2)
+        v.vlb_prof_enable(1 << v.K_PACK)
+        v.vlb_pack_weights(p, weights.w1, weights.w2, w1p, w2p)
+        torch.cuda.synchronize()
+        v.vlb_prof_enable(False)
+        n_pack, ms_pack = v.vlb_prof_read(v.K_PACK)
+        pack_us = round(1000.0 * ms_pack, 2) if n_pack else None  # both weights
+        del w1p, w2p
     feats, mask = d(t["features"]), d(t["mask"])
     nl, sep = d(t["newline"]), d(t["separator"])
     seq = d(t["seq"])
@@ -194,6 +206,11 @@ def main():
         "kernels": kernels,
     }
 
+    out["weight_pack_us"] = pack_us
+
+    if not args.no_sclk:
+        out["sclk"] = sclk_under_load(step, torch, sec)
+
     if not args.no_hbm_kernels:
         out["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
 
@@ -240,6 +257,42 @@ def hbm_kernels(v, torch, w, p, b, t, d, T, K1, steps):
         res[name] = {"mean_us": round(sec * 1e6, 2), "bytes": nbytes[name], "GB/s": round(gbs, 1),
                      "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
     return res
+
+
+def sclk_under_load(step, torch, sec_per_step, seconds=2.5):
+    """GFX clock of every XCD sampled with amd-smi (a child process) while the
+    step runs back to back for a few seconds after the timed region; the
+    samples' median and range in MHz, or None when amd-smi is unavailable."""
+    import re
+    import subprocess
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True,
+                                   timeout=10)
+            except Exception:  # noqa: BLE001 - no tool, no sample
+                return
+            samples.extend(int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+) MHz",
+                                                      r.stdout))
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    n = max(1, int(seconds / max(sec_per_step, 1e-6)))
+    for i in range(n):
+        step()
+        if i % 200 == 199:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    samples.sort()
+    q = lambda f: samples[min(len(samples) - 1, int(f * len(samples)))]
+    return {"median_mhz": q(0.5), "p10_mhz": q(0.1), "p90_mhz": q(0.9), "samples": len(samples),
+            "how": "amd-smi metric -c, per-XCD GFX clocks, sampled during an untimed burst of steps"}
 
 
 def train_step(v, torch, wl, w, p, b, t, d, T, K1, steps):
