@@ -224,19 +224,26 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   const bool ok = status[kStatusWord] == 0;
   const int end = c.slot0[c.n];
+  // Lane i keeps image i's table entry (vector loads); a slot's image is the
+  // number of images starting at or before it, less one, found with one
+  // ballot, and its entry is taken from that lane with shuffles.  The table is
+  // never indexed with a wave-uniform image number: a scalar load from such a
+  // computed kernel-argument address ignores the low address bits, which the
+  // 16-bit entries do not keep dword-aligned.
+  const bool have = lane < c.n;
+  const int32_t l_slot0 = have ? c.slot0[lane] : INT32_MAX;
+  const int32_t l_row0 = have ? c.row0[lane] : 0, l_nl0 = have ? c.nl0[lane] : 0;
+  const int32_t l_hp = have ? c.hp[lane] : 1, l_wp = have ? c.wp[lane] : 1;
+  const int32_t l_tw = have ? c.tw[lane] : 1, l_th = have ? c.th[lane] : 1;
   for (int64_t jj = c.slot0[0] + wave; jj < end; jj += nwaves) {
     const int j = static_cast<int>(jj);
-    int lo = 0, hi = c.n - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (c.slot0[mid] <= j) lo = mid;
-      else hi = mid - 1;
-    }
-    const int im = lo;
-    const int hp = c.hp[im], wp = c.wp[im], tw = c.tw[im], th = c.th[im];
+    const int im = __popcll(__ballot(l_slot0 <= j)) - 1;
+    const int hp = __shfl(l_hp, im), wp = __shfl(l_wp, im), tw = __shfl(l_tw, im),
+              th = __shfl(l_th, im);
+    const int row0 = __shfl(l_row0, im), nl0 = __shfl(l_nl0, im);
     const int G = hp * (wp + 1);             // global block
     const int L = th * hp * (tw * wp + 1);   // local mosaic block
-    int q = j - c.slot0[im];
+    int q = j - __shfl(l_slot0, im);
     int row = -1;                            // token row, or -1 newline, -2 separator
     int nl_ord = 0;                          // newline ordinal inside the image
     bool global;
@@ -252,7 +259,7 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
     if (row != -2) {
       if (global) {
         const int R = q / (wp + 1), X = q % (wp + 1);
-        row = (X == wp) ? -1 : c.row0[im] + R * wp + X;
+        row = (X == wp) ? -1 : row0 + R * wp + X;
         nl_ord = (c.tail ? th * hp : 0) + R;
       } else {
         const int W = tw * wp + 1;
@@ -262,7 +269,7 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
           row = -1;
         } else {
           const int tile = (R / hp) * tw + X / wp;
-          row = c.row0[im] + (1 + tile) * hp * wp + (R % hp) * wp + (X % wp);
+          row = row0 + (1 + tile) * hp * wp + (R % hp) * wp + (X % wp);
         }
       }
     }
@@ -271,7 +278,7 @@ __global__ void k_place_tiled(PlaceChunk c, const int32_t *slot_pos, const int32
     } else if (REC) {
       if (lane == 0) {
         const int32_t pos = ok ? slot_pos[j] : -1;
-        if (row == -1) nl_pos[c.nl0[im] + nl_ord] = pos;
+        if (row == -1) nl_pos[nl0 + nl_ord] = pos;
         else sep_pos[c.img0 + im] = pos;
       }
     } else if (ok) {
