@@ -358,6 +358,9 @@ enum {
  * runs on.  A nonzero mask clears earlier records; 0 stops recording; -1
  * times every kernel. */
 vlb_status vlb_prof_enable(int32_t mask);
+/* Sets the mask like vlb_prof_enable but keeps the records taken so far, so
+ * that only some launches of a run are bracketed (0 pauses recording). */
+vlb_status vlb_prof_resume(int32_t mask);
 /* Waits for the recorded events and returns, for kernel id kid, the number of
  * launches and their summed duration in milliseconds. */
 vlb_status vlb_prof_read(int32_t kid, int64_t *launches, double *total_ms);

@@ -989,6 +989,12 @@ vlb_status vlb_prof_enable(int32_t mask) {
   return VLB_OK;
 }
 
+vlb_status vlb_prof_resume(int32_t mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_mask = static_cast<uint32_t>(mask);
+  return VLB_OK;
+}
+
 vlb_status vlb_prof_read(int32_t kid, int64_t *launches, double *total_ms) {
   if (!launches || !total_ms) return VLB_ERR_NULL;
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -116,6 +116,7 @@ def lib():
             "vlb_check": (st, [vp, vp]),
             "vlb_status_str": (ct.c_char_p, [st]),
             "vlb_prof_enable": (st, [ct.c_int32]),
+            "vlb_prof_resume": (st, [ct.c_int32]),
             "vlb_prof_read": (st, [ct.c_int32, ct.POINTER(ct.c_int64), ct.POINTER(ct.c_double)]),
         }
         for name, (res, args) in sigs.items():
@@ -551,6 +552,11 @@ def vlb_prof_enable(mask):
     elif mask is False:
         mask = 0
     _check(lib().vlb_prof_enable(int(mask)), "vlb_prof_enable")
+
+
+def vlb_prof_resume(mask: int):
+    """Like vlb_prof_enable(mask) but keeps the records taken so far."""
+    _check(lib().vlb_prof_resume(int(mask)), "vlb_prof_resume")
 
 
 def vlb_prof_read(kid: int):
