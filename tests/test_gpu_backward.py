@@ -6,7 +6,7 @@ the fp64 oracle's gradients.
     the gradients that pass through bf16-rounded activations (dW1, db1, dW2,
     dgamma, dbeta, the features), <= 1e-5 for the plain sums of bf16 gradient
     rows (db2, newline, separator);
-  * workloads 1 and 3 at full size, in the benchmark's launch configuration:
+  * the four bf16 workloads at full size, in the benchmark's launch configuration:
     db2, newline and separator gradients whole; sampled hidden units (row of
     dW1, db1 entry, column of dW2) and sampled pixels (feature gradient);
   * the training forward writes the same sequence as vlb_bridge_fused, and two
@@ -126,7 +126,7 @@ def test_small_backward_activations(act):
         assert e <= TOL_ACT, (act, name, e)
 
 
-@pytest.mark.parametrize("i", [1, 3])
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
 def test_full_backward_sampled(i):
     w, t = full(i)
     dseq = wl.seq_grad(w)
