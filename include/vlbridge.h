@@ -218,7 +218,7 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
                             int64_t vocab, int64_t seq_len, void *seq, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* ---- training the projector (VLB_BF16) -------------------------------- */
+/* ---- training the projector ------------------------------------------- */
 /*
  * The projector is the trained part of the bridge: [V4V header] trains only
  * its parameters (tower and text model frozen), and [VOIE "Pendant le
@@ -230,8 +230,8 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
  */
 
 /* Bytes of the saved-activation buffer of a batch (the merged tokens and the
- * first Linear's pre-activation, in the GEMMs' tile-blocked layouts; the
- * contents are opaque); 0 on invalid input, for VLB_F32 or for depth > 2. */
+ * first Linear's pre-activation: tile-blocked for VLB_BF16, row-major for
+ * VLB_F32; the contents are opaque); 0 on invalid input or for depth > 2. */
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b);
 
 /* Device workspace bytes of vlb_bridge_backward for this batch and sequence
@@ -240,8 +240,8 @@ size_t vlb_backward_workspace_bytes(const vlb_projector *p, const vlb_batch *b, 
 
 /* vlb_bridge_fused (same arguments, errors and sequence values), and the
  * activations the backward needs written to saved (vlb_saved_bytes bytes,
- * which must not overlap any other argument).  VLB_BF16 and depth 2 only
- * (otherwise VLB_ERR_UNSUPPORTED). */
+ * which must not overlap any other argument).  Depth 2 only (otherwise
+ * VLB_ERR_UNSUPPORTED). */
 vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
                                   const void *features, const vlb_weights *w,
                                   const void *newline, const void *separator,
@@ -268,8 +268,8 @@ typedef struct {
  * ln_beta are not read).  Every token row's gradient is the dseq row of its
  * slot; the newline and separator gradients sum the rows of all their slots;
  * padded merge cells take no gradient.
- * Unsupported (VLB_ERR_UNSUPPORTED): VLB_F32, p->packed, depth > 2, has_ln
- * with C > 2048.  Device-detected placeholder-count mismatch: nothing is written
+ * Unsupported (VLB_ERR_UNSUPPORTED): p->packed, depth > 2, has_ln with
+ * C > 2048.  Device-detected placeholder-count mismatch: nothing is written
  * and vlb_check(ws) returns VLB_ERR_MASK_COUNT.  With no token rows
  * (n_views = 0) every gradient is set to zero and the mask is not read.
  * Workspace: vlb_backward_workspace_bytes(p, b, seq_len). */

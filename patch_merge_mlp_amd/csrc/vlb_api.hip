@@ -180,8 +180,9 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   return VLB_OK;
 }
 
-// Saved activations of a training forward (bf16): the merged tokens (Linear1's
-// operand) and Linear1's pre-activation, both tile-blocked.
+// Saved activations of a training forward: the merged tokens (Linear1's
+// operand) and Linear1's pre-activation, both tile-blocked (bf16) or
+// row-major (fp32).
 struct SavedLayout {
   size_t off_xm = 0, off_z1 = 0, total = 0;
 };
@@ -189,6 +190,14 @@ struct SavedLayout {
 SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
   SavedLayout L;
   size_t off = 0;
+  if (p->dtype == VLB_F32) {  // row-major merged rows (the pages' order) and Z1
+    L.off_xm = off;
+    off = align256(off + static_cast<size_t>(pl.T) * pl.K1 * 4);
+    L.off_z1 = off;
+    off = align256(off + static_cast<size_t>(pl.T) * p->hidden * 4);
+    L.total = off;
+    return L;
+  }
   L.off_xm = off;
   off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, pl.K1)) * 2);
   L.off_z1 = off;
@@ -210,7 +219,7 @@ struct BwdLayout {
 
 vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                       int64_t seq_len, BwdLayout *L) {
-  if (p->dtype != VLB_BF16 || p->packed || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
+  if (p->packed || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && p->C > vlb::kBwdMaxChannels) return VLB_ERR_UNSUPPORTED;
   const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1;
   L->Tk = (T + 31) / 32 * 32;
@@ -221,13 +230,14 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
       const int v = pl.img_view0[im];
       L->NL += ceil_div(b->grid_h[v], p->k) * (1 + b->tile_h[im]);
     }
-  // 32-bit byte extents of the GEMM operands
+  // 32-bit byte extents of the bf16 GEMM operands
   const int64_t Tk = L->Tk, Op = L->Op;
-  for (const int64_t e : {vlb::blocked_elems(T, Op), vlb::blocked_elems(O, Tk),
-                          vlb::blocked_elems(H, Tk), vlb::blocked_elems(H, Op),
-                          vlb::blocked_elems(K1, Tk), vlb::blocked_elems(K1, H),
-                          vlb::blocked_elems(T, H)})
-    if (e * 2 > kI32Max) return VLB_ERR_SHAPE;
+  if (p->dtype == VLB_BF16)
+    for (const int64_t e : {vlb::blocked_elems(T, Op), vlb::blocked_elems(O, Tk),
+                            vlb::blocked_elems(H, Tk), vlb::blocked_elems(H, Op),
+                            vlb::blocked_elems(K1, Tk), vlb::blocked_elems(K1, H),
+                            vlb::blocked_elems(T, H)})
+      if (e * 2 > kI32Max) return VLB_ERR_SHAPE;
   L->ln_grid.clear();
   L->ln_rows = 0;
   for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews) {
@@ -248,6 +258,17 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
   L->off_slot = take(off, static_cast<size_t>(seq_len) * 4);
   L->off_nl = take(off, static_cast<size_t>(L->NL) * 4);
   L->off_sep = take(off, static_cast<size_t>(b->n_images) * 4);
+  if (p->dtype == VLB_F32) {  // row-major: dY [T][O], act(Z1) [T][H], dA1 / dZ1 [T][H], dXm [T][K1]
+    L->off_dy = take(off, static_cast<size_t>(T) * O * 4);
+    L->off_a1t = take(off, static_cast<size_t>(T) * H * 4);
+    L->off_da1 = take(off, static_cast<size_t>(T) * H * 4);
+    L->off_dxm = take(off, static_cast<size_t>(T) * K1 * 4);
+    L->off_pln = take(off, static_cast<size_t>(2 * L->ln_rows) * p->C * 4);
+    L->off_pnl = take(off, static_cast<size_t>(ceil_div(L->NL, 64)) * O * 4);
+    L->off_psep = take(off, static_cast<size_t>(ceil_div(b->n_images, 64)) * O * 4);
+    L->total = off;
+    return VLB_OK;
+  }
   L->off_dy = take(off, static_cast<size_t>(vlb::blocked_elems(T, Op)) * 2);
   L->off_dyt = take(off, static_cast<size_t>(vlb::blocked_elems(O, Tk)) * 2);
   L->off_a1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
@@ -357,6 +378,9 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
                                        w->ln_beta, p->ln_eps, xn, s));
       x = xn;
     }
+    if (saved)  // the training forward keeps the merged rows (Linear1 then reads them)
+      VLB_LAUNCH(VLB_K_MERGE, s,
+                 vlb::launch_merge(p->dtype, x, desc, pl.T, p->C, p->k, saved + sl.off_xm, s));
   }
   void *hbuf = ws + pl.off_h;
   vlb::GemmArgs g1{};
@@ -432,7 +456,11 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(vlb::kGemmRows, g2, s));
   } else {
     g1.B = w->w1;
-    VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_f32(true, g1, s));
+    if (saved) {  // from the kept merged rows, keeping Z1 as well
+      g1.A = saved + sl.off_xm;
+      g1.out2 = saved + sl.off_z1;
+    }
+    VLB_LAUNCH(VLB_K_GEMM1, s, vlb::launch_gemm_f32(!saved, g1, s));
     for (int q = 0; q + 2 < proj_depth(p); ++q) {
       vlb::GemmArgs gm{};
       gm.A = g2.A;
@@ -697,7 +725,7 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
   Plan pl;
-  if (make_plan(p, b, 0, &pl) != VLB_OK || p->dtype != VLB_BF16 || proj_depth(p) > 2) return 0;
+  if (make_plan(p, b, 0, &pl) != VLB_OK || proj_depth(p) > 2) return 0;
   return saved_layout(p, pl).total;
 }
 
@@ -717,7 +745,7 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
   Plan pl;
   vlb_status st = make_plan(p, b, seq_len, &pl);
   if (st != VLB_OK) return st;
-  if (p->dtype != VLB_BF16 || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
+  if (proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (pl.T == 0) return VLB_OK;
   if ((st = check_weights(p, w)) != VLB_OK) return st;
   if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;
@@ -771,7 +799,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
                     zero(g->d_w2, O * H * 4) && zero(g->d_b2, O * 4) &&
                     (!ln || (zero(g->d_ln_gamma, C * 4) && zero(g->d_ln_beta, C * 4))) &&
                     (!tiled || (zero(g->d_newline, O * 4) && zero(g->d_separator, O * 4))) &&
-                    zero(g->d_features, static_cast<size_t>(pl.npix) * C * 2);
+                    zero(g->d_features, static_cast<size_t>(pl.npix) * C * pl.es);
     return ok ? VLB_OK : VLB_ERR_HIP;
   }
   uint8_t *w8 = static_cast<uint8_t *>(ws);
@@ -814,6 +842,82 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
       VLB_LAUNCH(VLB_K_PLACE, s,
                  vlb::launch_place_tiled_record(c, slot_pos, status, dst_row, nl_pos, sep_pos, s));
     }
+  }
+  if (p->dtype == VLB_F32) {  // row-major operands, strided fp32 GEMMs
+    float *dy = reinterpret_cast<float *>(w8 + L.off_dy);
+    float *a1 = reinterpret_cast<float *>(w8 + L.off_a1t);
+    float *dz = reinterpret_cast<float *>(w8 + L.off_da1);
+    float *dxm = reinterpret_cast<float *>(w8 + L.off_dxm);
+    const void *z1 = sv + sl.off_z1, *xm = sv + sl.off_xm;
+    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_gather_rows_f32(dseq, dst_row, Ti, Oi, dy, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(dy, Ti, Oi, g->d_b2, status, s));
+    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, z1, T * H, a1, nullptr, s));
+    auto gemm = [&](const void *A, int64_t sam, int64_t sak, const void *B, int64_t sbn,
+                    int64_t sbk, void *out, int64_t M, int64_t N, int64_t K,
+                    const int32_t *st_word) {
+      vlb::GemmArgs ga{};
+      ga.A = A;
+      ga.B = B;
+      ga.out = out;
+      ga.M = static_cast<int32_t>(M);
+      ga.N = static_cast<int32_t>(N);
+      ga.K = static_cast<int32_t>(K);
+      ga.ldo = static_cast<int32_t>(N);
+      ga.act = VLB_ACT_NONE;
+      ga.sa_m = sam;
+      ga.sa_k = sak;
+      ga.sb_n = sbn;
+      ga.sb_k = sbk;
+      ga.status = st_word;
+      return ga;
+    };
+    // dW2[o][h] = sum_t dY[t][o] act(Z1)[t][h]; dA1[t][h] = sum_o dY[t][o] W2[o][h]
+    VLB_LAUNCH(VLB_K_BWD_DW2, s,
+               vlb::launch_gemm_f32(false, gemm(dy, 1, O, a1, 1, H, g->d_w2, O, H, T, status), s));
+    VLB_LAUNCH(VLB_K_BWD_DA1, s,
+               vlb::launch_gemm_f32(false, gemm(dy, O, 1, w->w2, 1, H, dz, T, H, O, nullptr), s));
+    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, z1, T * H, nullptr, dz, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(dz, Ti, Hi, g->d_b1, status, s));
+    // dW1[h][i] = sum_t dZ1[t][h] Xm[t][i]; dXm[t][i] = sum_h dZ1[t][h] W1[h][i]
+    VLB_LAUNCH(VLB_K_BWD_DW1, s,
+               vlb::launch_gemm_f32(false, gemm(dz, 1, H, xm, 1, K1, g->d_w1, H, K1, T, status),
+                                    s));
+    if (ln || g->d_features) {
+      VLB_LAUNCH(VLB_K_BWD_DX, s,
+                 vlb::launch_gemm_f32(false, gemm(dz, H, 1, w->w1, 1, K1, dxm, T, K1, H, nullptr),
+                                      s));
+      float *pg = reinterpret_cast<float *>(w8 + L.off_pln);
+      float *pbeta = pg + L.ln_rows * C;
+      int64_t row = 0;
+      for (int v0 = 0, ci = 0; v0 < b->n_views; v0 += vlb::kPlanViews, ++ci) {
+        const int grid = L.ln_grid[ci];
+        VLB_LAUNCH(VLB_K_BWD_UNMERGE, s,
+                   vlb::launch_bwd_unmerge_f32(dxm, features, view_chunk(p, b, pl, v0), p->C,
+                                               ln ? w->ln_gamma : nullptr, p->ln_eps,
+                                               g->d_features, pg + row * C, pbeta + row * C,
+                                               status, grid, s));
+        row += grid;
+      }
+      if (ln) {
+        const int32_t R = static_cast<int32_t>(L.ln_rows);
+        VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pg, R, p->C, g->d_ln_gamma, status, s));
+        VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pbeta, R, p->C, g->d_ln_beta, status, s));
+      }
+    }
+    if (tiled) {
+      float *pnl = reinterpret_cast<float *>(w8 + L.off_pnl);
+      float *psep = reinterpret_cast<float *>(w8 + L.off_psep);
+      const int32_t NL = static_cast<int32_t>(L.NL);
+      VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(p->dtype, dseq, nl_pos, NL, Oi, pnl, s));
+      VLB_LAUNCH(VLB_K_BWD_SUM, s,
+                 vlb::launch_colsum(pnl, (NL + 63) / 64, Oi, g->d_newline, status, s));
+      VLB_LAUNCH(VLB_K_BWD_SUM, s,
+                 vlb::launch_rows_sum(p->dtype, dseq, sep_pos, b->n_images, Oi, psep, s));
+      VLB_LAUNCH(VLB_K_BWD_SUM, s,
+                 vlb::launch_colsum(psep, (b->n_images + 63) / 64, Oi, g->d_separator, status,
+                                    s));
+    }
+    return VLB_OK;
   }
   // 2. dY, its transpose, db2
   float *pb2 = reinterpret_cast<float *>(w8 + L.off_pb2);
@@ -912,10 +1016,11 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     float *pnl = reinterpret_cast<float *>(w8 + L.off_pnl);
     float *psep = reinterpret_cast<float *>(w8 + L.off_psep);
     const int32_t NL = static_cast<int32_t>(L.NL);
-    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(dseq, nl_pos, NL, Oi, pnl, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(p->dtype, dseq, nl_pos, NL, Oi, pnl, s));
     VLB_LAUNCH(VLB_K_BWD_SUM, s,
                vlb::launch_colsum(pnl, (NL + 63) / 64, Oi, g->d_newline, status, s));
-    VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_rows_sum(dseq, sep_pos, b->n_images, Oi, psep, s));
+    VLB_LAUNCH(VLB_K_BWD_SUM, s,
+               vlb::launch_rows_sum(p->dtype, dseq, sep_pos, b->n_images, Oi, psep, s));
     VLB_LAUNCH(VLB_K_BWD_SUM, s,
                vlb::launch_colsum(psep, (b->n_images + 63) / 64, Oi, g->d_separator, status, s));
   }

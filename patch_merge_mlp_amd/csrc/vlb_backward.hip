@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "vlb_common.h"
 #include "vlb_internal.h"
 
@@ -398,17 +400,175 @@ __global__ __launch_bounds__(256) void k_colsum(const float *part, int32_t R, in
 
 // part[b][o] = sum of G[pos[i]][o] over list entries i of block b (64 each;
 // negative positions add nothing).
-__global__ __launch_bounds__(256) void k_rows_sum(const uint16_t *G, const int32_t *pos,
-                                                  int32_t n, int32_t O, float *part) {
+template <typename T>
+__global__ __launch_bounds__(256) void k_rows_sum(const T *G, const int32_t *pos, int32_t n,
+                                                  int32_t O, float *part) {
   const int o = blockIdx.x * 256 + threadIdx.x;
   if (o >= O) return;
   const int i0 = blockIdx.y * 64, i1 = min(n, i0 + 64);
   float s = 0.f;
   for (int i = i0; i < i1; ++i) {
     const int32_t p = pos[i];
-    if (p >= 0) s += bf2f(G[static_cast<int64_t>(p) * O + o]);
+    if (p >= 0) s += Elem<T>::load(G[static_cast<int64_t>(p) * O + o]);
   }
   part[static_cast<int64_t>(blockIdx.y) * O + o] = s;
+}
+
+// ---- fp32 backward (row-major operands; the products use the strided fp32 GEMM)
+
+// dY[t] = G[dst_row[t]] (zero where the row was not placed); one wave per row.
+__global__ __launch_bounds__(256) void k_gather_rows_f32(const float *G, const int32_t *dst_row,
+                                                         int32_t T, int32_t O, float *dy) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t t = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6; t < T;
+       t += nw) {
+    const int32_t d = dst_row[t];
+    for (int o = lane; o < O; o += 64)
+      dy[t * O + o] = d >= 0 ? G[static_cast<int64_t>(d) * O + o] : 0.f;
+  }
+}
+
+// d/dz of activate(z, act) in fp32: erf form Phi(z) + z phi(z); tanh form the
+// derivative of 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3).
+__device__ __forceinline__ float slope_f32(float z, int act) {
+  if (act == 0)
+    return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+           z * 0.39894228040143268f * expf(-0.5f * z * z);
+  if (act == 1) {
+    const float k0 = 0.79788456080286536f;
+    const float th = tanhf(k0 * (z + 0.044715f * z * z * z));
+    return 0.5f * (1.0f + th) + 0.5f * z * (1.0f - th * th) * k0 * (1.0f + 3.0f * 0.044715f * z * z);
+  }
+  return 1.0f;
+}
+
+// a = activate(z) (da == nullptr), or in place dz = da * act'(z).
+__global__ __launch_bounds__(256) void k_act_f32(const float *z, int64_t n, int act, float *a,
+                                                 float *da) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (da) da[i] *= slope_f32(z[i], act);
+    else a[i] = activate(z[i], act);
+  }
+}
+
+// fp32 feature gradient, one wave per (token row, block position) like
+// k_bwd_unmerge, with dXm in the pages' feature order (dn[c] = dXm[m][c*k*k +
+// p]); lane l holds channels l, l + 64, ... (NC of them).
+template <bool LN, int NC>
+__global__ __launch_bounds__(256) void k_bwd_unmerge_f32(const float *dxm, const float *x,
+                                                         PlanChunk c, int C, const float *gamma,
+                                                         float eps, float *dx, float *part_g,
+                                                         float *part_b, const int32_t *status) {
+  if (status[kStatusWord] != 0) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = c.k, kk = k * k;
+  const int64_t K1 = static_cast<int64_t>(C) * kk;
+  const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
+  const int64_t items = static_cast<int64_t>(t_end - t_begin) * kk;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const bool have = lane < c.n;
+  const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
+  const int32_t l_pix0 = have ? c.pix0[lane] : 0;
+  const int32_t l_gh = have ? c.gh[lane] : 0, l_gw = have ? c.gw[lane] : 1;
+  float ag[NC], ab[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) ag[i] = ab[i] = 0.f;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 4 + wid; it < items; it += nw) {
+    const int m = t_begin + static_cast<int>(it / kk), p = static_cast<int>(it % kk);
+    const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
+    const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
+    const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
+    const int wp = (gw + k - 1) / k, t = m - tok0;
+    const int y = (t / wp) * k + p / k, xx = (t % wp) * k + p % k;
+    if (y >= gh || xx >= gw) continue;
+    const int64_t pix = pix0 + static_cast<int64_t>(y) * gw + xx;
+    float dn[NC], xv[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int ch = lane + 64 * i;
+      dn[i] = ch < C ? dxm[m * K1 + static_cast<int64_t>(ch) * kk + p] : 0.f;
+      xv[i] = (LN && ch < C) ? x[pix * C + ch] : 0.f;
+    }
+    if (!LN) {
+      if (dx)
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+          if (lane + 64 * i < C) dx[pix * C + lane + 64 * i] = dn[i];
+      continue;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) sum += xv[i];
+    const float mean = wave_sum(sum) / C;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      if (lane + 64 * i < C) ss += (xv[i] - mean) * (xv[i] - mean);
+    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int ch = lane + 64 * i;
+      const float gm = ch < C ? gamma[ch] : 0.f;
+      const float xh = (xv[i] - mean) * rstd, gv = gm * dn[i];
+      xv[i] = xh;
+      ag[i] += dn[i] * xh;
+      ab[i] += dn[i];
+      sg += gv;
+      sgx += gv * xh;
+    }
+    const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+    if (dx)
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int ch = lane + 64 * i;
+        if (ch < C) dx[pix * C + ch] = rstd * (gamma[ch] * dn[i] - mg - xv[i] * mgx);
+      }
+  }
+  if (!LN) return;
+  extern __shared__ float red_f32[];  // [2][C]
+  for (int w = 0; w < 4; ++w) {
+    if (wid == w)
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int ch = lane + 64 * i;
+        if (ch < C) {
+          red_f32[ch] = (w == 0 ? 0.f : red_f32[ch]) + ag[i];
+          red_f32[C + ch] = (w == 0 ? 0.f : red_f32[C + ch]) + ab[i];
+        }
+      }
+    __syncthreads();
+  }
+  for (int ch = threadIdx.x; ch < C; ch += 256) {
+    part_g[static_cast<int64_t>(blockIdx.x) * C + ch] = red_f32[ch];
+    part_b[static_cast<int64_t>(blockIdx.x) * C + ch] = red_f32[C + ch];
+  }
+}
+
+template <bool LN, int NC>
+hipError_t unmerge_f32_launch(const void *dxm, const void *x, const PlanChunk &c, int C,
+                              const void *gamma, float eps, void *dx, float *part_g,
+                              float *part_b, const int32_t *status, int grid, hipStream_t s) {
+  const size_t lds = LN ? static_cast<size_t>(2) * C * sizeof(float) : 0;
+  hipLaunchKernelGGL((k_bwd_unmerge_f32<LN, NC>), dim3(grid), dim3(256), lds, s,
+                     static_cast<const float *>(dxm), static_cast<const float *>(x), c, C,
+                     static_cast<const float *>(gamma), eps, static_cast<float *>(dx), part_g,
+                     part_b, status);
+  return hipGetLastError();
+}
+
+template <bool LN>
+hipError_t unmerge_f32_dispatch(const void *dxm, const void *x, const PlanChunk &c, int C,
+                                const void *gamma, float eps, void *dx, float *part_g,
+                                float *part_b, const int32_t *status, int grid, hipStream_t s) {
+  const int nc = (C + 63) / 64;
+  if (nc <= 1) return unmerge_f32_launch<LN, 1>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+  if (nc <= 4) return unmerge_f32_launch<LN, 4>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+  if (nc <= 16) return unmerge_f32_launch<LN, 16>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+  if (nc <= 32) return unmerge_f32_launch<LN, 32>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
+  return hipErrorInvalidValue;
 }
 
 template <bool LN, int NCH>
@@ -519,12 +679,44 @@ hipError_t launch_colsum(const float *part, int32_t R, int32_t N, float *out,
   return hipGetLastError();
 }
 
-hipError_t launch_rows_sum(const void *G, const int32_t *pos, int32_t n, int32_t O, float *part,
-                           hipStream_t s) {
+hipError_t launch_rows_sum(int dtype, const void *G, const int32_t *pos, int32_t n, int32_t O,
+                           float *part, hipStream_t s) {
   if (n <= 0 || O <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rows_sum, dim3((O + 255) / 256, (n + 63) / 64), dim3(256), 0, s,
-                     static_cast<const uint16_t *>(G), pos, n, O, part);
+  const dim3 grid((O + 255) / 256, (n + 63) / 64);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_rows_sum<float>, grid, dim3(256), 0, s, static_cast<const float *>(G),
+                       pos, n, O, part);
+  else
+    hipLaunchKernelGGL(k_rows_sum<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(G), pos, n, O, part);
   return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_f32(const void *G, const int32_t *dst_row, int32_t T, int32_t O,
+                                  void *dy, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int grid = static_cast<int>(std::min<int64_t>((T + 3) / 4, 4096));
+  hipLaunchKernelGGL(k_gather_rows_f32, dim3(grid), dim3(256), 0, s,
+                     static_cast<const float *>(G), dst_row, T, O, static_cast<float *>(dy));
+  return hipGetLastError();
+}
+
+hipError_t launch_act_f32(int act, const void *z, int64_t n, void *a, void *da, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int grid = static_cast<int>(std::min<int64_t>((n + 255) / 256, 8192));
+  hipLaunchKernelGGL(k_act_f32, dim3(grid), dim3(256), 0, s, static_cast<const float *>(z), n, act,
+                     static_cast<float *>(a), static_cast<float *>(da));
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_unmerge_f32(const void *dxm, const void *x, const PlanChunk &c, int C,
+                                  const void *gamma, float eps, void *dx, float *part_g,
+                                  float *part_b, const int32_t *status, int grid, hipStream_t s) {
+  if (c.tok0[c.n] <= c.tok0[0]) return hipSuccess;
+  return gamma ? unmerge_f32_dispatch<true>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status,
+                                            grid, s)
+               : unmerge_f32_dispatch<false>(dxm, x, c, C, gamma, eps, dx, part_g, part_b,
+                                             status, grid, s);
 }
 
 }  // namespace vlb

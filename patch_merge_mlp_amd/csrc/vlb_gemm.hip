@@ -481,14 +481,21 @@ namespace {
 // ---------------------------------------------------------------------------
 // fp32 path: 64x64 tile, 16 K per stage, 4x4 outputs per thread, plain FMA.
 // In gather mode K runs in the pages' feature order c*k*k + dy*k + dx and each
-// A element is fetched from its pixel (zero in the padding).
+// A element is fetched from its pixel (zero in the padding).  Otherwise A and
+// B are read through strides (GemmArgs::sa_m ...; zero strides mean row-major
+// [M][K] and [N][K]), so the backward's products read transposed operands in
+// place.  A null bias counts as zero; with out2 the pre-activation is written
+// there as well (row-major, ldo); a set status word skips the output.
 constexpr int FT = 64, FK = 16;
 
 template <bool GATHER>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   __shared__ float As[FK][FT + 4];
   __shared__ float Bs[FK][FT + 4];
+  if (g.status && g.status[kStatusWord] != 0) return;
   const int tid = threadIdx.x;
+  const int64_t sam = g.sa_k ? g.sa_m : g.K, sak = g.sa_k ? g.sa_k : 1;
+  const int64_t sbn = g.sb_k ? g.sb_n : g.K, sbk = g.sb_k ? g.sb_k : 1;
   const int tm = blockIdx.x / g.tiles_n, tn = blockIdx.x % g.tiles_n;
   const int m0 = tm * FT, n0 = tn * FT;
   const float *A = static_cast<const float *>(g.A);
@@ -509,12 +516,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
           if ((d.geo >> (16 + p)) & 1)
             v = A[static_cast<int64_t>(d.pix + dy * (d.geo & 0xffff) + dx) * g.C + c];
         } else {
-          v = A[static_cast<int64_t>(m) * g.K + kidx];
+          v = A[m * sam + kidx * sak];
         }
       }
       As[kq][r] = v;
       const int n = n0 + r;
-      Bs[kq][r] = (n < g.N && kidx < g.K) ? B[static_cast<int64_t>(n) * g.K + kidx] : 0.f;
+      Bs[kq][r] = (n < g.N && kidx < g.K) ? B[n * sbn + kidx * sbk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -533,6 +540,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   }
   const float *bias = static_cast<const float *>(g.bias);
   float *out = static_cast<float *>(g.out);
+  float *out2 = static_cast<float *>(g.out2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
@@ -542,8 +550,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
-      if (n < g.N)
-        out[static_cast<int64_t>(dst) * g.ldo + n] = activate(acc[i][j] + bias[n], g.act);
+      if (n < g.N) {
+        const float z = acc[i][j] + (bias ? bias[n] : 0.f);
+        out[static_cast<int64_t>(dst) * g.ldo + n] = activate(z, g.act);
+        if (out2) out2[static_cast<int64_t>(dst) * g.ldo + n] = z;
+      }
     }
   }
 }

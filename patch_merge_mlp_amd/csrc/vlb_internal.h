@@ -70,7 +70,10 @@ struct GemmArgs {
   // tiles, the rest as 128x128 tiles (see tile_plan).
   int32_t n_full;
   void *out2;              // kGemmBlockedSave: the pre-activation, tile-blocked like out
-  const int32_t *status;   // kGemmF32: nothing is written when status[0] != 0 (may be null)
+  const int32_t *status;   // kGemmF32 / fp32: nothing is written when status[0] != 0 (may be null)
+  // fp32 path, not gather mode: element (m, k) of A at A[m * sa_m + k * sa_k] and
+  // (n, k) of B at B[n * sb_n + k * sb_k]; sa_k == 0 (sb_k == 0) means row-major.
+  int64_t sa_m, sa_k, sb_n, sb_k;
 };
 
 // Epilogues of the bf16 GEMM.
@@ -202,7 +205,17 @@ hipError_t launch_bwd_unmerge(const void *dxm, const void *x, const PlanChunk &c
 hipError_t launch_colsum(const float *part, int32_t R, int32_t N, float *out,
                          const int32_t *status, hipStream_t s);
 // part[ceil(n/64)][O]: sums of G rows pos[i] (negative: none), 64 entries per row.
-hipError_t launch_rows_sum(const void *G, const int32_t *pos, int32_t n, int32_t O, float *part,
-                           hipStream_t s);
+hipError_t launch_rows_sum(int dtype, const void *G, const int32_t *pos, int32_t n, int32_t O,
+                           float *part, hipStream_t s);
+// fp32: dY[t] = G[dst_row[t]] (zero where negative), row-major [T][O].
+hipError_t launch_gather_rows_f32(const void *G, const int32_t *dst_row, int32_t T, int32_t O,
+                                  void *dy, hipStream_t s);
+// fp32: a = act(z) when da is null, else da *= act'(z) in place (n elements).
+hipError_t launch_act_f32(int act, const void *z, int64_t n, void *a, void *da, hipStream_t s);
+// fp32 feature gradient of one chunk of views from dXm (row-major [T][C*k*k],
+// the pages' feature order), as launch_bwd_unmerge (C <= 2048).
+hipError_t launch_bwd_unmerge_f32(const void *dxm, const void *x, const PlanChunk &c, int C,
+                                  const void *gamma, float eps, void *dx, float *part_g,
+                                  float *part_b, const int32_t *status, int grid, hipStream_t s);
 
 }  // namespace vlb

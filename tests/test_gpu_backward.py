@@ -66,6 +66,11 @@ def _np(x):
 
 
 BWD_SMALL = [small_workloads()[i] for i in (0, 1, 2, 3, 4)]
+BWD_F32 = [small_workloads()[5], wl.config(0),
+           wl.Workload("small-f32-ln-tiled", 17, "f32", C=32, k=2, hidden=48, out_dim=40,
+                       seq_len=900, grids=[(9, 11)] * 7 + [(6, 6)] * 3, views_per_image=[7, 3],
+                       has_ln=True, tiled=True, tiles=[(2, 3), (1, 2)])]
+TOL_F32 = 1e-5   # fp32 throughout
 
 
 @pytest.mark.parametrize("w", BWD_SMALL, ids=lambda w: w.name)
@@ -95,6 +100,28 @@ def test_small_backward_vs_oracle(w):
     for k, e in errs.items():
         tol = TOL_SUM if k in ("db2", "d_newline", "d_separator") else TOL_ACT
         assert e <= tol, (k, e)
+
+
+@pytest.mark.parametrize("w", BWD_F32, ids=lambda w: w.name)
+def test_small_backward_f32_vs_oracle(w):
+    t = common.draw(w)
+    dseq = wl.seq_grad(w)
+    st, seq, g, _ = run_train(w, t, dseq)
+    assert st == v.OK
+    st_f, seq_f = run_fused(w, t)
+    assert st_f == v.OK
+    assert torch.equal(seq.view(torch.int32), seq_f.view(torch.int32)), "training forward differs"
+    ref = oracle_grads(w, t, dseq)
+    pairs = [("dw1", g.d_w1), ("db1", g.d_b1), ("dw2", g.d_w2), ("db2", g.d_b2),
+             ("dx", g.d_features)]
+    if w.has_ln:
+        pairs += [("dgamma", g.d_ln_gamma), ("dbeta", g.d_ln_beta)]
+    if w.tiled:
+        pairs += [("d_newline", g.d_newline), ("d_separator", g.d_separator)]
+    errs = {k: common.rel_frob(_np(x), ref[k]) for k, x in pairs}
+    print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= TOL_F32, (k, e)
 
 
 @pytest.mark.parametrize("act", [v.GELU_TANH, v.ACT_NONE])

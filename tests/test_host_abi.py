@@ -200,10 +200,11 @@ def test_training_entry_points_validate():
     T = v.vlb_num_tokens(p, b)
     K1 = p.C * p.k * p.k
     assert v.vlb_saved_bytes(p, b) == 256 * K1 * 2 + 256 * p.hidden * 2
-    assert v.vlb_saved_bytes(_proj(dtype=v.F32), b) == 0
+    # fp32: row-major merged rows (4 x 256) and Z1 (4 x 128), 256-byte aligned
+    assert v.vlb_saved_bytes(_proj(dtype=v.F32), b) == 4 * K1 * 4 + 4 * p.hidden * 4
     need = v.vlb_backward_workspace_bytes(p, b, 32)
     assert need > 0
-    assert v.vlb_backward_workspace_bytes(_proj(dtype=v.F32), b, 32) == 0
+    assert v.vlb_backward_workspace_bytes(_proj(dtype=v.F32), b, 32) > 0
     assert v.vlb_backward_workspace_bytes(_proj(packed=True), b, 32) == 0
     assert v.vlb_backward_workspace_bytes(_proj(has_ln=True, C=2112), b, 32) == 0
     w = v.vlb_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
@@ -215,7 +216,6 @@ def test_training_entry_points_validate():
         return L.vlb_bridge_fused_train(ct.byref(proj), ct.byref(b.c), FAKE, ct.byref(w), None,
                                         None, FAKE, 32, FAKE + G, saved, saved_bytes, FAKE + 3 * G,
                                         ws_bytes, None)
-    assert train(proj=_proj(dtype=v.F32)) == v.ERR_UNSUPPORTED
     assert train(saved=None) == v.ERR_NULL
     assert train(saved=FAKE + 2 * G + 8) == v.ERR_ALIGN
     assert train(saved_bytes=sneed - 1) == v.ERR_WORKSPACE
@@ -228,7 +228,6 @@ def test_training_entry_points_validate():
         return L.vlb_bridge_backward(ct.byref(proj), ct.byref(b.c), feats, ct.byref(wts), FAKE, S,
                                      FAKE, FAKE, saved_bytes, ct.byref(g) if g else None, FAKE,
                                      ws_bytes, None)
-    assert bwd(proj=_proj(dtype=v.F32)) == v.ERR_UNSUPPORTED
     assert bwd(proj=_proj(has_ln=True, packed=True)) == v.ERR_UNSUPPORTED
     assert bwd(g=None) == v.ERR_NULL
     assert bwd(g=v.vlb_grads(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)) == v.ERR_NULL
