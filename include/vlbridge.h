@@ -264,12 +264,11 @@ typedef struct {
  * the loss with respect to the sequence vlb_bridge_fused_train wrote; its rows
  * at text positions (mask == 0) are not read.  features, w, mask and saved
  * must be those of that forward call (features and w->ln_gamma are read only
- * with the LayerNorm; w->w1 and w->w2 unpacked, p->packed == 0; biases and
- * ln_beta are not read).  Every token row's gradient is the dseq row of its
+ * with the LayerNorm; w->w1 and w->w2 as the projector says, unpacked or
+ * packed; biases and ln_beta are not read).  Every token row's gradient is the dseq row of its
  * slot; the newline and separator gradients sum the rows of all their slots;
  * padded merge cells take no gradient.
- * Unsupported (VLB_ERR_UNSUPPORTED): p->packed, depth > 2, has_ln with
- * C > 2048.  Device-detected placeholder-count mismatch: nothing is written
+ * Unsupported (VLB_ERR_UNSUPPORTED): depth > 2, has_ln with C > 2048.  Device-detected placeholder-count mismatch: nothing is written
  * and vlb_check(ws) returns VLB_ERR_MASK_COUNT.  With no token rows
  * (n_views = 0) every gradient is set to zero and the mask is not read.
  * Workspace: vlb_backward_workspace_bytes(p, b, seq_len). */

@@ -219,7 +219,7 @@ struct BwdLayout {
 
 vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                       int64_t seq_len, BwdLayout *L) {
-  if (p->packed || proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
+  if (proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && p->C > vlb::kBwdMaxChannels) return VLB_ERR_UNSUPPORTED;
   const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1;
   L->Tk = (T + 31) / 32 * 32;
@@ -943,7 +943,9 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw2, s));
   // 4. dA1 = dY W2, then dZ1 = dA1 * act'(Z1) and db1
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
-             vlb::launch_bwd_weight_t(w->w2, Oi, Hi, p->C, 1, Op, w8 + L.off_w2t, s));
+             p->packed  // the packed W2 is tile-blocked [O][H]: transpose it as it is
+                 ? vlb::launch_bwd_act_t(VLB_ACT_NONE, w->w2, Oi, Hi, Op, w8 + L.off_w2t, s)
+                 : vlb::launch_bwd_weight_t(w->w2, Oi, Hi, p->C, 1, Op, w8 + L.off_w2t, s));
   vlb::GemmArgs ga{};
   ga.A = w8 + L.off_dy;
   ga.B = w8 + L.off_w2t;
@@ -980,7 +982,10 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   // 6. dXm = dZ1 W1 (K position-major), unmerge, LayerNorm backward
   if (ln || g->d_features) {
     VLB_LAUNCH(VLB_K_BWD_PACK, s,
-               vlb::launch_bwd_weight_t(w->w1, Hi, K1i, p->C, p->k, Hi, w8 + L.off_w1t, s));
+               p->packed  // packed W1: tile-blocked [H][K1], K1 already position-major
+                   ? vlb::launch_bwd_act_t(VLB_ACT_NONE, w->w1, Hi, K1i, Hi, w8 + L.off_w1t, s)
+                   : vlb::launch_bwd_weight_t(w->w1, Hi, K1i, p->C, p->k, Hi, w8 + L.off_w1t,
+                                              s));
     vlb::GemmArgs gx{};
     gx.A = w8 + L.off_dz1;
     gx.B = w8 + L.off_w1t;

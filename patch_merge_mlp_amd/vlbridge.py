@@ -455,8 +455,8 @@ def vlb_bridge_backward(p, b: Batch, features, w: Weights, mask, dseq, saved, g:
     dt = _tdtype(p)
     _check_seq(p, mask, dseq)
     _need(features, _pixels(b) * p.C, dt, "features")
-    _need(w.w1, p.hidden * p.C * p.k * p.k, dt, "w1")
-    _need(w.w2, p.out_dim * p.hidden, dt, "w2")
+    _need(w.w1, vlb_packed_bytes(p, 1) // 2 if p.packed else p.hidden * p.C * p.k * p.k, dt, "w1")
+    _need(w.w2, vlb_packed_bytes(p, 2) // 2 if p.packed else p.out_dim * p.hidden, dt, "w2")
     _need(w.ln_gamma, p.C, dt, "ln_gamma")
     f32 = torch.float32
     _need(g.d_w1, p.hidden * p.C * p.k * p.k, f32, "d_w1")

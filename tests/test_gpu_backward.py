@@ -200,6 +200,35 @@ def test_full_backward_sampled(i):
     assert e <= TOL_ACT
 
 
+@pytest.mark.parametrize("wi", [0, 2])
+def test_backward_packed_equals_unpacked(wi):
+    """With weights packed by vlb_pack_weights the backward gives the same bits."""
+    w = small_workloads()[wi]
+    t = common.draw(w)
+    dseq = wl.seq_grad(w)
+    _, _, g_ref, _ = run_train(w, t, dseq)
+    p, b = common.lib_projector(w), common.lib_batch(w)
+    br = v.Bridge(p, _weights(t))  # packs W1 and W2
+    seq = _dev(t["seq"]).clone()
+    mask = _dev(t["mask"])
+    fws = torch.empty(v.vlb_workspace_bytes(br.p, b, seq.shape[0]), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(v.vlb_saved_bytes(br.p, b), dtype=torch.uint8, device="cuda")
+    v.vlb_bridge_fused_train(br.p, b, _dev(t["features"]), br.w, _dev(t["newline"]),
+                             _dev(t["separator"]), mask, seq, saved, fws)
+    g = v.Grads.empty(br.p, b)
+    bws = torch.empty(v.vlb_backward_workspace_bytes(br.p, b, seq.shape[0]), dtype=torch.uint8,
+                      device="cuda")
+    v.vlb_bridge_backward(br.p, b, _dev(t["features"]), br.w, mask, _dev(dseq), saved, g, bws)
+    assert v.vlb_check(bws) == v.OK
+    for name in ("d_w1", "d_b1", "d_w2", "d_b2", "d_features", "d_ln_gamma", "d_ln_beta",
+                 "d_newline", "d_separator"):
+        a_, b_ = getattr(g, name), getattr(g_ref, name)
+        if b_ is None:
+            continue
+        view = torch.int16 if a_.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a_.view(view), b_.view(view)), name
+
+
 def test_backward_deterministic():
     w = small_workloads()[2]
     t = common.draw(w)

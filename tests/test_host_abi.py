@@ -205,7 +205,7 @@ def test_training_entry_points_validate():
     need = v.vlb_backward_workspace_bytes(p, b, 32)
     assert need > 0
     assert v.vlb_backward_workspace_bytes(_proj(dtype=v.F32), b, 32) > 0
-    assert v.vlb_backward_workspace_bytes(_proj(packed=True), b, 32) == 0
+    assert v.vlb_backward_workspace_bytes(_proj(packed=True), b, 32) > 0
     assert v.vlb_backward_workspace_bytes(_proj(has_ln=True, C=2112), b, 32) == 0
     w = v.vlb_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     fneed = v.vlb_workspace_bytes(p, b, 32)
@@ -228,7 +228,6 @@ def test_training_entry_points_validate():
         return L.vlb_bridge_backward(ct.byref(proj), ct.byref(b.c), feats, ct.byref(wts), FAKE, S,
                                      FAKE, FAKE, saved_bytes, ct.byref(g) if g else None, FAKE,
                                      ws_bytes, None)
-    assert bwd(proj=_proj(has_ln=True, packed=True)) == v.ERR_UNSUPPORTED
     assert bwd(g=None) == v.ERR_NULL
     assert bwd(g=v.vlb_grads(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)) == v.ERR_NULL
     assert bwd(g=v.vlb_grads(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None)) == v.ERR_NULL
