@@ -151,6 +151,8 @@ def _declare(L):
     L.orc_scatter_backward.argtypes = [_I64, i64, _U8, i64, ct.c_int32, _D, i64, _D, _D, _D]
     L.orc_project_backward.restype = None
     L.orc_project_backward.argtypes = [ct.POINTER(_Spec)] + [_D] * 14
+    L.orc_project_backward_deep.restype = None
+    L.orc_project_backward_deep.argtypes = [ct.POINTER(_Spec)] + [_D] * 18
     L.orc_hidden_unit_grads.restype = None
     L.orc_hidden_unit_grads.argtypes = [ct.POINTER(_Spec)] + [_D] * 7 + [ct.c_int32, _D, _D, _D]
     L.orc_pixel_grad.restype = None
@@ -402,6 +404,30 @@ def project_backward(spec: Spec, x, gamma, beta, W1, b1, W2, dY) -> dict:
     lib().orc_project_backward(ct.byref(s), *[_dp(a) for a in ins],
                                *[_dp(out[n]) for n in ("dx", "dw1", "db1", "dw2", "db2",
                                                        "dgamma", "dbeta")])
+    if not spec.has_ln:
+        del out["dgamma"], out["dbeta"]
+    return out
+
+
+def project_backward_deep(spec: Spec, x, gamma, beta, W1, b1, W_mid, b_mid, W2, dY) -> dict:
+    """project_backward for depth = spec.depth, with "dw_mid" [depth-2][H][H] and
+    "db_mid" [depth-2][H] as well."""
+    s = spec.c()
+    x = _f64(x)
+    n_mid, H = spec.depth - 2, spec.hidden
+    K1 = spec.C * spec.k * spec.k
+    wm = np.ascontiguousarray(np.stack([_f64(a) for a in W_mid]) if n_mid else np.zeros((1, H, H)))
+    bm = np.ascontiguousarray(np.stack([_f64(a) for a in b_mid]) if n_mid else np.zeros((1, H)))
+    out = {"dx": np.zeros_like(x), "dw1": np.zeros((H, K1)), "db1": np.zeros(H),
+           "dw_mid": np.zeros((max(n_mid, 1), H, H)), "db_mid": np.zeros((max(n_mid, 1), H)),
+           "dw2": np.zeros((spec.out_dim, H)), "db2": np.zeros(spec.out_dim),
+           "dgamma": np.zeros(spec.C), "dbeta": np.zeros(spec.C)}
+    ins = [x] + [_f64(a) for a in (gamma, beta, W1, b1)]
+    lib().orc_project_backward_deep(ct.byref(s), *[_dp(a) for a in ins], _dp(wm), _dp(bm),
+                                    _dp(_f64(W2)), _dp(_f64(dY)),
+                                    *[_dp(out[n]) for n in ("dx", "dw1", "db1", "dw_mid", "db_mid",
+                                                            "dw2", "db2", "dgamma", "dbeta")])
+    out["dw_mid"], out["db_mid"] = out["dw_mid"][:n_mid], out["db_mid"][:n_mid]
     if not spec.has_ln:
         del out["dgamma"], out["dbeta"]
     return out

@@ -525,7 +525,19 @@ void orc_project_backward(const orc_spec *s, const double *x, const double *gamm
                           const double *W2, const double *dY, double *dx, double *dW1,
                           double *db1, double *dW2, double *db2, double *dgamma,
                           double *dbeta) {
-  const int32_t C = s->C, k = s->k, H = s->hidden, O = s->out_dim;
+  orc_spec s2 = *s;
+  s2.n_mid = 0;
+  orc_project_backward_deep(&s2, x, gamma, beta, W1, b1, NULL, NULL, W2, dY, dx, dW1, db1, NULL,
+                            NULL, dW2, db2, dgamma, dbeta);
+}
+
+void orc_project_backward_deep(const orc_spec *s, const double *x, const double *gamma,
+                               const double *beta, const double *W1, const double *b1,
+                               const double *W_mid, const double *b_mid, const double *W2,
+                               const double *dY, double *dx, double *dW1, double *db1,
+                               double *dW_mid, double *db_mid, double *dW2, double *db2,
+                               double *dgamma, double *dbeta) {
+  const int32_t C = s->C, k = s->k, H = s->hidden, O = s->out_dim, n_mid = s->n_mid;
   const int64_t K1 = (int64_t)C * k * k;
   int64_t npix = 0;
   for (int32_t v = 0; v < s->n_views; v++) npix += (int64_t)s->grid_h[v] * s->grid_w[v];
@@ -533,13 +545,19 @@ void orc_project_backward(const orc_spec *s, const double *x, const double *gamm
   memset(db1, 0, sizeof(double) * H);
   memset(dW2, 0, sizeof(double) * O * H);
   memset(db2, 0, sizeof(double) * O);
+  if (n_mid > 0) {
+    memset(dW_mid, 0, sizeof(double) * n_mid * H * H);
+    memset(db_mid, 0, sizeof(double) * n_mid * H);
+  }
   if (s->has_ln) {
     memset(dgamma, 0, sizeof(double) * C);
     memset(dbeta, 0, sizeof(double) * C);
   }
   double *m = (double *)malloc(sizeof(double) * K1);
-  double *z = (double *)malloc(sizeof(double) * H);
+  double *zs = (double *)malloc(sizeof(double) * (n_mid + 1) * H); /* pre-activations per Linear */
+  double *a = (double *)malloc(sizeof(double) * H);
   double *dz = (double *)malloc(sizeof(double) * H);
+  double *dzp = (double *)malloc(sizeof(double) * H);
   double *dm = (double *)malloc(sizeof(double) * K1);
   double *dn = (double *)calloc((size_t)npix * C, sizeof(double)); /* d(LN output) per pixel */
   int64_t r = 0, pix = 0;
@@ -548,18 +566,44 @@ void orc_project_backward(const orc_spec *s, const double *x, const double *gamm
     const int64_t wp = orc_merged_side(gw, k), nt = orc_view_tokens(gh, gw, k);
     for (int64_t t = 0; t < nt; t++, r++) {
       const double *dy = dY + r * O;
-      /* forward of the row: merged features, Linear1 pre-activation */
+      /* forward of the row: merged features, Linear1 pre-activation, then the
+       * middle Linears' pre-activations z_{q+1} = W_mid[q] act(z_q) + b_mid[q] */
       orc_merged_row(s, x, gamma, beta, r, m);
-      orc_linear(m, 1, (int32_t)K1, W1, b1, H, z, 1);
+      orc_linear(m, 1, (int32_t)K1, W1, b1, H, zs, 1);
+      for (int32_t q = 0; q < n_mid; q++) {
+        for (int32_t h = 0; h < H; h++) a[h] = act_value(s->act, zs[(int64_t)q * H + h]);
+        orc_linear(a, 1, H, W_mid + (int64_t)q * H * H, b_mid + (int64_t)q * H, H,
+                   zs + (int64_t)(q + 1) * H, 1);
+      }
+      const double *z = zs + (int64_t)n_mid * H; /* the last pre-activation */
       /* Linear2: y = W2 a + b2 */
       for (int32_t o = 0; o < O; o++) db2[o] += dy[o];
       for (int32_t o = 0; o < O; o++)
         for (int32_t h = 0; h < H; h++) dW2[(int64_t)o * H + h] += dy[o] * act_value(s->act, z[h]);
-      /* activation, then Linear1: z = W1 m + b1 */
+      /* the last activation */
       for (int32_t h = 0; h < H; h++) {
         double da = 0.0;
         for (int32_t o = 0; o < O; o++) da += dy[o] * W2[(int64_t)o * H + h];
         dz[h] = da * act_slope(s->act, z[h]);
+      }
+      /* middle Linears, last to first: layer q maps act(z_q) to z_{q+1} */
+      for (int32_t q = n_mid - 1; q >= 0; q--) {
+        const double *zq = zs + (int64_t)q * H;
+        const double *Wq = W_mid + (int64_t)q * H * H;
+        for (int32_t j = 0; j < H; j++) {
+          db_mid[(int64_t)q * H + j] += dz[j];
+          for (int32_t h = 0; h < H; h++)
+            dW_mid[((int64_t)q * H + j) * H + h] += dz[j] * act_value(s->act, zq[h]);
+        }
+        for (int32_t h = 0; h < H; h++) {
+          double da = 0.0;
+          for (int32_t j = 0; j < H; j++) da += dz[j] * Wq[(int64_t)j * H + h];
+          dzp[h] = da * act_slope(s->act, zq[h]);
+        }
+        memcpy(dz, dzp, sizeof(double) * H);
+      }
+      /* Linear1: z_0 = W1 m + b1 */
+      for (int32_t h = 0; h < H; h++) {
         db1[h] += dz[h];
         for (int64_t i = 0; i < K1; i++) dW1[h * K1 + i] += dz[h] * m[i];
       }
@@ -589,8 +633,10 @@ void orc_project_backward(const orc_spec *s, const double *x, const double *gamm
       memcpy(dx + p * C, dn + p * C, sizeof(double) * C);
   }
   free(m);
-  free(z);
+  free(zs);
+  free(a);
   free(dz);
+  free(dzp);
   free(dm);
   free(dn);
 }

@@ -146,7 +146,8 @@ int32_t orc_scatter_backward(const int64_t *src, int64_t P, const uint8_t *mask,
                              int32_t D, const double *dseq, int64_t T, double *drows,
                              double *dnewline, double *dseparator);
 
-/* The backward functions below take a projector of depth 2 (s->n_mid == 0). */
+/* orc_project_backward, orc_hidden_unit_grads and orc_pixel_grad take a
+ * projector of depth 2 (s->n_mid is not read); orc_project_backward_deep any. */
 
 /* Gradients of the projector for the gradient dY [T][out_dim] of its output
  * rows: dx [n_pixels][C] (of the features), dW1 [hidden][C*k*k] (pages' feature
@@ -158,6 +159,16 @@ void orc_project_backward(const orc_spec *s, const double *x, const double *gamm
                           const double *W2, const double *dY, double *dx, double *dW1,
                           double *db1, double *dW2, double *db2, double *dgamma,
                           double *dbeta);
+
+/* orc_project_backward for a projector of depth 2 + s->n_mid: also the
+ * gradients of the middle Linears, dW_mid [n_mid][hidden][hidden] and db_mid
+ * [n_mid][hidden] (W_mid, b_mid as for orc_project_rows_deep). */
+void orc_project_backward_deep(const orc_spec *s, const double *x, const double *gamma,
+                               const double *beta, const double *W1, const double *b1,
+                               const double *W_mid, const double *b_mid, const double *W2,
+                               const double *dY, double *dx, double *dW1, double *db1,
+                               double *dW_mid, double *db_mid, double *dW2, double *db2,
+                               double *dgamma, double *dbeta);
 
 /* The same gradients restricted to hidden unit h: row h of dW1, db1[h] and
  * column h of dW2 (dW2_col [out_dim]). */

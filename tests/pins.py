@@ -402,6 +402,57 @@ def pin_project_backward_autograd(o):
                     (has_ln, act, mine)
 
 
+def pin_project_backward_deep_autograd(o):
+    """Depth 3 and 4: every gradient, the middle Linears' included, equals torch
+    autograd through the library forward; depth 2 equals project_backward."""
+    d, grids, C, k, H, O = _bwd_problem(14, C=4, H=7, O=5, grids=((3, 5), (4, 4)))
+    rng = np.random.default_rng(15)
+    Wm = [rng.standard_normal((H, H)) / 2 for _ in range(2)]
+    bm = [rng.standard_normal(H) for _ in range(2)]
+    for has_ln, act in ((True, o.GELU_ERF), (False, o.GELU_TANH), (True, o.ACT_NONE)):
+        for depth in (2, 3, 4):
+            n = depth - 2
+            spec = o.Spec(grids=grids, C=C, k=k, hidden=H, out_dim=O, views_per_image=[2],
+                          has_ln=has_ln, ln_eps=0.3, act=act, depth=depth)
+            ts = {nm: torch.from_numpy(d[nm]).requires_grad_(True)
+                  for nm in ("x", "g", "bb", "W1", "b1", "W2", "b2")}
+            tm = [torch.from_numpy(w_).requires_grad_(True) for w_ in Wm[:n]]
+            tb = [torch.from_numpy(b_).requires_grad_(True) for b_ in bm[:n]]
+            actf = {o.GELU_ERF: F.gelu, o.GELU_TANH: lambda z: F.gelu(z, approximate="tanh"),
+                    o.ACT_NONE: lambda z: z}[act]
+            merged, p = [], 0
+            for gh, gw in grids:
+                v = ts["x"][p:p + gh * gw].reshape(gh, gw, C)
+                p += gh * gw
+                if has_ln:
+                    v = F.layer_norm(v, (C,), ts["g"], ts["bb"], eps=0.3)
+                hp, wp = -(-gh // k), -(-gw // k)
+                tt = F.pad(v.permute(2, 0, 1).unsqueeze(0), (0, wp * k - gw, 0, hp * k - gh))
+                merged.append(F.pixel_unshuffle(tt, k)[0].permute(1, 2, 0).reshape(hp * wp, C * k * k))
+            h = F.linear(torch.cat(merged), ts["W1"], ts["b1"])
+            for q in range(n):
+                h = F.linear(actf(h), tm[q], tb[q])
+            y = F.linear(actf(h), ts["W2"], ts["b2"])
+            (y * torch.from_numpy(d["dY"])).sum().backward()
+            got = o.project_backward_deep(spec, d["x"], d["g"], d["bb"], d["W1"], d["b1"], Wm[:n],
+                                          bm[:n], d["W2"], d["dY"])
+            pairs = [("dx", ts["x"]), ("dw1", ts["W1"]), ("db1", ts["b1"]), ("dw2", ts["W2"]),
+                     ("db2", ts["b2"])]
+            if has_ln:
+                pairs += [("dgamma", ts["g"]), ("dbeta", ts["bb"])]
+            for mine, t_ in pairs:
+                assert np.allclose(got[mine], t_.grad.numpy(), rtol=1e-10, atol=1e-11), \
+                    (depth, has_ln, act, mine)
+            for q in range(n):
+                assert np.allclose(got["dw_mid"][q], tm[q].grad.numpy(), rtol=1e-10, atol=1e-11)
+                assert np.allclose(got["db_mid"][q], tb[q].grad.numpy(), rtol=1e-10, atol=1e-11)
+            if depth == 2:
+                ref = o.project_backward(spec, d["x"], d["g"], d["bb"], d["W1"], d["b1"], d["W2"],
+                                         d["dY"])
+                for nm in ref:
+                    assert np.array_equal(ref[nm], got[nm]), nm
+
+
 def pin_project_backward_fd(o):
     """Central finite differences of the (pinned) forward: L = sum(dY * Y)."""
     d, grids, C, k, H, O = _bwd_problem(12, C=3, H=5, O=4, grids=((3, 3), (2, 5)))
@@ -559,7 +610,8 @@ PROCESSOR_PINS = [pin_processor_page_examples, pin_processor_best_fit, pin_proce
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
        pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
        pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
-       pin_embed_scatter, pin_project_rows_deep_library, pin_project_backward_autograd, pin_project_backward_fd,
+       pin_embed_scatter, pin_project_rows_deep_library, pin_project_backward_autograd,
+       pin_project_backward_deep_autograd, pin_project_backward_fd,
        pin_backward_samples, pin_scatter_backward] + PROCESSOR_PINS
 
 

@@ -101,6 +101,13 @@ MUTANTS = {
                                                      "for (int32_t d = 0; d < D; d++) to[d] = g[d];"),
     "scatter backward count check misses too few": ("if (count != P) return -1;\n  memset(drows",
                                                     "if (count > P) return -1;\n  memset(drows"),
+    "middle dW from the pre-activation": ("dW_mid[((int64_t)q * H + j) * H + h] += dz[j] * act_value(s->act, zq[h]);",
+                                          "dW_mid[((int64_t)q * H + j) * H + h] += dz[j] * zq[h];"),
+    "middle backward without the slope": ("dzp[h] = da * act_slope(s->act, zq[h]);", "dzp[h] = da;"),
+    "middle dA through W transposed": ("da += dz[j] * Wq[(int64_t)j * H + h];",
+                                       "da += dz[j] * Wq[(int64_t)h * H + j];"),
+    "middle bias gradient dropped": ("db_mid[(int64_t)q * H + j] += dz[j];",
+                                     "db_mid[(int64_t)q * H + j] += 0.0 * dz[j];"),
     "sampled unit misses the bias": ("    z += b1[h];\n    const double a = act_value(s->act, z);",
                                      "    const double a = act_value(s->act, z);"),
     "sampled pixel at the transposed block position": ("const int32_t p = (y % k) * k + xx % k;",
