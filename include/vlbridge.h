@@ -230,8 +230,9 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
  */
 
 /* Bytes of the saved-activation buffer of a batch (the merged tokens and the
- * first Linear's pre-activation: tile-blocked for VLB_BF16, row-major for
- * VLB_F32; the contents are opaque); 0 on invalid input or for depth > 2. */
+ * pre-activation of the first and every middle Linear: tile-blocked for
+ * VLB_BF16, row-major for VLB_F32; the contents are opaque); 0 on invalid
+ * input. */
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b);
 
 /* Device workspace bytes of vlb_bridge_backward for this batch and sequence
@@ -240,8 +241,7 @@ size_t vlb_backward_workspace_bytes(const vlb_projector *p, const vlb_batch *b, 
 
 /* vlb_bridge_fused (same arguments, errors and sequence values), and the
  * activations the backward needs written to saved (vlb_saved_bytes bytes,
- * which must not overlap any other argument).  Depth 2 only (otherwise
- * VLB_ERR_UNSUPPORTED). */
+ * which must not overlap any other argument). */
 vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
                                   const void *features, const vlb_weights *w,
                                   const void *newline, const void *separator,
@@ -258,17 +258,20 @@ typedef struct {
   float *d_b2;                    /* [out_dim] */
   float *d_ln_gamma, *d_ln_beta;  /* [C]; has_ln only (ignored otherwise) */
   float *d_newline, *d_separator; /* [out_dim]; TILED_2D only (ignored otherwise) */
+  float *const *d_w_mid;          /* (host) [depth - 2] device pointers, each [hidden][hidden];
+                                     depth > 2 only */
+  float *const *d_b_mid;          /* (host) [depth - 2] device pointers, each [hidden] */
 } vlb_grads;
 
 /* Backward of the bridge.  dseq [seq_len][out_dim] (dtype) is the gradient of
  * the loss with respect to the sequence vlb_bridge_fused_train wrote; its rows
  * at text positions (mask == 0) are not read.  features, w, mask and saved
  * must be those of that forward call (features and w->ln_gamma are read only
- * with the LayerNorm; w->w1 and w->w2 as the projector says, unpacked or
- * packed; biases and ln_beta are not read).  Every token row's gradient is the dseq row of its
+ * with the LayerNorm; w->w1, w->w2 and w->w_mid as the projector says,
+ * unpacked or packed; biases and ln_beta are not read).  Every token row's gradient is the dseq row of its
  * slot; the newline and separator gradients sum the rows of all their slots;
  * padded merge cells take no gradient.
- * Unsupported (VLB_ERR_UNSUPPORTED): depth > 2, has_ln with C > 2048.  Device-detected placeholder-count mismatch: nothing is written
+ * Unsupported (VLB_ERR_UNSUPPORTED): has_ln with C > 2048.  Device-detected placeholder-count mismatch: nothing is written
  * and vlb_check(ws) returns VLB_ERR_MASK_COUNT.  With no token rows
  * (n_views = 0) every gradient is set to zero and the mask is not read.
  * Workspace: vlb_backward_workspace_bytes(p, b, seq_len). */

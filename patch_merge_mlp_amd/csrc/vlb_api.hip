@@ -181,28 +181,31 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
 }
 
 // Saved activations of a training forward: the merged tokens (Linear1's
-// operand) and Linear1's pre-activation, both tile-blocked (bf16) or
-// row-major (fp32).
+// operand) and the pre-activation of Linear1 and of every middle Linear,
+// tile-blocked (bf16) or row-major (fp32).
 struct SavedLayout {
-  size_t off_xm = 0, off_z1 = 0, total = 0;
+  size_t off_xm = 0, off_z1 = 0, z_stride = 0, total = 0;
+  // pre-activation of Linear1 (q = 0) or of middle Linear q (1 <= q <= depth - 2)
+  size_t off_z(int q) const { return off_z1 + static_cast<size_t>(q) * z_stride; }
 };
 
 SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
   SavedLayout L;
   size_t off = 0;
-  if (p->dtype == VLB_F32) {  // row-major merged rows (the pages' order) and Z1
+  const int nz = proj_depth(p) - 1;  // pre-activations kept: Linear1 and the middle ones
+  if (p->dtype == VLB_F32) {  // row-major merged rows (the pages' order) and Z per Linear
     L.off_xm = off;
     off = align256(off + static_cast<size_t>(pl.T) * pl.K1 * 4);
     L.off_z1 = off;
-    off = align256(off + static_cast<size_t>(pl.T) * p->hidden * 4);
-    L.total = off;
+    L.z_stride = align256(static_cast<size_t>(pl.T) * p->hidden * 4);
+    L.total = off + nz * L.z_stride;
     return L;
   }
   L.off_xm = off;
   off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, pl.K1)) * 2);
   L.off_z1 = off;
-  off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, p->hidden)) * 2);
-  L.total = off;
+  L.z_stride = align256(static_cast<size_t>(vlb::blocked_elems(pl.T, p->hidden)) * 2);
+  L.total = off + nz * L.z_stride;
   return L;
 }
 
@@ -211,7 +214,7 @@ struct BwdLayout {
   int64_t Tk = 0, Op = 0, NL = 0;  // NL: newline slots of the batch
   size_t off_status = 0, off_dst = 0, off_slot = 0, off_nl = 0, off_sep = 0, off_dy = 0,
          off_dyt = 0, off_a1t = 0, off_w2t = 0, off_da1 = 0, off_dz1 = 0, off_dz1t = 0,
-         off_xmt = 0, off_w1t = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
+         off_xmt = 0, off_w1t = 0, off_wmt = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
          off_pnl = 0, off_psep = 0, total = 0;
   std::vector<int> ln_grid;  // unmerge workgroups per chunk of views
   int64_t ln_rows = 0;       // their sum: rows of each LayerNorm partial
@@ -219,7 +222,6 @@ struct BwdLayout {
 
 vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                       int64_t seq_len, BwdLayout *L) {
-  if (proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (p->has_ln && p->C > vlb::kBwdMaxChannels) return VLB_ERR_UNSUPPORTED;
   const int64_t T = pl.T, H = p->hidden, O = p->out_dim, K1 = pl.K1;
   L->Tk = (T + 31) / 32 * 32;
@@ -278,6 +280,8 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
   L->off_dz1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
   L->off_xmt = take(off, static_cast<size_t>(vlb::blocked_elems(K1, Tk)) * 2);
   L->off_w1t = take(off, static_cast<size_t>(vlb::blocked_elems(K1, H)) * 2);
+  if (proj_depth(p) > 2)  // a middle weight transposed, one at a time
+    L->off_wmt = take(off, static_cast<size_t>(vlb::blocked_elems(H, H)) * 2);
   L->off_dxm = take(off, static_cast<size_t>(T) * K1 * 2);
   L->off_pb2 = take(off, static_cast<size_t>(Tk / 32) * O * 4);
   L->off_pb1 = take(off, static_cast<size_t>(Tk / 32) * H * 4);
@@ -450,7 +454,9 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
       gm.act = p->act;
       gm.a_bytes = g2.a_bytes;
       gm.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->hidden, p->hidden) * 2);
-      VLB_LAUNCH(VLB_K_GEMM_MID, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, gm, s));
+      gm.out2 = saved ? saved + sl.off_z(q + 1) : nullptr;
+      VLB_LAUNCH(VLB_K_GEMM_MID, s,
+                 vlb::launch_gemm_bf16(saved ? vlb::kGemmBlockedSave : vlb::kGemmBlocked, gm, s));
       g2.A = gm.out;
     }
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(vlb::kGemmRows, g2, s));
@@ -472,6 +478,7 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
       gm.K = p->hidden;
       gm.ldo = p->hidden;
       gm.act = p->act;
+      gm.out2 = saved ? saved + sl.off_z(q + 1) : nullptr;
       VLB_LAUNCH(VLB_K_GEMM_MID, s, vlb::launch_gemm_f32(false, gm, s));
       g2.A = gm.out;
     }
@@ -725,7 +732,7 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
   Plan pl;
-  if (make_plan(p, b, 0, &pl) != VLB_OK || proj_depth(p) > 2) return 0;
+  if (make_plan(p, b, 0, &pl) != VLB_OK) return 0;
   return saved_layout(p, pl).total;
 }
 
@@ -745,7 +752,6 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
   Plan pl;
   vlb_status st = make_plan(p, b, seq_len, &pl);
   if (st != VLB_OK) return st;
-  if (proj_depth(p) > 2) return VLB_ERR_UNSUPPORTED;
   if (pl.T == 0) return VLB_OK;
   if ((st = check_weights(p, w)) != VLB_OK) return st;
   if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;
@@ -778,6 +784,15 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   const bool ln = p->has_ln != 0, tiled = b->layout == VLB_LAYOUT_TILED_2D;
   if (!g || !w || !mask || !dseq || !saved || !ws) return VLB_ERR_NULL;
   if (!g->d_w1 || !g->d_b1 || !g->d_w2 || !g->d_b2 || !w->w1 || !w->w2) return VLB_ERR_NULL;
+  const int n_mid = proj_depth(p) - 2;
+  if (n_mid > 0) {
+    if (!w->w_mid || !g->d_w_mid || !g->d_b_mid) return VLB_ERR_NULL;
+    for (int q = 0; q < n_mid; ++q) {
+      if (!w->w_mid[q] || !g->d_w_mid[q] || !g->d_b_mid[q]) return VLB_ERR_NULL;
+      if (!aligned16(w->w_mid[q]) || !aligned16(g->d_w_mid[q]) || !aligned16(g->d_b_mid[q]))
+        return VLB_ERR_ALIGN;
+    }
+  }
   if (ln && (!g->d_ln_gamma || !g->d_ln_beta || !w->ln_gamma)) return VLB_ERR_NULL;
   if (ln && pl.T > 0 && !features) return VLB_ERR_NULL;
   if (tiled && (!g->d_newline || !g->d_separator)) return VLB_ERR_NULL;
@@ -795,7 +810,10 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     auto zero = [&](void *q, size_t bytes) {
       return q == nullptr || hipMemsetAsync(q, 0, bytes, s) == hipSuccess;
     };
-    const bool ok = zero(g->d_w1, H * K1 * 4) && zero(g->d_b1, H * 4) &&
+    bool ok = true;
+    for (int q = 0; q < n_mid; ++q)
+      ok = ok && zero(g->d_w_mid[q], H * H * 4) && zero(g->d_b_mid[q], H * 4);
+    ok = ok && zero(g->d_w1, H * K1 * 4) && zero(g->d_b1, H * 4) &&
                     zero(g->d_w2, O * H * 4) && zero(g->d_b2, O * 4) &&
                     (!ln || (zero(g->d_ln_gamma, C * 4) && zero(g->d_ln_beta, C * 4))) &&
                     (!tiled || (zero(g->d_newline, O * 4) && zero(g->d_separator, O * 4))) &&
@@ -848,10 +866,11 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     float *a1 = reinterpret_cast<float *>(w8 + L.off_a1t);
     float *dz = reinterpret_cast<float *>(w8 + L.off_da1);
     float *dxm = reinterpret_cast<float *>(w8 + L.off_dxm);
-    const void *z1 = sv + sl.off_z1, *xm = sv + sl.off_xm;
+    const void *xm = sv + sl.off_xm;
     VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_gather_rows_f32(dseq, dst_row, Ti, Oi, dy, s));
     VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(dy, Ti, Oi, g->d_b2, status, s));
-    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, z1, T * H, a1, nullptr, s));
+    const void *zl = sv + sl.off_z(n_mid);  // the last Linear's input is act(Z_last)
+    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, zl, T * H, a1, nullptr, s));
     auto gemm = [&](const void *A, int64_t sam, int64_t sak, const void *B, int64_t sbn,
                     int64_t sbk, void *out, int64_t M, int64_t N, int64_t K,
                     const int32_t *st_word) {
@@ -876,7 +895,21 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
                vlb::launch_gemm_f32(false, gemm(dy, 1, O, a1, 1, H, g->d_w2, O, H, T, status), s));
     VLB_LAUNCH(VLB_K_BWD_DA1, s,
                vlb::launch_gemm_f32(false, gemm(dy, O, 1, w->w2, 1, H, dz, T, H, O, nullptr), s));
-    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, z1, T * H, nullptr, dz, s));
+    VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, zl, T * H, nullptr, dz, s));
+    // middle Linears, last to first: layer q maps act(Z_{q-1}) to Z_q
+    for (int q = n_mid; q >= 1; --q) {
+      const void *zp = sv + sl.off_z(q - 1);
+      VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(dz, Ti, Hi, g->d_b_mid[q - 1], status, s));
+      VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, zp, T * H, a1, nullptr, s));
+      VLB_LAUNCH(VLB_K_BWD_DW2, s,
+                 vlb::launch_gemm_f32(
+                     false, gemm(dz, 1, H, a1, 1, H, g->d_w_mid[q - 1], H, H, T, status), s));
+      VLB_LAUNCH(VLB_K_BWD_DA1, s,
+                 vlb::launch_gemm_f32(false, gemm(dz, H, 1, w->w_mid[q - 1], 1, H, a1, T, H, H,
+                                                  nullptr), s));
+      VLB_LAUNCH(VLB_K_BWD_PACK, s, vlb::launch_act_f32(p->act, zp, T * H, nullptr, a1, s));
+      std::swap(dz, a1);  // dZ_{q-1}
+    }
     VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(dz, Ti, Hi, g->d_b1, status, s));
     // dW1[h][i] = sum_t dZ1[t][h] Xm[t][i]; dXm[t][i] = sum_h dZ1[t][h] W1[h][i]
     VLB_LAUNCH(VLB_K_BWD_DW1, s,
@@ -927,7 +960,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pb2, Tk / 32, Oi, g->d_b2, status, s));
   // 3. dW2 = dY^T act(Z1)
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
-             vlb::launch_bwd_act_t(p->act, sv + sl.off_z1, Ti, Hi, Tk, w8 + L.off_a1t, s));
+             vlb::launch_bwd_act_t(p->act, sv + sl.off_z(n_mid), Ti, Hi, Tk, w8 + L.off_a1t, s));
   vlb::GemmArgs gw2{};
   gw2.A = w8 + L.off_dyt;
   gw2.B = w8 + L.off_a1t;
@@ -960,8 +993,49 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   VLB_LAUNCH(VLB_K_BWD_DA1, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, ga, s));
   float *pb1 = reinterpret_cast<float *>(w8 + L.off_pb1);
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
-             vlb::launch_bwd_dact(p->act, w8 + L.off_da1, sv + sl.off_z1, Ti, Hi, Tk,
+             vlb::launch_bwd_dact(p->act, w8 + L.off_da1, sv + sl.off_z(n_mid), Ti, Hi, Tk,
                                   w8 + L.off_dz1, w8 + L.off_dz1t, pb1, s));
+  // middle Linears, last to first: layer q maps act(Z_{q-1}) to Z_q
+  for (int q = n_mid; q >= 1; --q) {
+    VLB_LAUNCH(VLB_K_BWD_SUM, s,
+               vlb::launch_colsum(pb1, Tk / 32, Hi, g->d_b_mid[q - 1], status, s));
+    // dW_q = dZ_q^T act(Z_{q-1})
+    VLB_LAUNCH(VLB_K_BWD_PACK, s,
+               vlb::launch_bwd_act_t(p->act, sv + sl.off_z(q - 1), Ti, Hi, Tk, w8 + L.off_a1t, s));
+    vlb::GemmArgs gwm{};
+    gwm.A = w8 + L.off_dz1t;
+    gwm.B = w8 + L.off_a1t;
+    gwm.out = g->d_w_mid[q - 1];
+    gwm.status = status;
+    gwm.M = Hi;
+    gwm.N = Hi;
+    gwm.K = Tk;
+    gwm.ldo = Hi;
+    gwm.act = VLB_ACT_NONE;
+    gwm.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+    gwm.b_bytes = gwm.a_bytes;
+    VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gwm, s));
+    // dA_{q-1} = dZ_q W_q, then dZ_{q-1} = dA_{q-1} * act'(Z_{q-1})
+    const void *wq = w->w_mid[q - 1];
+    VLB_LAUNCH(VLB_K_BWD_PACK, s,
+               p->packed ? vlb::launch_bwd_act_t(VLB_ACT_NONE, wq, Hi, Hi, Hi, w8 + L.off_wmt, s)
+                         : vlb::launch_bwd_weight_t(wq, Hi, Hi, p->C, 1, Hi, w8 + L.off_wmt, s));
+    vlb::GemmArgs gam{};
+    gam.A = w8 + L.off_dz1;
+    gam.B = w8 + L.off_wmt;
+    gam.out = w8 + L.off_da1;
+    gam.M = Ti;
+    gam.N = Hi;
+    gam.K = Hi;
+    gam.ldo = Hi;
+    gam.act = VLB_ACT_NONE;
+    gam.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, H) * 2);
+    gam.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, H) * 2);
+    VLB_LAUNCH(VLB_K_BWD_DA1, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, gam, s));
+    VLB_LAUNCH(VLB_K_BWD_PACK, s,
+               vlb::launch_bwd_dact(p->act, w8 + L.off_da1, sv + sl.off_z(q - 1), Ti, Hi, Tk,
+                                    w8 + L.off_dz1, w8 + L.off_dz1t, pb1, s));
+  }
   VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pb1, Tk / 32, Hi, g->d_b1, status, s));
   // 5. dW1 = dZ1^T Xm (columns in the pages' order)
   VLB_LAUNCH(VLB_K_BWD_PACK, s,

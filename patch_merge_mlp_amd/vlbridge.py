@@ -57,7 +57,8 @@ class vlb_grads(ct.Structure):
     _fields_ = [("d_features", ct.c_void_p), ("d_w1", ct.c_void_p), ("d_b1", ct.c_void_p),
                 ("d_w2", ct.c_void_p), ("d_b2", ct.c_void_p), ("d_ln_gamma", ct.c_void_p),
                 ("d_ln_beta", ct.c_void_p), ("d_newline", ct.c_void_p),
-                ("d_separator", ct.c_void_p)]
+                ("d_separator", ct.c_void_p), ("d_w_mid", ct.POINTER(ct.c_void_p)),
+                ("d_b_mid", ct.POINTER(ct.c_void_p))]
 
 
 class vlb_batch(ct.Structure):
@@ -427,6 +428,8 @@ class Grads:
     d_ln_beta: Optional[torch.Tensor] = None
     d_newline: Optional[torch.Tensor] = None
     d_separator: Optional[torch.Tensor] = None
+    d_w_mid: Sequence[torch.Tensor] = ()   # depth > 2: [hidden][hidden] each
+    d_b_mid: Sequence[torch.Tensor] = ()   # [hidden] each
 
     @staticmethod
     def empty(p: vlb_projector, b: Batch, features=True, device="cuda") -> "Grads":
@@ -442,12 +445,21 @@ class Grads:
         if b.layout == LAYOUT_TILED_2D:
             g.d_newline = torch.empty(p.out_dim, **f32)
             g.d_separator = torch.empty(p.out_dim, **f32)
+        n_mid = _depth(p) - 2
+        g.d_w_mid = [torch.empty(p.hidden, p.hidden, **f32) for _ in range(n_mid)]
+        g.d_b_mid = [torch.empty(p.hidden, **f32) for _ in range(n_mid)]
         return g
 
     def c(self) -> vlb_grads:
-        return vlb_grads(_ptr(self.d_features), _ptr(self.d_w1), _ptr(self.d_b1), _ptr(self.d_w2),
-                         _ptr(self.d_b2), _ptr(self.d_ln_gamma), _ptr(self.d_ln_beta),
-                         _ptr(self.d_newline), _ptr(self.d_separator))
+        wm = (ct.c_void_p * max(len(self.d_w_mid), 1))(*[_ptr(t) for t in self.d_w_mid])
+        bm = (ct.c_void_p * max(len(self.d_b_mid), 1))(*[_ptr(t) for t in self.d_b_mid])
+        c = vlb_grads(_ptr(self.d_features), _ptr(self.d_w1), _ptr(self.d_b1), _ptr(self.d_w2),
+                      _ptr(self.d_b2), _ptr(self.d_ln_gamma), _ptr(self.d_ln_beta),
+                      _ptr(self.d_newline), _ptr(self.d_separator),
+                      ct.cast(wm, ct.POINTER(ct.c_void_p)) if self.d_w_mid else None,
+                      ct.cast(bm, ct.POINTER(ct.c_void_p)) if self.d_b_mid else None)
+        c._keep = (wm, bm)
+        return c
 
 
 def vlb_bridge_backward(p, b: Batch, features, w: Weights, mask, dseq, saved, g: Grads, ws,
@@ -468,6 +480,12 @@ def vlb_bridge_backward(p, b: Batch, features, w: Weights, mask, dseq, saved, g:
                        (g.d_newline, p.out_dim, "d_newline"),
                        (g.d_separator, p.out_dim, "d_separator")):
         _need(t, n, f32, what)
+    n_mid = _depth(p) - 2
+    if len(g.d_w_mid) != n_mid or len(g.d_b_mid) != n_mid or len(w.w_mid) != n_mid:
+        raise ValueError(f"depth {_depth(p)}: {n_mid} middle weights and gradients needed")
+    for q in range(n_mid):
+        _need(g.d_w_mid[q], p.hidden * p.hidden, f32, f"d_w_mid[{q}]")
+        _need(g.d_b_mid[q], p.hidden, f32, f"d_b_mid[{q}]")
     wc = w.c()
     gc = g.c()
     _check(lib().vlb_bridge_backward(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),

@@ -229,6 +229,53 @@ def test_backward_packed_equals_unpacked(wi):
         assert torch.equal(a_.view(view), b_.view(view)), name
 
 
+DEEP_CASES = [(0, 3), (0, 4), (2, 3), (5, 3), (5, 4)]
+
+
+@pytest.mark.parametrize("wi,depth", DEEP_CASES,
+                         ids=[f"{small_workloads()[i].name}-d{d}" for i, d in DEEP_CASES])
+def test_small_backward_deep_vs_oracle(wi, depth):
+    """Depth 3 and 4: every gradient, the middle Linears' included, against the oracle."""
+    w = small_workloads()[wi]
+    t = common.draw(w)
+    dseq = wl.seq_grad(w)
+    mids = wl.mid_weights(w, depth)
+    p, b = common.lib_projector(w), common.lib_batch(w)
+    p.depth = depth
+    wt = v.Weights(*(_dev(t[n]) for n in ("w1", "b1", "w2", "b2", "ln_gamma", "ln_beta")),
+                   w_mid=[_dev(a) for a, _ in mids], b_mid=[_dev(c) for _, c in mids])
+    seq = _dev(t["seq"]).clone()
+    mask = _dev(t["mask"])
+    fws = torch.empty(v.vlb_workspace_bytes(p, b, seq.shape[0]), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(v.vlb_saved_bytes(p, b), dtype=torch.uint8, device="cuda")
+    v.vlb_bridge_fused_train(p, b, _dev(t["features"]), wt, _dev(t["newline"]),
+                             _dev(t["separator"]), mask, seq, saved, fws)
+    g = v.Grads.empty(p, b)
+    bws = torch.empty(v.vlb_backward_workspace_bytes(p, b, seq.shape[0]), dtype=torch.uint8,
+                      device="cuda")
+    v.vlb_bridge_backward(p, b, _dev(t["features"]), wt, mask, _dev(dseq), saved, g, bws)
+    assert v.vlb_check(bws) == v.OK
+    spec = common.oracle_spec(w)
+    spec.depth = depth
+    T = o.total_tokens(spec)
+    st, drows, dnl, dsep = o.scatter_backward(o.assemble(spec), t["mask"].numpy(), dseq, T)
+    assert st == 0
+    ref = o.project_backward_deep(spec, t["features"], t["ln_gamma"], t["ln_beta"], t["w1"],
+                                  t["b1"], [a for a, _ in mids], [c for _, c in mids], t["w2"],
+                                  drows)
+    tol = TOL_F32 if w.dtype == "f32" else TOL_ACT
+    pairs = [("dw1", g.d_w1), ("db1", g.d_b1), ("dw2", g.d_w2), ("dx", g.d_features)]
+    if w.has_ln:
+        pairs += [("dgamma", g.d_ln_gamma), ("dbeta", g.d_ln_beta)]
+    errs = {k: common.rel_frob(_np(x_), ref[k]) for k, x_ in pairs}
+    for q in range(depth - 2):
+        errs[f"dw_mid{q}"] = common.rel_frob(_np(g.d_w_mid[q]), ref["dw_mid"][q])
+        errs[f"db_mid{q}"] = common.rel_frob(_np(g.d_b_mid[q]), ref["db_mid"][q])
+    print(w.name, depth, {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+
+
 def test_backward_deterministic():
     w = small_workloads()[2]
     t = common.draw(w)

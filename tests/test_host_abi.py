@@ -256,7 +256,9 @@ def test_depth_validation():
     n2, n3 = v.vlb_workspace_bytes(_proj(), b, 32), v.vlb_workspace_bytes(p3, b, 32)
     # a second hidden buffer (256 x 128 bf16) and one packed middle weight (256 x 128)
     assert n3 - n2 == 2 * 256 * 128 * 2
-    assert v.vlb_saved_bytes(p3, b) == 0 and v.vlb_backward_workspace_bytes(p3, b, 32) == 0
+    # saved: merged tokens and the pre-activations of Linear1 and the middle Linear
+    assert v.vlb_saved_bytes(p3, b) == 256 * 256 * 2 + 2 * 256 * 128 * 2
+    assert v.vlb_backward_workspace_bytes(p3, b, 32) > v.vlb_backward_workspace_bytes(_proj(), b, 32)
 
     def fused(w, proj=p3):
         return L.vlb_bridge_fused(ct.byref(proj), ct.byref(b.c), FAKE, ct.byref(w), None, None,
@@ -268,7 +270,12 @@ def test_depth_validation():
     assert fused(v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE, arr(FAKE + 2), arr(FAKE))) == v.ERR_ALIGN
     assert L.vlb_bridge_fused_train(ct.byref(p3), ct.byref(b.c), FAKE, ct.byref(w_none), None,
                                     None, FAKE, 32, FAKE, FAKE, 1 << 30, FAKE, 1 << 30,
-                                    None) == v.ERR_UNSUPPORTED
+                                    None) == v.ERR_NULL  # the middle weights are missing
+    g_no_mid = v.vlb_grads(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None, None)
+    w_mid = v.vlb_weights(None, None, FAKE, FAKE, FAKE, FAKE, arr(FAKE), arr(FAKE))
+    assert L.vlb_bridge_backward(ct.byref(p3), ct.byref(b.c), FAKE, ct.byref(w_mid), FAKE, 32,
+                                 FAKE, FAKE, 1 << 30, ct.byref(g_no_mid), FAKE, 1 << 30,
+                                 None) == v.ERR_NULL  # the middle gradients are missing
     assert L.vlb_pack_mid(ct.byref(p3), FAKE, FAKE + 1024, None) == v.ERR_UNSUPPORTED  # overlap
     assert L.vlb_pack_mid(ct.byref(_proj(dtype=v.F32)), FAKE, FAKE + (1 << 26), None) == v.ERR_UNSUPPORTED
     assert L.vlb_pack_mid(ct.byref(p3), None, FAKE, None) == v.ERR_NULL
