@@ -360,17 +360,24 @@ vlb_status run_plan(const vlb_projector *p, const vlb_batch *b, const Plan &pl, 
 vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                        const void *features, const vlb_weights *w, void *out,
                        const int32_t *dst_row, uint8_t *ws, hipStream_t s,
-                       uint8_t *saved = nullptr) {
+                       uint8_t *saved = nullptr, const vlb::ScanJob *scan = nullptr) {
   RowDesc *desc = reinterpret_cast<RowDesc *>(ws + pl.off_desc);
   const void *x = features;
   const SavedLayout sl = saved ? saved_layout(p, pl) : SavedLayout{};
+  if (scan && (p->dtype != VLB_BF16 || b->n_views < 1)) {  // no merge launch to carry it
+    VLB_LAUNCH(VLB_K_SCAN, s,
+               vlb::launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
+                                scan->P, scan->slot_pos, scan->status, scan->direct, s));
+    scan = nullptr;
+  }
   if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
     void *xm = saved ? saved + sl.off_xm : ws + pl.off_xn;
     for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
       VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
                  vlb::launch_merge_blocked(features, view_chunk(p, b, pl, v0), p->C,
                                            p->has_ln ? w->ln_gamma : nullptr,
-                                           p->has_ln ? w->ln_beta : nullptr, p->ln_eps, xm, s));
+                                           p->has_ln ? w->ln_beta : nullptr, p->ln_eps, xm, s,
+                                           v0 == 0 ? scan : nullptr));
     x = xm;
   } else {
     vlb_status st = run_plan(p, b, pl, desc, s);
@@ -532,6 +539,19 @@ vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                                        seq, p->out_dim, s));
   }
   return VLB_OK;
+}
+
+// Plain layout, bf16: the placeholder scan (mask form, writing dst_row) runs
+// as one extra workgroup of the first merge launch instead of a launch of its
+// own; Linear2, which reads dst_row, comes after the merge either way.
+bool scan_in_merge(const vlb_projector *p, const vlb_batch *b) {
+  return p->dtype == VLB_BF16 && b->layout == VLB_LAYOUT_PLAIN;
+}
+
+vlb::ScanJob plain_scan(const Plan &pl, const uint8_t *mask, int64_t seq_len, uint8_t *ws) {
+  return vlb::ScanJob{mask, nullptr, 0, 0, seq_len, pl.P,
+                      reinterpret_cast<int32_t *>(ws + pl.off_dst),
+                      reinterpret_cast<int32_t *>(ws + pl.off_status), true};
 }
 
 vlb_status check_weights(const vlb_projector *p, const vlb_weights *w) {
@@ -724,10 +744,16 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8, s);
-  if (st != VLB_OK) return st;
+  const vlb::ScanJob sj = plain_scan(pl, mask, seq_len, w8);
+  const bool fused_scan = scan_in_merge(p, b);
+  if (!fused_scan) {
+    st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8,
+                   s);
+    if (st != VLB_OK) return st;
+  }
   return run_project(p, b, pl, features, w, seq,
-                     reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s);
+                     reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s, nullptr,
+                     fused_scan ? &sj : nullptr);
 }
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
@@ -765,11 +791,16 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
     return VLB_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8, s);
-  if (st != VLB_OK) return st;
+  const vlb::ScanJob sj = plain_scan(pl, mask, seq_len, w8);
+  const bool fused_scan = scan_in_merge(p, b);
+  if (!fused_scan) {
+    st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8,
+                   s);
+    if (st != VLB_OK) return st;
+  }
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s,
-                     static_cast<uint8_t *>(saved));
+                     static_cast<uint8_t *>(saved), fused_scan ? &sj : nullptr);
 }
 
 vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const void *features,

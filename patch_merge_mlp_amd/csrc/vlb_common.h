@@ -73,10 +73,28 @@ struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t store(float v) { return f2bf(v); }
 };
 
+// Lane exchange inside rows of 16 lanes (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 64 lanes of a wave, the same value in every lane.  The whole
+// wave must be active.  Inside each row of 16 lanes: lane ^ 1, lane ^ 2 (quad
+// permutes), then the mirrored 8-lane halves and the mirrored rows; every
+// lane of a row then holds the row's sum (each step adds the same two values
+// in both partners), and the four row sums are added in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 }  // namespace vlb

@@ -50,13 +50,14 @@ __global__ void k_plan(PlanChunk c, RowDesc *desc) {
 // The placeholders are the nonzero bytes of a mask, or (token-id form) the
 // positions whose id equals the image token; in the id form every other id
 // must lie in [0, vocab).  One workgroup streams the sequence in chunks of
-// 16K positions with a running carry.  status[kCountWord] = number of
+// 16K positions with a running carry; each chunk's positions are gathered in
+// LDS and written out with coalesced stores.  status[kCountWord] = number of
 // placeholders; status[kStatusWord] = 0, VLB_ERR_MASK_COUNT when the count
 // differs from P, else VLB_ERR_TOKEN_ID when a text id is out of range.
 // Plain layout (direct): token row r goes to the r-th placeholder, so the
-// positions are the rows' destinations.  A checking pass runs first and the
-// positions are written to dst_row only when everything is valid; otherwise
-// every dst_row entry (P of them) is -1 and nothing is placed.
+// positions are the rows' destinations.  When the input is invalid, the same
+// workgroup then overwrites every dst_row entry (P of them) with -1, so
+// nothing is placed.
 constexpr int kScanThreads = 1024;
 constexpr int kErrTokenId = 9;  // VLB_ERR_TOKEN_ID
 
@@ -107,42 +108,44 @@ __device__ __forceinline__ int scan_load(const ScanSrc &src, int64_t S, int64_t 
   return cnt;
 }
 
-__device__ __forceinline__ int block_sum(int v, int32_t *shared_slot) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  if (threadIdx.x == 0) *shared_slot = 0;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) atomicAdd(shared_slot, v);
-  __syncthreads();
-  return *shared_slot;
+constexpr int kScanChunk = kScanThreads * 16;  // positions per pass
+
+// Kernel arguments of the scan (on == 0: no scan in this launch).
+struct ScanArgs {
+  ScanSrc src;
+  int64_t S, P;
+  int32_t *slot_pos;
+  int32_t *status;
+  int32_t direct;
+  int32_t on;
+};
+
+ScanArgs scan_args(const ScanJob *j) {
+  ScanArgs a{};
+  if (j) {
+    a.src = ScanSrc{j->mask, j->ids, j->image_id, j->vocab};
+    a.S = j->S;
+    a.P = j->P;
+    a.slot_pos = j->slot_pos;
+    a.status = j->status;
+    a.direct = j->direct ? 1 : 0;
+    a.on = 1;
+  }
+  return a;
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_scan(ScanSrc src, int64_t S, int64_t P,
-                                                      int32_t *slot_pos, int32_t *status,
-                                                      bool direct) {
+// The scan, run by one workgroup of kScanThreads threads; s_pos is LDS for
+// kScanChunk positions.
+__device__ __forceinline__ void scan_body(const ScanArgs &a, int32_t *s_pos) {
   __shared__ int32_t wsum[kScanThreads / 64];
-  __shared__ int32_t s_total, s_bad;
+  __shared__ int32_t s_bad;
+  const ScanSrc &src = a.src;
+  const int64_t S = a.S, P = a.P;
+  int32_t *slot_pos = a.slot_pos;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (direct) {  // checking pass
-    int cnt = 0, bad = 0;
-    for (int64_t base = 0; base < S; base += kScanThreads * 16) {
-      uint8_t b[16];
-      cnt += scan_load(src, S, base + static_cast<int64_t>(tid) * 16, b, bad);
-    }
-    const int total = block_sum(cnt, &s_total);
-    const int nbad = block_sum(bad, &s_bad);
-    if (total != P || nbad != 0) {
-      for (int64_t r = tid; r < P; r += kScanThreads) slot_pos[r] = -1;
-      if (tid == 0) {
-        status[kCountWord] = total;
-        status[kStatusWord] = total != P ? kErrMaskCount : kErrTokenId;
-      }
-      return;
-    }
-  }
-  int32_t carry = 0;
+  int64_t carry = 0;
   int bad = 0;
-  for (int64_t base = 0; base < S; base += kScanThreads * 16) {
+  for (int64_t base = 0; base < S; base += kScanChunk) {
     const int64_t off = base + static_cast<int64_t>(tid) * 16;
     uint8_t b[16];
     const int cnt = scan_load(src, S, off, b, bad);
@@ -164,18 +167,33 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(ScanSrc src, int64_t S, i
       if (lane < kScanThreads / 64) wsum[lane] = w;
     }
     __syncthreads();
-    int32_t pos = carry + (x - cnt) + (wid > 0 ? wsum[wid - 1] : 0);
+    int pos = (x - cnt) + (wid > 0 ? wsum[wid - 1] : 0);  // inside this pass
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (b[i] && pos < P) slot_pos[pos++] = static_cast<int32_t>(off + i);
-    carry += wsum[kScanThreads / 64 - 1];
+      if (b[i]) s_pos[pos++] = static_cast<int32_t>(off + i);
+    const int n = wsum[kScanThreads / 64 - 1];
     __syncthreads();
+    for (int q = tid; q < n; q += kScanThreads)
+      if (carry + q < P) slot_pos[carry + q] = s_pos[q];
+    carry += n;
+    __syncthreads();  // s_pos and wsum are reused by the next pass
   }
-  const int nbad = block_sum(bad, &s_bad);
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (bad) atomicAdd(&s_bad, bad);
+  __syncthreads();
+  const bool fail = carry != P || s_bad != 0;
+  if (fail && a.direct)  // after the barrier: these stores land after the positions above
+    for (int64_t r = tid; r < P; r += kScanThreads) slot_pos[r] = -1;
   if (tid == 0) {
-    status[kCountWord] = carry;
-    status[kStatusWord] = carry != P ? kErrMaskCount : (nbad ? kErrTokenId : 0);
+    a.status[kCountWord] = static_cast<int32_t>(carry);
+    a.status[kStatusWord] = carry != P ? kErrMaskCount : (s_bad ? kErrTokenId : 0);
   }
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
+  __shared__ int32_t s_pos[kScanChunk];  // this pass's placeholder positions, in order
+  scan_body(a, s_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -368,20 +386,30 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
 constexpr int kMbRows = 16;  // rows per item = waves per workgroup
+static_assert(kPlanViews >= 64, "each lane reads one view-table entry");
 
 template <bool LN, int NCH>
 __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *x, PlanChunk c,
                                                                 int C, const uint16_t *gamma,
                                                                 const uint16_t *beta, float eps,
-                                                                uint16_t *out) {
+                                                                uint16_t *out, ScanArgs scan) {
   extern __shared__ uint4 mb_lds[];
+  static_assert(64 * kMbRows == kScanThreads, "the scan workgroup has the merge's shape");
+  int item = blockIdx.x;
+  if (scan.on) {  // workgroup 0 runs the placeholder scan (LDS >= kScanChunk positions)
+    if (item == 0) {
+      scan_body(scan, reinterpret_cast<int32_t *>(mb_lds));
+      return;
+    }
+    --item;
+  }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int k = c.k, kk = k * k, nch = C / 8;
   const int rs = nch + 1;  // LDS row stride in 16-byte chunks (odd: rows hit distinct banks)
   const int64_t KB = static_cast<int64_t>(C) * kk / 32;
   const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
   const int g0 = t_begin / kMbRows;
-  const int grp = g0 + blockIdx.x / kk, p = blockIdx.x % kk;
+  const int grp = g0 + item / kk, p = item % kk;
   const int dy = p / k, dx = p - dy * k;
 
   // This wave's row and its pixel (wave-uniform): the view is the number of
@@ -394,10 +422,14 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
   bool inside = false;
   int64_t off = 0;
   if (m >= t_begin && m < t_end) {
+    // Every lane loads (the tables hold kPlanViews = 64 entries), so the four
+    // loads go out together; entries past n are then masked.
     const bool have = lane < c.n;
-    const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
-    const int32_t l_pix0 = have ? c.pix0[lane] : 0;
-    const int32_t l_gh = have ? c.gh[lane] : 0, l_gw = have ? c.gw[lane] : 1;
+    const int32_t e_tok0 = c.tok0[lane], e_pix0 = c.pix0[lane];
+    const int32_t e_gh = c.gh[lane], e_gw = c.gw[lane];
+    const int32_t l_tok0 = have ? e_tok0 : INT32_MAX;
+    const int32_t l_pix0 = have ? e_pix0 : 0;
+    const int32_t l_gh = have ? e_gh : 0, l_gw = have ? e_gw : 1;
     const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
     const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
     const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
@@ -605,9 +637,8 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s) {
 hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
                        int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
                        hipStream_t s) {
-  const ScanSrc src{mask, ids, image_id, vocab};
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, src, S, P, slot_pos, status,
-                     direct);
+  const ScanJob j{mask, ids, image_id, vocab, S, P, slot_pos, status, direct};
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, scan_args(&j));
   return hipGetLastError();
 }
 
@@ -691,10 +722,16 @@ int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 
 
 template <bool LN, int NCH>
 static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void *gamma,
-                            const void *beta, float eps, void *out, hipStream_t s) {
+                            const void *beta, float eps, void *out, hipStream_t s,
+                            const ScanArgs &scan) {
   const int64_t items =
-      ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k;
-  const size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16;  // <= 131 KiB
+      ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k +
+      (scan.on ? 1 : 0);
+  size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16;  // <= 131 KiB
+  // The scan workgroup stages kScanChunk positions in the same LDS.  Two
+  // 1024-thread workgroups per CU is the thread limit anyway, so 64 KiB each
+  // costs the merge no occupancy.
+  if (scan.on) lds = std::max(lds, kScanChunk * sizeof(int32_t));
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&k_merge_blocked<LN, NCH>),
@@ -704,29 +741,35 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
   hipLaunchKernelGGL((k_merge_blocked<LN, NCH>), dim3(static_cast<uint32_t>(items)),
                      dim3(64 * kMbRows), lds, s, static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
-                     eps, static_cast<uint16_t *>(out));
+                     eps, static_cast<uint16_t *>(out), scan);
   return hipGetLastError();
 }
 
 template <bool LN>
 static hipError_t mb_dispatch(const void *x, const PlanChunk &c, int C, const void *gamma,
-                              const void *beta, float eps, void *out, hipStream_t s) {
+                              const void *beta, float eps, void *out, hipStream_t s,
+                              const ScanArgs &sa) {
   switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane per pixel
-    case 1: return mb_launch<LN, 1>(x, c, C, gamma, beta, eps, out, s);
-    case 2: return mb_launch<LN, 2>(x, c, C, gamma, beta, eps, out, s);
-    case 3: return mb_launch<LN, 3>(x, c, C, gamma, beta, eps, out, s);
-    case 4: return mb_launch<LN, 4>(x, c, C, gamma, beta, eps, out, s);
-    case 5: case 6: return mb_launch<LN, 6>(x, c, C, gamma, beta, eps, out, s);
-    case 7: case 8: return mb_launch<LN, kLnChunks>(x, c, C, gamma, beta, eps, out, s);
+    case 1: return mb_launch<LN, 1>(x, c, C, gamma, beta, eps, out, s, sa);
+    case 2: return mb_launch<LN, 2>(x, c, C, gamma, beta, eps, out, s, sa);
+    case 3: return mb_launch<LN, 3>(x, c, C, gamma, beta, eps, out, s, sa);
+    case 4: return mb_launch<LN, 4>(x, c, C, gamma, beta, eps, out, s, sa);
+    case 5: case 6: return mb_launch<LN, 6>(x, c, C, gamma, beta, eps, out, s, sa);
+    case 7: case 8: return mb_launch<LN, kLnChunks>(x, c, C, gamma, beta, eps, out, s, sa);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const void *gamma,
-                                const void *beta, float eps, void *out, hipStream_t s) {
-  if (c.n <= 0 || c.tok0[c.n] <= c.tok0[0]) return hipSuccess;
-  return gamma ? mb_dispatch<true>(x, c, C, gamma, beta, eps, out, s)
-               : mb_dispatch<false>(x, c, C, nullptr, nullptr, 0.f, out, s);
+                                const void *beta, float eps, void *out, hipStream_t s,
+                                const ScanJob *scan) {
+  if (c.n <= 0 || c.tok0[c.n] <= c.tok0[0])  // no rows: the scan (if any) runs on its own
+    return scan ? launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
+                              scan->P, scan->slot_pos, scan->status, scan->direct, s)
+                : hipSuccess;
+  const ScanArgs sa = scan_args(scan);
+  return gamma ? mb_dispatch<true>(x, c, C, gamma, beta, eps, out, s, sa)
+               : mb_dispatch<false>(x, c, C, nullptr, nullptr, 0.f, out, s, sa);
 }
 
 hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const int32_t *dst_row,

@@ -125,6 +125,19 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
 hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
                        int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
                        hipStream_t s);
+// The same scan, carried by a merge launch (launch_merge_blocked) as one extra
+// workgroup that runs beside the merge: it reads neither the features nor
+// the merged rows, so the two need no ordering.
+struct ScanJob {
+  const uint8_t *mask;
+  const int32_t *ids;
+  int32_t image_id;
+  int64_t vocab;
+  int64_t S, P;
+  int32_t *slot_pos;
+  int32_t *status;
+  bool direct;
+};
 // seq[s] = embed[ids[s]] where ids[s] != image_id (nothing if the scan failed).
 hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
                              const void *embed, int D, const int32_t *status, void *seq,
@@ -160,8 +173,10 @@ hipError_t launch_pack(const void *w, int64_t R, int64_t K, int C, int k, void *
 // of Linear1 for the token rows of one chunk of views, K position-major, zeros
 // for cells past the grid; LayerNorm over C applied on the way when gamma is
 // non-null (C <= layernorm_max_channels).
+// With scan non-null, the launch also runs that placeholder scan (workgroup 0).
 hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const void *gamma,
-                                const void *beta, float eps, void *out, hipStream_t s);
+                                const void *beta, float eps, void *out, hipStream_t s,
+                                const ScanJob *scan = nullptr);
 
 // bf16 MFMA GEMMs on blocked operands (K a multiple of 32), epilogue by mode
 // (GemmMode).  A null bias counts as zero.

@@ -92,6 +92,11 @@ def small_workloads():
         wl.Workload("small-f32-3x3", 16, "f32", C=24, k=3, hidden=72, out_dim=40, seq_len=300,
                     grids=[(20, 17), (6, 6)], views_per_image=[2]),
         wl.config(0),
+        # a sequence longer than one pass of the placeholder scan (16K positions),
+        # the first image's span straddling the boundary between two passes
+        wl.Workload("small-2x2-long-seq", 17, "bf16", C=64, k=2, hidden=128, out_dim=64,
+                    seq_len=40000, grids=[(34, 34), (20, 17)], views_per_image=[1, 1],
+                    fixed_offset=16200),
     ]
 
 
@@ -300,7 +305,7 @@ def test_scatter_tokens_exact(w):
 # ---- error path and degenerate cases -------------------------------------------------
 
 @pytest.mark.parametrize("delta", [+1, -1])
-@pytest.mark.parametrize("idx", [0, 2])
+@pytest.mark.parametrize("idx", [0, 2, 7])
 def test_mask_count_mismatch_writes_nothing(delta, idx):
     w = small_workloads()[idx]
     t = common.draw(w)
