@@ -56,6 +56,10 @@ def parse():
                     help="skip sampling the GFX clock under load (amd-smi, after the timed region)")
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing the training step (forward + backward)")
+    ap.add_argument("--no-depth", action="store_true",
+                    help="skip timing the depth-3 projector (one middle Linear hidden -> hidden)")
+    ap.add_argument("--no-embed", action="store_true",
+                    help="skip timing the call that also writes the text rows from an embedding table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -230,9 +234,94 @@ def main():
     if not args.no_train and w.dtype == "bf16":
         out["train_step"] = train_step(v, torch, wl, w, p, b, t, d, T, K1, args.steps)
 
+    if not args.no_depth and w.dtype == "bf16":
+        out["depth3_step"] = depth3_step(v, torch, wl, w, b, t, d, T, args.steps)
+
+    if not args.no_embed and w.dtype == "bf16":
+        out["embed_step"] = embed_step(v, torch, wl, w, b, t, d, br, args.steps)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, T, args.cpu_seconds)
     print(json.dumps(out))
+
+
+def depth3_step(v, torch, wl, w, b, t, d, T, steps):
+    """The same fused call with a depth-3 projector (Linear1 + act, one middle
+    Linear(hidden -> hidden) + act, Linear2), seeded middle weights, packed
+    once.  Wall time per call over `steps` calls, and the middle GEMM's rate
+    (2 * T * hidden * hidden FLOP) from a pass with its launches timed."""
+    (wm, bm), = wl.mid_weights(w, 3)
+    p3 = v.projector(v.BF16, w.C, w.k, w.hidden, w.out_dim, has_ln=w.has_ln, ln_eps=w.ln_eps,
+                     depth=3)
+    weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
+                        d(t["ln_beta"]), w_mid=[d(wm)], b_mid=[d(bm)])
+    br3 = v.Bridge(p3, weights)
+    feats, mask = d(t["features"]), d(t["mask"])
+    nl, sep, seq = d(t["newline"]), d(t["separator"]), d(t["seq"])
+    ws = br3.workspace(b, seq.shape[0])
+
+    def one():
+        v.vlb_bridge_fused(br3.p, b, feats, br3.w, nl, sep, mask, seq, ws)
+
+    for _ in range(10):
+        one()
+    torch.cuda.synchronize()
+    assert v.vlb_check(ws) == v.OK
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    v.vlb_prof_enable(1 << v.K_GEMM_MID)
+    for _ in range(max(3, steps // 4)):
+        one()
+    torch.cuda.synchronize()
+    v.vlb_prof_enable(False)
+    n, ms = v.vlb_prof_read(v.K_GEMM_MID)
+    us = 1000.0 * ms / n
+    return {"ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(T / sec, 1),
+            "gemm_mid": {"mean_us": round(us, 2),
+                         "TFLOP/s": round(2.0 * T * w.hidden * w.hidden / (us * 1e-6) / 1e12, 1)}}
+
+
+def embed_step(v, torch, wl, w, b, t, d, br, steps):
+    """vlb_bridge_embed: the same bridge, with every text row of the sequence
+    written from a seeded embedding table of 102,400 rows (token-id scan, then
+    k_embed_rows).  Wall time per call over `steps` calls, and the embedding
+    kernel's rate in algorithmic bytes: each text row read from the table once
+    and written once, plus the 4-byte id of every position."""
+    ids, table = wl.token_inputs(w, t["mask"])
+    n_text = int((ids != wl.IMAGE_TOKEN_ID).sum())
+    ids, table = d(ids), d(table)
+    seq = torch.empty(w.seq_len, w.out_dim, dtype=w.torch_dtype, device="cuda")
+    ws = br.workspace(b, w.seq_len)
+    feats, nl, sep = d(t["features"]), d(t["newline"]), d(t["separator"])
+
+    def one():
+        v.vlb_bridge_embed(br.p, b, feats, br.w, nl, sep, ids, wl.IMAGE_TOKEN_ID, table, seq, ws)
+
+    for _ in range(10):
+        one()
+    torch.cuda.synchronize()
+    assert v.vlb_check(ws) == v.OK
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    v.vlb_prof_enable(1 << v.K_EMBED)
+    reps = max(3, steps // 4)
+    for _ in range(reps):
+        one()
+    torch.cuda.synchronize()
+    v.vlb_prof_enable(False)
+    n, ms = v.vlb_prof_read(v.K_EMBED)
+    us = 1000.0 * ms / n
+    nbytes = 2 * n_text * w.out_dim * 2 + 4 * w.seq_len
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"ms_per_step": round(sec * 1e3, 4), "text_rows": n_text,
+            "embed_kernel": {"mean_us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+                             "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
 def hbm_kernels(v, torch, w, p, b, t, d, T, K1, steps):
