@@ -1161,15 +1161,29 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
   if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
+  const int32_t *status = reinterpret_cast<const int32_t *>(w8 + pl.off_status);
+  const int32_t *dst_row = reinterpret_cast<const int32_t *>(w8 + pl.off_dst);
+  if (pl.T > 0 && scan_in_merge(p, b)) {
+    // The token-id scan rides in the first merge launch; the text rows, which
+    // wait for its verdict, follow the projector (they touch other rows).
+    const vlb::ScanJob sj{nullptr, ids, image_token_id, vocab, seq_len, pl.P,
+                          reinterpret_cast<int32_t *>(w8 + pl.off_dst),
+                          reinterpret_cast<int32_t *>(w8 + pl.off_status), true};
+    st = run_project(p, b, pl, features, w, seq, dst_row, w8, s, nullptr, &sj);
+    if (st != VLB_OK) return st;
+    VLB_LAUNCH(VLB_K_EMBED, s,
+               vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
+                                      status, seq, s));
+    return VLB_OK;
+  }
   st = run_place(p, b, pl, newline, separator, PlaceSrc{nullptr, ids, image_token_id, vocab},
                  seq_len, seq, w8, s);
   if (st != VLB_OK) return st;
   VLB_LAUNCH(VLB_K_EMBED, s,
              vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
-                                    reinterpret_cast<const int32_t *>(w8 + pl.off_status), seq, s));
+                                    status, seq, s));
   if (pl.T == 0) return VLB_OK;
-  return run_project(p, b, pl, features, w, seq,
-                     reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s);
+  return run_project(p, b, pl, features, w, seq, dst_row, w8, s);
 }
 
 vlb_status vlb_check(void *ws, void *stream) {

@@ -204,17 +204,34 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_embed_rows(const int32_t *ids, int64_t S, int32_t image_id,
                                                     const T *embed, int D, const int32_t *status,
                                                     T *seq) {
+  constexpr int V = 8;  // 16-byte chunks per lane per pass: up to 8 KiB of a row in flight
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  if (status[kStatusWord] != 0) return;
+  const int32_t st = status[kStatusWord];  // read together with the first id
   const int n16 = D * static_cast<int>(sizeof(T)) / 16;
   for (int64_t s = wave; s < S; s += nwaves) {
     const int32_t id = ids[s];
+    if (st != 0) return;
     if (id == image_id) continue;
     const uint4 *from = reinterpret_cast<const uint4 *>(embed + static_cast<int64_t>(id) * D);
     uint4 *to = reinterpret_cast<uint4 *>(seq + s * D);
-    for (int q = lane; q < n16; q += 64) to[q] = from[q];
+    // All of a pass's loads are issued before its stores (the table and the
+    // sequence may not be assumed apart, so a plain copy loop would wait on
+    // every load in turn).
+    for (int base = 0; base < n16; base += 64 * V) {
+      uint4 v[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int q = base + lane + 64 * i;
+        v[i] = q < n16 ? from[q] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int q = base + lane + 64 * i;
+        if (q < n16) to[q] = v[i];
+      }
+    }
   }
 }
 

@@ -36,7 +36,7 @@ def oracle_embed(w, t, ids, table, rows64):
                            table, w.out_dim)
 
 
-@pytest.mark.parametrize("w", [small_workloads()[i] for i in (0, 2, 5)], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [small_workloads()[i] for i in (0, 2, 5, 7)], ids=lambda w: w.name)
 def test_small_embed_vs_oracle(w):
     t = common.draw(w)
     ids, table = wl.token_inputs(w, t["mask"])
@@ -81,7 +81,7 @@ def test_full_embed(i):
                        seq.cpu()[torch.from_numpy(img)].view(torch.int16))
 
 
-@pytest.mark.parametrize("wi", [0, 2])
+@pytest.mark.parametrize("wi", [0, 2, 7])
 @pytest.mark.parametrize("fault", ["id_past_vocab", "negative_id", "extra_placeholder",
                                    "missing_placeholder"])
 def test_embed_errors_write_nothing(wi, fault):
