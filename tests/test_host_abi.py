@@ -299,3 +299,32 @@ def test_status_strings():
     for s in range(10):
         assert v.status_str(s)
     assert "placeholder" in v.status_str(v.ERR_MASK_COUNT)
+
+
+def test_operand_size_limits():
+    """Every GEMM operand is addressed with 32-bit byte offsets (buffer loads), so each must
+    stay under 2 GiB: the features, the packed W1, the hidden activation and the sequence.
+    One past each limit is rejected before any launch, the largest size inside is accepted."""
+    L = v.lib()
+
+    def tokens(p, b):
+        return L.vlb_num_tokens(ct.byref(p), ct.byref(b.c))
+
+    # features: 1024 x 910 x 1152 bf16 = 2,146,959,360 B; one more column passes 2^31 - 1
+    p = v.projector(v.BF16, 1152, 2, 4608, 4096)
+    assert tokens(p, v.Batch([(1024, 910)], [1])) == 512 * 455
+    assert tokens(p, v.Batch([(1024, 911)], [1])) == -v.ERR_SHAPE
+    # packed W1 (256-row blocks): 58112 x 18432 bf16 fits, 58368 x 18432 does not
+    small = v.Batch([(6, 6)], [1])
+    assert tokens(v.projector(v.BF16, 2048, 3, 58112, 64), small) == 4
+    assert tokens(v.projector(v.BF16, 2048, 3, 58368, 64), small) == -v.ERR_SHAPE
+    # hidden activation, tile-blocked in 256-row blocks: 32512 x 32768 bf16 fits; 32513 rows
+    # round up to 32768 rows = 2^31 bytes
+    ph = v.projector(v.BF16, 64, 1, 32768, 64)
+    assert tokens(ph, v.Batch([(32512, 1)], [1])) == 32512
+    assert tokens(ph, v.Batch([(32513, 1)], [1])) == -v.ERR_SHAPE
+    # sequence: seq_len x out_dim elements
+    ps = v.projector(v.BF16, 64, 2, 128, 4096)
+    b = v.Batch([(4, 4)], [1])
+    assert L.vlb_workspace_bytes(ct.byref(ps), ct.byref(b.c), (1 << 19) - 1) > 0
+    assert L.vlb_workspace_bytes(ct.byref(ps), ct.byref(b.c), 1 << 19) == 0
