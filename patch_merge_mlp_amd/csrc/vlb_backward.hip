@@ -246,112 +246,145 @@ __global__ __launch_bounds__(64 * kUmWaves) void k_bwd_unmerge(const uint16_t *d
                                                      float eps, uint16_t *dx, float *part_g,
                                                      float *part_b, const int32_t *status) {
   if (status[kStatusWord] != 0) return;
+  extern __shared__ float red[];  // [2][C] workgroup sums, then (LN) gamma as bf16 [C]
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int k = c.k, kk = k * k, nch = C / 8;
   const int64_t K1 = static_cast<int64_t>(C) * kk;
   const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
   const int64_t items = static_cast<int64_t>(t_end - t_begin) * kk;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kUmWaves;
+  // View table: every lane loads its entry (64 of them), entries past n masked.
   const bool have = lane < c.n;
-  const int32_t l_tok0 = have ? c.tok0[lane] : INT32_MAX;
-  const int32_t l_pix0 = have ? c.pix0[lane] : 0;
-  const int32_t l_gh = have ? c.gh[lane] : 0, l_gw = have ? c.gw[lane] : 1;
-  float ag[NCH][8], ab[NCH][8];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
-  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kUmWaves + wid; it < items; it += nw) {
+  const int32_t e_tok0 = c.tok0[lane], e_pix0 = c.pix0[lane];
+  const int32_t e_gh = c.gh[lane], e_gw = c.gw[lane];
+  const int32_t l_tok0 = have ? e_tok0 : INT32_MAX;
+  const int32_t l_pix0 = have ? e_pix0 : 0;
+  const int32_t l_gh = have ? e_gh : 0, l_gw = have ? e_gw : 1;
+  const uint4 *s_gamma = reinterpret_cast<const uint4 *>(red + 2 * C);
+  if (LN) {  // gamma is read for every pixel: once into LDS
+    for (int q = threadIdx.x; q < nch; q += 64 * kUmWaves)
+      reinterpret_cast<uint4 *>(red + 2 * C)[q] = reinterpret_cast<const uint4 *>(gamma)[q];
+    __syncthreads();
+  }
+  // Item it = (token row, k x k position): its dXm segment and its pixel, or
+  // false for a padded cell (no pixel).  Wave-uniform.
+  auto locate = [&](int64_t it, int64_t &drow, int64_t &pix) -> bool {
     const int m = t_begin + static_cast<int>(it / kk), p = static_cast<int>(it % kk);
     const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
     const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
     const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
     const int wp = (gw + k - 1) / k, t = m - tok0;
     const int y = (t / wp) * k + p / k, xx = (t % wp) * k + p % k;
-    if (y >= gh || xx >= gw) continue;  // padding: no pixel
-    const int64_t pix = pix0 + static_cast<int64_t>(y) * gw + xx;
-    const uint4 *dsrc = reinterpret_cast<const uint4 *>(dxm + m * K1 + static_cast<int64_t>(p) * C);
-    uint4 dv[NCH];
+    if (y >= gh || xx >= gw) return false;
+    pix = pix0 + static_cast<int64_t>(y) * gw + xx;
+    drow = m * K1 + static_cast<int64_t>(p) * C;
+    return true;
+  };
+  auto fetch = [&](int64_t drow, int64_t pix, uint4 (&dv)[NCH], uint4 (&xv)[NCH]) {
+    const uint4 *dsrc = reinterpret_cast<const uint4 *>(dxm + drow);
+    const uint4 *xs = reinterpret_cast<const uint4 *>(x + pix * C);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
       dv[i] = q < nch ? dsrc[q] : make_uint4(0, 0, 0, 0);
+      if (LN) xv[i] = q < nch ? xs[q] : make_uint4(0, 0, 0, 0);
     }
-    uint4 *ddst = dx ? reinterpret_cast<uint4 *>(dx + pix * C) : nullptr;
-    if (!LN) {
-      if (ddst) {
+  };
+  float ag[NCH][8], ab[NCH][8];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[i][e] = ab[i][e] = 0.f;
+  int64_t it = static_cast<int64_t>(blockIdx.x) * kUmWaves + wid;
+  int64_t drow = 0, pix = 0;
+  bool ok = it < items && locate(it, drow, pix);
+  uint4 dv[NCH] = {}, xv[NCH] = {};
+  if (ok) fetch(drow, pix, dv, xv);
+  for (; it < items; it += nw) {
+    // The next item's loads go out before this item's arithmetic.
+    int64_t drow2 = 0, pix2 = 0;
+    const bool ok2 = it + nw < items && locate(it + nw, drow2, pix2);
+    uint4 dv2[NCH] = {}, xv2[NCH] = {};
+    if (ok2) fetch(drow2, pix2, dv2, xv2);
+    if (ok) {
+      uint4 *ddst = dx ? reinterpret_cast<uint4 *>(dx + pix * C) : nullptr;
+      if (!LN) {
+        if (ddst) {
+#pragma unroll
+          for (int i = 0; i < NCH; ++i)
+            if (lane + 64 * i < nch) ddst[lane + 64 * i] = dv[i];
+        }
+      } else {
+        float xf[NCH][8];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const uint16_t *e = reinterpret_cast<const uint16_t *>(&xv[i]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            xf[i][j] = bf2f(e[j]);
+            sum += xf[i][j];
+          }
+        }
+        const float mean = wave_sum(sum) / C;
+        float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i)
-          if (lane + 64 * i < nch) ddst[lane + 64 * i] = dv[i];
-      }
-      continue;
-    }
-    const uint4 *xs = reinterpret_cast<const uint4 *>(x + pix * C);
-    const uint4 *g4 = reinterpret_cast<const uint4 *>(gamma);
-    float xf[NCH][8];
-    float sum = 0.f;
+          if (lane + 64 * i < nch)
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int q = lane + 64 * i;
-      const uint4 xv = q < nch ? xs[q] : make_uint4(0, 0, 0, 0);
-      const uint16_t *e = reinterpret_cast<const uint16_t *>(&xv);
+            for (int j = 0; j < 8; ++j) {
+              const float d = xf[i][j] - mean;
+              ss += d * d;
+            }
+        const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+        float sg = 0.f, sgx = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xf[i][j] = bf2f(e[j]);
-        sum += xf[i][j];
-      }
-    }
-    const float mean = wave_sum(sum) / C;
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      if (lane + 64 * i < nch)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float d = xf[i][j] - mean;
-          ss += d * d;
-        }
-    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
-    float sg = 0.f, sgx = 0.f;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int q = lane + 64 * i;
-      const uint4 gq = q < nch ? g4[q] : make_uint4(0, 0, 0, 0);
-      const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
-      const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float xh = (xf[i][j] - mean) * rstd, dn = bf2f(de[j]);
-        const float gv = bf2f(ge[j]) * dn;
-        xf[i][j] = xh;
-        ag[i][j] += dn * xh;
-        ab[i][j] += dn;
-        sg += gv;
-        sgx += gv * xh;
-      }
-    }
-    const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
-    if (ddst) {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int q = lane + 64 * i;
-        if (q < nch) {
-          const uint4 gq = g4[q];
+        for (int i = 0; i < NCH; ++i) {
+          const int q = lane + 64 * i;
+          const uint4 gq = q < nch ? s_gamma[q] : make_uint4(0, 0, 0, 0);
           const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
           const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
-          uint4 o;
-          uint16_t *oe = reinterpret_cast<uint16_t *>(&o);
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            oe[j] = f2bf(rstd * (bf2f(ge[j]) * bf2f(de[j]) - mg - xf[i][j] * mgx));
-          ddst[q] = o;
+          for (int j = 0; j < 8; ++j) {
+            const float xh = (xf[i][j] - mean) * rstd, dn = bf2f(de[j]);
+            const float gv = bf2f(ge[j]) * dn;
+            xf[i][j] = xh;
+            ag[i][j] += dn * xh;
+            ab[i][j] += dn;
+            sg += gv;
+            sgx += gv * xh;
+          }
+        }
+        const float mg = wave_sum(sg) / C, mgx = wave_sum(sgx) / C;
+        if (ddst) {
+#pragma unroll
+          for (int i = 0; i < NCH; ++i) {
+            const int q = lane + 64 * i;
+            if (q < nch) {
+              const uint4 gq = s_gamma[q];
+              const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+              const uint16_t *de = reinterpret_cast<const uint16_t *>(&dv[i]);
+              uint4 o;
+              uint16_t *oe = reinterpret_cast<uint16_t *>(&o);
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                oe[j] = f2bf(rstd * (bf2f(ge[j]) * bf2f(de[j]) - mg - xf[i][j] * mgx));
+              ddst[q] = o;
+            }
+          }
         }
       }
+    }
+    ok = ok2;
+    pix = pix2;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      dv[i] = dv2[i];
+      xv[i] = xv2[i];
     }
   }
   if (!LN) return;
   // Workgroup sum of the waves' accumulators, wave 0 first, then one row each.
-  extern __shared__ float red[];  // [2][C]
   for (int w = 0; w < kUmWaves; ++w) {
     if (wid == w) {
 #pragma unroll
@@ -575,7 +608,8 @@ template <bool LN, int NCH>
 hipError_t unmerge_launch(const void *dxm, const void *x, const PlanChunk &c, int C,
                           const void *gamma, float eps, void *dx, float *part_g, float *part_b,
                           const int32_t *status, int grid, hipStream_t s) {
-  const size_t lds = LN ? static_cast<size_t>(2) * C * sizeof(float) : 0;
+  // [2][C] fp32 sums, then gamma (bf16) staged once per workgroup
+  const size_t lds = LN ? static_cast<size_t>(2) * C * sizeof(float) + C * sizeof(uint16_t) : 0;
   hipLaunchKernelGGL((k_bwd_unmerge<LN, NCH>), dim3(grid), dim3(64 * kUmWaves), lds, s,
                      static_cast<const uint16_t *>(dxm), static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), eps, static_cast<uint16_t *>(dx),
