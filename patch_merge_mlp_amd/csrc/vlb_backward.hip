@@ -83,6 +83,26 @@ __device__ __forceinline__ void store_column(const uint16_t *tile, int r, uint16
   for (int q = 0; q < 4; ++q) d[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
+// Columns [0, ncol) of the staged 32 x 256 tile when they map to consecutive
+// rows of the transposed operand (the tile's first column a multiple of 256,
+// its first row of 32): their pieces are one contiguous run from dst, 64
+// bytes each.  Lane -> (column, 16-byte chunk), so each store instruction of a
+// wave writes 16 whole pieces, one contiguous KiB.
+__device__ __forceinline__ void store_columns(const uint16_t *tile, int ncol, uint16_t *dst) {
+#pragma unroll
+  for (int u = threadIdx.x; u < kTC * 4; u += 256) {
+    const int col = u >> 2, ch = u & 3;
+    if (col >= ncol) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ch * 8 + 2 * i;
+      w[i] = tile[r * kPitch + col] | (static_cast<uint32_t>(tile[(r + 1) * kPitch + col]) << 16);
+    }
+    *reinterpret_cast<uint4 *>(dst + col * 32 + ch * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 __device__ __forceinline__ float col_sum(const uint16_t *tile, int r) {
   float s = 0.f;
 #pragma unroll
@@ -118,11 +138,9 @@ __global__ __launch_bounds__(256) void k_bwd_gather_dy(const uint16_t *G, const 
       *reinterpret_cast<uint4 *>(dy + blk(t0 + row, o, Op)) =
           *reinterpret_cast<const uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8);
   }
+  store_columns(tile, min(kTC, O - n0), dyt + blk(n0, t0, Tk));
   const int o = n0 + tid;
-  if (o < O) {
-    store_column(tile, tid, dyt + blk(o, t0, Tk));
-    part[static_cast<int64_t>(blockIdx.x) * O + o] = col_sum(tile, tid);
-  }
+  if (o < O) part[static_cast<int64_t>(blockIdx.x) * O + o] = col_sum(tile, tid);
 }
 
 // act(Z1)^T: Z1 tile-blocked [T][H] (rows past T unused) -> [H][Tk].
@@ -145,8 +163,7 @@ __global__ __launch_bounds__(256) void k_bwd_act_t(const uint16_t *z1, int32_t T
     *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
   }
   __syncthreads();
-  const int h = n0 + tid;
-  if (h < H) store_column(tile, tid, a1t + blk(h, t0, Tk));
+  store_columns(tile, min(kTC, H - n0), a1t + blk(n0, t0, Tk));
 }
 
 // dZ1 = dA1 * act'(Z1) (both tile-blocked [T][H]): dZ1 tile-blocked, its
@@ -177,11 +194,9 @@ __global__ __launch_bounds__(256) void k_bwd_dact(const uint16_t *da1, const uin
     *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
   }
   __syncthreads();
+  store_columns(tile, min(kTC, H - n0), dz1t + blk(n0, t0, Tk));
   const int h = n0 + tid;
-  if (h < H) {
-    store_column(tile, tid, dz1t + blk(h, t0, Tk));
-    part[static_cast<int64_t>(blockIdx.x) * H + h] = col_sum(tile, tid);
-  }
+  if (h < H) part[static_cast<int64_t>(blockIdx.x) * H + h] = col_sum(tile, tid);
 }
 
 // Xm (tile-blocked [T][K1], K position-major j = p*C + c) -> its transpose
@@ -221,11 +236,12 @@ __global__ __launch_bounds__(256) void k_bwd_weight_t(const uint16_t *w, int32_t
     *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
   }
   __syncthreads();
-  const int i = n0 + tid;
-  if (i < Cs) {
-    const int64_t orow = kk > 1 ? static_cast<int64_t>(i % kk) * C + i / kk : i;
-    store_column(tile, tid, out + blk(orow, r0, Rk));
+  if (kk == 1) {
+    store_columns(tile, min(kTC, Cs - n0), out + blk(n0, r0, Rk));
+    return;
   }
+  const int i = n0 + tid;
+  if (i < Cs) store_column(tile, tid, out + blk(static_cast<int64_t>(i % kk) * C + i / kk, r0, Rk));
 }
 
 // Feature gradient of the pixels of one chunk of views (see PlanChunk), one
