@@ -455,12 +455,25 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
     inside = y < gh && xx < gw;
     off = static_cast<int64_t>(pix0 + y * gw + xx) * C;
   }
+  // gamma and beta (LN) are staged once per workgroup in LDS after the rows.
+  // Their loads go out before the pixel's, so waiting for them (loads return
+  // in order) never waits on the pixel.
+  uint4 *s_gb = mb_lds + kMbRows * rs;  // [2 * nch]: gamma chunks, then beta's
+  const int tid = threadIdx.x;
+  uint4 gb = make_uint4(0, 0, 0, 0);
+  if (LN && tid < 2 * nch)
+    gb = tid < nch ? reinterpret_cast<const uint4 *>(gamma)[tid]
+                   : reinterpret_cast<const uint4 *>(beta)[tid - nch];
   uint4 v[NCH];
   const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int q = lane + 64 * i;
     v[i] = (inside && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
+  }
+  if (LN) {
+    if (tid < 2 * nch) s_gb[tid] = gb;
+    __syncthreads();
   }
   if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
     float sum = 0.f;
@@ -488,8 +501,8 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
       if (q < nch) {
-        const uint4 gq = reinterpret_cast<const uint4 *>(gamma)[q];
-        const uint4 bq = reinterpret_cast<const uint4 *>(beta)[q];
+        const uint4 gq = s_gb[q];
+        const uint4 bq = s_gb[nch + q];
         uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
         const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
         const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
@@ -744,7 +757,8 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
   const int64_t items =
       ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k +
       (scan.on ? 1 : 0);
-  size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16;  // <= 131 KiB
+  // staged rows, then (LN) gamma and beta: <= 145 KiB (C <= 4096)
+  size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16 + (LN ? 2 * (C / 8) * 16 : 0);
   // The scan workgroup stages kScanChunk positions in the same LDS.  Two
   // 1024-thread workgroups per CU is the thread limit anyway, so 64 KiB each
   // costs the merge no occupancy.
