@@ -73,6 +73,14 @@ struct Elem<uint16_t> {
   static __device__ __forceinline__ uint16_t store(float v) { return f2bf(v); }
 };
 
+// 16-byte store marked non-temporal (streamed: the data is not read again
+// soon, so it need not stay in the caches).
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+}
+
 // Lane exchange inside rows of 16 lanes (DPP control CTRL).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

@@ -531,7 +531,9 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
 // ---------------------------------------------------------------------------
 // Standalone scatter: row r of rows[T][D] -> seq[dst_row[r]] (skipped if < 0).
 // One wave per row; the row's data (up to 8 KiB at a time) is loaded together
-// with its destination, so the loads never wait on the index.
+// with its destination, so the loads never wait on the index.  The sequence
+// rows are written with non-temporal stores (74.6% of 8 TB/s against 67.5%
+// with ordinary stores on workload 1).
 template <typename T>
 __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, int D,
                                                  const int32_t *dst_row, T *seq) {
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, i
 #pragma unroll
         for (int i = 0; i < V; ++i) {
           const int q = base + lane + 64 * i;
-          if (q < n16) to[q] = v[i];
+          if (q < n16) store_nt(to + q, v[i]);
         }
       }
     }
@@ -596,9 +598,10 @@ __global__ __launch_bounds__(256) void k_merge(const T *x, const RowDesc *desc, 
     // The unit's run in the merged row: elements (U*u + i) * KK + p, i.e.
     // KK*U values = KK dwords starting at dword u*KK.
     uint32_t *dst = m32 + (r * C * KK) / U + static_cast<int64_t>(u) * KK;
+    uint32_t o[KK];
     if constexpr (U == 1) {
 #pragma unroll
-      for (int p = 0; p < KK; ++p) dst[p] = cell[p];
+      for (int p = 0; p < KK; ++p) o[p] = cell[p];
     } else {
       // run element e = i*KK + p holds channel half i of cell p; dword j packs
       // elements 2j (low half) and 2j+1.
@@ -607,7 +610,21 @@ __global__ __launch_bounds__(256) void k_merge(const T *x, const RowDesc *desc, 
         return i == 0 ? (cell[p] & 0xffffu) : (cell[p] >> 16);
       };
 #pragma unroll
-      for (int j = 0; j < KK; ++j) dst[j] = elem(2 * j) | (elem(2 * j + 1) << 16);
+      for (int j = 0; j < KK; ++j) o[j] = elem(2 * j) | (elem(2 * j + 1) << 16);
+    }
+    // The run as one vector store where it can be (consecutive threads then
+    // write one contiguous span per instruction): 16 bytes for KK = 4 (the
+    // run starts on a 16-byte boundary: C*KK/U is a multiple of 4), three
+    // 12-byte stores for KK = 9.
+    if constexpr (KK == 4) {
+      *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    } else if constexpr (KK == 9) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<uint3 *>(dst + 3 * q) = make_uint3(o[3 * q], o[3 * q + 1], o[3 * q + 2]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KK; ++j) dst[j] = o[j];
     }
   }
 }
