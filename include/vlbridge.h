@@ -335,13 +335,15 @@ int64_t vlb_expand_prompt(const int32_t *ids, int64_t n_ids, int32_t image_token
 /* Kernel ids for the timing records. */
 enum {
   VLB_K_PLAN = 0,    /* per-token gather descriptors */
-  VLB_K_SCAN = 1,    /* mask prefix sum -> slot positions */
+  VLB_K_SCAN = 1,    /* mask / token-id prefix sum -> slot positions (on the plain bf16
+                        path of the fused calls it runs inside the merge launch, timed
+                        as VLB_K_LN or VLB_K_MERGE) */
   VLB_K_PLACE = 2,   /* assembly map, newline/separator rows */
-  VLB_K_LN = 3,      /* LayerNorm */
-  VLB_K_GEMM1 = 4,   /* merge-gather + Linear1 + bias + activation */
+  VLB_K_LN = 3,      /* LayerNorm (bf16: fused with the merge into Linear1's operand) */
+  VLB_K_GEMM1 = 4,   /* Linear1 + bias + activation (fp32: gathering the merge itself) */
   VLB_K_GEMM2 = 5,   /* Linear2 + bias + row/slot store */
   VLB_K_SCATTER = 6, /* standalone row scatter */
-  VLB_K_MERGE = 7,   /* standalone space-to-depth */
+  VLB_K_MERGE = 7,   /* space-to-depth (bf16 without LayerNorm: into Linear1's operand) */
   VLB_K_PACK = 8,    /* weight re-layout */
   VLB_K_EMBED = 9,   /* token-embedding rows */
   VLB_K_BWD_PACK = 10,    /* backward: gradient gather and operand transposes */
