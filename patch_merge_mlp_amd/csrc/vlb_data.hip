@@ -403,6 +403,11 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
 constexpr int kMbRows = 16;  // rows per item = waves per workgroup
+// LayerNorm's gamma and beta are staged in fp32 when the LDS has room next to
+// the staged rows: up to NCH = 6 16-byte chunks per lane (C <= 3072).  At
+// NCH = 8 (C <= 4096) rows take 16 * 513 * 16 B, and fp32 gamma and beta
+// would pass the 160 KiB of a workgroup.
+constexpr bool mb_gb32(int nch_per_lane) { return nch_per_lane <= 6; }
 static_assert(kPlanViews >= 64, "each lane reads one view-table entry");
 
 template <bool LN, int NCH>
@@ -455,10 +460,14 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
     inside = y < gh && xx < gw;
     off = static_cast<int64_t>(pix0 + y * gw + xx) * C;
   }
-  // gamma and beta (LN) are staged once per workgroup in LDS after the rows.
-  // Their loads go out before the pixel's, so waiting for them (loads return
-  // in order) never waits on the pixel.
-  uint4 *s_gb = mb_lds + kMbRows * rs;  // [2 * nch]: gamma chunks, then beta's
+  // gamma and beta (LN) are staged once per workgroup in LDS after the rows,
+  // widened to fp32 (no conversion per element later) while that fits: up to
+  // 6 chunks per lane (C <= 3072); for C up to 4096 they stay bf16.  Their
+  // loads go out before the pixel's, so waiting for them (loads return in
+  // order) never waits on the pixel.
+  constexpr bool GB32 = mb_gb32(NCH);
+  float4 *s_gb = reinterpret_cast<float4 *>(mb_lds + kMbRows * rs);  // GB32: [2][C] fp32
+  uint4 *s_gb16 = mb_lds + kMbRows * rs;                              // else [2][C] bf16
   const int tid = threadIdx.x;
   uint4 gb = make_uint4(0, 0, 0, 0);
   if (LN && tid < 2 * nch)
@@ -472,7 +481,16 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
     v[i] = (inside && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
   }
   if (LN) {
-    if (tid < 2 * nch) s_gb[tid] = gb;
+    if (tid < 2 * nch) {  // chunk tid: 8 values (GB32: two float4 entries)
+      if (GB32) {
+        s_gb[2 * tid] = make_float4(bf2f(gb.x & 0xffff), bf2f(gb.x >> 16), bf2f(gb.y & 0xffff),
+                                    bf2f(gb.y >> 16));
+        s_gb[2 * tid + 1] = make_float4(bf2f(gb.z & 0xffff), bf2f(gb.z >> 16),
+                                        bf2f(gb.w & 0xffff), bf2f(gb.w >> 16));
+      } else {
+        s_gb16[tid] = gb;
+      }
+    }
     __syncthreads();
   }
   if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
@@ -501,14 +519,27 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
       if (q < nch) {
-        const uint4 gq = s_gb[q];
-        const uint4 bq = s_gb[nch + q];
-        uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
-        const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
-        const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
+        float gf[8], bfv[8];
+        if (GB32) {
+          const float4 g0 = s_gb[2 * q], g1 = s_gb[2 * q + 1];
+          const float4 b0 = s_gb[2 * (nch + q)], b1 = s_gb[2 * (nch + q) + 1];
+          gf[0] = g0.x; gf[1] = g0.y; gf[2] = g0.z; gf[3] = g0.w;
+          gf[4] = g1.x; gf[5] = g1.y; gf[6] = g1.z; gf[7] = g1.w;
+          bfv[0] = b0.x; bfv[1] = b0.y; bfv[2] = b0.z; bfv[3] = b0.w;
+          bfv[4] = b1.x; bfv[5] = b1.y; bfv[6] = b1.z; bfv[7] = b1.w;
+        } else {
+          const uint4 gq = s_gb16[q], bq = s_gb16[nch + q];
+          const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+          const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          e[j] = f2bf((bf2f(e[j]) - mean) * rstd * bf2f(ge[j]) + bf2f(be[j]));
+          for (int j = 0; j < 8; ++j) {
+            gf[j] = bf2f(ge[j]);
+            bfv[j] = bf2f(be[j]);
+          }
+        }
+        uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = f2bf(fmaf((bf2f(e[j]) - mean) * rstd, gf[j], bfv[j]));
       }
     }
   }
@@ -774,8 +805,10 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
   const int64_t items =
       ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k +
       (scan.on ? 1 : 0);
-  // staged rows, then (LN) gamma and beta: <= 145 KiB (C <= 4096)
-  size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16 + (LN ? 2 * (C / 8) * 16 : 0);
+  // staged rows, then (LN) gamma and beta (fp32 or bf16, see mb_gb32):
+  // <= 160 KiB for every C the dispatch takes
+  size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16 +
+               (LN ? static_cast<size_t>(2) * C * (mb_gb32(NCH) ? 4 : 2) : 0);
   // The scan workgroup stages kScanChunk positions in the same LDS.  Two
   // 1024-thread workgroups per CU is the thread limit anyway, so 64 KiB each
   // costs the merge no occupancy.

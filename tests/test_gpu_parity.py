@@ -120,6 +120,25 @@ def test_small_fused_vs_oracle(w):
             assert np.array_equal(out.float().numpy()[pos], torch.from_numpy(ref[pos]).float().numpy())
 
 
+@pytest.mark.parametrize("C", [2048, 3072, 4096])
+def test_wide_channel_layernorm(C):
+    """LayerNorm + merge at wide channel counts: 4, 6 and 8 16-byte chunks per
+    lane, the last keeping gamma and beta in bf16 in LDS (fp32 would not fit
+    beside the staged rows).  Whole output against the oracle."""
+    w = wl.Workload(f"wide-ln-{C}", 20 + C // 1024, "bf16", C=C, k=2, hidden=256, out_dim=128,
+                    seq_len=96, grids=[(9, 10), (4, 4)], views_per_image=[1, 1], has_ln=True)
+    t = common.draw(w)
+    rows = o.project_rows(common.oracle_spec(w), t["features"], t["ln_gamma"], t["ln_beta"],
+                          t["w1"], t["b1"], t["w2"], t["b2"])
+    ref = expected_seq(w, t, rows)
+    st, out = run_fused(w, t)
+    assert st == v.OK
+    check_text_rows(t, out)
+    errs = per_image_errors(w, t, out.double().numpy(), ref)
+    print(w.name, "max rel err", max(errs))
+    assert max(errs) <= TOL["bf16"], errs
+
+
 @pytest.mark.parametrize("act", [v.GELU_TANH, v.ACT_NONE])
 def test_small_activations(act):
     w = small_workloads()[0]
