@@ -120,6 +120,30 @@ def test_small_fused_vs_oracle(w):
             assert np.array_equal(out.float().numpy()[pos], torch.from_numpy(ref[pos]).float().numpy())
 
 
+def test_many_views_plain():
+    """70 views (more than the 64 of one merge launch), plain layout, LayerNorm: the
+    merge runs as two launches and the placeholder scan rides in the first.  Whole
+    output against the oracle, text rows untouched; then a count mismatch on the same
+    batch writes nothing."""
+    grids = [(4 + i % 3, 6 - i % 2) for i in range(70)]
+    w = wl.Workload("many-views", 31, "bf16", C=64, k=2, hidden=128, out_dim=64, seq_len=900,
+                    grids=grids, views_per_image=[1] * 70, has_ln=True)
+    t = common.draw(w)
+    rows = o.project_rows(common.oracle_spec(w), t["features"], t["ln_gamma"], t["ln_beta"],
+                          t["w1"], t["b1"], t["w2"], t["b2"])
+    ref = expected_seq(w, t, rows)
+    st, out = run_fused(w, t)
+    assert st == v.OK
+    check_text_rows(t, out)
+    errs = per_image_errors(w, t, out.double().numpy(), ref)
+    assert max(errs) <= TOL["bf16"], errs
+    mask = t["mask"].clone()
+    mask[int(np.flatnonzero(mask.numpy())[-1])] = 0
+    st, out = run_fused(w, dict(t, mask=mask))
+    assert st == v.ERR_MASK_COUNT
+    assert torch.equal(out.view(torch.int16), t["seq"].view(torch.int16))
+
+
 @pytest.mark.parametrize("C", [2048, 3072, 4096])
 def test_wide_channel_layernorm(C):
     """LayerNorm + merge at wide channel counts: 4, 6 and 8 16-byte chunks per
