@@ -466,6 +466,7 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
                  vlb::launch_gemm_bf16(saved ? vlb::kGemmBlockedSave : vlb::kGemmBlocked, gm, s));
       g2.A = gm.out;
     }
+    g2.stream_out = 1;  // the sequence rows are not read back here
     VLB_LAUNCH(VLB_K_GEMM2, s, vlb::launch_gemm_bf16(vlb::kGemmRows, g2, s));
   } else {
     g1.B = w->w1;

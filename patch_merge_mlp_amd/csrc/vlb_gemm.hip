@@ -180,7 +180,7 @@ __device__ __forceinline__ void write_blocked(uint8_t *const (&bufs)[4], const G
 }
 
 // Whole rows of a staged tile with 16-byte stores to row s_dst[r] (skipped
-// when negative).
+// when negative), non-temporal when g.stream_out is set.
 template <int BMT>
 __device__ __forceinline__ void write_rows(uint8_t *const (&bufs)[4], const GemmArgs &g, int n0,
                                            const int32_t *s_dst) {
@@ -199,7 +199,11 @@ __device__ __forceinline__ void write_rows(uint8_t *const (&bufs)[4], const Gemm
       if (dst < 0 || col >= g.N) continue;
       const uint4 v = *reinterpret_cast<const uint4 *>(pick(bufs, bi) + row * G::ROWB +
                                                        ((chunk ^ (row & (G::CCH - 1))) << 4));
-      *reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col) = v;
+      uint4 *p = reinterpret_cast<uint4 *>(out + static_cast<int64_t>(dst) * g.ldo + col);
+      if (g.stream_out)
+        store_nt(p, v);
+      else
+        *p = v;
     }
   }
 }

@@ -74,6 +74,9 @@ struct GemmArgs {
   // fp32 path, not gather mode: element (m, k) of A at A[m * sa_m + k * sa_k] and
   // (n, k) of B at B[n * sb_n + k * sb_k]; sa_k == 0 (sb_k == 0) means row-major.
   int64_t sa_m, sa_k, sb_n, sb_k;
+  // kGemmRows: 1 = rows written with non-temporal stores (rows nobody reads
+  // back soon: Linear2's rows into the sequence), 0 = ordinary stores.
+  int32_t stream_out;
 };
 
 // Epilogues of the bf16 GEMM.
