@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void k_bwd_gather_dy(const uint16_t *G, const 
     uint4 v = make_uint4(0, 0, 0, 0);
     if (t < T && o < O) {
       const int32_t d = dst_row[t];
-      if (d >= 0) v = *reinterpret_cast<const uint4 *>(G + static_cast<int64_t>(d) * O + o);
+      if (d >= 0) v = load_nt(reinterpret_cast<const uint4 *>(G + static_cast<int64_t>(d) * O + o));
     }
     *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
   }
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_bwd_xm_t(const uint16_t *xm, int32_t T,
     const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
     const int t = t0 + row, j = n0 + sl * 32 + c4 * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < T && j < K1) v = *reinterpret_cast<const uint4 *>(xm + blk(t, j, K1));
+    if (t < T && j < K1) v = load_nt(reinterpret_cast<const uint4 *>(xm + blk(t, j, K1)));
     *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
   }
   __syncthreads();
@@ -302,8 +302,8 @@ __global__ __launch_bounds__(64 * kUmWaves) void k_bwd_unmerge(const uint16_t *d
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
-      dv[i] = q < nch ? dsrc[q] : make_uint4(0, 0, 0, 0);
-      if (LN) xv[i] = q < nch ? xs[q] : make_uint4(0, 0, 0, 0);
+      dv[i] = q < nch ? load_nt(dsrc + q) : make_uint4(0, 0, 0, 0);  // both read once
+      if (LN) xv[i] = q < nch ? load_nt(xs + q) : make_uint4(0, 0, 0, 0);
     }
   };
   float ag[NCH][8], ab[NCH][8];

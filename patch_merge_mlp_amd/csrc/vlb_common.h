@@ -81,6 +81,14 @@ __device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
   __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
 }
 
+// 16-byte load marked non-temporal (data read once: it need not displace
+// what the caches hold for the kernels that follow).
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // Lane exchange inside rows of 16 lanes (DPP control CTRL).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

@@ -473,12 +473,15 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
   if (LN && tid < 2 * nch)
     gb = tid < nch ? reinterpret_cast<const uint4 *>(gamma)[tid]
                    : reinterpret_cast<const uint4 *>(beta)[tid - nch];
+  // The features are read once: non-temporal loads keep them from displacing
+  // the GEMMs' operands in the caches (interleaved A/B, workload 1: step
+  // 0.5291 -> 0.5232 ms, the GEMMs faster, this kernel 0.6 us slower).
   uint4 v[NCH];
   const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int q = lane + 64 * i;
-    v[i] = (inside && q < nch) ? src[q] : make_uint4(0, 0, 0, 0);
+    v[i] = (inside && q < nch) ? load_nt(src + q) : make_uint4(0, 0, 0, 0);
   }
   if (LN) {
     if (tid < 2 * nch) {  // chunk tid: 8 values (GB32: two float4 entries)
