@@ -402,6 +402,11 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // loads row r's pixel (NCH 16-byte chunks per lane), normalises it and stages
 // it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
+// Rows of at least this many bytes are read by the standalone scatter with
+// non-temporal loads (they no longer fit the 256 MiB Infinity Cache beside
+// the sequence; see k_scatter).
+constexpr int64_t kScatterStreamBytes = int64_t{96} << 20;
+
 constexpr int kMbRows = 16;  // rows per item = waves per workgroup
 // LayerNorm's gamma and beta are staged in fp32 when the LDS has room next to
 // the staged rows: up to NCH = 6 16-byte chunks per lane (C <= 3072).  At
@@ -567,8 +572,11 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
 // One wave per row; the row's data (up to 8 KiB at a time) is loaded together
 // with its destination, so the loads never wait on the index.  The sequence
 // rows are written with non-temporal stores (74.6% of 8 TB/s against 67.5%
-// with ordinary stores on workload 1).
-template <typename T>
+// with ordinary stores on workload 1).  NTL: the rows are also read with
+// non-temporal loads, which pays once they no longer fit the Infinity Cache
+// beside the rest (112 MB of rows: 51.4 -> 42.8 us; 197 MB: 90.5 -> 75.1 us)
+// and costs while they do (67 MB: 22.5 -> 25.5 us).
+template <typename T, bool NTL>
 __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, int D,
                                                  const int32_t *dst_row, T *seq) {
   constexpr int V = 8;  // 16-byte chunks per lane per pass
@@ -584,7 +592,7 @@ __global__ __launch_bounds__(256) void k_scatter(const T *rows, int64_t Trows, i
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const int q = base + lane + 64 * i;
-        v[i] = q < n16 ? from[q] : make_uint4(0, 0, 0, 0);
+        v[i] = q < n16 ? (NTL ? load_nt(from + q) : from[q]) : make_uint4(0, 0, 0, 0);
       }
       if (d >= 0) {
         uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(d) * D);
@@ -860,13 +868,23 @@ hipError_t launch_scatter(int dtype, const void *rows, int64_t T, int D, const i
                           void *seq, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int grid = grid_for(T, 4, 8192);
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_scatter<float>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const float *>(rows), T, D, dst_row, static_cast<float *>(seq));
-  else
-    hipLaunchKernelGGL(k_scatter<uint16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(rows), T, D, dst_row,
-                       static_cast<uint16_t *>(seq));
+  const int64_t row_bytes = static_cast<int64_t>(D) * (dtype == 0 ? 4 : 2);
+  const bool ntl = T * row_bytes >= kScatterStreamBytes;
+  if (dtype == 0) {
+    const float *r = static_cast<const float *>(rows);
+    float *q = static_cast<float *>(seq);
+    if (ntl)
+      hipLaunchKernelGGL((k_scatter<float, true>), dim3(grid), dim3(256), 0, s, r, T, D, dst_row, q);
+    else
+      hipLaunchKernelGGL((k_scatter<float, false>), dim3(grid), dim3(256), 0, s, r, T, D, dst_row, q);
+  } else {
+    const uint16_t *r = static_cast<const uint16_t *>(rows);
+    uint16_t *q = static_cast<uint16_t *>(seq);
+    if (ntl)
+      hipLaunchKernelGGL((k_scatter<uint16_t, true>), dim3(grid), dim3(256), 0, s, r, T, D, dst_row, q);
+    else
+      hipLaunchKernelGGL((k_scatter<uint16_t, false>), dim3(grid), dim3(256), 0, s, r, T, D, dst_row, q);
+  }
   return hipGetLastError();
 }
 
