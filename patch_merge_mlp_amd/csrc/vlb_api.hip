@@ -357,13 +357,25 @@ vlb_status run_plan(const vlb_projector *p, const vlb_batch *b, const Plan &pl, 
 // otherwise row m goes to out + dst_row[m] * out_dim.
 // saved (bf16 training forward, else null): the merged tokens and Linear1's
 // pre-activation are kept there (saved_layout).
+// The tiled slot map (defined below), and what it needs when run_project
+// launches it after the merge.
+vlb_status run_place_tiled(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
+                           const void *newline, const void *separator, void *seq, uint8_t *ws,
+                           hipStream_t s);
+struct TiledPlace {
+  const void *newline, *separator;
+  void *seq;
+};
+
 vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                        const void *features, const vlb_weights *w, void *out,
                        const int32_t *dst_row, uint8_t *ws, hipStream_t s,
-                       uint8_t *saved = nullptr, const vlb::ScanJob *scan = nullptr) {
+                       uint8_t *saved = nullptr, const vlb::ScanJob *scan = nullptr,
+                       const TiledPlace *place = nullptr) {
   RowDesc *desc = reinterpret_cast<RowDesc *>(ws + pl.off_desc);
   const void *x = features;
   const SavedLayout sl = saved ? saved_layout(p, pl) : SavedLayout{};
+  vlb_status st;
   if (scan && (p->dtype != VLB_BF16 || b->n_views < 1)) {  // no merge launch to carry it
     VLB_LAUNCH(VLB_K_SCAN, s,
                vlb::launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
@@ -380,8 +392,7 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
                                            v0 == 0 ? scan : nullptr));
     x = xm;
   } else {
-    vlb_status st = run_plan(p, b, pl, desc, s);
-    if (st != VLB_OK) return st;
+    if ((st = run_plan(p, b, pl, desc, s)) != VLB_OK) return st;
     if (p->has_ln) {
       void *xn = ws + pl.off_xn;
       VLB_LAUNCH(VLB_K_LN, s,
@@ -393,6 +404,11 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
       VLB_LAUNCH(VLB_K_MERGE, s,
                  vlb::launch_merge(p->dtype, x, desc, pl.T, p->C, p->k, saved + sl.off_xm, s));
   }
+  // Tiled: the slot map follows the merge that carried the scan (Linear2 is
+  // the first reader of dst_row).
+  if (place && (st = run_place_tiled(p, b, pl, place->newline, place->separator, place->seq, ws,
+                                     s)) != VLB_OK)
+    return st;
   void *hbuf = ws + pl.off_h;
   vlb::GemmArgs g1{};
   g1.A = x;
@@ -506,21 +522,14 @@ struct PlaceSrc {
   int64_t vocab;
 };
 
-vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
-                     const void *newline, const void *separator, const PlaceSrc &src,
-                     int64_t seq_len, void *seq, uint8_t *ws, hipStream_t s) {
+// Slot map of a tiled batch from the scan's slot positions: dst_row of every
+// token row; newline and separator rows written to their slots.
+vlb_status run_place_tiled(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
+                           const void *newline, const void *separator, void *seq, uint8_t *ws,
+                           hipStream_t s) {
   int32_t *status = reinterpret_cast<int32_t *>(ws + pl.off_status);
   int32_t *slot_pos = reinterpret_cast<int32_t *>(ws + pl.off_slot);
   int32_t *dst_row = reinterpret_cast<int32_t *>(ws + pl.off_dst);
-  if (b->layout == VLB_LAYOUT_PLAIN) {  // token row r -> the r-th placeholder: the scan writes dst_row
-    VLB_LAUNCH(VLB_K_SCAN, s,
-               vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, dst_row,
-                                status, true, s));
-    return VLB_OK;
-  }
-  VLB_LAUNCH(VLB_K_SCAN, s,
-             vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, slot_pos,
-                              status, false, s));
   for (int i0 = 0; i0 < b->n_images; i0 += vlb::kPlaceImages) {
     PlaceChunk c{};
     c.n = std::min(vlb::kPlaceImages, b->n_images - i0);
@@ -542,17 +551,39 @@ vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
   return VLB_OK;
 }
 
-// Plain layout, bf16: the placeholder scan (mask form, writing dst_row) runs
-// as one extra workgroup of the first merge launch instead of a launch of its
-// own; Linear2, which reads dst_row, comes after the merge either way.
-bool scan_in_merge(const vlb_projector *p, const vlb_batch *b) {
-  return p->dtype == VLB_BF16 && b->layout == VLB_LAYOUT_PLAIN;
+vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
+                     const void *newline, const void *separator, const PlaceSrc &src,
+                     int64_t seq_len, void *seq, uint8_t *ws, hipStream_t s) {
+  int32_t *status = reinterpret_cast<int32_t *>(ws + pl.off_status);
+  int32_t *slot_pos = reinterpret_cast<int32_t *>(ws + pl.off_slot);
+  int32_t *dst_row = reinterpret_cast<int32_t *>(ws + pl.off_dst);
+  if (b->layout == VLB_LAYOUT_PLAIN) {  // token row r -> the r-th placeholder: the scan writes dst_row
+    VLB_LAUNCH(VLB_K_SCAN, s,
+               vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, dst_row,
+                                status, true, s));
+    return VLB_OK;
+  }
+  VLB_LAUNCH(VLB_K_SCAN, s,
+             vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, slot_pos,
+                              status, false, s));
+  return run_place_tiled(p, b, pl, newline, separator, seq, ws, s);
 }
 
-vlb::ScanJob plain_scan(const Plan &pl, const uint8_t *mask, int64_t seq_len, uint8_t *ws) {
-  return vlb::ScanJob{mask, nullptr, 0, 0, seq_len, pl.P,
-                      reinterpret_cast<int32_t *>(ws + pl.off_dst),
-                      reinterpret_cast<int32_t *>(ws + pl.off_status), true};
+// bf16: the placeholder scan runs as one extra workgroup of the first merge
+// launch instead of a launch of its own.  In the plain layout it writes
+// dst_row itself; in the tiled layout it writes the slot positions, and the
+// slot map runs after the merge (TiledPlace).  Linear2, the first reader of
+// dst_row, comes after both either way.
+bool scan_in_merge(const vlb_projector *p) { return p->dtype == VLB_BF16; }
+
+// The scan of the mask (ids == nullptr) or of the token ids.
+vlb::ScanJob merge_scan(const vlb_batch *b, const Plan &pl, const uint8_t *mask,
+                        const int32_t *ids, int32_t image_id, int64_t vocab, int64_t seq_len,
+                        uint8_t *ws) {
+  const bool plain = b->layout == VLB_LAYOUT_PLAIN;
+  return vlb::ScanJob{mask, ids, image_id, vocab, seq_len, pl.P,
+                      reinterpret_cast<int32_t *>(ws + (plain ? pl.off_dst : pl.off_slot)),
+                      reinterpret_cast<int32_t *>(ws + pl.off_status), plain};
 }
 
 vlb_status check_weights(const vlb_projector *p, const vlb_weights *w) {
@@ -745,8 +776,9 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const vlb::ScanJob sj = plain_scan(pl, mask, seq_len, w8);
-  const bool fused_scan = scan_in_merge(p, b);
+  const vlb::ScanJob sj = merge_scan(b, pl, mask, nullptr, 0, 0, seq_len, w8);
+  const TiledPlace tp{newline, separator, seq};
+  const bool fused_scan = scan_in_merge(p), tiled = b->layout == VLB_LAYOUT_TILED_2D;
   if (!fused_scan) {
     st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8,
                    s);
@@ -754,7 +786,7 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   }
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s, nullptr,
-                     fused_scan ? &sj : nullptr);
+                     fused_scan ? &sj : nullptr, fused_scan && tiled ? &tp : nullptr);
 }
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
@@ -792,8 +824,9 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
     return VLB_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *w8 = static_cast<uint8_t *>(ws);
-  const vlb::ScanJob sj = plain_scan(pl, mask, seq_len, w8);
-  const bool fused_scan = scan_in_merge(p, b);
+  const vlb::ScanJob sj = merge_scan(b, pl, mask, nullptr, 0, 0, seq_len, w8);
+  const TiledPlace tp{newline, separator, seq};
+  const bool fused_scan = scan_in_merge(p), tiled = b->layout == VLB_LAYOUT_TILED_2D;
   if (!fused_scan) {
     st = run_place(p, b, pl, newline, separator, PlaceSrc{mask, nullptr, 0, 0}, seq_len, seq, w8,
                    s);
@@ -801,7 +834,8 @@ vlb_status vlb_bridge_fused_train(const vlb_projector *p, const vlb_batch *b,
   }
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s,
-                     static_cast<uint8_t *>(saved), fused_scan ? &sj : nullptr);
+                     static_cast<uint8_t *>(saved), fused_scan ? &sj : nullptr,
+                     fused_scan && tiled ? &tp : nullptr);
 }
 
 vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const void *features,
@@ -1164,13 +1198,14 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   const int32_t *status = reinterpret_cast<const int32_t *>(w8 + pl.off_status);
   const int32_t *dst_row = reinterpret_cast<const int32_t *>(w8 + pl.off_dst);
-  if (pl.T > 0 && scan_in_merge(p, b)) {
-    // The token-id scan rides in the first merge launch; the text rows, which
-    // wait for its verdict, follow the projector (they touch other rows).
-    const vlb::ScanJob sj{nullptr, ids, image_token_id, vocab, seq_len, pl.P,
-                          reinterpret_cast<int32_t *>(w8 + pl.off_dst),
-                          reinterpret_cast<int32_t *>(w8 + pl.off_status), true};
-    st = run_project(p, b, pl, features, w, seq, dst_row, w8, s, nullptr, &sj);
+  if (pl.T > 0 && scan_in_merge(p)) {
+    // The token-id scan rides in the first merge launch (the tiled slot map
+    // follows the merge); the text rows, which wait for its verdict, follow
+    // the projector (they touch other rows).
+    const vlb::ScanJob sj = merge_scan(b, pl, nullptr, ids, image_token_id, vocab, seq_len, w8);
+    const TiledPlace tp{newline, separator, seq};
+    st = run_project(p, b, pl, features, w, seq, dst_row, w8, s, nullptr, &sj,
+                     b->layout == VLB_LAYOUT_TILED_2D ? &tp : nullptr);
     if (st != VLB_OK) return st;
     VLB_LAUNCH(VLB_K_EMBED, s,
                vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
