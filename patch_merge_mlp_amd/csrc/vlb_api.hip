@@ -353,10 +353,6 @@ vlb_status run_plan(const vlb_projector *p, const vlb_batch *b, const Plan &pl, 
   return VLB_OK;
 }
 
-// LN (optional) + both GEMMs.  dst_row == nullptr: rows[m] = projected row m;
-// otherwise row m goes to out + dst_row[m] * out_dim.
-// saved (bf16 training forward, else null): the merged tokens and Linear1's
-// pre-activation are kept there (saved_layout).
 // The tiled slot map (defined below), and what it needs when run_project
 // launches it after the merge.
 vlb_status run_place_tiled(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
@@ -367,6 +363,13 @@ struct TiledPlace {
   void *seq;
 };
 
+// LN (optional) + merge + the Linears.  dst_row == nullptr: rows[m] =
+// projected row m; otherwise row m goes to out + dst_row[m] * out_dim.
+// saved (training forward, else null): the merged tokens and the
+// pre-activation of every Linear but the last are kept there (saved_layout).
+// scan (bf16 fused calls, else null): the placeholder scan, carried by the
+// first merge launch.  place (tiled layout with scan, else null): the slot
+// map, launched after the merge and before the Linears.
 vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                        const void *features, const vlb_weights *w, void *out,
                        const int32_t *dst_row, uint8_t *ws, hipStream_t s,
@@ -511,8 +514,6 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   return VLB_OK;
 }
 
-// Prefix sum of the mask and the assembly map -> dst_row; newline / separator
-// rows are written to their slots here.
 // Where the placeholders are: a uint8 mask, or token ids equal to image_id
 // (the other ids must lie in [0, vocab)).
 struct PlaceSrc {
@@ -551,6 +552,8 @@ vlb_status run_place_tiled(const vlb_projector *p, const vlb_batch *b, const Pla
   return VLB_OK;
 }
 
+// Prefix sum of the placeholders and (tiled) the assembly map -> dst_row, as
+// launches of their own; newline / separator rows are written to their slots.
 vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
                      const void *newline, const void *separator, const PlaceSrc &src,
                      int64_t seq_len, void *seq, uint8_t *ws, hipStream_t s) {
