@@ -402,11 +402,9 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // loads row r's pixel (NCH 16-byte chunks per lane), normalises it and stages
 // it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
-// Rows of at least this many bytes are read by the standalone scatter with
-// non-temporal loads (they no longer fit the 256 MiB Infinity Cache beside
-// the sequence; see k_scatter).
-constexpr int64_t kScatterStreamBytes = int64_t{96} << 20;
-
+// gamma and beta are staged once per workgroup in LDS.  With a ScanArgs job,
+// workgroup 0 of the launch runs the placeholder scan instead (scan_body),
+// beside the merge: the two touch different data.
 constexpr int kMbRows = 16;  // rows per item = waves per workgroup
 // LayerNorm's gamma and beta are staged in fp32 when the LDS has room next to
 // the staged rows: up to NCH = 6 16-byte chunks per lane (C <= 3072).  At
@@ -568,6 +566,11 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
 }
 
 // ---------------------------------------------------------------------------
+// Rows of at least this many bytes are read by the standalone scatter with
+// non-temporal loads (they no longer fit the 256 MiB Infinity Cache beside
+// the sequence; see k_scatter).
+constexpr int64_t kScatterStreamBytes = int64_t{96} << 20;
+
 // Standalone scatter: row r of rows[T][D] -> seq[dst_row[r]] (skipped if < 0).
 // One wave per row; the row's data (up to 8 KiB at a time) is loaded together
 // with its destination, so the loads never wait on the index.  The sequence
