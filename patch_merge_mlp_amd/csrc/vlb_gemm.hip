@@ -256,35 +256,19 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
   }
 }
 
-// One launch covers either the whole-tile part of the problem (BMT = 256:
-// tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
-// quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
-// whole 128-grid).
-template <int MODE, int ACT, int BMT>
-__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
+// One output tile: BMT x BMT at (tm, tn) of the BMT-grid, staged through
+// smem0..3 (each at least Geo<BMT>::STAGE bytes) with s_bias / s_dst (at least
+// BMT entries).  Inlined into the kernels below, so the four stage arrays stay
+// distinct LDS objects to the compiler.
+template <int MODE, int ACT, int BMT, int SZ>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uint8_t (&smem0)[SZ],
+                                          uint8_t (&smem1)[SZ], uint8_t (&smem2)[SZ],
+                                          uint8_t (&smem3)[SZ], uint16_t *s_bias,
+                                          int32_t *s_dst) {
   using G = Geo<BMT>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BMT];  // this tile's bias
-  __shared__ int32_t s_dst[BMT];                                 // destination row per tile row
+  static_assert(SZ >= G::STAGE, "stage buffers too small");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in an SGPR
-  int tm, tn;
-  if (BMT == 256) {
-    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
-  } else if (g.n_full > 0) {
-    const int rem = g.tiles_m * g.tiles_n - g.n_full;
-    const int q = xcd_remap(blockIdx.x, 4 * rem);  // quarters of one 256-tile stay together
-    int bm, bn;
-    tile_coords(g.n_full + (q >> 2), g.tiles_m, g.tiles_n, bm, bn);
-    tm = 2 * bm + ((q >> 1) & 1);
-    tn = 2 * bn + (q & 1);
-  } else {
-    const int tm128 = (g.M + 127) / 128, tn128 = (g.N + 127) / 128;
-    tile_coords(xcd_remap(blockIdx.x, tm128 * tn128), tm128, tn128, tm, tn);
-  }
   const int m0 = tm * BMT, n0 = tn * BMT;
   // A gradient GEMM writes nothing when the placeholder scan failed.
   if (MODE == kGemmF32 && g.status && g.status[kStatusWord] != 0) return;
@@ -434,12 +418,83 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   store_tile<MODE, ACT, BMT>(acc, g, m0, n0, bufs, s_bias, s_dst);
 }
 
+// Tile coordinates of the quarter tiles: workgroup index q of the 128-tile
+// part covers quarter q%4 of the 256-tile n_full + q/4 (the quarters of one
+// 256-tile stay together), or -- when n_full == 0 -- tile q of the 128-grid.
+__device__ __forceinline__ void tail_coords(const GemmArgs &g, int bid, int &tm, int &tn) {
+  if (g.n_full > 0) {
+    const int rem = g.tiles_m * g.tiles_n - g.n_full;
+    const int q = xcd_remap(bid, 4 * rem);
+    int bm, bn;
+    tile_coords(g.n_full + (q >> 2), g.tiles_m, g.tiles_n, bm, bn);
+    tm = 2 * bm + ((q >> 1) & 1);
+    tn = 2 * bn + (q & 1);
+  } else {
+    const int tm128 = (g.M + 127) / 128, tn128 = (g.N + 127) / 128;
+    tile_coords(xcd_remap(bid, tm128 * tn128), tm128, tn128, tm, tn);
+  }
+}
+
+// One launch covers either the whole-tile part of the problem (BMT = 256:
+// tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
+// quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
+// whole 128-grid).
+template <int MODE, int ACT, int BMT>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
+  using G = Geo<BMT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BMT];  // this tile's bias
+  __shared__ int32_t s_dst[BMT];                                 // destination row per tile row
+  int tm, tn;
+  if (BMT == 256)
+    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+  else
+    tail_coords(g, blockIdx.x, tm, tn);
+  gemm_tile<MODE, ACT, BMT>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+}
+
+// Both parts in one launch: workgroups [0, n_full) take the 256-tiles, the
+// rest the quarter tiles.  Workgroups are dispatched in index order, so a CU
+// whose last whole tile is done starts a quarter tile at once instead of
+// waiting for the slowest whole tile of the launch.  n_full is a multiple of
+// 256, so workgroup n_full + q still runs on XCD q % 8.
+template <int MODE, int ACT>
+__global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
+  using G = Geo<256>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bias[256];
+  __shared__ int32_t s_dst[256];
+  int tm, tn;
+  if (static_cast<int>(blockIdx.x) < g.n_full) {
+    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+    gemm_tile<MODE, ACT, 256>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  } else {
+    tail_coords(g, blockIdx.x - g.n_full, tm, tn);
+    gemm_tile<MODE, ACT, 128>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  }
+}
+
 template <int MODE, int ACT>
 void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
-  if (blocks256 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
-  if (blocks128 > 0)
-    hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+  // Whole tiles and the quarter-tile tail in one launch while the quarter
+  // tiles fit one round at one per CU; beyond that the quarter-tile kernel of
+  // its own (two per CU: a third of the registers and half the LDS) is faster
+  // (dW1 of workload 1, 272 quarter tiles: 340 against 367 us).
+  if (blocks256 > 0 && blocks128 > 0 && blocks128 <= kPlanCUs)
+    hipLaunchKernelGGL((k_gemm_bf16_mixed<MODE, ACT>), dim3(blocks256 + blocks128),
+                       dim3(NTHREADS), 0, s, g);
+  else {
+    if (blocks256 > 0)
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
+    if (blocks128 > 0)
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+  }
 }
 
 template <int MODE>
