@@ -210,7 +210,7 @@ def main():
         "roofline": {
             "bound": "mfma",
             "kernel": "Linear1 (GEMM + bias + GELU on the blocked merged tokens; 256-tile body "
-                      "and 128-tile tail dispatches)",
+                      "and 128-tile tail in one dispatch)",
             "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
         },
