@@ -16,6 +16,15 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two fp32 values -> one dword of two bf16 (a in the low half), round to
+// nearest even: one packed hardware conversion.
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 t = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(t, bf16x2));
+}
+
 // Activation between the two Linears (vlb_act): exact GELU x*Phi(x) through
 // the device erff, the tanh approximation, or none.
 __device__ __forceinline__ float activate(float x, int act) {
@@ -87,6 +96,9 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t *p) {
+  return __builtin_nontemporal_load(p);
 }
 
 // Lane exchange inside rows of 16 lanes (DPP control CTRL).

@@ -399,8 +399,8 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 // every wave keeps view v's table entry, so a row's view is found with one
 // ballot.  A workgroup of 16 waves takes one item: 16 consecutive rows
 // (aligned to 16, so they share a 256-row block) at one position.  Wave r
-// loads row r's pixel (NCH 16-byte chunks per lane), normalises it and stages
-// it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
+// loads row r's pixel (NCH 16-byte chunks per lane, or with DW NCH dwords),
+// normalises it and stages it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
 // gamma and beta are staged once per workgroup in LDS.  With a ScanArgs job,
 // workgroup 0 of the launch runs the placeholder scan instead (scan_body),
@@ -413,13 +413,14 @@ constexpr int kMbRows = 16;  // rows per item = waves per workgroup
 constexpr bool mb_gb32(int nch_per_lane) { return nch_per_lane <= 6; }
 static_assert(kPlanViews >= 64, "each lane reads one view-table entry");
 
-template <bool LN, int NCH>
+template <bool LN, int NCH, bool DW>
 __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *x, PlanChunk c,
                                                                 int C, const uint16_t *gamma,
                                                                 const uint16_t *beta, float eps,
                                                                 uint16_t *out, ScanArgs scan) {
   extern __shared__ uint4 mb_lds[];
   static_assert(64 * kMbRows == kScanThreads, "the scan workgroup has the merge's shape");
+  static_assert(LN || !DW, "the dword layout is for the LayerNorm path");
   int item = blockIdx.x;
   if (scan.on) {  // workgroup 0 runs the placeholder scan (LDS >= kScanChunk positions)
     if (item == 0) {
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
   // 6 chunks per lane (C <= 3072); for C up to 4096 they stay bf16.  Their
   // loads go out before the pixel's, so waiting for them (loads return in
   // order) never waits on the pixel.
-  constexpr bool GB32 = mb_gb32(NCH);
+  constexpr bool GB32 = DW || mb_gb32(NCH);
   float4 *s_gb = reinterpret_cast<float4 *>(mb_lds + kMbRows * rs);  // GB32: [2][C] fp32
   uint4 *s_gb16 = mb_lds + kMbRows * rs;                              // else [2][C] bf16
   const int tid = threadIdx.x;
@@ -476,17 +477,8 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
   if (LN && tid < 2 * nch)
     gb = tid < nch ? reinterpret_cast<const uint4 *>(gamma)[tid]
                    : reinterpret_cast<const uint4 *>(beta)[tid - nch];
-  // The features are read once: non-temporal loads keep them from displacing
-  // the GEMMs' operands in the caches (interleaved A/B, workload 1: step
-  // 0.5291 -> 0.5232 ms, the GEMMs faster, this kernel 0.6 us slower).
-  uint4 v[NCH];
-  const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int q = lane + 64 * i;
-    v[i] = (inside && q < nch) ? load_nt(src + q) : make_uint4(0, 0, 0, 0);
-  }
-  if (LN) {
+  // Stage gamma and beta in LDS; every thread of the workgroup reaches it.
+  auto stage_gb = [&]() {
     if (tid < 2 * nch) {  // chunk tid: 8 values (GB32: two float4 entries)
       if (GB32) {
         s_gb[2 * tid] = make_float4(bf2f(gb.x & 0xffff), bf2f(gb.x >> 16), bf2f(gb.y & 0xffff),
@@ -498,61 +490,125 @@ __global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *
       }
     }
     __syncthreads();
-  }
-  if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
-    float sum = 0.f;
+  };
+  uint4 *row = mb_lds + wid * rs;
+  // The features are read once: non-temporal loads keep them from displacing
+  // the GEMMs' operands in the caches (interleaved A/B, workload 1: step
+  // 0.5291 -> 0.5232 ms, the GEMMs faster, this kernel 0.6 us slower).
+  if constexpr (DW) {
+    // One dword (two channels) per lane and step: at C = 1152 a pixel is 9
+    // dwords on every lane, where 16-byte chunks leave 48 lanes idle in the
+    // third step.  x - mean is kept for the normalisation, the mean and
+    // variance scale by 1/C, and 1/sqrt is the hardware reciprocal root.
+    // The launcher takes this form only for C = 128 * NCH, so every lane of
+    // every step holds a dword of the pixel.  inside is the same on all lanes
+    // of the wave (one row per wave): made scalar, it branches the wave.
+    constexpr int ndw = 64 * NCH;  // dwords per pixel (C / 2)
+    const bool in_w = __builtin_amdgcn_readfirstlane(inside ? 1 : 0) != 0;
+    uint32_t d[NCH];
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(x + off);
+    if (in_w) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
+      for (int i = 0; i < NCH; ++i) d[i] = load_nt(src + lane + 64 * i);
+    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
+      for (int i = 0; i < NCH; ++i) d[i] = 0u;
     }
-    const float mean = wave_sum(sum) / C;
-    float ss = 0.f;
+    stage_gb();
+    if (in_w) {  // rows outside the grid stay zero (padding comes after the norm)
+      float lo[NCH], hi[NCH];
+      float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      if (lane + 64 * i < nch) {
-        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
+      for (int i = 0; i < NCH; ++i) {
+        lo[i] = __uint_as_float(d[i] << 16);
+        hi[i] = __uint_as_float(d[i] & 0xffff0000u);
+        sum += lo[i] + hi[i];
+      }
+      constexpr float inv_c = 1.0f / static_cast<float>(2 * ndw);
+      const float mean = wave_sum(sum) * inv_c;
+      float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float dlt = bf2f(e[j]) - mean;
-          ss += dlt * dlt;
-        }
+      for (int i = 0; i < NCH; ++i) {
+        lo[i] -= mean;
+        hi[i] -= mean;
+        ss = fmaf(lo[i], lo[i], ss);
+        ss = fmaf(hi[i], hi[i], ss);
+      }
+      const float rstd = rsqrtf(wave_sum(ss) * inv_c + eps);
+      const float2 *g2 = reinterpret_cast<const float2 *>(s_gb);  // [C] gamma, then [C] beta
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int q = lane + 64 * i;
+        const float2 g = g2[q], be = g2[ndw + q];
+        d[i] = f2bf2(fmaf(lo[i] * rstd, g.x, be.x), fmaf(hi[i] * rstd, g.y, be.y));
       }
     }
-    const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
+    uint32_t *row32 = reinterpret_cast<uint32_t *>(row);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) row32[lane + 64 * i] = d[i];
+  } else {
+    uint4 v[NCH];
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = lane + 64 * i;
-      if (q < nch) {
-        float gf[8], bfv[8];
-        if (GB32) {
-          const float4 g0 = s_gb[2 * q], g1 = s_gb[2 * q + 1];
-          const float4 b0 = s_gb[2 * (nch + q)], b1 = s_gb[2 * (nch + q) + 1];
-          gf[0] = g0.x; gf[1] = g0.y; gf[2] = g0.z; gf[3] = g0.w;
-          gf[4] = g1.x; gf[5] = g1.y; gf[6] = g1.z; gf[7] = g1.w;
-          bfv[0] = b0.x; bfv[1] = b0.y; bfv[2] = b0.z; bfv[3] = b0.w;
-          bfv[4] = b1.x; bfv[5] = b1.y; bfv[6] = b1.z; bfv[7] = b1.w;
-        } else {
-          const uint4 gq = s_gb16[q], bq = s_gb16[nch + q];
-          const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
-          const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
+      v[i] = (inside && q < nch) ? load_nt(src + q) : make_uint4(0, 0, 0, 0);
+    }
+    if (LN) stage_gb();
+    if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
+      }
+      const float mean = wave_sum(sum) / C;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        if (lane + 64 * i < nch) {
+          const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            gf[j] = bf2f(ge[j]);
-            bfv[j] = bf2f(be[j]);
+            const float dlt = bf2f(e[j]) - mean;
+            ss += dlt * dlt;
           }
         }
-        uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(ss) / C + eps);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = f2bf(fmaf((bf2f(e[j]) - mean) * rstd, gf[j], bfv[j]));
+      for (int i = 0; i < NCH; ++i) {
+        const int q = lane + 64 * i;
+        if (q < nch) {
+          float gf[8], bfv[8];
+          if (GB32) {
+            const float4 g0 = s_gb[2 * q], g1 = s_gb[2 * q + 1];
+            const float4 b0 = s_gb[2 * (nch + q)], b1 = s_gb[2 * (nch + q) + 1];
+            gf[0] = g0.x; gf[1] = g0.y; gf[2] = g0.z; gf[3] = g0.w;
+            gf[4] = g1.x; gf[5] = g1.y; gf[6] = g1.z; gf[7] = g1.w;
+            bfv[0] = b0.x; bfv[1] = b0.y; bfv[2] = b0.z; bfv[3] = b0.w;
+            bfv[4] = b1.x; bfv[5] = b1.y; bfv[6] = b1.z; bfv[7] = b1.w;
+          } else {
+            const uint4 gq = s_gb16[q], bq = s_gb16[nch + q];
+            const uint16_t *ge = reinterpret_cast<const uint16_t *>(&gq);
+            const uint16_t *be = reinterpret_cast<const uint16_t *>(&bq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              gf[j] = bf2f(ge[j]);
+              bfv[j] = bf2f(be[j]);
+            }
+          }
+          uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = f2bf(fmaf((bf2f(e[j]) - mean) * rstd, gf[j], bfv[j]));
+        }
       }
     }
-  }
-  uint4 *row = mb_lds + wid * rs;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
-    if (lane + 64 * i < nch) row[lane + 64 * i] = v[i];
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nch) row[lane + 64 * i] = v[i];
+  }
   __syncthreads();
   // Per K slice: lane -> (row lane/4, chunk lane%4); only this chunk's rows are written.
   const int r = lane >> 2, c4 = lane & 3;
@@ -812,7 +868,7 @@ hipError_t launch_layernorm(int dtype, const void *x, int64_t npix, int C, const
 
 int layernorm_max_channels(int dtype) { return kLnChunks * 64 * (dtype == 0 ? 4 : 8); }
 
-template <bool LN, int NCH>
+template <bool LN, int NCH, bool DW = false>
 static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void *gamma,
                             const void *beta, float eps, void *out, hipStream_t s,
                             const ScanArgs &scan) {
@@ -822,18 +878,18 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
   // staged rows, then (LN) gamma and beta (fp32 or bf16, see mb_gb32):
   // <= 160 KiB for every C the dispatch takes
   size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16 +
-               (LN ? static_cast<size_t>(2) * C * (mb_gb32(NCH) ? 4 : 2) : 0);
+               (LN ? static_cast<size_t>(2) * C * (DW || mb_gb32(NCH) ? 4 : 2) : 0);
   // The scan workgroup stages kScanChunk positions in the same LDS.  Two
   // 1024-thread workgroups per CU is the thread limit anyway, so 64 KiB each
   // costs the merge no occupancy.
   if (scan.on) lds = std::max(lds, kScanChunk * sizeof(int32_t));
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_merge_blocked<LN, NCH>),
+        reinterpret_cast<const void *>(&k_merge_blocked<LN, NCH, DW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_merge_blocked<LN, NCH>), dim3(static_cast<uint32_t>(items)),
+  hipLaunchKernelGGL((k_merge_blocked<LN, NCH, DW>), dim3(static_cast<uint32_t>(items)),
                      dim3(64 * kMbRows), lds, s, static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
                      eps, static_cast<uint16_t *>(out), scan);
@@ -844,6 +900,17 @@ template <bool LN>
 static hipError_t mb_dispatch(const void *x, const PlanChunk &c, int C, const void *gamma,
                               const void *beta, float eps, void *out, hipStream_t s,
                               const ScanArgs &sa) {
+  // LayerNorm at C = 768, 1152 or 1280: 16-byte chunks would leave lanes idle
+  // in the last step (C / 8 not a multiple of 64); one dword per lane and
+  // step fills every lane (C / 128 dwords per lane).
+  if constexpr (LN) {
+    switch (C) {
+      case 768: return mb_launch<LN, 6, true>(x, c, C, gamma, beta, eps, out, s, sa);
+      case 1152: return mb_launch<LN, 9, true>(x, c, C, gamma, beta, eps, out, s, sa);
+      case 1280: return mb_launch<LN, 10, true>(x, c, C, gamma, beta, eps, out, s, sa);
+      default: break;
+    }
+  }
   switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane per pixel
     case 1: return mb_launch<LN, 1>(x, c, C, gamma, beta, eps, out, s, sa);
     case 2: return mb_launch<LN, 2>(x, c, C, gamma, beta, eps, out, s, sa);
