@@ -423,6 +423,149 @@ __global__ __launch_bounds__(64 * kUmWaves) void k_bwd_unmerge(const uint16_t *d
   }
 }
 
+// The LayerNorm form of k_bwd_unmerge at C = 128 * ND (768, 1152, 1280):
+// one dword (two channels) per lane and step, so every lane holds channels
+// (16-byte chunks leave lanes idle in the last step at these C).  Same
+// contract, items and order of the parameter-gradient sums.  gamma is staged
+// in fp32; g = gamma * dn is kept for the output, which is written as
+// rstd * g - rstd * mean(g) - rstd * mean(g * xh) * xh with two fmas.
+template <int ND>
+__global__ __launch_bounds__(64 * kUmWaves) void k_bwd_unmerge_dw(
+    const uint16_t *dxm, const uint16_t *x, PlanChunk c, float eps, const uint16_t *gamma,
+    uint16_t *dx, float *part_g, float *part_b, const int32_t *status) {
+  if (status[kStatusWord] != 0) return;
+  constexpr int ndw = 64 * ND;  // dwords per pixel
+  constexpr int C = 2 * ndw;
+  constexpr float inv_c = 1.0f / static_cast<float>(C);
+  extern __shared__ float red[];  // [2][C] workgroup sums, then gamma as fp32 [C]
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int k = c.k, kk = k * k;
+  const int64_t K1 = static_cast<int64_t>(C) * kk;
+  const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
+  const int64_t items = static_cast<int64_t>(t_end - t_begin) * kk;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kUmWaves;
+  const bool have = lane < c.n;
+  const int32_t e_tok0 = c.tok0[lane], e_pix0 = c.pix0[lane];
+  const int32_t e_gh = c.gh[lane], e_gw = c.gw[lane];
+  const int32_t l_tok0 = have ? e_tok0 : INT32_MAX;
+  const int32_t l_pix0 = have ? e_pix0 : 0;
+  const int32_t l_gh = have ? e_gh : 0, l_gw = have ? e_gw : 1;
+  float2 *s_gamma = reinterpret_cast<float2 *>(red + 2 * C);
+  for (int q = threadIdx.x; q < ndw; q += 64 * kUmWaves) {
+    const uint32_t g = reinterpret_cast<const uint32_t *>(gamma)[q];
+    s_gamma[q] = make_float2(__uint_as_float(g << 16), __uint_as_float(g & 0xffff0000u));
+  }
+  __syncthreads();
+  auto locate = [&](int64_t it, int64_t &drow, int64_t &pix) -> bool {
+    const int m = t_begin + static_cast<int>(it / kk), p = static_cast<int>(it % kk);
+    const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
+    const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
+    const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
+    const int wp = (gw + k - 1) / k, t = m - tok0;
+    const int y = (t / wp) * k + p / k, xx = (t % wp) * k + p % k;
+    if (y >= gh || xx >= gw) return false;
+    pix = pix0 + static_cast<int64_t>(y) * gw + xx;
+    drow = m * K1 + static_cast<int64_t>(p) * C;
+    return true;
+  };
+  auto fetch = [&](int64_t drow, int64_t pix, uint32_t (&dv)[ND], uint32_t (&xv)[ND]) {
+    const uint32_t *dsrc = reinterpret_cast<const uint32_t *>(dxm + drow);
+    const uint32_t *xs = reinterpret_cast<const uint32_t *>(x + pix * C);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {  // both read once
+      dv[i] = load_nt(dsrc + lane + 64 * i);
+      xv[i] = load_nt(xs + lane + 64 * i);
+    }
+  };
+  float ag[ND][2], ab[ND][2];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) ag[i][0] = ag[i][1] = ab[i][0] = ab[i][1] = 0.f;
+  int64_t it = static_cast<int64_t>(blockIdx.x) * kUmWaves + wid;
+  int64_t drow = 0, pix = 0;
+  bool ok = it < items && locate(it, drow, pix);
+  uint32_t dv[ND] = {}, xv[ND] = {};
+  if (ok) fetch(drow, pix, dv, xv);
+  for (; it < items; it += nw) {
+    // The next item's loads go out before this item's arithmetic.
+    int64_t drow2 = 0, pix2 = 0;
+    const bool ok2 = it + nw < items && locate(it + nw, drow2, pix2);
+    uint32_t dv2[ND] = {}, xv2[ND] = {};
+    if (ok2) fetch(drow2, pix2, dv2, xv2);
+    if (ok) {
+      float xl[ND], xh[ND];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        xl[i] = __uint_as_float(xv[i] << 16);
+        xh[i] = __uint_as_float(xv[i] & 0xffff0000u);
+        sum += xl[i] + xh[i];
+      }
+      const float mean = wave_sum(sum) * inv_c;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        xl[i] -= mean;
+        xh[i] -= mean;
+        ss = fmaf(xl[i], xl[i], ss);
+        ss = fmaf(xh[i], xh[i], ss);
+      }
+      const float rstd = rsqrtf(wave_sum(ss) * inv_c + eps);
+      float gl[ND], gh[ND];
+      float sg = 0.f, sgx = 0.f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        const float2 g = s_gamma[lane + 64 * i];
+        const float dl = __uint_as_float(dv[i] << 16), dh = __uint_as_float(dv[i] & 0xffff0000u);
+        xl[i] *= rstd;  // xh, the normalised pixel
+        xh[i] *= rstd;
+        ag[i][0] = fmaf(dl, xl[i], ag[i][0]);
+        ag[i][1] = fmaf(dh, xh[i], ag[i][1]);
+        ab[i][0] += dl;
+        ab[i][1] += dh;
+        gl[i] = g.x * dl;
+        gh[i] = g.y * dh;
+        sg += gl[i] + gh[i];
+        sgx = fmaf(gl[i], xl[i], sgx);
+        sgx = fmaf(gh[i], xh[i], sgx);
+      }
+      if (dx) {
+        const float b = rstd * (wave_sum(sg) * inv_c), a = rstd * (wave_sum(sgx) * inv_c);
+        uint32_t *ddst = reinterpret_cast<uint32_t *>(dx + pix * C);
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+          ddst[lane + 64 * i] = f2bf2(fmaf(-a, xl[i], fmaf(rstd, gl[i], -b)),
+                                      fmaf(-a, xh[i], fmaf(rstd, gh[i], -b)));
+      }
+    }
+    ok = ok2;
+    pix = pix2;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      dv[i] = dv2[i];
+      xv[i] = xv2[i];
+    }
+  }
+  // Workgroup sum of the waves' accumulators, wave 0 first, then one row each.
+  float2 *r2 = reinterpret_cast<float2 *>(red);  // channel pairs: [C/2] gamma, [C/2] beta
+  for (int w = 0; w < kUmWaves; ++w) {
+    if (wid == w) {
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        const int q = lane + 64 * i;
+        const float2 pg = w == 0 ? make_float2(0.f, 0.f) : r2[q];
+        const float2 pb = w == 0 ? make_float2(0.f, 0.f) : r2[ndw + q];
+        r2[q] = make_float2(pg.x + ag[i][0], pg.y + ag[i][1]);
+        r2[ndw + q] = make_float2(pb.x + ab[i][0], pb.y + ab[i][1]);
+      }
+    }
+    __syncthreads();
+  }
+  for (int ch = threadIdx.x; ch < C; ch += 64 * kUmWaves) {
+    part_g[static_cast<int64_t>(blockIdx.x) * C + ch] = red[ch];
+    part_b[static_cast<int64_t>(blockIdx.x) * C + ch] = red[C + ch];
+  }
+}
+
 // out[n] = sum over r of part[r][n] (nothing when the scan failed).  A
 // workgroup takes 32 columns; row group g (of 8) sums rows g, g + 8, ... in
 // order, then the 8 group sums are added in order: the same result every run.
@@ -633,10 +776,28 @@ hipError_t unmerge_launch(const void *dxm, const void *x, const PlanChunk &c, in
   return hipGetLastError();
 }
 
+template <int ND>
+hipError_t unmerge_dw_launch(const void *dxm, const void *x, const PlanChunk &c, const void *gamma,
+                             float eps, void *dx, float *part_g, float *part_b,
+                             const int32_t *status, int grid, hipStream_t s) {
+  // [2][C] fp32 sums, then gamma (fp32) staged once per workgroup
+  const size_t lds = static_cast<size_t>(3) * 128 * ND * sizeof(float);
+  hipLaunchKernelGGL((k_bwd_unmerge_dw<ND>), dim3(grid), dim3(64 * kUmWaves), lds, s,
+                     static_cast<const uint16_t *>(dxm), static_cast<const uint16_t *>(x), c, eps,
+                     static_cast<const uint16_t *>(gamma), static_cast<uint16_t *>(dx), part_g,
+                     part_b, status);
+  return hipGetLastError();
+}
+
 template <bool LN>
 hipError_t unmerge_dispatch(const void *dxm, const void *x, const PlanChunk &c, int C,
                             const void *gamma, float eps, void *dx, float *part_g, float *part_b,
                             const int32_t *status, int grid, hipStream_t s) {
+  if constexpr (LN) {  // C = 768, 1152, 1280: one dword per lane and step
+    if (C == 768) return unmerge_dw_launch<6>(dxm, x, c, gamma, eps, dx, part_g, part_b, status, grid, s);
+    if (C == 1152) return unmerge_dw_launch<9>(dxm, x, c, gamma, eps, dx, part_g, part_b, status, grid, s);
+    if (C == 1280) return unmerge_dw_launch<10>(dxm, x, c, gamma, eps, dx, part_g, part_b, status, grid, s);
+  }
   switch ((C / 8 + 63) / 64) {  // 16-byte chunks per lane
     case 1: return unmerge_launch<LN, 1>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);
     case 2: return unmerge_launch<LN, 2>(dxm, x, c, C, gamma, eps, dx, part_g, part_b, status, grid, s);

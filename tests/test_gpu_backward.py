@@ -102,6 +102,27 @@ def test_small_backward_vs_oracle(w):
         assert e <= tol, (k, e)
 
 
+@pytest.mark.parametrize("C", [768, 1152, 1280])
+def test_layernorm_backward_channels(C):
+    """The LayerNorm backward at the channel counts that take one dword per
+    lane and step (6, 9 and 10 per lane), with a 9 x 10 grid whose last cells
+    are padding: every gradient against the oracle."""
+    w = wl.Workload(f"bwd-ln-{C}", 30 + C // 128, "bf16", C=C, k=2, hidden=256, out_dim=128,
+                    seq_len=96, grids=[(9, 10), (4, 4)], views_per_image=[1, 1], has_ln=True)
+    t = common.draw(w)
+    dseq = wl.seq_grad(w)
+    st, _, g, _ = run_train(w, t, dseq)
+    assert st == v.OK
+    ref = oracle_grads(w, t, dseq)
+    errs = {"dx": common.rel_frob(_np(g.d_features), ref["dx"]),
+            "dgamma": common.rel_frob(_np(g.d_ln_gamma), ref["dgamma"]),
+            "dbeta": common.rel_frob(_np(g.d_ln_beta), ref["dbeta"]),
+            "dw1": common.rel_frob(_np(g.d_w1), ref["dw1"])}
+    print(w.name, {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= TOL_ACT, (k, e)
+
+
 @pytest.mark.parametrize("w", BWD_F32, ids=lambda w: w.name)
 def test_small_backward_f32_vs_oracle(w):
     t = common.draw(w)

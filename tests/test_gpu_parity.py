@@ -144,11 +144,14 @@ def test_many_views_plain():
     assert torch.equal(out.view(torch.int16), t["seq"].view(torch.int16))
 
 
-@pytest.mark.parametrize("C", [2048, 3072, 4096])
+@pytest.mark.parametrize("C", [768, 1280, 2048, 3072, 4096])
 def test_wide_channel_layernorm(C):
-    """LayerNorm + merge at wide channel counts: 4, 6 and 8 16-byte chunks per
+    """LayerNorm + merge at other channel counts: 768 and 1280 take one dword
+    per lane and step (6 and 10 per lane; 1152, the same form with 9, is the
+    main workload's); 2048, 3072 and 4096 take 4, 6 and 8 16-byte chunks per
     lane, the last keeping gamma and beta in bf16 in LDS (fp32 would not fit
-    beside the staged rows).  Whole output against the oracle."""
+    beside the staged rows).  The 9 x 10 grid pads its last column and row of
+    cells.  Whole output against the oracle."""
     w = wl.Workload(f"wide-ln-{C}", 20 + C // 1024, "bf16", C=C, k=2, hidden=256, out_dim=128,
                     seq_len=96, grids=[(9, 10), (4, 4)], views_per_image=[1, 1], has_ln=True)
     t = common.draw(w)
