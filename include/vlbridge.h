@@ -347,9 +347,9 @@ enum {
   VLB_K_PACK = 8,    /* weight re-layout */
   VLB_K_EMBED = 9,   /* token-embedding rows */
   VLB_K_BWD_PACK = 10,    /* backward: gradient gather and operand transposes */
-  VLB_K_BWD_DW2 = 11,     /* backward: dW2 = dY^T act(Z1) */
+  VLB_K_BWD_DW2 = 11,     /* backward: dW2 = dY^T act(Z1) (and the sum of its K-split tail tiles) */
   VLB_K_BWD_DA1 = 12,     /* backward: dA1 = dY W2 */
-  VLB_K_BWD_DW1 = 13,     /* backward: dW1 = dZ1^T Xm */
+  VLB_K_BWD_DW1 = 13,     /* backward: dW1 = dZ1^T Xm (and the sum of its K-split tail tiles) */
   VLB_K_BWD_DX = 14,      /* backward: dXm = dZ1 W1 */
   VLB_K_BWD_UNMERGE = 15, /* backward: unmerge + LayerNorm backward */
   VLB_K_BWD_SUM = 16,     /* backward: bias / LayerNorm / newline sums */

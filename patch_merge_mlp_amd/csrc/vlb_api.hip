@@ -215,7 +215,8 @@ struct BwdLayout {
   size_t off_status = 0, off_dst = 0, off_slot = 0, off_nl = 0, off_sep = 0, off_dy = 0,
          off_dyt = 0, off_a1t = 0, off_w2t = 0, off_da1 = 0, off_dz1 = 0, off_dz1t = 0,
          off_xmt = 0, off_w1t = 0, off_wmt = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
-         off_pnl = 0, off_psep = 0, total = 0;
+         off_pnl = 0, off_psep = 0, off_split = 0, total = 0;
+  size_t split_bytes = 0;    // K-split partial tiles of the weight gradients (0: none)
   std::vector<int> ln_grid;  // unmerge workgroups per chunk of views
   int64_t ln_rows = 0;       // their sum: rows of each LayerNorm partial
 };
@@ -288,6 +289,10 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
   L->off_pln = take(off, static_cast<size_t>(2 * L->ln_rows) * p->C * 4);
   L->off_pnl = take(off, static_cast<size_t>(ceil_div(L->NL, 64)) * O * 4);
   L->off_psep = take(off, static_cast<size_t>(ceil_div(b->n_images, 64)) * O * 4);
+  // partial tiles of the weight-gradient products' split K ranges
+  L->split_bytes = std::max(vlb::gemm_split_bytes(O, H, Tk), vlb::gemm_split_bytes(H, K1, Tk));
+  if (proj_depth(p) > 2) L->split_bytes = std::max(L->split_bytes, vlb::gemm_split_bytes(H, H, Tk));
+  L->off_split = take(off, L->split_bytes);
   L->total = off;
   return VLB_OK;
 }
@@ -1030,6 +1035,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   // 3. dW2 = dY^T act(Z1)
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
              vlb::launch_bwd_act_t(p->act, sv + sl.off_z(n_mid), Ti, Hi, Tk, w8 + L.off_a1t, s));
+  float *split_part = L.split_bytes ? reinterpret_cast<float *>(w8 + L.off_split) : nullptr;
   vlb::GemmArgs gw2{};
   gw2.A = w8 + L.off_dyt;
   gw2.B = w8 + L.off_a1t;
@@ -1042,6 +1048,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   gw2.act = VLB_ACT_NONE;
   gw2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(O, Tk) * 2);
   gw2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+  gw2.split_part = split_part;
   VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw2, s));
   // 4. dA1 = dY W2, then dZ1 = dA1 * act'(Z1) and db1
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
@@ -1083,6 +1090,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     gwm.act = VLB_ACT_NONE;
     gwm.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
     gwm.b_bytes = gwm.a_bytes;
+    gwm.split_part = split_part;
     VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gwm, s));
     // dA_{q-1} = dZ_q W_q, then dZ_{q-1} = dA_{q-1} * act'(Z_{q-1})
     const void *wq = w->w_mid[q - 1];
@@ -1121,6 +1129,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   gw1.act = VLB_ACT_NONE;
   gw1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
   gw1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(K1, Tk) * 2);
+  gw1.split_part = split_part;
   VLB_LAUNCH(VLB_K_BWD_DW1, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw1, s));
   // 6. dXm = dZ1 W1 (K position-major), unmerge, LayerNorm backward
   if (ln || g->d_features) {

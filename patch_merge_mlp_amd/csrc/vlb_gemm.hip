@@ -259,12 +259,14 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 // One output tile: BMT x BMT at (tm, tn) of the BMT-grid, staged through
 // smem0..3 (each at least Geo<BMT>::STAGE bytes) with s_bias / s_dst (at least
 // BMT entries).  Inlined into the kernels below, so the four stage arrays stay
-// distinct LDS objects to the compiler.
+// distinct LDS objects to the compiler.  K steps [ks0, ks0 + ksn) of the
+// product are accumulated; with part set (kGemmF32 only) the whole BMT x BMT
+// fp32 tile goes to part, row-major, instead of to out.
 template <int MODE, int ACT, int BMT, int SZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uint8_t (&smem0)[SZ],
                                           uint8_t (&smem1)[SZ], uint8_t (&smem2)[SZ],
                                           uint8_t (&smem3)[SZ], uint16_t *s_bias,
-                                          int32_t *s_dst) {
+                                          int32_t *s_dst, int ks0, int ksn, float *part) {
   using G = Geo<BMT>;
   static_assert(SZ >= G::STAGE, "stage buffers too small");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -303,18 +305,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     b_off[i] = n < g.N ? blocked(n) + c_off : kOOB;
   }
 
-  // Loads of K step kt into `stage`.  Steps at or past the end of K read zeros
-  // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
-  const int KT = g.K / BK;
-  // Loads of K step kt into `stage` (the first or second half of them when
-  // part is 0 or 1, all when -1).  Steps at or past the end of K read zeros
-  // (the loop runs a multiple of NSTAGE steps and prefetches beyond).
-  auto issue = [&](int kt, uint8_t *stage, int part) {
+  // Loads of step kt of the range into `stage` (the first or second half of
+  // them when half is 0 or 1, all when -1).  Steps at or past the end of the
+  // range read zeros (the loop runs a multiple of NSTAGE steps and prefetches
+  // beyond).
+  const int KT = ksn;
+  auto issue = [&](int kt, uint8_t *stage, int half) {
     const uint32_t dead = kt < KT ? 0u : kOOB;  // OR-ed in: keeps the loads branch-free
-    const uint32_t step_off = kt * (256 * 64);
+    const uint32_t step_off = (ks0 + kt) * (256 * 64);
     uint8_t *sa = stage + wid * G::LPW * 1024;
     uint8_t *sb = stage + G::HALF + wid * G::LPW * 1024;
-    const int i0 = part == 1 ? G::LPW / 2 : 0, i1 = part == 0 ? G::LPW / 2 : G::LPW;
+    const int i0 = half == 1 ? G::LPW / 2 : 0, i1 = half == 0 ? G::LPW / 2 : G::LPW;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
@@ -414,6 +415,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     step(smem0, smem2, kt + 3, fa1, fb1, fa0, fb0);
   }
   __syncthreads();  // every load and fragment read has finished: the stages become the C tile
+  if constexpr (MODE == kGemmF32) {
+    if (part) {  // one K range of a split tile: the whole tile, no bounds
+      GemmArgs gp = g;
+      gp.out = part;
+      gp.M = gp.N = gp.ldo = BMT;
+      write_f32<BMT>(acc, gp, 0, 0);
+      return;
+    }
+  }
   uint8_t *const bufs[4] = {smem0, smem1, smem2, smem3};
   store_tile<MODE, ACT, BMT>(acc, g, m0, n0, bufs, s_bias, s_dst);
 }
@@ -453,7 +463,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   else
     tail_coords(g, blockIdx.x, tm, tn);
-  gemm_tile<MODE, ACT, BMT>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  gemm_tile<MODE, ACT, BMT>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, g.K / BK,
+                            nullptr);
 }
 
 // Both parts in one launch: workgroups [0, n_full) take the 256-tiles, the
@@ -470,14 +481,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[256];
   __shared__ int32_t s_dst[256];
-  int tm, tn;
-  if (static_cast<int>(blockIdx.x) < g.n_full) {
-    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
-    gemm_tile<MODE, ACT, 256>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+  int tm, tn, ks0 = 0, ksn = g.K / BK;
+  float *part = nullptr;
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < g.n_full) {
+    tile_coords(xcd_remap(bid, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+  } else if (MODE == kGemmF32 && g.k_splits > 1) {
+    // K range r of tail tile q, as a whole tile: workgroup n_full + q*S + r
+    // (S = k_splits), its partial tile at split_part + (q*S + r) tiles.
+    const int u = bid - g.n_full, q = u / g.k_splits, r = u - q * g.k_splits;
+    tile_coords(g.n_full + q, g.tiles_m, g.tiles_n, tm, tn);
+    ks0 = r * ksn / g.k_splits;
+    ksn = (r + 1) * ksn / g.k_splits - ks0;
+    part = g.split_part + static_cast<int64_t>(u) * (256 * 256);
   } else {
-    tail_coords(g, blockIdx.x - g.n_full, tm, tn);
-    gemm_tile<MODE, ACT, 128>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst);
+    tail_coords(g, bid - g.n_full, tm, tn);
+    gemm_tile<MODE, ACT, 128>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, ksn,
+                              nullptr);
+    return;
   }
+  gemm_tile<MODE, ACT, 256>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, ks0, ksn, part);
+}
+
+// out rows of the split tail tiles: tile q's k_splits partial tiles added in
+// order (the same result every run).  Grid (64, tail tiles): a thread adds
+// one float4 of the 256 x 256 tile.  Nothing is written when the placeholder
+// scan failed.
+__global__ __launch_bounds__(256) void k_split_sum(GemmArgs g) {
+  if (g.status && g.status[kStatusWord] != 0) return;
+  const int q = blockIdx.y;
+  int tm, tn;
+  tile_coords(g.n_full + q, g.tiles_m, g.tiles_n, tm, tn);
+  const int e = blockIdx.x * 256 + threadIdx.x;  // float4 of the tile
+  const int r = e >> 6, c = (e & 63) * 4;
+  const int m = tm * 256 + r, n = tn * 256 + c;
+  if (m >= g.M || n >= g.N) return;
+  const f32x4 *p = reinterpret_cast<const f32x4 *>(g.split_part) +
+                   static_cast<int64_t>(q) * g.k_splits * (256 * 64) + e;
+  f32x4 acc = p[0];
+  for (int k = 1; k < g.k_splits; ++k) acc += p[static_cast<int64_t>(k) * (256 * 64)];
+  *reinterpret_cast<f32x4 *>(static_cast<float *>(g.out) + static_cast<int64_t>(m) * g.ldo + n) =
+      acc;
 }
 
 template <int MODE, int ACT>
@@ -526,10 +570,20 @@ hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
       if (g.act != 2) return hipErrorInvalidValue;
       launch_bf16<kGemmRows, 2>(g, tp.n_full, tp.blocks128, s);
       break;
-    case kGemmF32:  // no bias, no activation
+    case kGemmF32: {  // no bias, no activation
       if (g.act != 2 || g.N % 4 || g.ldo % 4) return hipErrorInvalidValue;
-      launch_bf16<kGemmF32, 2>(g, tp.n_full, tp.blocks128, s);
+      const int S = g.split_part ? gemm_k_splits(tp, g.K) : 1;
+      g.k_splits = S;
+      if (S > 1) {  // whole tiles and the split tail in one launch, then the sums
+        const int rem = tp.tiles_m * tp.tiles_n - tp.n_full;
+        hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2>), dim3(tp.n_full + rem * S),
+                           dim3(NTHREADS), 0, s, g);
+        hipLaunchKernelGGL(k_split_sum, dim3(64, rem), dim3(256), 0, s, g);
+      } else {
+        launch_bf16<kGemmF32, 2>(g, tp.n_full, tp.blocks128, s);
+      }
       break;
+    }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

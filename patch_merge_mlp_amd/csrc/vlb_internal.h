@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace vlb {
 
 // ---- per-token gather descriptor ------------------------------------------
@@ -77,6 +79,12 @@ struct GemmArgs {
   // kGemmRows: 1 = rows written with non-temporal stores (rows nobody reads
   // back soon: Linear2's rows into the sequence), 0 = ordinary stores.
   int32_t stream_out;
+  // kGemmF32 only: with split_part set (gemm_split_bytes of room), tiles past
+  // n_full that gemm_k_splits splits are computed as k_splits K ranges each,
+  // every range a whole 256x256 fp32 tile in split_part, and the ranges of a
+  // tile are added in order into out by a second kernel.  Set by the launcher.
+  float *split_part;
+  int32_t k_splits;
 };
 
 // Epilogues of the bf16 GEMM.
@@ -117,6 +125,27 @@ inline TilePlan tile_plan(int64_t M, int64_t N) {
     tp.blocks128 = 0;
   }
   return tp;
+}
+
+// K splits of the tiles past n_full of an fp32-output product (weight
+// gradients: K = tokens, long).  Their quarter tiles would need two rounds
+// (more than 256 of them), or each would run K through a 128x128 tile at a
+// third of a whole tile's rate; as S whole 256x256 tiles over a K range each
+// (S * rem <= 256 CUs, one round) they finish in about 1/S of a whole tile,
+// plus a pass adding the S partial tiles.  1: no split.
+inline int gemm_k_splits(const TilePlan &tp, int64_t K) {
+  const int rem = tp.tiles_m * tp.tiles_n - tp.n_full;
+  if (tp.n_full == 0 || tp.blocks128 == 0 || rem <= 0) return 1;
+  const int S = std::min(8, kPlanCUs / rem);
+  if (S < 2 || K / kGemmBK < 16 * S) return 1;  // at least 16 K steps per range
+  return (4 * rem > kPlanCUs || S >= 6) ? S : 1;
+}
+// Bytes of GemmArgs::split_part that an M x N x K kGemmF32 product needs (0: none).
+inline size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const TilePlan tp = tile_plan(M, N);
+  const int S = gemm_k_splits(tp, K);
+  if (S < 2) return 0;
+  return static_cast<size_t>(tp.tiles_m * tp.tiles_n - tp.n_full) * S * 256 * 256 * sizeof(float);
 }
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------
