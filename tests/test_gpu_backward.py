@@ -221,6 +221,21 @@ def test_full_backward_sampled(i):
     assert e <= TOL_ACT
 
 
+def test_full_backward_repeatable():
+    """Workload 1's weight gradients split their tail tiles along K (dW2 into
+    8 ranges, dW1 into 3) and add the partial tiles in range order: two runs
+    give the same bits, as do the other gradients."""
+    w, t = full(1)
+    dseq = wl.seq_grad(w)
+    st1, _, g1, _ = run_train(w, t, dseq)
+    st2, _, g2, _ = run_train(w, t, dseq)
+    assert st1 == v.OK and st2 == v.OK
+    for name in ("d_w1", "d_w2", "d_b1", "d_b2", "d_ln_gamma", "d_ln_beta", "d_features"):
+        a, b = getattr(g1, name), getattr(g2, name)
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                           b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16)), name
+
+
 @pytest.mark.parametrize("wi", [0, 2])
 def test_backward_packed_equals_unpacked(wi):
     """With weights packed by vlb_pack_weights the backward gives the same bits."""
