@@ -129,10 +129,11 @@ inline TilePlan tile_plan(int64_t M, int64_t N) {
 
 // K splits of the tiles past n_full of an fp32-output product (weight
 // gradients: K = tokens, long).  Their quarter tiles would need two rounds
-// (more than 256 of them), or each would run K through a 128x128 tile at a
-// third of a whole tile's rate; as S whole 256x256 tiles over a K range each
-// (S * rem <= 256 CUs, one round) they finish in about 1/S of a whole tile,
-// plus a pass adding the S partial tiles.  1: no split.
+// (more than 256 of them), or each would run the whole K through a 128x128
+// tile at about two thirds of a whole tile's rate; as S whole 256x256 tiles
+// over a K range each (S * rem <= 256 CUs, one round) they finish in about
+// 1/S of a whole tile's time, plus a pass adding the S partial tiles.
+// 1: no split.
 inline int gemm_k_splits(const TilePlan &tp, int64_t K) {
   const int rem = tp.tiles_m * tp.tiles_n - tp.n_full;
   if (tp.n_full == 0 || tp.blocks128 == 0 || rem <= 0) return 1;
