@@ -36,6 +36,8 @@ namespace {
 constexpr int kTR = 32;            // rows t per workgroup (one K slice)
 constexpr int kTC = 256;           // columns per workgroup
 constexpr int kPitch = kTC + 8;    // LDS row pitch in bf16 (16-byte aligned rows)
+constexpr int kPackIters = kTR * (kTC / 8) / 256;  // 16-byte pieces per thread (256 threads)
+static_assert(kPackIters * 256 == kTR * (kTC / 8), "a tile is a whole number of pieces per thread");
 
 __device__ __forceinline__ int64_t blk(int64_t r, int64_t c, int64_t K) {
   return ((r >> 8) * (K >> 5) + (c >> 5)) * 8192 + (r & 255) * 32 + (c & 31);
@@ -120,15 +122,25 @@ __global__ __launch_bounds__(256) void k_bwd_gather_dy(const uint16_t *G, const 
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
-    const int row = q >> 5, ch = q & 31;
-    const int t = t0 + row, o = n0 + ch * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < T && o < O) {
-      const int32_t d = dst_row[t];
-      if (d >= 0) v = load_nt(reinterpret_cast<const uint4 *>(G + static_cast<int64_t>(d) * O + o));
-    }
-    *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
+  // Each thread moves kPackIters 16-byte pieces; all their loads go out before
+  // the first is used (the destination rows first, then the gradient rows).
+  int32_t d[kPackIters];
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, row = q >> 5, o = n0 + (q & 31) * 8;
+    d[i] = (t0 + row < T && o < O) ? dst_row[t0 + row] : -1;
+  }
+  uint4 v[kPackIters];
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, o = n0 + (q & 31) * 8;
+    v[i] = d[i] >= 0 ? load_nt(reinterpret_cast<const uint4 *>(G + static_cast<int64_t>(d[i]) * O + o))
+                     : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i;
+    *reinterpret_cast<uint4 *>(tile + (q >> 5) * kPitch + (q & 31) * 8) = v[i];
   }
   __syncthreads();
   for (int q = tid; q < kTR * (kTC / 8); q += 256) {  // dY: 8 slices of 32 rows x 64 bytes
@@ -150,17 +162,22 @@ __global__ __launch_bounds__(256) void k_bwd_act_t(const uint16_t *z1, int32_t T
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
-    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
-    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < T && h < H) {
-      v = *reinterpret_cast<const uint4 *>(z1 + blk(t, h, H));
-      uint16_t *e = reinterpret_cast<uint16_t *>(&v);
+  uint4 v[kPackIters];  // all loads out before the first is used
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = f2bf(act_fn<ACT>(bf2f(e[i])));
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
+    v[i] = (t < T && h < H) ? *reinterpret_cast<const uint4 *>(z1 + blk(t, h, H)) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    if (t0 + row < T && n0 + sl * 32 + c4 * 8 < H) {
+      uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = f2bf(act_fn<ACT>(bf2f(e[j])));
     }
-    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v[i];
   }
   __syncthreads();
   store_columns(tile, min(kTC, H - n0), a1t + blk(n0, t0, Tk));
@@ -176,20 +193,28 @@ __global__ __launch_bounds__(256) void k_bwd_dact(const uint16_t *da1, const uin
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
-    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+  uint4 a[kPackIters], z[kPackIters];  // all loads out before the first is used
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
+    const bool in = t < T && h < H;
+    const int64_t e = in ? blk(t, h, H) : 0;
+    a[i] = in ? *reinterpret_cast<const uint4 *>(da1 + e) : make_uint4(0, 0, 0, 0);
+    z[i] = in ? *reinterpret_cast<const uint4 *>(z1 + e) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
     const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (t < T && h < H) {
-      const int64_t e = blk(t, h, H);
-      const uint4 a = *reinterpret_cast<const uint4 *>(da1 + e);
-      const uint4 z = *reinterpret_cast<const uint4 *>(z1 + e);
-      const uint16_t *ae = reinterpret_cast<const uint16_t *>(&a);
-      const uint16_t *ze = reinterpret_cast<const uint16_t *>(&z);
+      const uint16_t *ae = reinterpret_cast<const uint16_t *>(&a[i]);
+      const uint16_t *ze = reinterpret_cast<const uint16_t *>(&z[i]);
       uint16_t *ve = reinterpret_cast<uint16_t *>(&v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ve[i] = f2bf(bf2f(ae[i]) * act_slope<ACT>(bf2f(ze[i])));
-      *reinterpret_cast<uint4 *>(dz1 + e) = v;
+      for (int j = 0; j < 8; ++j) ve[j] = f2bf(bf2f(ae[j]) * act_slope<ACT>(bf2f(ze[j])));
+      *reinterpret_cast<uint4 *>(dz1 + blk(t, h, H)) = v;
     }
     *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
   }
@@ -207,12 +232,17 @@ __global__ __launch_bounds__(256) void k_bwd_xm_t(const uint16_t *xm, int32_t T,
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
-    const int sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+  uint4 v[kPackIters];  // all loads out before the first is used
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
     const int t = t0 + row, j = n0 + sl * 32 + c4 * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < T && j < K1) v = load_nt(reinterpret_cast<const uint4 *>(xm + blk(t, j, K1)));
-    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v;
+    v[i] = (t < T && j < K1) ? load_nt(reinterpret_cast<const uint4 *>(xm + blk(t, j, K1))) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kPackIters; ++i) {
+    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
+    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v[i];
   }
   __syncthreads();
   const int j = n0 + tid;
@@ -228,12 +258,17 @@ __global__ __launch_bounds__(256) void k_bwd_weight_t(const uint16_t *w, int32_t
   __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  for (int q = tid; q < kTR * (kTC / 8); q += 256) {
-    const int row = q >> 5, ch = q & 31;
-    const int r = r0 + row, i = n0 + ch * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < R && i < Cs) v = *reinterpret_cast<const uint4 *>(w + static_cast<int64_t>(r) * Cs + i);
-    *reinterpret_cast<uint4 *>(tile + row * kPitch + ch * 8) = v;
+  uint4 v[kPackIters];  // all loads out before the first is used
+#pragma unroll
+  for (int k = 0; k < kPackIters; ++k) {
+    const int q = tid + 256 * k, r = r0 + (q >> 5), i = n0 + (q & 31) * 8;
+    v[k] = (r < R && i < Cs) ? *reinterpret_cast<const uint4 *>(w + static_cast<int64_t>(r) * Cs + i)
+                             : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < kPackIters; ++k) {
+    const int q = tid + 256 * k;
+    *reinterpret_cast<uint4 *>(tile + (q >> 5) * kPitch + (q & 31) * 8) = v[k];
   }
   __syncthreads();
   if (kk == 1) {
