@@ -1,25 +1,28 @@
 """Benchmark of the vision-to-language bridge on one MI355X.
 
 One step = one vlb_bridge_fused call over one batch: LayerNorm (when the
-workload has it) fused with the k x k space-to-depth into Linear1's
-tile-blocked operand, Linear + bias + GELU, Linear + bias, and the scatter of
-every row into its placeholder slot (plus newline / separator rows for tiled
-images).  Inputs, the packed weights and the workspace are resident in HBM
-before timing starts.
+workload has it), the k x k space-to-depth, Linear + bias + GELU, Linear +
+bias, and the scatter of every row into its placeholder slot (plus newline /
+separator rows for tiled images).  Inputs, the packed weights and the
+workspace are resident in HBM before timing starts.
 
-Prints one JSON line.  value = visual tokens (projected rows) per second.
-roofline = the first GEMM (the dominant kernel): algorithmic FLOPs per launch
-over its mean duration from HIP events recorded around its launches in every
-4th step of the timed region, on the stream it runs on (each event pair adds
-about 12 us to its step, so the other steps run without; the per-kernel table
-and Linear2's rate come from a separate untimed pass in which every launch is
-bracketed).
-cpu_baseline = the fp64 oracle on the host's cores over a bounded sample of
-the same workload's rows.
+Every one of the five workloads is timed in the same run (`configs`); the
+headline line is the largest one, ragged-3x3 (32 DeepSeek-ViT-style images of
+48..96 patches a side, 3x3 pixel-unshuffle, 9216 -> 5120 -> 5120).
 
-The defaults (50 warm-up steps, 500 timed steps: about 0.3 s of GPU work on
-workload 1) measure the steady state.  The GPU clock ramps up for the first
-few milliseconds after idle, so a 20-step run reads about 13% slower.
+Prints one JSON line.  value = visual tokens (projected rows) per second of
+the headline workload.  roofline = its first GEMM (the dominant kernel):
+algorithmic FLOPs per launch over the mean duration from HIP events recorded
+around its launches in every 4th step of the timed region, on the stream it
+runs on (an event pair adds a few microseconds to its step, so the other
+steps run without; the per-kernel table and Linear2's rate come from a
+separate untimed pass in which every launch is bracketed).  cpu_baseline =
+the fp64 oracle on the host's cores over a bounded sample of the same
+workload's rows.
+
+The defaults (50 warm-up steps, 500 timed steps per workload) measure the
+steady state.  The GPU clock ramps up for the first few milliseconds after
+idle, so a 20-step run reads slower.
 """
 from __future__ import annotations
 
@@ -38,6 +41,8 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector / MFMA) dense
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "visual tokens/sec through merge+projector+scatter"
 PROF_EVERY = 4              # Linear1 is bracketed by HIP events in every 4th timed step
+HEADLINE = 4                # ragged-3x3: the largest workload that fits one GPU
+EXTRAS = 1                  # training step, depth 3 and embedding call: MoonViT 2x2 + LN
 
 
 def parse():
@@ -45,11 +50,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1,
-                    help="workload index (1 = MoonViT-style 2x2 bridge with LayerNorm)")
+    ap.add_argument("--config", default="all",
+                    help="'all' (default: every workload, the headline line on ragged-3x3) or "
+                         "one workload index 0..4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target duration of the CPU-baseline sample")
+                    help="target duration of the headline CPU-baseline sample")
+    ap.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                    help="target duration of the other workloads' CPU-baseline samples")
     ap.add_argument("--no-hbm-kernels", action="store_true",
                     help="skip timing the standalone merge and scatter entry points")
     ap.add_argument("--no-sclk", action="store_true",
@@ -66,8 +74,11 @@ def parse():
 
 
 def kernel_sha() -> str:
-    with open(os.path.join(ROOT, "patch_merge_mlp_amd", "csrc", "vlb_gemm.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("vlb_gemm.hip", "vlb_common.h"):
+        with open(os.path.join(ROOT, "patch_merge_mlp_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str):
@@ -89,13 +100,32 @@ def traffic_from_profiles(workload: str):
         return None
 
 
+def host_threads():
+    """Threads the oracle uses: the CPU share of one GPU on the measurement box
+    (16), or fewer when the host has fewer; and what the host reports."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return min(avail, 16), os.cpu_count(), avail
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this bridge is measured on one GPU; images are independent, so a "
               "multi-GPU run would only replicate the weights and split the images", file=sys.stderr)
         sys.exit(2)
+    # The clock sampler is started before anything touches the GPU.
+    args.sampler = None if (args.no_sclk or args.copy_calibration) else ClockSampler()
+    try:
+        run(args)
+    finally:
+        if args.sampler is not None:
+            args.sampler.stop()
 
+
+def run(args):
     import torch
 
     from patch_merge_mlp_amd import vlbridge as v
@@ -112,8 +142,29 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n}))
         return
 
-    w = wl.config(args.config)
+    which = list(range(wl.N_CONFIGS)) if args.config == "all" else [int(args.config)]
+    head = HEADLINE if HEADLINE in which else which[-1]
+    configs, head_res = {}, None
+    for i in which:
+        res = measure_config(args, v, wl, torch, i, headline=(i == head),
+                             extras=(i == EXTRAS and len(which) > 1) or len(which) == 1)
+        print(f"bench: {res['summary']['workload']} {res['summary']['tokens_per_s']:.4g} tok/s, "
+              f"{res['summary']['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        configs[res["summary"]["workload"]] = res["summary"]
+        if i == head:
+            head_res = res
+        torch.cuda.empty_cache()
+    out = head_res["line"]
+    out["configs"] = configs
+    print(json.dumps(out))
+
+
+def measure_config(args, v, wl, torch, i, headline, extras):
+    """Time workload i; returns {"summary": per-workload figures, "line": the JSON
+    line this workload would give as the headline}."""
+    w = wl.config(i)
     gen = wl.Generator(w)
+    bf16 = w.dtype == "bf16"
     p = v.projector(v.F32 if w.dtype == "f32" else v.BF16, w.C, w.k, w.hidden, w.out_dim,
                     has_ln=w.has_ln, ln_eps=w.ln_eps)
     b = v.Batch(w.grids, w.views_per_image, v.LAYOUT_TILED_2D if w.tiled else v.LAYOUT_PLAIN,
@@ -121,8 +172,9 @@ def main():
     T = v.vlb_num_tokens(p, b)
     P = v.vlb_num_slots(p, b)
     K1 = w.C * w.k * w.k
-    t = gen.tensors(sum(gh * gw for gh, gw in w.grids), K1, v.vlb_image_slots(p, b))
-    d = lambda x: None if x is None else x.to(dev)
+    npix = sum(gh * gw for gh, gw in w.grids)
+    t = gen.tensors(npix, K1, v.vlb_image_slots(p, b))
+    d = lambda x: None if x is None else x.to("cuda")
     weights = v.Weights(d(t["w1"]), d(t["b1"]), d(t["w2"]), d(t["b2"]), d(t["ln_gamma"]),
                         d(t["ln_beta"]))
     br = v.Bridge(p, weights)            # packs W1 and W2 once (weight preprocessing, untimed)
@@ -151,13 +203,13 @@ def main():
 
     # Timed region: HIP events bracket the Linear1 launches of every
     # PROF_EVERY-th step (on the stream they run on); every other launch runs
-    # unbracketed, since an event pair costs the step about 12 us.
+    # unbracketed.
     v.vlb_prof_enable(1 << v.K_GEMM1)
     v.vlb_prof_resume(0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        if i % PROF_EVERY == 0:
+    for s in range(args.steps):
+        if s % PROF_EVERY == 0:
             v.vlb_prof_resume(1 << v.K_GEMM1)
             step()
             v.vlb_prof_resume(0)
@@ -170,7 +222,8 @@ def main():
     gemm1_us = 1000.0 * ms / n
     # Per-kernel breakdown from a separate, untimed pass with every launch timed.
     v.vlb_prof_enable(True)
-    for _ in range(max(3, args.steps // 4)):
+    reps = max(3, args.steps // 4)
+    for _ in range(reps):
         step()
     torch.cuda.synchronize()
     v.vlb_prof_enable(False)
@@ -183,12 +236,49 @@ def main():
     sec = (t1 - t0) / args.steps
     flops1 = 2.0 * T * K1 * w.hidden
     flops2 = 2.0 * T * w.hidden * w.out_dim
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     g1 = gemm1_us * 1e-6  # from the timed region
-    g2 = kernels["gemm2"]["mean_us"] * 1e-6  # from the profiled pass
+    g2 = kernels["gemm2"]["mean_us"] * kernels["gemm2"]["launches"] / reps * 1e-6
     achieved = flops1 / g1 / 1e12
     traffic = traffic_from_profiles(w.name)
-    out = {
+    es = 2 if bf16 else 4
+    # The merge kernel on the fused path (with the LayerNorm when the workload
+    # has it): read the grid once, write Linear1's merged operand once.
+    fused_merge = None
+    for name in ("layernorm", "merge"):
+        if name in kernels and bf16:
+            us = kernels[name]["mean_us"] * kernels[name]["launches"] / reps
+            nbytes = (npix * w.C + T * K1) * es
+            gbs = nbytes / (us * 1e-6) / 1e9
+            fused_merge = {"kernel": name, "us_per_step": round(us, 2), "bytes": nbytes,
+                           "GB/s": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+    config = {
+        "workload": w.name, "images": w.n_images, "views": len(w.grids),
+        "grid": list(w.grids[0]) if len(set(w.grids)) == 1 else "ragged",
+        "C": w.C, "k": w.k, "hidden": w.hidden,
+        "out_dim": w.out_dim, "layernorm": w.has_ln, "seq_len": w.seq_len,
+        "visual_tokens": T, "placeholder_slots": P, "layout": "tiled_2d" if w.tiled else "plain",
+    }
+    summary = {
+        "workload": w.name,
+        "dtype": "bf16" if bf16 else "f32",
+        "visual_tokens": T,
+        "placeholder_slots": P,
+        "tokens_per_s": round(T / sec, 1),
+        "ms_per_step": round(sec * 1e3, 4),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "gemm1": {"mean_us": round(gemm1_us, 2), "TFLOP/s": round(achieved, 1),
+                  "frac": round(achieved / peak, 4)},
+        "gemm2": {"mean_us": round(g2 * 1e6, 2), "TFLOP/s": round(flops2 / g2 / 1e12, 1),
+                  "frac": round(flops2 / g2 / 1e12 / peak, 4)},
+        "step_tflops": round((flops1 + flops2) / sec / 1e12, 1),
+        "peak_tflops": peak,
+        "kernels": kernels,
+        "fused_path_merge": fused_merge,
+        "weight_pack_us": pack_us,
+    }
+    line = {
         "metric": METRIC,
         "value": round(T / sec, 1),
         "unit": "tokens/s",
@@ -199,18 +289,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded N(0,1) features; random-init weights)",
-        "config": {
-            "workload": w.name, "images": w.n_images, "views": len(w.grids),
-            "grid": list(w.grids[0]), "C": w.C, "k": w.k, "hidden": w.hidden,
-            "out_dim": w.out_dim, "layernorm": w.has_ln, "seq_len": w.seq_len,
-            "visual_tokens": T, "placeholder_slots": P, "layout": "tiled_2d" if w.tiled else "plain",
-        },
+        "config": config,
         "roofline": {
             "bound": "mfma",
-            "kernel": "Linear1 (GEMM + bias + GELU on the blocked merged tokens; 256-tile body "
-                      "and 128-tile tail in one dispatch)",
+            "kernel": "Linear1 (GEMM + bias + GELU over the merged tokens)",
             "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
         },
@@ -221,28 +305,33 @@ def main():
             "step": round((flops1 + flops2) / sec / 1e12, 1),
         },
         "kernels": kernels,
+        "weight_pack_us": pack_us,
     }
 
-    out["weight_pack_us"] = pack_us
-
-    if not args.no_sclk:
-        out["sclk"] = sclk_under_load(step, torch, sec)
+    if not args.no_sclk and headline:
+        line["sclk"] = sclk_under_load(args.sampler, step, torch, sec)
 
     if not args.no_hbm_kernels:
-        out["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
-
-    if not args.no_train and w.dtype == "bf16":
-        out["train_step"] = train_step(v, torch, wl, w, p, b, t, d, T, K1, args.steps)
-
-    if not args.no_depth and w.dtype == "bf16":
-        out["depth3_step"] = depth3_step(v, torch, wl, w, b, t, d, T, args.steps)
-
-    if not args.no_embed and w.dtype == "bf16":
-        out["embed_step"] = embed_step(v, torch, wl, w, b, t, d, br, args.steps)
-
+        summary["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
+        line["hbm_kernels"] = summary["hbm_kernels"]
+    del ws, seq, feats
+    if extras and bf16:
+        if not args.no_train:
+            line["train_step"] = summary["train_step"] = train_step(v, torch, wl, w, p, b, t, d, T,
+                                                                    K1, args.steps)
+        if not args.no_depth:
+            line["depth3_step"] = summary["depth3_step"] = depth3_step(v, torch, wl, w, b, t, d, T,
+                                                                       args.steps)
+        if not args.no_embed:
+            line["embed_step"] = summary["embed_step"] = embed_step(v, torch, wl, w, b, t, d, br,
+                                                                    args.steps)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, t, T, args.cpu_seconds)
-    print(json.dumps(out))
+        target = args.cpu_seconds if headline else args.cpu_seconds_other
+        cb = cpu_baseline(w, t, T, target)
+        summary["cpu_baseline"] = cb
+        if headline:
+            line["cpu_baseline"] = cb
+    return {"summary": summary, "line": line}
 
 
 def depth3_step(v, torch, wl, w, b, t, d, T, steps):
@@ -361,40 +450,82 @@ def hbm_kernels(v, torch, w, p, b, t, d, T, K1, steps):
     return res
 
 
-def sclk_under_load(step, torch, sec_per_step, seconds=2.5):
-    """GFX clock of every XCD sampled with amd-smi (a child process) while the
-    step runs back to back for a few seconds after the timed region; the
-    samples' median and range in MHz, or None when amd-smi is unavailable."""
-    import re
-    import subprocess
-    import threading
-    samples, stop = [], threading.Event()
+_SAMPLER = r"""
+import re, subprocess, sys, time
+pat = re.compile(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+) MHz")
+while True:
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True, timeout=10)
+    except Exception:
+        sys.exit(0)
+    mhz = pat.findall(r.stdout)
+    if not mhz:
+        sys.exit(0)
+    print(time.monotonic(), *mhz, flush=True)
+"""
 
-    def sample():
-        while not stop.is_set():
+
+class ClockSampler:
+    """GFX clocks of every XCD from amd-smi, sampled back to back by a child
+    process that is started before this process touches the GPU (a process that
+    has initialised the GPU must not start programs itself).  Each output line is
+    a CLOCK_MONOTONIC time stamp and the clocks in MHz."""
+
+    def __init__(self):
+        import subprocess
+        import threading
+        self.lines = []
+        try:
+            self.proc = subprocess.Popen([sys.executable, "-c", _SAMPLER], stdout=subprocess.PIPE,
+                                         stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            self.proc = None
+            return
+        self.reader = threading.Thread(target=self._read, daemon=True)
+        self.reader.start()
+
+    def _read(self):
+        for line in self.proc.stdout:
+            self.lines.append(line.split())
+
+    def window(self, t0, t1):
+        """Samples taken in [t0, t1] (time.monotonic()), flattened over XCDs."""
+        out = []
+        for f in list(self.lines):
+            if len(f) > 1 and t0 <= float(f[0]) <= t1:
+                out.extend(int(x) for x in f[1:])
+        return out
+
+    def stop(self):
+        if self.proc is not None and self.proc.poll() is None:
+            self.proc.terminate()
             try:
-                r = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True,
-                                   timeout=10)
-            except Exception:  # noqa: BLE001 - no tool, no sample
-                return
-            samples.extend(int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+) MHz",
-                                                      r.stdout))
-    th = threading.Thread(target=sample, daemon=True)
-    th.start()
+                self.proc.wait(timeout=10)
+            except Exception:  # noqa: BLE001
+                self.proc.kill()
+
+
+def sclk_under_load(sampler, step, torch, sec_per_step, seconds=2.5):
+    """GFX clock while the step runs back to back for a few seconds after the
+    timed region: the samples' median and range in MHz, or None when amd-smi
+    gave none."""
+    if sampler is None or sampler.proc is None:
+        return None
     n = max(1, int(seconds / max(sec_per_step, 1e-6)))
+    t0 = time.monotonic()
     for i in range(n):
         step()
         if i % 200 == 199:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    stop.set()
-    th.join(timeout=15)
+    t1 = time.monotonic()
+    samples = sorted(sampler.window(t0, t1))
     if not samples:
         return None
-    samples.sort()
     q = lambda f: samples[min(len(samples) - 1, int(f * len(samples)))]
     return {"median_mhz": q(0.5), "p10_mhz": q(0.1), "p90_mhz": q(0.9), "samples": len(samples),
-            "how": "amd-smi metric -c, per-XCD GFX clocks, sampled during an untimed burst of steps"}
+            "how": "amd-smi metric -c (per-XCD GFX clocks) in a child process, samples taken "
+                   "during an untimed burst of steps"}
 
 
 def train_step(v, torch, wl, w, p, b, t, d, T, K1, steps):
@@ -467,7 +598,7 @@ def cpu_baseline(w, t, T, target_s):
     spec = o.Spec(grids=w.grids, C=w.C, k=w.k, hidden=w.hidden, out_dim=w.out_dim,
                   views_per_image=w.views_per_image, has_ln=w.has_ln, ln_eps=w.ln_eps,
                   tiled=w.tiled, tiles=w.tiles, global_tail=w.global_tail)
-    cores = min(os.cpu_count() or 1, 16)
+    cores, cpu_count, avail = host_threads()
     args = [t["features"], t["ln_gamma"], t["ln_beta"], t["w1"], t["b1"], t["w2"], t["b2"]]
     wide = [o._f64(a) for a in args]  # widening is input marshalling, outside the timed part
     n = cores
@@ -482,9 +613,11 @@ def cpu_baseline(w, t, T, target_s):
     t0 = time.perf_counter()
     o.project_rows(spec, *wide, row_ids=list(range(n)), nthreads=cores)
     dt = time.perf_counter() - t0
+    steps = "LayerNorm, merge" if w.has_ln else "merge"
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {T} token rows of the same workload through the fp64 oracle "
-                      f"(LayerNorm, merge, Linear, GELU, Linear), {dt:.1f} s on {cores} threads"}
+            "host_cpu_count": cpu_count, "host_cpus_available": avail,
+            "sample": f"first {n} of {T} token rows of {w.name} through the fp64 oracle "
+                      f"({steps}, Linear, GELU, Linear), {dt:.1f} s on {cores} threads"}
 
 
 if __name__ == "__main__":

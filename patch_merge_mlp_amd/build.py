@@ -29,24 +29,30 @@ def compile_flags():
     ]
 
 
+def _compile(src: str, build_dir: str, verbose: bool) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *compile_flags(), "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    return obj
+
+
 def build(verbose: bool = False) -> str:
-    """Always recompiles (this is the does-it-build check) and returns the .so path."""
-    objs = []
+    """Always recompiles (this is the does-it-build check) and returns the .so path.
+    The sources compile in parallel, at most 8 at a time."""
+    from concurrent.futures import ThreadPoolExecutor
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src in sources():
-        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *compile_flags(), "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), file=sys.stderr)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "is not a recognized feature for this target"
-        err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
-        if err.strip() and verbose:
-            print(err, file=sys.stderr)
-        objs.append(obj)
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, build_dir, verbose), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
