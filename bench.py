@@ -314,6 +314,10 @@ def measure_config(args, v, wl, torch, i, headline, extras):
     if not args.no_hbm_kernels:
         summary["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
         line["hbm_kernels"] = summary["hbm_kernels"]
+    if bf16 and not w.has_ln:
+        summary["operand_source"] = operand_sources(v, torch, w, p, b, br, feats, nl, sep, mask,
+                                                    seq, T, args.steps)
+        line["operand_source"] = summary["operand_source"]
     del ws, seq, feats
     if extras and bf16:
         if not args.no_train:
@@ -332,6 +336,46 @@ def measure_config(args, v, wl, torch, i, headline, extras):
         if headline:
             line["cpu_baseline"] = cb
     return {"summary": summary, "line": line}
+
+
+def operand_sources(v, torch, w, p, b, br, feats, nl, sep, mask, seq, T, steps):
+    """Both sources of Linear1's operand, timed alike (steps // 2 calls after 10
+    warm-ups): the grid merged into a blocked operand first, or gathered by
+    Linear1's loads (vlb_projector.gather); which one the automatic choice
+    (the timed step above) took, and Linear1's mean time in each."""
+    res = {}
+    on = v.vlb_projector.from_buffer_copy(br.p)
+    on.gather = v.GATHER_ON
+    off = v.vlb_projector.from_buffer_copy(br.p)
+    off.gather = v.GATHER_OFF
+    n_auto = v.vlb_workspace_bytes(br.p, b, w.seq_len)
+    res["auto_picks"] = "gather" if n_auto == v.vlb_workspace_bytes(on, b, w.seq_len) else "merge"
+    for name, pm in (("merge", off), ("gather", on)):
+        ws = torch.empty(v.vlb_workspace_bytes(pm, b, w.seq_len), dtype=torch.uint8, device="cuda")
+
+        def one():
+            v.vlb_bridge_fused(pm, b, feats, br.w, nl, sep, mask, seq, ws)
+
+        for _ in range(10):
+            one()
+        torch.cuda.synchronize()
+        assert v.vlb_check(ws) == v.OK
+        n = max(10, steps // 2)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            one()
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / n
+        v.vlb_prof_enable(1 << v.K_GEMM1)
+        for _ in range(max(3, n // 4)):
+            one()
+        torch.cuda.synchronize()
+        v.vlb_prof_enable(False)
+        k, ms = v.vlb_prof_read(v.K_GEMM1)
+        res[name] = {"ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(T / sec, 1),
+                     "gemm1_us": round(1000.0 * ms / k, 2)}
+        del ws
+    return res
 
 
 def depth3_step(v, torch, wl, w, b, t, d, T, steps):

@@ -76,6 +76,18 @@ typedef enum { VLB_GELU_ERF = 0, VLB_GELU_TANH = 1, VLB_ACT_NONE = 2 } vlb_act;
  * mosaic with one newline per mosaic row [VL2 Tile-sequence assembly]. */
 typedef enum { VLB_LAYOUT_PLAIN = 0, VLB_LAYOUT_TILED_2D = 1 } vlb_layout;
 
+/* VLB_GATHER_ON: the first Linear reads each merged token straight from the
+ * patch grid -- the space-to-depth [VL2 Projector 2] happens inside its operand
+ * loads -- so the merged tokens never exist in memory and the workspace is
+ * T * C * k * k * 2 bytes smaller (T rounded up to 256).  VLB_BF16 without
+ * LayerNorm only (else VLB_ERR_UNSUPPORTED).  VLB_GATHER_OFF: the grid is first
+ * merged (with the LayerNorm, when on) into the GEMM's blocked operand.
+ * VLB_GATHER_AUTO: the library chooses -- the gather for VLB_BF16 without
+ * LayerNorm and hidden <= 4096, where the merge pass costs more than the
+ * slower gathered loads.  Both forms give the same bits.  The training forward
+ * keeps the merged tokens, so it always merges. */
+typedef enum { VLB_GATHER_AUTO = 0, VLB_GATHER_ON = 1, VLB_GATHER_OFF = 2 } vlb_gather;
+
 /* The projector: LN(C) (optional, per patch, biased variance, eps inside the
  * square root, affine) -> pad to a multiple of k -> k x k space-to-depth with
  * feature index c*k*k + dy*k + dx [VL2 Projector 1-2] -> Linear(C*k*k ->
@@ -96,6 +108,7 @@ typedef struct {
                         vlb_pack_weights, and weights.w_mid[i] those made by
                         vlb_pack_mid (VLB_BF16 only) */
   int32_t depth;     /* Linears in the projector: 2..16; 0 is read as 2 */
+  int32_t gather;    /* vlb_gather: where the first Linear's operand comes from */
 } vlb_projector;
 
 /* Weights in PyTorch Linear layout (out_features, in_features), as stored and

@@ -52,6 +52,19 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Linear1 reads the merged tokens straight from the grid (vlb_projector.gather).
+// Gathered operand loads slow Linear1 by 8-11% (16 separate 64-byte pieces per
+// load instruction instead of one contiguous KiB), which grows with its
+// hidden width, while the merge pass it saves moves a fixed T * C * k * k * 4
+// bytes.  Measured: hidden 2560 (the tiled 2x2 workload) runs 3% faster per
+// call with the gather, hidden 5120 (both 3x3 workloads) 1.7% slower; the
+// automatic choice takes the gather up to hidden 4096.
+constexpr int kGatherMaxHidden = 4096;
+bool gathers(const vlb_projector *p) {
+  if (p->dtype != VLB_BF16 || p->has_ln || p->gather == VLB_GATHER_OFF) return false;
+  return p->gather == VLB_GATHER_ON || p->hidden <= kGatherMaxHidden;
+}
+
 vlb_status check_projector(const vlb_projector *p) {
   if (!p) return VLB_ERR_NULL;
   if (p->dtype != VLB_F32 && p->dtype != VLB_BF16) return VLB_ERR_DTYPE;
@@ -66,6 +79,9 @@ vlb_status check_projector(const vlb_projector *p) {
   if ((p->has_ln || p->dtype == VLB_BF16) && p->C > vlb::layernorm_max_channels(p->dtype))
     return VLB_ERR_UNSUPPORTED;
   if (p->packed && p->dtype != VLB_BF16) return VLB_ERR_UNSUPPORTED;
+  if (p->gather < VLB_GATHER_AUTO || p->gather > VLB_GATHER_OFF) return VLB_ERR_UNSUPPORTED;
+  if (p->gather == VLB_GATHER_ON && (p->dtype != VLB_BF16 || p->has_ln))
+    return VLB_ERR_UNSUPPORTED;
   if (p->depth < 0 || p->depth == 1) return VLB_ERR_SHAPE;
   if (p->depth > kMaxDepth) return VLB_ERR_UNSUPPORTED;
   const int64_t K1 = static_cast<int64_t>(p->C) * p->k * p->k;
@@ -151,8 +167,10 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   off = align256(off + static_cast<size_t>(pl->T) * 4);
   pl->off_desc = off;
   off = align256(off + static_cast<size_t>(pl->T) * sizeof(RowDesc));
-  pl->off_xn = off;  // bf16: merged tokens, tile-blocked; fp32: the normalised grid
-  if (p->dtype == VLB_BF16)
+  // bf16: the (normalised) merged tokens, tile-blocked -- not kept when
+  // Linear1 gathers its operand from the grid; fp32: the normalised grid
+  pl->off_xn = off;
+  if (p->dtype == VLB_BF16 && !gathers(p))
     off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl->T, pl->K1)) * 2);
   else if (p->has_ln)
     off = align256(off + static_cast<size_t>(pl->npix) * p->C * pl->es);
@@ -390,7 +408,15 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
                                 scan->P, scan->slot_pos, scan->status, scan->direct, s));
     scan = nullptr;
   }
-  if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
+  // Gather mode (the projector's gather flag; bf16 without LayerNorm, and no
+  // merged tokens to keep): Linear1 reads its operand straight from the grid
+  // through per-token descriptors, and the scan rides in the descriptor launch.
+  const bool gather = gathers(p) && !saved;
+  if (gather) {
+    for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
+      VLB_LAUNCH(VLB_K_PLAN, s,
+                 vlb::launch_plan(view_chunk(p, b, pl, v0), desc, s, v0 == 0 ? scan : nullptr));
+  } else if (p->dtype == VLB_BF16) {  // LN (optional) + merge into Linear1's blocked operand
     void *xm = saved ? saved + sl.off_xm : ws + pl.off_xn;
     for (int v0 = 0; v0 < b->n_views; v0 += vlb::kPlanViews)
       VLB_LAUNCH(p->has_ln ? VLB_K_LN : VLB_K_MERGE, s,
@@ -460,11 +486,15 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
     g1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->hidden, pl.K1) * 2);
     g2.B = w2p;
     g2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(p->out_dim, p->hidden) * 2);
-    g1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, pl.K1) * 2);
+    g1.a_bytes = gather ? static_cast<uint32_t>(pl.npix * p->C * 2)
+                        : static_cast<uint32_t>(vlb::blocked_elems(pl.T, pl.K1) * 2);
     g2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(pl.T, p->hidden) * 2);
     g1.out2 = saved ? saved + sl.off_z1 : nullptr;
     VLB_LAUNCH(VLB_K_GEMM1, s,
-               vlb::launch_gemm_bf16(saved ? vlb::kGemmBlockedSave : vlb::kGemmBlocked, g1, s));
+               vlb::launch_gemm_bf16(saved    ? vlb::kGemmBlockedSave
+                                     : gather ? vlb::kGemmGatherBlocked
+                                              : vlb::kGemmBlocked,
+                                     g1, s));
     // middle Linears: act(H W^T + b), blocked in and out, alternating buffers
     for (int q = 0; q + 2 < proj_depth(p); ++q) {
       const void *wm = w->w_mid[q];

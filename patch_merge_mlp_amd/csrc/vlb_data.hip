@@ -22,30 +22,6 @@ constexpr int kErrMaskCount = 6;  // VLB_ERR_MASK_COUNT
 constexpr int kLnChunks = 8;      // LayerNorm: most 16-byte chunks a lane holds
 
 // ---------------------------------------------------------------------------
-// Gather descriptor of every token row of a chunk of views.
-__global__ void k_plan(PlanChunk c, RowDesc *desc) {
-  const int32_t r = c.tok0[0] + blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= c.tok0[c.n]) return;
-  int lo = 0, hi = c.n - 1;
-  while (lo < hi) {  // last view whose first token is <= r
-    const int mid = (lo + hi + 1) >> 1;
-    if (c.tok0[mid] <= r) lo = mid;
-    else hi = mid - 1;
-  }
-  const int v = lo, k = c.k;
-  const int gh = c.gh[v], gw = c.gw[v];
-  const int wp = (gw + k - 1) / k;
-  const int t = r - c.tok0[v];
-  const int y0 = (t / wp) * k, x0 = (t % wp) * k;
-  uint32_t inside = 0;
-  for (int dy = 0; dy < k; ++dy)
-    for (int dx = 0; dx < k; ++dx)
-      if (y0 + dy < gh && x0 + dx < gw) inside |= 1u << (dy * k + dx);
-  desc[r].pix = c.pix0[v] + y0 * gw + x0;
-  desc[r].geo = gw | static_cast<int32_t>(inside << 16);
-}
-
-// ---------------------------------------------------------------------------
 // Placeholder prefix sum: slot_pos[j] = position of the j-th placeholder.
 // The placeholders are the nonzero bytes of a mask, or (token-id form) the
 // positions whose id equals the image token; in the id form every other id
@@ -194,6 +170,42 @@ __device__ __forceinline__ void scan_body(const ScanArgs &a, int32_t *s_pos) {
 __global__ __launch_bounds__(kScanThreads) void k_scan(ScanArgs a) {
   __shared__ int32_t s_pos[kScanChunk];  // this pass's placeholder positions, in order
   scan_body(a, s_pos);
+}
+
+// ---------------------------------------------------------------------------
+// Gather descriptor of every token row of a chunk of views, 1024 rows per
+// workgroup.  With a ScanArgs job, workgroup 0 of the launch runs the
+// placeholder scan instead (scan_body; dynamic LDS of kScanChunk positions),
+// beside the descriptors: the two touch different data.
+__global__ __launch_bounds__(kScanThreads) void k_plan(PlanChunk c, RowDesc *desc, ScanArgs scan) {
+  extern __shared__ int32_t plan_lds[];
+  int blk = blockIdx.x;
+  if (scan.on) {
+    if (blk == 0) {
+      scan_body(scan, plan_lds);
+      return;
+    }
+    --blk;
+  }
+  const int32_t r = c.tok0[0] + blk * kScanThreads + threadIdx.x;
+  if (r >= c.tok0[c.n]) return;
+  int lo = 0, hi = c.n - 1;
+  while (lo < hi) {  // last view whose first token is <= r
+    const int mid = (lo + hi + 1) >> 1;
+    if (c.tok0[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int v = lo, k = c.k;
+  const int gh = c.gh[v], gw = c.gw[v];
+  const int wp = (gw + k - 1) / k;
+  const int t = r - c.tok0[v];
+  const int y0 = (t / wp) * k, x0 = (t % wp) * k;
+  uint32_t inside = 0;
+  for (int dy = 0; dy < k; ++dy)
+    for (int dx = 0; dx < k; ++dx)
+      if (y0 + dy < gh && x0 + dx < gw) inside |= 1u << (dy * k + dx);
+  desc[r].pix = c.pix0[v] + y0 * gw + x0;
+  desc[r].geo = gw | static_cast<int32_t>(inside << 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -775,10 +787,16 @@ int grid_for(int64_t waves_or_items, int per_block, int cap) {
 
 }  // namespace
 
-hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s) {
+hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s, const ScanJob *scan) {
   const int64_t n = c.tok0[c.n] - c.tok0[0];
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_plan, dim3(grid_for(n, 256, 1 << 30)), dim3(256), 0, s, c, desc);
+  if (n <= 0)  // no rows: the scan (if any) runs on its own
+    return scan ? launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
+                              scan->P, scan->slot_pos, scan->status, scan->direct, s)
+                : hipSuccess;
+  const ScanArgs sa = scan_args(scan);
+  const int grid = grid_for(n, kScanThreads, 1 << 30) + (sa.on ? 1 : 0);
+  const size_t lds = sa.on ? kScanChunk * sizeof(int32_t) : 0;
+  hipLaunchKernelGGL(k_plan, dim3(grid), dim3(kScanThreads), lds, s, c, desc, sa);
   return hipGetLastError();
 }
 

@@ -262,7 +262,7 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 // distinct LDS objects to the compiler.  K steps [ks0, ks0 + ksn) of the
 // product are accumulated; with part set (kGemmF32 only) the whole BMT x BMT
 // fp32 tile goes to part, row-major, instead of to out.
-template <int MODE, int ACT, int BMT, int SZ>
+template <int MODE, int ACT, int BMT, bool GA, int SZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uint8_t (&smem0)[SZ],
                                           uint8_t (&smem1)[SZ], uint8_t (&smem2)[SZ],
                                           uint8_t (&smem3)[SZ], uint16_t *s_bias,
@@ -295,16 +295,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   auto blocked = [&](int r) {
     return (static_cast<uint32_t>(r >> 8) * KB * 256 + static_cast<uint32_t>(r & 255)) * 64;
   };
+  // GA (gathered A, kGemmGatherBlocked): A is the bf16 patch grid itself,
+  // NHWC, and row m's merged token is read through its gather descriptor.  K
+  // runs position-major (k' = p*C + c, the packed W1's order), so the 32-wide
+  // K step kt covers channels [32 c, 32 c + 32) of block position p = (dy, dx)
+  // -- one 64-byte piece of pixel (y0 + dy, x0 + dx) per row.  a_off holds the
+  // piece's offset at p = 0, a_gw the bytes of one grid row, a_inv the
+  // complement of the row's inside-the-grid bits: a position outside the grid
+  // (the high-end zero padding) or a row past M gets bit 31 set, which lies
+  // past every buffer, so the load returns zeros.  Each load instruction then
+  // moves 16 separate 64-byte pieces (half lines, the other half read one step
+  // later) instead of one contiguous KiB, and this loop is sensitive to that:
+  // Linear1 runs 18-25% slower than on the blocked operand, which costs more
+  // than the merge pass it saves (so this is the memory-lean mode, not the
+  // default).
   uint32_t a_off[G::LPW], b_off[G::LPW];
+  uint32_t a_gw[GA ? G::LPW : 1], a_inv[GA ? G::LPW : 1];
+  const uint32_t c2 = static_cast<uint32_t>(g.C) * 2;  // bytes of one pixel (GA)
 #pragma unroll
   for (int i = 0; i < G::LPW; ++i) {
     const int row = wid * (BMT / 4) + 16 * i + (lane >> 2);
     const uint32_t c_off = ((lane & 3) ^ swz_xor(row)) * 16;
     const int m = m0 + row, n = n0 + row;
-    a_off[i] = m < g.M ? blocked(m) + c_off : kOOB;
+    if constexpr (GA) {
+      const RowDesc d = m < g.M ? g.desc[m] : RowDesc{0, 0};
+      a_off[i] = static_cast<uint32_t>(d.pix) * c2 + c_off;
+      a_gw[i] = static_cast<uint32_t>(d.geo & 0xffff) * c2;
+      a_inv[i] = ~(static_cast<uint32_t>(d.geo) >> 16);
+    } else {
+      a_off[i] = m < g.M ? blocked(m) + c_off : kOOB;
+    }
     b_off[i] = n < g.N ? blocked(n) + c_off : kOOB;
   }
-
+  // GA: step ka covers channels [32 c, 32 c + 32) of block position
+  // p = (dy, dx), ka = p * cps + c.  The divisions are multiplications by
+  // 2^20 / divisor rounded up, exact for dividends below 2^20 / divisor (ka <=
+  // K / 32 + 3 <= 1155, cps <= 128, k <= 3), so the loop has no branches.
+  const int ga_cps = g.C / BK;
+  const uint32_t ga_inv_cps = ((1u << 20) + ga_cps - 1) / ga_cps;
+  const uint32_t ga_inv_k = ((1u << 20) + g.k - 1) / g.k;
   // Loads of step kt of the range into `stage` (the first or second half of
   // them when half is 0 or 1, all when -1).  Steps at or past the end of the
   // range read zeros (the loop runs a multiple of NSTAGE steps and prefetches
@@ -316,9 +345,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     uint8_t *sa = stage + wid * G::LPW * 1024;
     uint8_t *sb = stage + G::HALF + wid * G::LPW * 1024;
     const int i0 = half == 1 ? G::LPW / 2 : 0, i1 = half == 0 ? G::LPW / 2 : G::LPW;
+    // GA: the wave-uniform part of the offset; dead (bit 31) is added, not
+    // OR-ed: the sum stays below 2^32 and keeps bit 31 set.
+    const uint32_t ka = static_cast<uint32_t>(ks0 + kt);
+    const uint32_t ga_p = (ka * ga_inv_cps) >> 20, ga_c = ka - ga_p * ga_cps;
+    const uint32_t ga_dy = (ga_p * ga_inv_k) >> 20, ga_dx = ga_p - ga_dy * g.k;
+    const uint32_t ga_s = ga_dx * c2 + ga_c * 64 + dead;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
+      if constexpr (GA) {
+        const uint32_t off = a_off[i] + ga_dy * a_gw[i] + ga_s;
+        load_lds16(rA, sa + i * 1024, off | ((a_inv[i] >> ga_p) << 31));
+      } else {
+        load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
+      }
       load_lds16(rB, sb + i * 1024, (b_off[i] + step_off) | dead);
     }
   };
@@ -449,7 +489,7 @@ __device__ __forceinline__ void tail_coords(const GemmArgs &g, int bid, int &tm,
 // tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
 // quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
 // whole 128-grid).
-template <int MODE, int ACT, int BMT>
+template <int MODE, int ACT, int BMT, bool GA>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   using G = Geo<BMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -463,8 +503,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   else
     tail_coords(g, blockIdx.x, tm, tn);
-  gemm_tile<MODE, ACT, BMT>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, g.K / BK,
-                            nullptr);
+  gemm_tile<MODE, ACT, BMT, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, g.K / BK,
+                                nullptr);
 }
 
 // Both parts in one launch: workgroups [0, n_full) take the 256-tiles, the
@@ -472,7 +512,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
 // whose last whole tile is done starts a quarter tile at once instead of
 // waiting for the slowest whole tile of the launch.  n_full is a multiple of
 // 256, so workgroup n_full + q still runs on XCD q % 8.
-template <int MODE, int ACT>
+template <int MODE, int ACT, bool GA>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   using G = Geo<256>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -486,7 +526,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   const int bid = static_cast<int>(blockIdx.x);
   if (bid < g.n_full) {
     tile_coords(xcd_remap(bid, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
-  } else if (MODE == kGemmF32 && g.k_splits > 1) {
+  } else if (!GA && MODE == kGemmF32 && g.k_splits > 1) {
     // K range r of tail tile q, as a whole tile: workgroup n_full + q*S + r
     // (S = k_splits), its partial tile at split_part + (q*S + r) tiles.
     const int u = bid - g.n_full, q = u / g.k_splits, r = u - q * g.k_splits;
@@ -496,11 +536,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
     part = g.split_part + static_cast<int64_t>(u) * (256 * 256);
   } else {
     tail_coords(g, bid - g.n_full, tm, tn);
-    gemm_tile<MODE, ACT, 128>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, ksn,
-                              nullptr);
+    gemm_tile<MODE, ACT, 128, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, ksn,
+                                  nullptr);
     return;
   }
-  gemm_tile<MODE, ACT, 256>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, ks0, ksn, part);
+  gemm_tile<MODE, ACT, 256, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, ks0, ksn,
+                                part);
 }
 
 // out rows of the split tail tiles: tile q's k_splits partial tiles added in
@@ -524,31 +565,33 @@ __global__ __launch_bounds__(256) void k_split_sum(GemmArgs g) {
       acc;
 }
 
-template <int MODE, int ACT>
+template <int MODE, int ACT, bool GA = false>
 void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
   // Whole tiles and the quarter-tile tail in one launch while the quarter
   // tiles fit one round at one per CU; beyond that the quarter-tile kernel of
   // its own (two per CU: a third of the registers and half the LDS) is faster
   // (dW1 of workload 1, 272 quarter tiles: 340 against 367 us).
   if (blocks256 > 0 && blocks128 > 0 && blocks128 <= kPlanCUs)
-    hipLaunchKernelGGL((k_gemm_bf16_mixed<MODE, ACT>), dim3(blocks256 + blocks128),
+    hipLaunchKernelGGL((k_gemm_bf16_mixed<MODE, ACT, GA>), dim3(blocks256 + blocks128),
                        dim3(NTHREADS), 0, s, g);
   else {
     if (blocks256 > 0)
-      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256>), dim3(blocks256), dim3(NTHREADS), 0, s, g);
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256, GA>), dim3(blocks256), dim3(NTHREADS), 0, s,
+                         g);
     if (blocks128 > 0)
-      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128>), dim3(blocks128), dim3(NTHREADS), 0, s, g);
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128, GA>), dim3(blocks128), dim3(NTHREADS), 0, s,
+                         g);
   }
 }
 
-template <int MODE>
+template <int MODE, bool GA = false>
 void launch_act(const GemmArgs &g, const TilePlan &tp, hipStream_t s) {
   if (g.act == 0)
-    launch_bf16<MODE, 0>(g, tp.n_full, tp.blocks128, s);
+    launch_bf16<MODE, 0, GA>(g, tp.n_full, tp.blocks128, s);
   else if (g.act == 1)
-    launch_bf16<MODE, 1>(g, tp.n_full, tp.blocks128, s);
+    launch_bf16<MODE, 1, GA>(g, tp.n_full, tp.blocks128, s);
   else
-    launch_bf16<MODE, 2>(g, tp.n_full, tp.blocks128, s);
+    launch_bf16<MODE, 2, GA>(g, tp.n_full, tp.blocks128, s);
 }
 
 }  // namespace
@@ -562,6 +605,10 @@ hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
   g.n_full = tp.n_full;
   switch (mode) {
     case kGemmBlocked: launch_act<kGemmBlocked>(g, tp, s); break;
+    case kGemmGatherBlocked:  // A gathered from the grid through g.desc
+      if (!g.desc || g.C % BK || g.k < 1 || g.k > 3) return hipErrorInvalidValue;
+      launch_act<kGemmBlocked, true>(g, tp, s);
+      break;
     case kGemmBlockedSave:
       if (!g.out2) return hipErrorInvalidValue;
       launch_act<kGemmBlockedSave>(g, tp, s);
@@ -576,7 +623,7 @@ hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
       g.k_splits = S;
       if (S > 1) {  // whole tiles and the split tail in one launch, then the sums
         const int rem = tp.tiles_m * tp.tiles_n - tp.n_full;
-        hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2>), dim3(tp.n_full + rem * S),
+        hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2, false>), dim3(tp.n_full + rem * S),
                            dim3(NTHREADS), 0, s, g);
         hipLaunchKernelGGL(k_split_sum, dim3(64, rem), dim3(256), 0, s, g);
       } else {

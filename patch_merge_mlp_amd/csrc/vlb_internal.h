@@ -93,6 +93,11 @@ enum GemmMode {
   kGemmRows = 1,         // bias, bf16 rows to dst(m) (Linear2)
   kGemmF32 = 2,          // fp32 rows out + m*ldo, no bias (weight gradients)
   kGemmBlockedSave = 3,  // kGemmBlocked, and bias without activation to out2 as well
+  // kGemmBlocked with A gathered from the bf16 patch grid (NHWC, g.A) through
+  // the per-token descriptors g.desc: the merge is never materialised.  K runs
+  // position-major (the packed W1's order); g.C (a multiple of 32) and g.k
+  // give the block geometry, g.a_bytes the grid's extent.
+  kGemmGatherBlocked = 4,
 };
 
 // Tile plan of the bf16 GEMM.  256x256 tiles keep the MFMAs busiest, but on
@@ -150,7 +155,6 @@ inline size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 // ---- launchers (return the launch error, hipSuccess otherwise) ------------
-hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s);
 // Placeholder scan over a uint8 mask (ids == nullptr) or over token ids
 // (placeholder = image_id; other ids must lie in [0, vocab)).
 // direct (plain layout): slot_pos is dst_row [P] and receives the positions
@@ -171,6 +175,10 @@ struct ScanJob {
   int32_t *status;
   bool direct;
 };
+// Gather descriptors of the token rows of one chunk of views; with scan
+// non-null, the launch also runs that placeholder scan (one extra workgroup).
+hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s,
+                       const ScanJob *scan = nullptr);
 // seq[s] = embed[ids[s]] where ids[s] != image_id (nothing if the scan failed).
 hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
                              const void *embed, int D, const int32_t *status, void *seq,

@@ -23,6 +23,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
 F32, BF16 = 0, 1
 GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
+GATHER_AUTO, GATHER_ON, GATHER_OFF = 0, 1, 2
 K_PLAN, K_SCAN, K_PLACE, K_LN, K_GEMM1, K_GEMM2, K_SCATTER, K_MERGE, K_PACK, K_EMBED, \
     K_BWD_PACK, K_BWD_DW2, K_BWD_DA1, K_BWD_DW1, K_BWD_DX, K_BWD_UNMERGE, K_BWD_SUM, \
     K_GEMM_MID = range(18)
@@ -41,7 +42,7 @@ class vlb_projector(ct.Structure):
     _fields_ = [("dtype", ct.c_int32), ("C", ct.c_int32), ("k", ct.c_int32),
                 ("hidden", ct.c_int32), ("out_dim", ct.c_int32), ("has_ln", ct.c_int32),
                 ("ln_eps", ct.c_float), ("act", ct.c_int32), ("packed", ct.c_int32),
-                ("depth", ct.c_int32)]
+                ("depth", ct.c_int32), ("gather", ct.c_int32)]
 
 
 class vlb_weights(ct.Structure):
@@ -139,9 +140,9 @@ def _check(status: int, where: str):
 
 def projector(dtype: int, C: int, k: int, hidden: int, out_dim: int, has_ln: bool = False,
               ln_eps: float = 1e-6, act: int = GELU_ERF, packed: bool = False,
-              depth: int = 2) -> vlb_projector:
+              depth: int = 2, gather: int = 0) -> vlb_projector:
     return vlb_projector(dtype, C, k, hidden, out_dim, int(has_ln), ln_eps, act, int(packed),
-                         depth)
+                         depth, int(gather))
 
 
 def _depth(p: vlb_projector) -> int:

@@ -36,9 +36,10 @@ def draw(w: wl.Workload) -> dict:
     return wl.make(w, oracle_spans, lambda ww: ww.C * ww.k * ww.k)
 
 
-def lib_projector(w: wl.Workload, act=v.GELU_ERF, has_ln=None) -> v.vlb_projector:
+def lib_projector(w: wl.Workload, act=v.GELU_ERF, has_ln=None, gather=False) -> v.vlb_projector:
     return v.projector(v.F32 if w.dtype == "f32" else v.BF16, w.C, w.k, w.hidden, w.out_dim,
-                       has_ln=w.has_ln if has_ln is None else has_ln, ln_eps=w.ln_eps, act=act)
+                       has_ln=w.has_ln if has_ln is None else has_ln, ln_eps=w.ln_eps, act=act,
+                       gather=gather)
 
 
 def lib_batch(w: wl.Workload) -> v.Batch:

@@ -34,8 +34,8 @@ def _weights(t):
     return v.Weights(*(_dev(t[n]) for n in ("w1", "b1", "w2", "b2", "ln_gamma", "ln_beta")))
 
 
-def run_fused(w, t, act=v.GELU_ERF, pack=True, has_ln=None, weights=None):
-    p = common.lib_projector(w, act, has_ln)
+def run_fused(w, t, act=v.GELU_ERF, pack=True, has_ln=None, weights=None, gather=v.GATHER_AUTO):
+    p = common.lib_projector(w, act, has_ln, gather)
     b = common.lib_batch(w)
     br = v.Bridge(p, weights or _weights(t), pack=pack)
     seq = _dev(t["seq"]).clone()
@@ -107,12 +107,17 @@ def test_small_fused_vs_oracle(w):
     rows = o.project_rows(spec, t["features"], t["ln_gamma"], t["ln_beta"], t["w1"], t["b1"],
                           t["w2"], t["b2"])
     ref = expected_seq(w, t, rows)
-    for pack in (True, False) if w.dtype == "bf16" else (True,):
-        st, out = run_fused(w, t, pack=pack)
+    modes = [(True, v.GATHER_AUTO)]
+    if w.dtype == "bf16":
+        modes.append((False, v.GATHER_AUTO))
+        if not w.has_ln:  # both sources of Linear1's operand
+            modes += [(True, v.GATHER_ON), (True, v.GATHER_OFF)]
+    for pack, gather in modes:
+        st, out = run_fused(w, t, pack=pack, gather=gather)
         assert st == v.OK
         check_text_rows(t, out)
         errs = per_image_errors(w, t, out.double().numpy(), ref)
-        print(w.name, "pack" if pack else "nopack", "max rel err", max(errs))
+        print(w.name, "pack" if pack else "nopack", "gather", gather, "max rel err", max(errs))
         assert max(errs) <= TOL[w.dtype], errs
         if w.tiled:  # newline / separator rows are copies
             spec_src = o.assemble(spec)
@@ -319,6 +324,59 @@ def test_full_config_exact_placement(i):
             "expected values are not exact bf16 values"
         bad = (out.float() != want.float()).any(dim=1)
         assert not bad.any(), f"{int(bad.sum())} rows differ, first at {int(bad.nonzero()[0])}"
+
+
+# ---- gather mode: Linear1 reads the merged tokens from the grid -------------------
+
+def _gather_workloads():
+    # bf16 without LayerNorm: 3x3 odd and rectangular grids, tiled head and tail,
+    # k = 1, grids of one cell and one row
+    ws = [w for w in small_workloads() if w.dtype == "bf16" and not w.has_ln]
+    ws.append(wl.Workload("tiny-grids", 21, "bf16", C=64, k=3, hidden=64, out_dim=64, seq_len=64,
+                          grids=[(1, 1), (1, 7), (4, 1)], views_per_image=[1, 1, 1]))
+    return ws
+
+
+@pytest.mark.parametrize("w", _gather_workloads(), ids=lambda w: w.name)
+def test_gather_mode_small_vs_oracle(w):
+    """Gather mode: the whole output against the oracle, and bit for bit the
+    merging path's (the same bf16 operand values in the same K order and tiles)."""
+    t = common.draw(w)
+    rows = o.project_rows(common.oracle_spec(w), t["features"], None, None, t["w1"], t["b1"],
+                          t["w2"], t["b2"])
+    ref = expected_seq(w, t, rows)
+    st, out = run_fused(w, t, gather=v.GATHER_ON)
+    assert st == v.OK
+    check_text_rows(t, out)
+    errs = per_image_errors(w, t, out.double().numpy(), ref)
+    assert max(errs) <= TOL["bf16"], errs
+    st, base = run_fused(w, t, gather=v.GATHER_OFF)
+    assert st == v.OK
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+@pytest.mark.parametrize("i", [2, 3, 4])
+def test_gather_mode_full_config_bits(i):
+    """Both operand sources at full size on the workloads without LayerNorm give
+    the same bits in every slot (test_full_config_all_rows holds the automatic
+    choice against the oracle row by row)."""
+    w, t = full(i)
+    st, out = run_fused(w, t, gather=v.GATHER_ON)
+    assert st == v.OK
+    st, base = run_fused(w, t, gather=v.GATHER_OFF)
+    assert st == v.OK
+    same = (out.view(torch.int16) == base.view(torch.int16)).all(dim=1)
+    assert bool(same.all()), f"{int((~same).sum())} rows differ, first at {int((~same).nonzero()[0])}"
+
+
+def test_gather_mode_count_mismatch_writes_nothing():
+    w = _gather_workloads()[0]
+    t = common.draw(w)
+    mask = t["mask"].clone()
+    mask[int(np.flatnonzero(mask.numpy())[-1])] = 0
+    st, out = run_fused(w, dict(t, mask=mask), gather=v.GATHER_ON)
+    assert st == v.ERR_MASK_COUNT
+    assert torch.equal(out.view(torch.int16), t["seq"].view(torch.int16))
 
 
 # ---- standalone merge and scatter ---------------------------------------------------

@@ -85,6 +85,9 @@ def _proj(**kw):
     (dict(C=4160), v.ERR_UNSUPPORTED), (dict(dtype=v.F32, C=2056, has_ln=True), v.ERR_UNSUPPORTED),
     (dict(act=5), v.ERR_UNSUPPORTED), (dict(has_ln=True, ln_eps=0.0), v.ERR_SHAPE),
     (dict(dtype=v.F32, packed=True), v.ERR_UNSUPPORTED),
+    (dict(gather=v.GATHER_ON, dtype=v.F32), v.ERR_UNSUPPORTED),
+    (dict(gather=v.GATHER_ON, has_ln=True), v.ERR_UNSUPPORTED),
+    (dict(gather=3), v.ERR_UNSUPPORTED), (dict(gather=-1), v.ERR_UNSUPPORTED),
 ])
 def test_bad_projector(kw, status):
     p = _proj(**kw)
@@ -328,3 +331,26 @@ def test_operand_size_limits():
     b = v.Batch([(4, 4)], [1])
     assert L.vlb_workspace_bytes(ct.byref(ps), ct.byref(b.c), (1 << 19) - 1) > 0
     assert L.vlb_workspace_bytes(ct.byref(ps), ct.byref(b.c), 1 << 19) == 0
+
+
+def test_gather_mode_workspace():
+    """Gathering drops the merged tokens from the workspace (T rounded up to 256
+    rows of C*k*k bf16).  The automatic choice gathers for bf16 without
+    LayerNorm up to hidden 4096; fp32 and the LayerNorm keep their own layout.
+    The training sizes do not depend on the flag."""
+    b = v.Batch([(9, 7), (4, 4)], [1, 1])
+    T = v.vlb_num_tokens(_proj(), b)
+    assert T == 5 * 4 + 4
+    merged = 256 * 64 * 4 * 2
+    off = v.vlb_workspace_bytes(_proj(gather=v.GATHER_OFF), b, 32)
+    on = v.vlb_workspace_bytes(_proj(gather=v.GATHER_ON), b, 32)
+    assert off - on == merged
+    assert v.vlb_workspace_bytes(_proj(), b, 32) == on                      # auto, hidden 128
+    big = dict(hidden=4160, out_dim=64)
+    assert (v.vlb_workspace_bytes(_proj(**big), b, 32)
+            - v.vlb_workspace_bytes(_proj(gather=v.GATHER_ON, **big), b, 32)) == merged
+    assert (v.vlb_workspace_bytes(_proj(has_ln=True), b, 32)
+            == v.vlb_workspace_bytes(_proj(has_ln=True, gather=v.GATHER_OFF), b, 32))
+    assert v.vlb_workspace_bytes(_proj(dtype=v.F32), b, 32) == \
+        v.vlb_workspace_bytes(_proj(dtype=v.F32, gather=v.GATHER_OFF), b, 32)
+    assert v.vlb_saved_bytes(_proj(gather=v.GATHER_ON), b) == v.vlb_saved_bytes(_proj(), b)
