@@ -60,7 +60,8 @@ typedef enum {
   VLB_ERR_MASK_COUNT = 6,  /* placeholder count != assembled slots (device-detected) */
   VLB_ERR_UNSUPPORTED = 7, /* a valid but unsupported setting */
   VLB_ERR_HIP = 8,         /* a HIP runtime call failed */
-  VLB_ERR_TOKEN_ID = 9     /* a text token id outside [0, vocab) (device-detected) */
+  VLB_ERR_TOKEN_ID = 9,    /* a text token id outside [0, vocab) (device-detected) */
+  VLB_ERR_SCRATCH = 10     /* the problem's workspace exceeds VLB_NOALLOC_SCRATCH_BYTES */
 } vlb_status;
 
 typedef enum { VLB_F32 = 0, VLB_BF16 = 1 } vlb_dtype;
@@ -211,6 +212,29 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
                             const vlb_weights *w, const void *newline, const void *separator,
                             const uint8_t *mask, int64_t seq_len, void *seq, void *ws,
                             size_t ws_bytes, void *stream);
+
+/* vlb_bridge_fused for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The workspace is a library-owned device array of
+ * VLB_NOALLOC_SCRATCH_BYTES (256 MiB) that every GPU running the library
+ * holds until the process ends; the call makes no allocation of any kind on
+ * the device.  Inputs, outputs and errors as vlb_bridge_fused, plus:
+ *   status: (device) int32[4], 16-byte aligned, written with the call's
+ *     status words (all zero when there are no token rows); vlb_check(status,
+ *     stream) returns VLB_ERR_MASK_COUNT for a placeholder-count mismatch.
+ *   VLB_GATHER_AUTO is taken as VLB_GATHER_ON where that is allowed, so the
+ *     merged tokens take no scratch; the bits are the same.
+ *   VLB_ERR_SCRATCH (nothing launched): vlb_workspace_bytes of the problem
+ *     (with that gather choice) exceeds VLB_NOALLOC_SCRATCH_BYTES.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. */
+#define VLB_NOALLOC_SCRATCH_BYTES (256u << 20)
+vlb_status vlb_bridge_fused_noalloc(const vlb_projector *p, const vlb_batch *b,
+                                    const void *features, const vlb_weights *w,
+                                    const void *newline, const void *separator,
+                                    const uint8_t *mask, int64_t seq_len, void *seq,
+                                    int32_t *status, void *stream);
 
 /* The whole embedded sequence in one call [VL2 Tile-sequence assembly, last
  * paragraph; VL2 language config: vocab_size 102400, image_token_index

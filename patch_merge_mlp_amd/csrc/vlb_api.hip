@@ -799,21 +799,16 @@ vlb_status vlb_scatter_tokens(const vlb_projector *p, const vlb_batch *b, const 
   return VLB_OK;
 }
 
-vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const void *features,
-                            const vlb_weights *w, const void *newline, const void *separator,
-                            const uint8_t *mask, int64_t seq_len, void *seq, void *ws,
-                            size_t ws_bytes, void *stream) {
-  Plan pl;
-  vlb_status st = make_plan(p, b, seq_len, &pl);
-  if (st != VLB_OK) return st;
-  if (pl.T == 0) return VLB_OK;
-  if ((st = check_weights(p, w)) != VLB_OK) return st;
-  if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;
-  if (!features || !ws) return VLB_ERR_NULL;
-  if (!aligned16(features) || !aligned16(ws)) return VLB_ERR_ALIGN;
-  if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t *w8 = static_cast<uint8_t *>(ws);
+}  // extern "C"
+
+namespace {
+
+// The fused call's launches on a validated plan, with workspace w8.
+vlb_status run_fused(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
+                     const void *features, const vlb_weights *w, const void *newline,
+                     const void *separator, const uint8_t *mask, int64_t seq_len, void *seq,
+                     uint8_t *w8, hipStream_t s) {
+  vlb_status st;
   const vlb::ScanJob sj = merge_scan(b, pl, mask, nullptr, 0, 0, seq_len, w8);
   const TiledPlace tp{newline, separator, seq};
   const bool fused_scan = scan_in_merge(p), tiled = b->layout == VLB_LAYOUT_TILED_2D;
@@ -825,6 +820,105 @@ vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const vo
   return run_project(p, b, pl, features, w, seq,
                      reinterpret_cast<const int32_t *>(w8 + pl.off_dst), w8, s, nullptr,
                      fused_scan ? &sj : nullptr, fused_scan && tiled ? &tp : nullptr);
+}
+
+// Argument checks of the fused call (after make_plan), workspace aside.
+vlb_status check_fused_args(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const vlb_weights *w, const void *newline, const void *separator,
+                            const uint8_t *mask, int64_t seq_len, const void *seq) {
+  vlb_status st;
+  if ((st = check_weights(p, w)) != VLB_OK) return st;
+  if ((st = check_scatter_args(p, b, newline, separator, mask, seq_len, seq)) != VLB_OK) return st;
+  if (!features) return VLB_ERR_NULL;
+  if (!aligned16(features)) return VLB_ERR_ALIGN;
+  return VLB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vlb_status vlb_bridge_fused(const vlb_projector *p, const vlb_batch *b, const void *features,
+                            const vlb_weights *w, const void *newline, const void *separator,
+                            const uint8_t *mask, int64_t seq_len, void *seq, void *ws,
+                            size_t ws_bytes, void *stream) {
+  Plan pl;
+  vlb_status st = make_plan(p, b, seq_len, &pl);
+  if (st != VLB_OK) return st;
+  if (pl.T == 0) return VLB_OK;
+  if ((st = check_fused_args(p, b, features, w, newline, separator, mask, seq_len, seq)) != VLB_OK)
+    return st;
+  if (!ws) return VLB_ERR_NULL;
+  if (!aligned16(ws)) return VLB_ERR_ALIGN;
+  if (ws_bytes < pl.total) return VLB_ERR_WORKSPACE;
+  return run_fused(p, b, pl, features, w, newline, separator, mask, seq_len, seq,
+                   static_cast<uint8_t *>(ws), static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- the allocation-free fused call -----------------------------------------
+// The workspace of vlb_bridge_fused_noalloc: one array per GPU (every device
+// that runs the library holds its own copy until the process ends).  Host code
+// never uses the array's name as an address -- on the host it is a stand-in --
+// but the device address that hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[VLB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // scratch's device address on each device, once taken
+
+// scratch's address on the current device, taken on the first call there.
+vlb_status scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VLB_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return VLB_ERR_HIP;
+    g_scratch[dev] = a;
+  }
+  *out = g_scratch[dev];
+  return VLB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vlb_status vlb_bridge_fused_noalloc(const vlb_projector *p, const vlb_batch *b,
+                                    const void *features, const vlb_weights *w,
+                                    const void *newline, const void *separator,
+                                    const uint8_t *mask, int64_t seq_len, void *seq,
+                                    int32_t *status, void *stream) {
+  if (!p) return VLB_ERR_NULL;
+  vlb_projector q = *p;  // the gather keeps the merged tokens out of the scratch
+  if (q.gather == VLB_GATHER_AUTO && q.dtype == VLB_BF16 && !q.has_ln) q.gather = VLB_GATHER_ON;
+  Plan pl;
+  vlb_status st = make_plan(&q, b, seq_len, &pl);
+  if (st != VLB_OK) return st;
+  if (!status) return VLB_ERR_NULL;
+  if (!aligned16(status)) return VLB_ERR_ALIGN;
+  if (pl.T > 0 &&
+      (st = check_fused_args(&q, b, features, w, newline, separator, mask, seq_len, seq)) != VLB_OK)
+    return st;
+  if (pl.total > VLB_NOALLOC_SCRATCH_BYTES) return VLB_ERR_SCRATCH;
+  void *scr = nullptr;
+  if ((st = scratch_address(&scr)) != VLB_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t *w8 = static_cast<uint8_t *>(scr);
+  if (pl.T > 0 &&
+      (st = run_fused(&q, b, pl, features, w, newline, separator, mask, seq_len, seq, w8, s)) !=
+          VLB_OK)
+    return st;
+  // The call's status words, into the caller's buffer (zeros when nothing ran).
+  VLB_LAUNCH(VLB_K_SCAN, s,
+             vlb::launch_copy_status(
+                 pl.T > 0 ? reinterpret_cast<const int32_t *>(w8 + pl.off_status) : nullptr,
+                 status, s));
+  return VLB_OK;
 }
 
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b) {
@@ -1285,6 +1379,7 @@ const char *vlb_status_str(vlb_status s) {
     case VLB_ERR_UNSUPPORTED: return "unsupported setting";
     case VLB_ERR_HIP: return "HIP runtime error";
     case VLB_ERR_TOKEN_ID: return "text token id outside the vocabulary";
+    case VLB_ERR_SCRATCH: return "problem too large for the no-allocation scratch";
   }
   return "unknown status";
 }

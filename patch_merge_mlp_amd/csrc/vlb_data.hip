@@ -800,6 +800,18 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s, const S
   return hipGetLastError();
 }
 
+namespace {
+__global__ void k_copy_status(const int32_t *src, int32_t *dst) {
+  const int i = threadIdx.x;
+  if (i < 4) dst[i] = src ? src[i] : 0;
+}
+}  // namespace
+
+hipError_t launch_copy_status(const int32_t *src, int32_t *dst, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(64), 0, s, src, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
                        int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
                        hipStream_t s) {

@@ -175,6 +175,8 @@ struct ScanJob {
   int32_t *status;
   bool direct;
 };
+// dst[0..3] = src[0..3] (the status words), or zeros when src is null.
+hipError_t launch_copy_status(const int32_t *src, int32_t *dst, hipStream_t s);
 // Gather descriptors of the token rows of one chunk of views; with scan
 // non-null, the launch also runs that placeholder scan (one extra workgroup).
 hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s,

@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvlbridge.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
-    ERR_UNSUPPORTED, ERR_HIP, ERR_TOKEN_ID = range(10)
+    ERR_UNSUPPORTED, ERR_HIP, ERR_TOKEN_ID, ERR_SCRATCH = range(11)
+NOALLOC_SCRATCH_BYTES = 256 << 20  # VLB_NOALLOC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 GELU_ERF, GELU_TANH, ACT_NONE = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_TILED_2D = 0, 1
@@ -101,6 +102,8 @@ def lib():
             "vlb_scatter_tokens": (st, [pp, pb, vp, vp, vp, vp, i64, vp, vp, sz, vp]),
             "vlb_bridge_fused": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, i64, vp,
                                       vp, sz, vp]),
+            "vlb_bridge_fused_noalloc": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp,
+                                              i64, vp, vp, vp]),
             "vlb_bridge_embed": (st, [pp, pb, vp, ct.POINTER(vlb_weights), vp, vp, vp, ct.c_int32,
                                       vp, i64, i64, vp, vp, sz, vp]),
             "vlb_saved_bytes": (sz, [pp, pb]),
@@ -364,6 +367,25 @@ def vlb_bridge_fused(p, b: Batch, features, w: Weights, newline, separator, mask
                                   _ptr(newline), _ptr(separator), _ptr(mask), seq.shape[0],
                                   _ptr(seq), _ptr(ws), ws.numel(), _stream(stream)),
            "vlb_bridge_fused")
+
+
+def vlb_bridge_fused_noalloc(p, b: Batch, features, w: Weights, newline, separator, mask, seq,
+                             status, stream=None):
+    """vlb_bridge_fused with the library's own device scratch instead of a
+    workspace; status: int32 [4] on the device, the call's status words (read
+    them with vlb_check(status))."""
+    dt = _tdtype(p)
+    _check_seq(p, mask, seq)
+    _need(features, _pixels(b) * p.C, dt, "features")
+    _check_weights(p, w)
+    _need(newline, p.out_dim, dt, "newline")
+    _need(separator, p.out_dim, dt, "separator")
+    _need(status, 4, torch.int32, "status")
+    wc = w.c()
+    _check(lib().vlb_bridge_fused_noalloc(ct.byref(p), ct.byref(b.c), _ptr(features), ct.byref(wc),
+                                          _ptr(newline), _ptr(separator), _ptr(mask), seq.shape[0],
+                                          _ptr(seq), _ptr(status), _stream(stream)),
+           "vlb_bridge_fused_noalloc")
 
 
 def vlb_bridge_embed(p, b: Batch, features, w: Weights, newline, separator, ids, image_token_id,

@@ -354,3 +354,31 @@ def test_gather_mode_workspace():
     assert v.vlb_workspace_bytes(_proj(dtype=v.F32), b, 32) == \
         v.vlb_workspace_bytes(_proj(dtype=v.F32, gather=v.GATHER_OFF), b, 32)
     assert v.vlb_saved_bytes(_proj(gather=v.GATHER_ON), b) == v.vlb_saved_bytes(_proj(), b)
+
+
+def test_noalloc_validates_before_launching():
+    """vlb_bridge_fused_noalloc: argument errors and the scratch limit are found on
+    the host, before any HIP call (no GPU here).  A LayerNorm batch keeps its
+    merged tokens, so 16 MoonViT-size images need 151 + 151 MB > 256 MiB."""
+    L = v.lib()
+    p = _proj(C=1152, hidden=4608, out_dim=4096, has_ln=True)
+    b = v.Batch([(64, 64)] * 16, [1] * 16)
+    S = 16 * 1024 + 8
+    need = v.vlb_workspace_bytes(p, b, S)
+    assert need > v.NOALLOC_SCRATCH_BYTES
+    w = v.vlb_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    call = lambda pp, bb, status: L.vlb_bridge_fused_noalloc(
+        ct.byref(pp), ct.byref(bb.c), FAKE, ct.byref(w), FAKE, FAKE, FAKE, S, FAKE, status, None)
+    assert call(p, b, FAKE) == v.ERR_SCRATCH
+    assert call(p, b, None) == v.ERR_NULL
+    assert call(p, b, FAKE + 4) == v.ERR_ALIGN
+    bad = _proj(C=1152, hidden=4608, out_dim=4096, has_ln=True, gather=v.GATHER_ON)
+    assert call(bad, b, FAKE) == v.ERR_UNSUPPORTED
+    # the same images without the LayerNorm fit: the merged tokens are gathered
+    p2 = _proj(C=1152, hidden=4608, out_dim=4096)
+    assert v.vlb_workspace_bytes(_proj(C=1152, hidden=4608, out_dim=4096,
+                                       gather=v.GATHER_ON), b, S) <= v.NOALLOC_SCRATCH_BYTES
+    assert v.vlb_workspace_bytes(_proj(C=1152, hidden=4608, out_dim=4096,
+                                       gather=v.GATHER_OFF), b, S) > v.NOALLOC_SCRATCH_BYTES
+    assert v.status_str(v.ERR_SCRATCH) == "problem too large for the no-allocation scratch"
+    del p2
