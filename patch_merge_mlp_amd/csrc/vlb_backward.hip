@@ -44,22 +44,13 @@ __device__ __forceinline__ int64_t blk(int64_t r, int64_t c, int64_t K) {
 }
 
 // d/dz of act_fn<ACT>, in fp32.
-//   erf form: Phi(z) + z phi(z), with Phi from the same tail polynomial as
-//   the forward (Phi(-a) = 2^(-h(a))) and phi(z) = exp(-z^2/2) / sqrt(2 pi);
+//   erf form: Phi(z) + z phi(z), with Phi from the forward's tail
+//   (gauss_tail: Phi(-a) = 2^(-h(a))) and phi(z) = exp(-z^2/2) / sqrt(2 pi);
 //   tanh form: 0.5 (1 + th) + 0.5 z (1 - th^2) sqrt(2/pi) (1 + 3 * 0.044715 z^2).
 template <int ACT>
 __device__ __forceinline__ float act_slope(float z) {
   if constexpr (ACT == 0) {
-    const float a = fminf(fabsf(z), 6.0f);
-    float h = 1.83484644e-06f;
-    h = fmaf(h, a, -6.15989775e-05f);
-    h = fmaf(h, a, 0.000930530019f);
-    h = fmaf(h, a, -0.00850791018f);
-    h = fmaf(h, a, 0.0539601035f);
-    h = fmaf(h, a, 0.458464354f);
-    h = fmaf(h, a, 1.15125108f);
-    h = fmaf(h, a, 0.999995291f);
-    const float tail = __builtin_amdgcn_exp2f(-h);  // Phi(-|z|)
+    const float tail = gauss_tail(z);  // Phi(-|z|)
     const float cdf = z >= 0.f ? 1.0f - tail : tail;
     const float pdf = 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z);
     return fmaf(z, pdf, cdf);

@@ -118,13 +118,31 @@ __device__ __forceinline__ uint8_t *pick(uint8_t *const (&b)[4], int i) {
 // lane / 16) of wave (wm, wn) owns token row wm*WT + 16 i + fr and features
 // wn*WT + 16 j + 4 fq + e in element e (e < 4).
 //
-// stage_tile: bias (and the activation when ACT_ON) applied in fp32, the tile
-// rounded to bf16 and staged in the stage buffers (64 rows each; rows of
-// 16-byte chunks XOR-swizzled by the row).  The caller has synchronised the
-// workgroup after its last use of the buffers.
+// Accumulators start from the bias (the tile's columns, staged in s_bias and
+// visible after the prologue's barrier), so the epilogue adds none.
+template <int BMT>
+__device__ __forceinline__ void init_acc(f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
+                                         const uint16_t *s_bias) {
+  using G = Geo<BMT>;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wn = wid & 1, fq = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < G::TI; ++j) {
+    const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + wn * G::WT + j * 16 + 4 * fq);
+    const f32x4 b = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff), bf2f(bb.y >> 16)};
+#pragma unroll
+    for (int i = 0; i < G::TI; ++i) acc[i][j] = b;
+  }
+}
+
+// stage_tile: the activation (when ACT_ON) applied in fp32 to the
+// accumulators (bias included), the tile rounded to bf16 and staged in the
+// stage buffers (64 rows each; rows of 16-byte chunks XOR-swizzled by the
+// row).  The caller has synchronised the workgroup after its last use of the
+// buffers.
 template <int ACT, int BMT, bool ACT_ON>
 __device__ __forceinline__ void stage_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
-                                           uint8_t *const (&bufs)[4], const uint16_t *s_bias) {
+                                           uint8_t *const (&bufs)[4]) {
   using G = Geo<BMT>;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -132,9 +150,6 @@ __device__ __forceinline__ void stage_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 #pragma unroll
   for (int j = 0; j < G::TI; ++j) {
     const int cl = wn * G::WT + j * 16 + 4 * fq;  // 4 consecutive features
-    const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + cl);
-    const float b[4] = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff),
-                        bf2f(bb.y >> 16)};
     const int chunk = cl >> 3, half = (cl >> 2) & 1;
 #pragma unroll
     for (int i = 0; i < G::TI; ++i) {
@@ -143,7 +158,7 @@ __device__ __forceinline__ void stage_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
       uint16_t h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = acc[i][j][e] + b[e];
+        const float v = acc[i][j][e];
         h[e] = f2bf(ACT_ON ? act_fn<ACT>(v) : v);
       }
       uint2 v;
@@ -235,22 +250,21 @@ __device__ __forceinline__ void write_f32(const f32x4 (&acc)[Geo<BMT>::TI][Geo<B
 template <int MODE, int ACT, int BMT>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
                                            const GemmArgs &g, int m0, int n0,
-                                           uint8_t *const (&bufs)[4], const uint16_t *s_bias,
-                                           const int32_t *s_dst) {
+                                           uint8_t *const (&bufs)[4], const int32_t *s_dst) {
   if constexpr (MODE == kGemmF32) {
     write_f32<BMT>(acc, g, m0, n0);
   } else if constexpr (MODE == kGemmRows) {
-    stage_tile<ACT, BMT, false>(acc, bufs, s_bias);
+    stage_tile<ACT, BMT, false>(acc, bufs);
     __syncthreads();
     write_rows<BMT>(bufs, g, n0, s_dst);
   } else {
     if constexpr (MODE == kGemmBlockedSave) {  // pre-activation first
-      stage_tile<ACT, BMT, false>(acc, bufs, s_bias);
+      stage_tile<ACT, BMT, false>(acc, bufs);
       __syncthreads();
       write_blocked<BMT>(bufs, g, m0, n0, static_cast<uint16_t *>(g.out2));
       __syncthreads();
     }
-    stage_tile<ACT, BMT, true>(acc, bufs, s_bias);
+    stage_tile<ACT, BMT, true>(acc, bufs);
     __syncthreads();
     write_blocked<BMT>(bufs, g, m0, n0, static_cast<uint16_t *>(g.out));
   }
@@ -363,13 +377,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     }
   };
 
-  f32x4 acc[G::TI][G::TI];
-#pragma unroll
-  for (int i = 0; i < G::TI; ++i)
-#pragma unroll
-    for (int j = 0; j < G::TI; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.f;
+  f32x4 acc[G::TI][G::TI];  // set from the bias once s_bias is visible (init_acc)
 
   const int wm = wid >> 1, wn = wid & 1;
   const int fr = lane & 15, fq = lane >> 4;  // fragment row / 8-wide K group of this lane
@@ -447,6 +455,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   issue(1, smem1, -1);
   issue(2, smem2, -1);
   stage_barrier<BMT>();  // step 0 landed (12 or 6 younger loads may be in flight)
+  init_acc<BMT>(acc, s_bias);
   rd(smem0, fa0, fb0);
   for (int kt = 0; kt < KT; kt += NSTAGE) {  // KT rounds up: the extra steps are all-zero
     step(smem1, smem3, kt, fa0, fb0, fa1, fb1);
@@ -465,7 +474,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     }
   }
   uint8_t *const bufs[4] = {smem0, smem1, smem2, smem3};
-  store_tile<MODE, ACT, BMT>(acc, g, m0, n0, bufs, s_bias, s_dst);
+  store_tile<MODE, ACT, BMT>(acc, g, m0, n0, bufs, s_dst);
 }
 
 // Tile coordinates of the quarter tiles: workgroup index q of the 128-tile
