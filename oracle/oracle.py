@@ -43,11 +43,26 @@ _lib = None
 
 
 def lib():
+    """The oracle library: the -O2 build, or the build that VLB_ORACLE_LIB names
+    (the CPU tests' sanitizer build)."""
     global _lib
     if _lib is None:
-        _lib = ct.CDLL(build())
+        _lib = ct.CDLL(os.environ.get("VLB_ORACLE_LIB") or build())
         _declare(_lib)
     return _lib
+
+
+def build_sanitized(out_dir: str) -> str:
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (ROCm's clang, the sanitizer runtime shared, so that one runtime serves it and
+    the library's sanitized host code in one process)."""
+    so = os.path.join(out_dir, "libvlb_oracle_san.so")
+    subprocess.check_call(
+        ["/opt/rocm/lib/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+         "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-shared-libsan",
+         "-ffp-contract=off", "-fPIC", "-shared", "-std=c11", "-D_GNU_SOURCE", "-o", so, _SRC,
+         "-lm", "-lpthread"])
+    return so
 
 
 class use_library:

@@ -62,5 +62,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-shared-libsan",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_SOURCES = ("vlb_api.hip", "vlb_processor.hip")  # argument checks, planner, launches
+
+
+def build_sanitized(out_dir: str) -> str:
+    """A build whose host code in HOST_SOURCES carries AddressSanitizer and
+    UndefinedBehaviorSanitizer (the device code is unchanged; the other sources
+    compile as usual).  Load it with the clang sanitizer runtime preloaded
+    (sanitizer_runtime()); used by the CPU tests only."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        extra = SANITIZE + ["-g"] if os.path.basename(src) in HOST_SOURCES else []
+        cmd = [HIPCC, *compile_flags(), *extra, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-3000:]}")
+        return obj
+
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    so = os.path.join(out_dir, "libvlbridge_san.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fsanitize=address,undefined",
+           "-shared-libsan", "-o", so, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return so
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime (it carries the UndefinedBehaviorSanitizer
+    handlers too) that the sanitized builds need preloaded."""
+    found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return found[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -16,7 +16,9 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvlbridge.so")
+# The in-tree build; VLBRIDGE_LIB names another build of the same sources (the
+# CPU tests' sanitizer build of the host code).
+LIB_PATH = os.environ.get("VLBRIDGE_LIB") or os.path.join(_HERE, "libvlbridge.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_MASK_COUNT, \
     ERR_UNSUPPORTED, ERR_HIP, ERR_TOKEN_ID, ERR_SCRATCH = range(11)
