@@ -30,9 +30,10 @@
  *    computes with fp32 accumulation and keeps the hidden activation in bf16;
  *    VLB_F32 computes in fp32 throughout.
  *  - Features: views stored back to back, each (grid_h, grid_w, C) row-major
- *    channels-last ("(tiles, N, input_dim)" with the token axis unflattened
- *    row-major, [VL2 Projector 1]).  Images own consecutive views; for the 2D
- *    tile layout an image's views are [global, local tiles row-major].
+ *    channels-last: the tower's per-view token sequence with its token index
+ *    read as grid row, then column [VL2 Projector 1].  Images own consecutive
+ *    views; for the 2D tile layout an image's views are [global, local tiles
+ *    row-major].
  *  - Token rows: the projected tokens of all views, concatenated in view order,
  *    each view's tokens row-major over its merged grid [VL2 Projector, Output].
  *  - Alignment: every device pointer must be 16-byte aligned.

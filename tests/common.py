@@ -62,3 +62,48 @@ def image_row_ranges(w: wl.Workload):
 def rel_frob(got: np.ndarray, ref: np.ndarray) -> float:
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+# ---- guard bands around device outputs -------------------------------------------
+
+GUARD_BYTES = 4096   # canary bytes before and after every guarded buffer
+CANARY = 0xA5
+
+
+class Guards:
+    """Device buffers with GUARD_BYTES of canary bytes on both sides.  check()
+    asserts that every canary byte is intact: a kernel that writes past an
+    output or past the workspace it was sized for changes them.  The buffers
+    stay 256-byte aligned (the canaries are a multiple of 256 bytes)."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def empty(self, shape, dtype, label="buffer", device="cuda"):
+        import torch
+        shape = tuple(shape) if isinstance(shape, (tuple, list)) else (int(shape),)
+        es = torch.empty(0, dtype=dtype).element_size()
+        n = 1
+        for d in shape:
+            n *= int(d)
+        g = GUARD_BYTES // es
+        raw = torch.full(((n + 2 * g) * es,), CANARY, dtype=torch.uint8, device=device)
+        inner = raw.view(dtype)[g:g + n].view(shape)
+        self.bufs.append((raw, n * es, label))
+        return inner
+
+    def like(self, t, label="buffer"):
+        x = self.empty(t.shape, t.dtype, label, device="cuda")
+        x.copy_(t.to(x.device))
+        return x
+
+    def workspace(self, nbytes, label="workspace"):
+        import torch
+        return self.empty((max(int(nbytes), 16),), torch.uint8, label)
+
+    def check(self):
+        for raw, nb, label in self.bufs:
+            head = raw[:GUARD_BYTES]
+            tail = raw[GUARD_BYTES + nb:]
+            assert bool((head == CANARY).all()), f"{label}: bytes before it were written"
+            assert bool((tail == CANARY).all()), f"{label}: bytes after it were written"

@@ -108,32 +108,51 @@ def pin_merge_pixel_unshuffle(o):
         assert np.array_equal(o.merge_view(x, k), _torch_merge(x, k)), (gh, gw, C, k)
 
 
-# --- assembly: the page's reshape / transpose / concatenate recipe ----------
+# --- assembly: closed-form slot of every token, newline and separator --------
 
-def _recipe(hp, wp, tw, th, tail):
-    """The tile-sequence assembly run with torch tensor ops on token ids (D = 1):
-    newline = -1, separator = -2."""
-    n = hp * wp
-    tok = torch.arange((1 + tw * th) * n, dtype=torch.int64).reshape(1 + tw * th, n, 1)
-    g = tok[0].reshape(hp, wp, 1)
-    g = torch.cat([g, torch.full((hp, 1, 1), -1)], dim=1).reshape(hp * (wp + 1), 1)
-    loc = tok[1:].reshape(th, tw, hp, wp, 1).permute(0, 2, 1, 3, 4).reshape(th * hp, tw * wp, 1)
-    loc = torch.cat([loc, torch.full((th * hp, 1, 1), -1)], dim=1)
-    loc = loc.reshape(th * hp * (tw * wp + 1), 1)
-    sep = torch.full((1, 1), -2)
-    parts = [loc, sep, g] if tail else [g, sep, loc]
-    return torch.cat(parts, dim=0).reshape(-1).numpy()
+def _slot_map(hp, wp, tw, th, tail):
+    """The assembled slots of one tiled image, built from the other direction than
+    the oracle: each token (view v, merged row y, column x), newline and separator
+    is placed at its slot index computed in closed form, then the slots are read
+    out in order.  Token ids: v * hp * wp + y * wp + x; newline -1, separator -2.
+    Layout ([VL2] Tile-sequence assembly): the global view as hp rows of wp tokens
+    and a newline; the separator; the local views as one mosaic of th * hp rows
+    by tw * wp columns (view 1 + i * tw + j covering rows i * hp .. and columns
+    j * wp ..), a newline after each mosaic row.  Tail: mosaic, separator, global."""
+    G = hp * (wp + 1)                # global block, newlines included
+    W = tw * wp + 1                  # one mosaic row, its newline included
+    L = th * hp * W                  # mosaic block
+    n = G + 1 + L
+    out = np.full(n, -99, dtype=np.int64)
+    g0, s0, l0 = (L + 1, L, 0) if tail else (0, G, G + 1)
+    for y in range(hp):
+        for x in range(wp):
+            out[g0 + y * (wp + 1) + x] = y * wp + x
+        out[g0 + y * (wp + 1) + wp] = -1
+    out[s0] = -2
+    for v in range(1, 1 + tw * th):
+        i, j = divmod(v - 1, tw)
+        for y in range(hp):
+            for x in range(wp):
+                out[l0 + (i * hp + y) * W + j * wp + x] = v * hp * wp + y * wp + x
+    for R in range(th * hp):
+        out[l0 + R * W + tw * wp] = -1
+    assert (out != -99).all(), "a slot was left unassigned"
+    return out
 
 
-def pin_assembly_recipe(o):
+def pin_assembly_slots(o):
+    """The oracle's assembly equals the closed-form slot map, for several tile
+    grids, head and tail; slot totals are h'(w'+1) + 1 + (th h')(tw w'+1)."""
     for hp, tw, th, tail in [(2, 2, 3, False), (3, 1, 1, False), (2, 3, 2, True), (14, 2, 1, False),
                              (4, 1, 3, False), (1, 2, 2, True)]:
         k = 2
         spec = _tiled_spec(o, hp * k - 1, k, tw, th, tail=tail)  # odd grid: padded to hp*k
         assert o.merged_side(hp * k - 1, k) == hp
         got = o.assemble(spec)
-        want = _recipe(hp, hp, tw, th, tail)
+        want = _slot_map(hp, hp, tw, th, tail)
         assert np.array_equal(got, want), (hp, tw, th, tail)
+        assert len(got) == hp * (hp + 1) + 1 + (th * hp) * (tw * hp + 1)
         assert (got == -1).sum() == hp + th * hp and (got == -2).sum() == 1
 
 
@@ -141,7 +160,7 @@ def pin_assembly_images(o):
     """Images are laid out one after another, each with its own token rows."""
     spec = _tiled_spec(o, 4, 2, 2, 1, n_images=3)
     got = o.assemble(spec)
-    one = _recipe(2, 2, 2, 1, False)
+    one = _slot_map(2, 2, 2, 1, False)
     per = 3 * 4  # three views of 2x2 tokens
     want = np.concatenate([np.where(one >= 0, one + i * per, one) for i in range(3)])
     assert np.array_equal(got, want)
@@ -608,7 +627,7 @@ PROCESSOR_PINS = [pin_processor_page_examples, pin_processor_best_fit, pin_proce
                   pin_processor_expand]
 
 ALL = [pin_page_counts, pin_param_count, pin_merged_width, pin_merge_roundtrip,
-       pin_merge_pixel_unshuffle, pin_assembly_recipe, pin_assembly_images, pin_gelu_values,
+       pin_merge_pixel_unshuffle, pin_assembly_slots, pin_assembly_images, pin_gelu_values,
        pin_gelu_library, pin_linear_library, pin_layer_norm, pin_project_rows_library, pin_scatter,
        pin_embed_scatter, pin_project_rows_deep_library, pin_project_backward_autograd,
        pin_project_backward_deep_autograd, pin_project_backward_fd,

@@ -32,22 +32,27 @@ def run_train(w, t, dseq, features_grad=True, mask=None):
     """Training forward then backward on the device; returns (status, seq, grads, ws)."""
     p, b = common.lib_projector(w), common.lib_batch(w)
     wt = _weights(t)
-    seq = _dev(t["seq"]).clone()
+    gd = common.Guards()  # guard bands around every output, workspace and saved buffer
+    seq = gd.like(t["seq"], "seq")
     mask = _dev(t["mask"] if mask is None else mask)
-    fws = torch.empty(max(v.vlb_workspace_bytes(p, b, seq.shape[0]), 16), dtype=torch.uint8,
-                      device="cuda")
-    saved = torch.empty(max(v.vlb_saved_bytes(p, b), 16), dtype=torch.uint8, device="cuda")
+    fws = gd.workspace(v.vlb_workspace_bytes(p, b, seq.shape[0]), "forward workspace")
+    saved = gd.workspace(v.vlb_saved_bytes(p, b), "saved activations")
     v.vlb_bridge_fused_train(p, b, _dev(t["features"]), wt, _dev(t["newline"]),
                              _dev(t["separator"]), mask, seq, saved, fws)
     g = v.Grads.empty(p, b, features=features_grad)
-    for x in (g.d_w1, g.d_b1, g.d_w2, g.d_b2, g.d_ln_gamma, g.d_ln_beta, g.d_newline,
-              g.d_separator):
+    for name in ("d_w1", "d_b1", "d_w2", "d_b2", "d_features", "d_ln_gamma", "d_ln_beta",
+                 "d_newline", "d_separator"):
+        x = getattr(g, name)
         if x is not None:
-            x.fill_(float("nan"))
-    bws = torch.empty(max(v.vlb_backward_workspace_bytes(p, b, seq.shape[0]), 16),
-                      dtype=torch.uint8, device="cuda")
+            x = gd.empty(x.shape, x.dtype, name)
+            if x.dtype == torch.float32:
+                x.fill_(float("nan"))
+            setattr(g, name, x)
+    bws = gd.workspace(v.vlb_backward_workspace_bytes(p, b, seq.shape[0]), "backward workspace")
     v.vlb_bridge_backward(p, b, _dev(t["features"]), wt, mask, _dev(dseq), saved, g, bws)
-    return v.vlb_check(bws), seq.cpu(), g, bws
+    st = v.vlb_check(bws)
+    gd.check()
+    return st, seq.cpu(), g, bws
 
 
 def oracle_grads(w, t, dseq):

@@ -22,12 +22,15 @@ IMG = wl.IMAGE_TOKEN_ID
 def run_embed(w, t, ids, table, seq0=None):
     p, b = common.lib_projector(w), common.lib_batch(w)
     br = v.Bridge(p, _weights(t))
-    seq = (_dev(seq0).clone() if seq0 is not None
-           else torch.zeros(len(ids), w.out_dim, dtype=w.torch_dtype, device="cuda"))
-    ws = br.workspace(b, seq.shape[0])
+    g = common.Guards()
+    seq = g.like(seq0 if seq0 is not None
+                 else torch.zeros(len(ids), w.out_dim, dtype=w.torch_dtype), "seq")
+    ws = g.workspace(v.vlb_workspace_bytes(br.p, b, seq.shape[0]))
     v.vlb_bridge_embed(br.p, b, _dev(t["features"]), br.w, _dev(t["newline"]),
                        _dev(t["separator"]), _dev(ids), IMG, _dev(table), seq, ws)
-    return v.vlb_check(ws), seq.cpu()
+    st = v.vlb_check(ws)
+    g.check()
+    return st, seq.cpu()
 
 
 def oracle_embed(w, t, ids, table, rows64):

@@ -35,13 +35,19 @@ def _weights(t):
 
 
 def run_fused(w, t, act=v.GELU_ERF, pack=True, has_ln=None, weights=None, gather=v.GATHER_AUTO):
+    """One fused call; the sequence and the workspace carry guard bands, checked
+    after the call."""
     p = common.lib_projector(w, act, has_ln, gather)
     b = common.lib_batch(w)
     br = v.Bridge(p, weights or _weights(t), pack=pack)
-    seq = _dev(t["seq"]).clone()
-    ws = br.fused(b, _dev(t["features"]), _dev(t["newline"]), _dev(t["separator"]),
-                  _dev(t["mask"]), seq)
-    return v.vlb_check(ws), seq.cpu()
+    g = common.Guards()
+    seq = g.like(t["seq"], "seq")
+    ws = g.workspace(v.vlb_workspace_bytes(br.p, b, seq.shape[0]))
+    v.vlb_bridge_fused(br.p, b, _dev(t["features"]), br.w, _dev(t["newline"]),
+                       _dev(t["separator"]), _dev(t["mask"]), seq, ws)
+    st = v.vlb_check(ws)
+    g.check()
+    return st, seq.cpu()
 
 
 def slot_positions(t):
@@ -193,12 +199,16 @@ def test_unfused_equals_fused(w):
     assert st == v.OK
     p, b = common.lib_projector(w), common.lib_batch(w)
     br = v.Bridge(p, _weights(t))
-    rows = br.project(b, _dev(t["features"]))
-    seq = _dev(t["seq"]).clone()
-    ws = v.workspace(br.p, b, seq.shape[0])
+    g = common.Guards()
+    rows = g.empty((v.vlb_num_tokens(br.p, b), w.out_dim), w.torch_dtype, "rows")
+    ws0 = g.workspace(v.vlb_workspace_bytes(br.p, b, 0))
+    v.vlb_merge_project(br.p, b, _dev(t["features"]), br.w, rows, ws0)
+    seq = g.like(t["seq"], "seq")
+    ws = g.workspace(v.vlb_workspace_bytes(br.p, b, seq.shape[0]))
     v.vlb_scatter_tokens(br.p, b, rows, _dev(t["newline"]), _dev(t["separator"]),
                          _dev(t["mask"]), seq, ws)
     assert v.vlb_check(ws) == v.OK
+    g.check()
     assert torch.equal(seq.cpu().view(torch.int16), fused.view(torch.int16))
 
 
@@ -389,9 +399,12 @@ def test_merge_tokens_exact(w):
         t = common.draw(w)
     p, b = common.lib_projector(w, has_ln=False), common.lib_batch(w)
     T = v.vlb_num_tokens(p, b)
-    merged = torch.empty(T, w.C * w.k * w.k, dtype=w.torch_dtype, device=DEV)
-    ws = v.workspace(p, b, 0)
+    g = common.Guards()
+    merged = g.empty((T, w.C * w.k * w.k), w.torch_dtype, "merged")
+    ws = g.workspace(v.vlb_workspace_bytes(p, b, 0))
     v.vlb_merge_tokens(p, b, _dev(t["features"]), None, None, merged, ws)
+    torch.cuda.synchronize()
+    g.check()
     got = merged.cpu().double().numpy()
     want, q = [], 0
     for gh, gw in w.grids:
@@ -427,11 +440,13 @@ def test_scatter_tokens_exact(w):
     T = v.vlb_num_tokens(p, b)
     g = torch.Generator().manual_seed(7)
     rows = torch.randn(T, w.out_dim, generator=g).to(w.torch_dtype)
-    seq = _dev(t["seq"]).clone()
-    ws = v.workspace(p, b, seq.shape[0])
+    gd = common.Guards()
+    seq = gd.like(t["seq"], "seq")
+    ws = gd.workspace(v.vlb_workspace_bytes(p, b, seq.shape[0]))
     v.vlb_scatter_tokens(p, b, _dev(rows), _dev(t["newline"]), _dev(t["separator"]),
                          _dev(t["mask"]), seq, ws)
     assert v.vlb_check(ws) == v.OK
+    gd.check()
     st, ref = o.scatter(o.assemble(common.oracle_spec(w)), rows, t["newline"], t["separator"],
                         t["mask"].numpy(), t["seq"])
     assert st == 0

@@ -41,12 +41,16 @@ def _fused(br, b, t):
 
 
 def _noalloc(br, b, t, mask=None):
-    seq = _dev(t["seq"]).clone()
-    status = torch.full((4,), -7, dtype=torch.int32, device=DEV)
+    g = common.Guards()  # guard bands around the outputs
+    seq = g.like(t["seq"], "seq")
+    status = g.empty((4,), torch.int32, "status")
+    status.fill_(-7)
     v.vlb_bridge_fused_noalloc(br.p, b, _dev(t["features"]), br.w, _dev(t["newline"]),
                                _dev(t["separator"]), _dev(t["mask"] if mask is None else mask),
                                seq, status)
-    return v.vlb_check(status), seq.cpu(), status.cpu()
+    st = v.vlb_check(status)
+    g.check()
+    return st, seq.cpu(), status.cpu()
 
 
 def _same(a, c):
