@@ -116,25 +116,9 @@ __device__ __forceinline__ uint8_t *pick(uint8_t *const (&b)[4], int i) {
 // Epilogue of one tile.  The weight fragment is the MFMA's first operand, so
 // acc[i][j] holds the transposed product: lane (fr, fq) = (lane % 16,
 // lane / 16) of wave (wm, wn) owns token row wm*WT + 16 i + fr and features
-// wn*WT + 16 j + 4 fq + e in element e (e < 4).
+// wn*WT + 16 j + 4 fq + e in element e (e < 4).  The accumulators start from
+// the bias (gemm_tile), so the epilogue adds none.
 //
-// Accumulators start from the bias (the tile's columns, staged in s_bias and
-// visible after the prologue's barrier), so the epilogue adds none.
-template <int BMT>
-__device__ __forceinline__ void init_acc(f32x4 (&acc)[Geo<BMT>::TI][Geo<BMT>::TI],
-                                         const uint16_t *s_bias) {
-  using G = Geo<BMT>;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wn = wid & 1, fq = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < G::TI; ++j) {
-    const uint2 bb = *reinterpret_cast<const uint2 *>(s_bias + wn * G::WT + j * 16 + 4 * fq);
-    const f32x4 b = {bf2f(bb.x & 0xffff), bf2f(bb.x >> 16), bf2f(bb.y & 0xffff), bf2f(bb.y >> 16)};
-#pragma unroll
-    for (int i = 0; i < G::TI; ++i) acc[i][j] = b;
-  }
-}
-
 // stage_tile: the activation (when ACT_ON) applied in fp32 to the
 // accumulators (bias included), the tile rounded to bf16 and staged in the
 // stage buffers (64 rows each; rows of 16-byte chunks XOR-swizzled by the
@@ -271,16 +255,16 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 }
 
 // One output tile: BMT x BMT at (tm, tn) of the BMT-grid, staged through
-// smem0..3 (each at least Geo<BMT>::STAGE bytes) with s_bias / s_dst (at least
-// BMT entries).  Inlined into the kernels below, so the four stage arrays stay
+// smem0..3 (each at least Geo<BMT>::STAGE bytes) with s_dst (at least BMT
+// entries).  Inlined into the kernels below, so the four stage arrays stay
 // distinct LDS objects to the compiler.  K steps [ks0, ks0 + ksn) of the
 // product are accumulated; with part set (kGemmF32 only) the whole BMT x BMT
 // fp32 tile goes to part, row-major, instead of to out.
 template <int MODE, int ACT, int BMT, bool GA, int SZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uint8_t (&smem0)[SZ],
                                           uint8_t (&smem1)[SZ], uint8_t (&smem2)[SZ],
-                                          uint8_t (&smem3)[SZ], uint16_t *s_bias,
-                                          int32_t *s_dst, int ks0, int ksn, float *part) {
+                                          uint8_t (&smem3)[SZ], int32_t *s_dst, int ks0, int ksn,
+                                          float *part) {
   using G = Geo<BMT>;
   static_assert(SZ >= G::STAGE, "stage buffers too small");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -288,11 +272,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   const int m0 = tm * BMT, n0 = tn * BMT;
   // A gradient GEMM writes nothing when the placeholder scan failed.
   if (MODE == kGemmF32 && g.status && g.status[kStatusWord] != 0) return;
-  // Epilogue operands are fetched now so their latency hides under the K loop.
+  // The epilogue's destination rows are fetched now so their latency hides
+  // under the K loop.
   if (tid < BMT) {
-    const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
-    const int c = n0 + tid;
-    s_bias[tid] = (bias && c < g.N) ? bias[c] : static_cast<uint16_t>(0);
     const int m = m0 + tid;
     s_dst[tid] = m >= g.M ? -1 : (g.dst_row ? g.dst_row[m] : m);
   }
@@ -377,7 +359,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     }
   };
 
-  f32x4 acc[G::TI][G::TI];  // set from the bias once s_bias is visible (init_acc)
+  // Accumulators start from the bias, so the epilogue adds none.  Each lane
+  // needs the 4 bias values of its features in every column tile j, 8 bytes
+  // per j, loaded here ahead of the prologue's operands (biases are 16-byte
+  // aligned and N is a multiple of 8, so a column below N has all 4 inside)
+  // and converted once the prologue's barrier has waited for them.  These
+  // kernels use every register; the bias comes straight from memory and is
+  // converted in place because reading it from LDS, or converting it in a
+  // helper, left the allocator copying accumulators inside the gathered-
+  // operand main loop (over 300 moves per four K steps).
+  f32x4 acc[G::TI][G::TI];
+  uint2 bias_v[G::TI];
+  {
+    const uint16_t *bias = static_cast<const uint16_t *>(g.bias);
+    const int wn = wid & 1, fq = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < G::TI; ++j) {
+      const int c = n0 + wn * G::WT + j * 16 + 4 * fq;
+      bias_v[j] = (bias && c < g.N) ? *reinterpret_cast<const uint2 *>(bias + c) : make_uint2(0, 0);
+    }
+  }
 
   const int wm = wid >> 1, wn = wid & 1;
   const int fr = lane & 15, fq = lane >> 4;  // fragment row / 8-wide K group of this lane
@@ -455,7 +456,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   issue(1, smem1, -1);
   issue(2, smem2, -1);
   stage_barrier<BMT>();  // step 0 landed (12 or 6 younger loads may be in flight)
-  init_acc<BMT>(acc, s_bias);
+  {  // the barrier's wait covered the bias loads, which are older
+#pragma unroll
+    for (int j = 0; j < G::TI; ++j) {
+      const f32x4 b = {bf2f(bias_v[j].x & 0xffff), bf2f(bias_v[j].x >> 16),
+                       bf2f(bias_v[j].y & 0xffff), bf2f(bias_v[j].y >> 16)};
+#pragma unroll
+      for (int i = 0; i < G::TI; ++i) acc[i][j] = b;
+    }
+  }
   rd(smem0, fa0, fb0);
   for (int kt = 0; kt < KT; kt += NSTAGE) {  // KT rounds up: the extra steps are all-zero
     step(smem1, smem3, kt, fa0, fb0, fa1, fb1);
@@ -505,14 +514,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s_bias[BMT];  // this tile's bias
-  __shared__ int32_t s_dst[BMT];                                 // destination row per tile row
+  __shared__ int32_t s_dst[BMT];  // destination row per tile row
   int tm, tn;
   if (BMT == 256)
     tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   else
     tail_coords(g, blockIdx.x, tm, tn);
-  gemm_tile<MODE, ACT, BMT, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, g.K / BK,
+  gemm_tile<MODE, ACT, BMT, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, g.K / BK,
                                 nullptr);
 }
 
@@ -528,7 +536,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[G::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem2[G::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t smem3[G::STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t s_bias[256];
   __shared__ int32_t s_dst[256];
   int tm, tn, ks0 = 0, ksn = g.K / BK;
   float *part = nullptr;
@@ -545,11 +552,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
     part = g.split_part + static_cast<int64_t>(u) * (256 * 256);
   } else {
     tail_coords(g, bid - g.n_full, tm, tn);
-    gemm_tile<MODE, ACT, 128, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, 0, ksn,
+    gemm_tile<MODE, ACT, 128, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, ksn,
                                   nullptr);
     return;
   }
-  gemm_tile<MODE, ACT, 256, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_bias, s_dst, ks0, ksn,
+  gemm_tile<MODE, ACT, 256, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, ks0, ksn,
                                 part);
 }
 

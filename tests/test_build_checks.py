@@ -70,3 +70,16 @@ def test_gemm_main_loops_hold_only_operand_loads(gemm_asm):
                 assert ins[0].startswith("buffer_load") and " lds" in ins[1], \
                     f"{name}: {ins[0]}{ins[1]} inside an MFMA loop"
     assert checked >= len(ks), "expected one MFMA loop per kernel at least"
+
+
+def test_gemm_main_loops_keep_accumulators_in_place(gemm_asm):
+    """The accumulators live in AGPRs for the whole product; a copy between
+    register files inside the main loop (register pressure pushing the
+    allocator to shuffle them) costs hundreds of VALU slots per step and once
+    slowed the gathered-operand Linear1 by 15%."""
+    for name, body in kernels(gemm_asm):
+        for lp in loops(body):
+            if "v_mfma" not in lp:
+                continue
+            moves = re.findall(r"^\s+v_accvgpr_(?:mov|read|write)_b32", lp, re.M)
+            assert not moves, f"{name}: {len(moves)} accumulator moves inside an MFMA loop"
