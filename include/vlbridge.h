@@ -268,9 +268,9 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
  */
 
 /* Bytes of the saved-activation buffer of a batch (the merged tokens and the
- * pre-activation of the first and every middle Linear: tile-blocked for
- * VLB_BF16, row-major for VLB_F32; the contents are opaque); 0 on invalid
- * input. */
+ * pre-activation of the first and every middle Linear, and for VLB_BF16 their
+ * activations too: tile-blocked for VLB_BF16, row-major for VLB_F32; the
+ * contents are opaque); 0 on invalid input. */
 size_t vlb_saved_bytes(const vlb_projector *p, const vlb_batch *b);
 
 /* Device workspace bytes of vlb_bridge_backward for this batch and sequence
@@ -306,7 +306,8 @@ typedef struct {
  * at text positions (mask == 0) are not read.  features, w, mask and saved
  * must be those of that forward call (features and w->ln_gamma are read only
  * with the LayerNorm; w->w1, w->w2 and w->w_mid as the projector says,
- * unpacked or packed; biases and ln_beta are not read).  Every token row's gradient is the dseq row of its
+ * unpacked or packed -- unpacked ones are packed into the workspace first;
+ * biases and ln_beta are not read).  Every token row's gradient is the dseq row of its
  * slot; the newline and separator gradients sum the rows of all their slots;
  * padded merge cells take no gradient.
  * Unsupported (VLB_ERR_UNSUPPORTED): has_ln with C > 2048.  Device-detected placeholder-count mismatch: nothing is written

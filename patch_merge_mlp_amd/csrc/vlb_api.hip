@@ -200,11 +200,15 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
 
 // Saved activations of a training forward: the merged tokens (Linear1's
 // operand) and the pre-activation of Linear1 and of every middle Linear,
-// tile-blocked (bf16) or row-major (fp32).
+// tile-blocked (bf16) or row-major (fp32); bf16 keeps their activations as
+// well (the next Linear's operand, written there instead of the workspace),
+// which the weight gradients read token-major.
 struct SavedLayout {
-  size_t off_xm = 0, off_z1 = 0, z_stride = 0, total = 0;
+  size_t off_xm = 0, off_z1 = 0, off_a1 = 0, z_stride = 0, total = 0;
   // pre-activation of Linear1 (q = 0) or of middle Linear q (1 <= q <= depth - 2)
   size_t off_z(int q) const { return off_z1 + static_cast<size_t>(q) * z_stride; }
+  // its activation (bf16)
+  size_t off_a(int q) const { return off_a1 + static_cast<size_t>(q) * z_stride; }
 };
 
 SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
@@ -223,7 +227,8 @@ SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
   off = align256(off + static_cast<size_t>(vlb::blocked_elems(pl.T, pl.K1)) * 2);
   L.off_z1 = off;
   L.z_stride = align256(static_cast<size_t>(vlb::blocked_elems(pl.T, p->hidden)) * 2);
-  L.total = off + nz * L.z_stride;
+  L.off_a1 = off + nz * L.z_stride;
+  L.total = L.off_a1 + nz * L.z_stride;
   return L;
 }
 
@@ -231,8 +236,8 @@ SavedLayout saved_layout(const vlb_projector *p, const Plan &pl) {
 struct BwdLayout {
   int64_t Tk = 0, Op = 0, NL = 0;  // NL: newline slots of the batch
   size_t off_status = 0, off_dst = 0, off_slot = 0, off_nl = 0, off_sep = 0, off_dy = 0,
-         off_dyt = 0, off_a1t = 0, off_w2t = 0, off_da1 = 0, off_dz1 = 0, off_dz1t = 0,
-         off_xmt = 0, off_w1t = 0, off_wmt = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
+         off_dyt = 0, off_a1t = 0, off_w1p = 0, off_w2p = 0, off_wmp = 0, off_da1 = 0,
+         off_dz1 = 0, off_dz1t = 0, off_xmt = 0, off_dxm = 0, off_pb2 = 0, off_pb1 = 0, off_pln = 0,
          off_pnl = 0, off_psep = 0, off_split = 0, total = 0;
   size_t split_bytes = 0;    // K-split partial tiles of the weight gradients (0: none)
   std::vector<int> ln_grid;  // unmerge workgroups per chunk of views
@@ -255,8 +260,8 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
   const int64_t Tk = L->Tk, Op = L->Op;
   if (p->dtype == VLB_BF16)
     for (const int64_t e : {vlb::blocked_elems(T, Op), vlb::blocked_elems(O, Tk),
-                            vlb::blocked_elems(H, Tk), vlb::blocked_elems(H, Op),
-                            vlb::blocked_elems(K1, Tk), vlb::blocked_elems(K1, H),
+                            vlb::blocked_elems(H, Tk), vlb::blocked_elems(O, H),
+                            vlb::blocked_elems(K1, Tk), vlb::blocked_elems(H, K1),
                             vlb::blocked_elems(T, H)})
       if (e * 2 > kI32Max) return VLB_ERR_SHAPE;
   L->ln_grid.clear();
@@ -292,15 +297,16 @@ vlb_status bwd_layout(const vlb_projector *p, const vlb_batch *b, const Plan &pl
   }
   L->off_dy = take(off, static_cast<size_t>(vlb::blocked_elems(T, Op)) * 2);
   L->off_dyt = take(off, static_cast<size_t>(vlb::blocked_elems(O, Tk)) * 2);
-  L->off_a1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
-  L->off_w2t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Op)) * 2);
   L->off_da1 = take(off, static_cast<size_t>(vlb::blocked_elems(T, H)) * 2);
   L->off_dz1 = take(off, static_cast<size_t>(vlb::blocked_elems(T, H)) * 2);
   L->off_dz1t = take(off, static_cast<size_t>(vlb::blocked_elems(H, Tk)) * 2);
   L->off_xmt = take(off, static_cast<size_t>(vlb::blocked_elems(K1, Tk)) * 2);
-  L->off_w1t = take(off, static_cast<size_t>(vlb::blocked_elems(K1, H)) * 2);
-  if (proj_depth(p) > 2)  // a middle weight transposed, one at a time
-    L->off_wmt = take(off, static_cast<size_t>(vlb::blocked_elems(H, H)) * 2);
+  if (!p->packed) {  // weights passed unpacked: packed here (the products read them token-major)
+    L->off_w1p = take(off, static_cast<size_t>(vlb::blocked_elems(H, K1)) * 2);
+    L->off_w2p = take(off, static_cast<size_t>(vlb::blocked_elems(O, H)) * 2);
+    if (proj_depth(p) > 2)  // one middle weight at a time
+      L->off_wmp = take(off, static_cast<size_t>(vlb::blocked_elems(H, H)) * 2);
+  }
   L->off_dxm = take(off, static_cast<size_t>(T) * K1 * 2);
   L->off_pb2 = take(off, static_cast<size_t>(Tk / 32) * O * 4);
   L->off_pb1 = take(off, static_cast<size_t>(Tk / 32) * H * 4);
@@ -443,7 +449,9 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   if (place && (st = run_place_tiled(p, b, pl, place->newline, place->separator, place->seq, ws,
                                      s)) != VLB_OK)
     return st;
-  void *hbuf = ws + pl.off_h;
+  // the hidden activation: the workspace, or the saved activation of Linear1
+  // in a bf16 training forward
+  void *hbuf = saved && p->dtype == VLB_BF16 ? saved + sl.off_a(0) : ws + pl.off_h;
   vlb::GemmArgs g1{};
   g1.A = x;
   g1.desc = desc;
@@ -507,7 +515,8 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
       gm.A = g2.A;
       gm.B = wm;
       gm.bias = w->b_mid[q];
-      gm.out = g2.A == ws + pl.off_h ? ws + pl.off_h2 : ws + pl.off_h;
+      gm.out = saved ? saved + sl.off_a(q + 1)
+               : g2.A == ws + pl.off_h ? ws + pl.off_h2 : ws + pl.off_h;
       gm.M = static_cast<int32_t>(pl.T);
       gm.N = p->hidden;
       gm.K = p->hidden;
@@ -1156,13 +1165,35 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
              vlb::launch_bwd_gather_dy(dseq, dst_row, Ti, Oi, Op, Tk, w8 + L.off_dy,
                                        w8 + L.off_dyt, pb2, s));
   VLB_LAUNCH(VLB_K_BWD_SUM, s, vlb::launch_colsum(pb2, Tk / 32, Oi, g->d_b2, status, s));
-  // 3. dW2 = dY^T act(Z1)
-  VLB_LAUNCH(VLB_K_BWD_PACK, s,
-             vlb::launch_bwd_act_t(p->act, sv + sl.off_z(n_mid), Ti, Hi, Tk, w8 + L.off_a1t, s));
+  // dW2 and the middle weight gradients read the saved activations
+  // token-major (GemmArgs::b_tmaj, rows past T read zero), and the products
+  // with a weight read the packed weight token-major, so neither needs a
+  // transposing pass; weights passed unpacked are packed here first.  dW1
+  // takes Xm^T, whose rows are in the pages' feature order (Xm's columns are
+  // position-major), so the gradient comes out in the pages' order.
   float *split_part = L.split_bytes ? reinterpret_cast<float *>(w8 + L.off_split) : nullptr;
+  auto tmaj_b = [&](vlb::GemmArgs &g, const void *B, int32_t width, int32_t k_valid,
+                    int64_t stored_rows) {
+    g.B = B;
+    g.b_tmaj = 1;
+    g.tb_w = width;
+    g.k_valid = k_valid;
+    g.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(stored_rows, width) * 2);
+  };
+  auto packed_weight = [&](const void *w_in, int64_t R, int64_t Kw, int kmerge, size_t off,
+                           const void **out) -> vlb_status {
+    if (p->packed) {
+      *out = w_in;
+      return VLB_OK;
+    }
+    VLB_LAUNCH(VLB_K_PACK, s, vlb::launch_pack(w_in, R, Kw, p->C, kmerge, w8 + off, s));
+    *out = w8 + off;
+    return VLB_OK;
+  };
+  vlb_status pst;
+  // 3. dW2 = dY^T act(Z1)
   vlb::GemmArgs gw2{};
   gw2.A = w8 + L.off_dyt;
-  gw2.B = w8 + L.off_a1t;
   gw2.out = g->d_w2;
   gw2.status = status;
   gw2.M = Oi;
@@ -1171,17 +1202,14 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   gw2.ldo = Hi;
   gw2.act = VLB_ACT_NONE;
   gw2.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(O, Tk) * 2);
-  gw2.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+  tmaj_b(gw2, sv + sl.off_a(n_mid), Hi, Ti, T);
   gw2.split_part = split_part;
   VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw2, s));
   // 4. dA1 = dY W2, then dZ1 = dA1 * act'(Z1) and db1
-  VLB_LAUNCH(VLB_K_BWD_PACK, s,
-             p->packed  // the packed W2 is tile-blocked [O][H]: transpose it as it is
-                 ? vlb::launch_bwd_act_t(VLB_ACT_NONE, w->w2, Oi, Hi, Op, w8 + L.off_w2t, s)
-                 : vlb::launch_bwd_weight_t(w->w2, Oi, Hi, p->C, 1, Op, w8 + L.off_w2t, s));
+  const void *w2p = nullptr;
+  if ((pst = packed_weight(w->w2, O, H, 1, L.off_w2p, &w2p)) != VLB_OK) return pst;
   vlb::GemmArgs ga{};
   ga.A = w8 + L.off_dy;
-  ga.B = w8 + L.off_w2t;
   ga.out = w8 + L.off_da1;
   ga.M = Ti;
   ga.N = Hi;
@@ -1189,7 +1217,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   ga.ldo = Hi;
   ga.act = VLB_ACT_NONE;
   ga.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, Op) * 2);
-  ga.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Op) * 2);
+  tmaj_b(ga, w2p, Hi, Op, O);  // packed W2 [O][H]: rows past O are zero
   VLB_LAUNCH(VLB_K_BWD_DA1, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, ga, s));
   float *pb1 = reinterpret_cast<float *>(w8 + L.off_pb1);
   VLB_LAUNCH(VLB_K_BWD_PACK, s,
@@ -1200,11 +1228,8 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     VLB_LAUNCH(VLB_K_BWD_SUM, s,
                vlb::launch_colsum(pb1, Tk / 32, Hi, g->d_b_mid[q - 1], status, s));
     // dW_q = dZ_q^T act(Z_{q-1})
-    VLB_LAUNCH(VLB_K_BWD_PACK, s,
-               vlb::launch_bwd_act_t(p->act, sv + sl.off_z(q - 1), Ti, Hi, Tk, w8 + L.off_a1t, s));
     vlb::GemmArgs gwm{};
     gwm.A = w8 + L.off_dz1t;
-    gwm.B = w8 + L.off_a1t;
     gwm.out = g->d_w_mid[q - 1];
     gwm.status = status;
     gwm.M = Hi;
@@ -1213,17 +1238,14 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     gwm.ldo = Hi;
     gwm.act = VLB_ACT_NONE;
     gwm.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
-    gwm.b_bytes = gwm.a_bytes;
+    tmaj_b(gwm, sv + sl.off_a(q - 1), Hi, Ti, T);
     gwm.split_part = split_part;
     VLB_LAUNCH(VLB_K_BWD_DW2, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gwm, s));
     // dA_{q-1} = dZ_q W_q, then dZ_{q-1} = dA_{q-1} * act'(Z_{q-1})
-    const void *wq = w->w_mid[q - 1];
-    VLB_LAUNCH(VLB_K_BWD_PACK, s,
-               p->packed ? vlb::launch_bwd_act_t(VLB_ACT_NONE, wq, Hi, Hi, Hi, w8 + L.off_wmt, s)
-                         : vlb::launch_bwd_weight_t(wq, Hi, Hi, p->C, 1, Hi, w8 + L.off_wmt, s));
+    const void *wqp = nullptr;
+    if ((pst = packed_weight(w->w_mid[q - 1], H, H, 1, L.off_wmp, &wqp)) != VLB_OK) return pst;
     vlb::GemmArgs gam{};
     gam.A = w8 + L.off_dz1;
-    gam.B = w8 + L.off_wmt;
     gam.out = w8 + L.off_da1;
     gam.M = Ti;
     gam.N = Hi;
@@ -1231,7 +1253,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     gam.ldo = Hi;
     gam.act = VLB_ACT_NONE;
     gam.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, H) * 2);
-    gam.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, H) * 2);
+    tmaj_b(gam, wqp, Hi, Hi, H);
     VLB_LAUNCH(VLB_K_BWD_DA1, s, vlb::launch_gemm_bf16(vlb::kGemmBlocked, gam, s));
     VLB_LAUNCH(VLB_K_BWD_PACK, s,
                vlb::launch_bwd_dact(p->act, w8 + L.off_da1, sv + sl.off_z(q - 1), Ti, Hi, Tk,
@@ -1243,7 +1265,6 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
              vlb::launch_bwd_xm_t(sv + sl.off_xm, Ti, p->C, p->k, Tk, w8 + L.off_xmt, s));
   vlb::GemmArgs gw1{};
   gw1.A = w8 + L.off_dz1t;
-  gw1.B = w8 + L.off_xmt;
   gw1.out = g->d_w1;
   gw1.status = status;
   gw1.M = Hi;
@@ -1252,19 +1273,17 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
   gw1.ldo = K1i;
   gw1.act = VLB_ACT_NONE;
   gw1.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(H, Tk) * 2);
+  gw1.B = w8 + L.off_xmt;
   gw1.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(K1, Tk) * 2);
   gw1.split_part = split_part;
   VLB_LAUNCH(VLB_K_BWD_DW1, s, vlb::launch_gemm_bf16(vlb::kGemmF32, gw1, s));
-  // 6. dXm = dZ1 W1 (K position-major), unmerge, LayerNorm backward
+  // 6. dXm = dZ1 W1 (K position-major, the packed W1's order), unmerge,
+  // LayerNorm backward
   if (ln || g->d_features) {
-    VLB_LAUNCH(VLB_K_BWD_PACK, s,
-               p->packed  // packed W1: tile-blocked [H][K1], K1 already position-major
-                   ? vlb::launch_bwd_act_t(VLB_ACT_NONE, w->w1, Hi, K1i, Hi, w8 + L.off_w1t, s)
-                   : vlb::launch_bwd_weight_t(w->w1, Hi, K1i, p->C, p->k, Hi, w8 + L.off_w1t,
-                                              s));
+    const void *w1p = nullptr;
+    if ((pst = packed_weight(w->w1, H, K1, p->k, L.off_w1p, &w1p)) != VLB_OK) return pst;
     vlb::GemmArgs gx{};
     gx.A = w8 + L.off_dz1;
-    gx.B = w8 + L.off_w1t;
     gx.out = w8 + L.off_dxm;
     gx.M = Ti;
     gx.N = K1i;
@@ -1272,7 +1291,7 @@ vlb_status vlb_bridge_backward(const vlb_projector *p, const vlb_batch *b, const
     gx.ldo = K1i;
     gx.act = VLB_ACT_NONE;
     gx.a_bytes = static_cast<uint32_t>(vlb::blocked_elems(T, H) * 2);
-    gx.b_bytes = static_cast<uint32_t>(vlb::blocked_elems(K1, H) * 2);
+    tmaj_b(gx, w1p, K1i, Hi, H);
     VLB_LAUNCH(VLB_K_BWD_DX, s, vlb::launch_gemm_bf16(vlb::kGemmRows, gx, s));
     float *pg = reinterpret_cast<float *>(w8 + L.off_pln);
     float *pbeta = pg + L.ln_rows * C;

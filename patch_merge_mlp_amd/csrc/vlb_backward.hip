@@ -12,15 +12,18 @@
 //   dXm unmerged to pixels, then through the LayerNorm.
 //
 // The four products run on the MFMA GEMM, which contracts over the 32-wide K
-// slices of two tile-blocked operands (element (r, c) of [R][K] at
-// ((r/256 * K/32 + c/32) * 256 + r%256) * 32 + c%32).  The kernels here build
-// those operands: a workgroup takes 32 consecutive rows t (one K slice of the
-// transposed operand) and 256 columns, stages them in LDS, and writes each
-// column's 32 values as one contiguous 64-byte piece of the transposed
-// operand -- 256 such pieces are one 16 KiB run.  Rows past T are zero, so the
-// padded part of every contraction over T adds nothing.  Column sums (the
-// bias gradients) are written per 32-row slice and reduced in a fixed order,
-// so every gradient is deterministic.
+// slices of tile-blocked operands (element (r, c) of [R][K] at
+// ((r/256 * K/32 + c/32) * 256 + r%256) * 32 + c%32).  Its B operand may also
+// be token-major (the saved activations, the packed weights), read through
+// LDS transpose reads; the A operands of the weight gradients, dY^T and
+// dZ^T, are written here by the kernels that produce dY and dZ anyway, and
+// Xm^T (dW1's B, rows in the pages' feature order) by a pass of its own: a
+// workgroup takes 32 consecutive rows t (one K slice of the transposed
+// operand) and 256 columns, stages them in LDS, and writes each column's 32
+// values as one contiguous 64-byte piece -- 256 such pieces are one 16 KiB
+// run.  Rows past T are zero, so the padded part of every contraction over T
+// adds nothing.  Column sums (the bias gradients) are written per 32-row
+// slice and reduced in a fixed order, so every gradient is deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -146,34 +149,6 @@ __global__ __launch_bounds__(256) void k_bwd_gather_dy(const uint16_t *G, const 
   if (o < O) part[static_cast<int64_t>(blockIdx.x) * O + o] = col_sum(tile, tid);
 }
 
-// act(Z1)^T: Z1 tile-blocked [T][H] (rows past T unused) -> [H][Tk].
-template <int ACT>
-__global__ __launch_bounds__(256) void k_bwd_act_t(const uint16_t *z1, int32_t T, int32_t H,
-                                                   int32_t Tk, uint16_t *a1t) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  uint4 v[kPackIters];  // all loads out before the first is used
-#pragma unroll
-  for (int i = 0; i < kPackIters; ++i) {
-    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
-    const int t = t0 + row, h = n0 + sl * 32 + c4 * 8;
-    v[i] = (t < T && h < H) ? *reinterpret_cast<const uint4 *>(z1 + blk(t, h, H)) : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kPackIters; ++i) {
-    const int q = tid + 256 * i, sl = q >> 7, row = (q >> 2) & 31, c4 = q & 3;
-    if (t0 + row < T && n0 + sl * 32 + c4 * 8 < H) {
-      uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = f2bf(act_fn<ACT>(bf2f(e[j])));
-    }
-    *reinterpret_cast<uint4 *>(tile + row * kPitch + sl * 32 + c4 * 8) = v[i];
-  }
-  __syncthreads();
-  store_columns(tile, min(kTC, H - n0), a1t + blk(n0, t0, Tk));
-}
-
 // dZ1 = dA1 * act'(Z1) (both tile-blocked [T][H]): dZ1 tile-blocked, its
 // transpose [H][Tk], and per-slice column sums of the rounded values (the
 // values dW1 and dXm are computed from).
@@ -238,36 +213,6 @@ __global__ __launch_bounds__(256) void k_bwd_xm_t(const uint16_t *xm, int32_t T,
   __syncthreads();
   const int j = n0 + tid;
   if (j < K1) store_column(tile, tid, xmt + blk(static_cast<int64_t>(j % C) * kk + j / C, t0, Tk));
-}
-
-// Transpose of a row-major weight W [R][Cs] into the tile-blocked [Cs][Rk]
-// (Rk = R rounded up to 32, zeros past R).  kk > 1 (W1, columns in the pages'
-// order c*k*k + p): output row of column i is the position-major p*C + c.
-__global__ __launch_bounds__(256) void k_bwd_weight_t(const uint16_t *w, int32_t R, int32_t Cs,
-                                                      int32_t C, int32_t kk, int32_t Rk,
-                                                      uint16_t *out) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTR * kPitch];
-  const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * kTR, n0 = blockIdx.y * kTC;
-  uint4 v[kPackIters];  // all loads out before the first is used
-#pragma unroll
-  for (int k = 0; k < kPackIters; ++k) {
-    const int q = tid + 256 * k, r = r0 + (q >> 5), i = n0 + (q & 31) * 8;
-    v[k] = (r < R && i < Cs) ? *reinterpret_cast<const uint4 *>(w + static_cast<int64_t>(r) * Cs + i)
-                             : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < kPackIters; ++k) {
-    const int q = tid + 256 * k;
-    *reinterpret_cast<uint4 *>(tile + (q >> 5) * kPitch + (q & 31) * 8) = v[k];
-  }
-  __syncthreads();
-  if (kk == 1) {
-    store_columns(tile, min(kTC, Cs - n0), out + blk(n0, r0, Rk));
-    return;
-  }
-  const int i = n0 + tid;
-  if (i < Cs) store_column(tile, tid, out + blk(static_cast<int64_t>(i % kk) * C + i / kk, r0, Rk));
 }
 
 // Feature gradient of the pixels of one chunk of views (see PlanChunk), one
@@ -851,21 +796,6 @@ hipError_t launch_bwd_gather_dy(const void *G, const int32_t *dst_row, int32_t T
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_act_t(int act, const void *z1, int32_t T, int32_t H, int32_t Tk, void *a1t,
-                            hipStream_t s) {
-  if (Tk <= 0) return hipSuccess;
-  const dim3 grid(Tk / kTR, (H + kTC - 1) / kTC);
-  const uint16_t *zz = static_cast<const uint16_t *>(z1);
-  uint16_t *o = static_cast<uint16_t *>(a1t);
-  if (act == 0)
-    hipLaunchKernelGGL(k_bwd_act_t<0>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
-  else if (act == 1)
-    hipLaunchKernelGGL(k_bwd_act_t<1>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
-  else
-    hipLaunchKernelGGL(k_bwd_act_t<2>, grid, dim3(256), 0, s, zz, T, H, Tk, o);
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_dact(int act, const void *da1, const void *z1, int32_t T, int32_t H,
                            int32_t Tk, void *dz1, void *dz1t, float *part, hipStream_t s) {
   if (Tk <= 0) return hipSuccess;
@@ -888,14 +818,6 @@ hipError_t launch_bwd_xm_t(const void *xm, int32_t T, int32_t C, int32_t k, int3
   const dim3 grid(Tk / kTR, (K1 + kTC - 1) / kTC);
   hipLaunchKernelGGL(k_bwd_xm_t, grid, dim3(256), 0, s, static_cast<const uint16_t *>(xm), T, K1,
                      C, k * k, Tk, static_cast<uint16_t *>(xmt));
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_weight_t(const void *w, int32_t R, int32_t Cs, int32_t C, int32_t k,
-                               int32_t Rk, void *out, hipStream_t s) {
-  const dim3 grid(Rk / kTR, (Cs + kTC - 1) / kTC);
-  hipLaunchKernelGGL(k_bwd_weight_t, grid, dim3(256), 0, s, static_cast<const uint16_t *>(w), R,
-                     Cs, C, k * k, Rk, static_cast<uint16_t *>(out));
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ namespace vlb {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = kGemmBK, NTHREADS = 256;
@@ -91,6 +92,23 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+
+// Token-major operand halves hold BMT/32 blocks of 2 KiB, one per 32 tile
+// rows: 32 contraction indices k of 64 bytes, the 16-byte pieces of row k
+// XOR-ed with tswz(k) (0 or 2).  With it the 16 lanes of a transposing read
+// (4 rows k x 32 bytes) fall on 32 distinct 4-byte banks, and two groups of
+// 16 lanes (k and k + 8) on all 64.
+__device__ __forceinline__ int tswz(int k) { return (((k >> 1) ^ (k >> 3)) & 1) << 1; }
+
+// Transposing LDS read (ds_read_b64_tr_b16): in every group of 16 lanes,
+// lane 4y + x supplies the address of 4 consecutive 16-bit values (row y,
+// columns 4x .. 4x + 3 of a 4 x 16 block) and lane l receives column l of
+// the block, rows 0..3.
+__device__ __forceinline__ bf16x4 tr16(lds_u8 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
 
 // Byte offset that lies past every buffer (buffers are < 2^31 bytes): a buffer
 // load from it returns zeros, which is how padding and out-of-range rows are
@@ -260,7 +278,7 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[Geo<BMT>::TI][Geo<
 // distinct LDS objects to the compiler.  K steps [ks0, ks0 + ksn) of the
 // product are accumulated; with part set (kGemmF32 only) the whole BMT x BMT
 // fp32 tile goes to part, row-major, instead of to out.
-template <int MODE, int ACT, int BMT, bool GA, int SZ>
+template <int MODE, int ACT, int BMT, bool GA, bool TB, int SZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uint8_t (&smem0)[SZ],
                                           uint8_t (&smem1)[SZ], uint8_t (&smem2)[SZ],
                                           uint8_t (&smem3)[SZ], int32_t *s_dst, int ks0, int ksn,
@@ -305,6 +323,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   // Linear1 runs 18-25% slower than on the blocked operand, which costs more
   // than the merge pass it saves (so this is the memory-lean mode, not the
   // default).
+  // Token-major B (TB; see GemmArgs::tb_w).  Instruction i of wave wid fills
+  // KiB gi = wid*LPW + i of the half: the 16 contraction indices k = 16 (gi &
+  // 1) + lane/4 of tile rows n0 + 32 (gi >> 1) + [0, 32), lane slot lane%4
+  // holding the logical 8-row piece (lane%4) ^ tswz(k).  t_off is the lane's
+  // offset at step 0; rows past the stored width W read zeros.
+  auto t_off = [&](int r0, int W, int i) -> uint32_t {
+    const int gi = wid * G::LPW + i;
+    const int k = (gi & 1) * 16 + (lane >> 2);
+    const int lp = (lane & 3) ^ tswz(k);
+    const int r = r0 + (gi >> 1) * 32 + lp * 8;
+    return r < W ? (static_cast<uint32_t>((r >> 5) * 256 + k) * 64 + lp * 16) : kOOB;
+  };
   uint32_t a_off[G::LPW], b_off[G::LPW];
   uint32_t a_gw[GA ? G::LPW : 1], a_inv[GA ? G::LPW : 1];
   const uint32_t c2 = static_cast<uint32_t>(g.C) * 2;  // bytes of one pixel (GA)
@@ -321,7 +351,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     } else {
       a_off[i] = m < g.M ? blocked(m) + c_off : kOOB;
     }
-    b_off[i] = n < g.N ? blocked(n) + c_off : kOOB;
+    if constexpr (TB)
+      b_off[i] = t_off(n0, g.tb_w, i);
+    else
+      b_off[i] = n < g.N ? blocked(n) + c_off : kOOB;
   }
   // GA: step ka covers channels [32 c, 32 c + 32) of block position
   // p = (dy, dx), ka = p * cps + c.  The divisions are multiplications by
@@ -347,15 +380,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     const uint32_t ga_p = (ka * ga_inv_cps) >> 20, ga_c = ka - ga_p * ga_cps;
     const uint32_t ga_dy = (ga_p * ga_inv_k) >> 20, ga_dx = ga_p - ga_dy * g.k;
     const uint32_t ga_s = ga_dx * c2 + ga_c * 64 + dead;
+    // Token-major B: step ka is rows k of the stored [K][W] blocks (k / 256 =
+    // ka / 8, 32 rows each); indices at or past k_valid read zero.
+    const int lim = g.k_valid - static_cast<int>(ka) * BK;
+    const uint32_t tb_s = ((ka >> 3) * static_cast<uint32_t>(g.tb_w >> 5) * 256 + (ka & 7) * 32) * 64;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
+      const uint32_t kdead = ((i & 1) * 16 + (lane >> 2)) < lim ? 0u : kOOB;
       if constexpr (GA) {
         const uint32_t off = a_off[i] + ga_dy * a_gw[i] + ga_s;
         load_lds16(rA, sa + i * 1024, off | ((a_inv[i] >> ga_p) << 31));
       } else {
         load_lds16(rA, sa + i * 1024, (a_off[i] + step_off) | dead);
       }
-      load_lds16(rB, sb + i * 1024, (b_off[i] + step_off) | dead);
+      if constexpr (TB)
+        load_lds16(rB, sb + i * 1024, (b_off[i] + tb_s) | dead | kdead);
+      else
+        load_lds16(rB, sb + i * 1024, (b_off[i] + step_off) | dead);
     }
   };
 
@@ -385,13 +426,39 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   // Fragments of one K step (32): TI tiles of 16 rows for each operand; two
   // sets, so the next step's are read while this step's multiply.
   bf16x8 fa0[G::TI], fb0[G::TI], fa1[G::TI], fb1[G::TI];
+  // LDS offsets of this lane's fragment reads.  Fragment t covers tile rows
+  // w0 + 16 t .. + 15 (w0 = wm*WT for A, wn*WT for B), and both stage layouts
+  // place it at a lane offset that depends on t only through its parity, plus
+  // (t >> 1) * 2048: so each operand needs two lane offsets and the rest are
+  // immediates.
+  //   row-major stage: row w0 + 16 t + fr, logical chunk fq (swz);
+  //   token-major stage: two transposing reads of 4 K rows each -- lane 4c + q
+  //   of a group reads K row 8 fq + c (then + 4: 256 bytes on, tswz(k + 4) ==
+  //   tswz(k)) at tile rows w0 + 16 t + 4q .. + 3, so lane fr receives row
+  //   w0 + 16 t + fr, K indices 8 fq .. 8 fq + 7.
+  auto rd_off = [&](bool tmaj, int w0, int par) -> int {
+    if (!tmaj) return swz(w0 + 16 * par + fr, fq);
+    const int c = fr >> 2, q = fr & 3, k0 = 8 * fq + c;
+    const int lp = 2 * par + (q >> 1);
+    return (w0 >> 5) * 2048 + k0 * 64 + ((lp ^ tswz(k0)) << 4) + (q & 1) * 8;
+  };
+  const int ra0 = rd_off(false, wm * G::WT, 0), ra1 = rd_off(false, wm * G::WT, 1);
+  const int rb0 = G::HALF + rd_off(TB, wn * G::WT, 0), rb1 = G::HALF + rd_off(TB, wn * G::WT, 1);
+  auto frag = [&](const uint8_t *stage, bool tmaj, int off) -> bf16x8 {
+    lds_u8 *p = (lds_u8 *)(stage) + off;
+    if (!tmaj) return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8 *>(p);
+    const bf16x4 lo = tr16(p), hi = tr16(p + 256);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
   auto rd = [&](const uint8_t *stage, bf16x8 *fa, bf16x8 *fb) {
 #pragma unroll
     for (int t = 0; t < G::TI; ++t) {
-      fa[t] = *reinterpret_cast<const bf16x8 *>(stage + swz(wm * G::WT + t * 16 + fr, fq));
-      fb[t] = *reinterpret_cast<const bf16x8 *>(stage + G::HALF + swz(wn * G::WT + t * 16 + fr, fq));
+      fa[t] = frag(stage, false, ((t & 1) ? ra1 : ra0) + (t >> 1) * 2048);
+      fb[t] = frag(stage, TB, ((t & 1) ? rb1 : rb0) + (t >> 1) * 2048);
     }
   };
+  // LDS read instructions per step: one per fragment, two for a token-major one
+  constexpr int NRD = G::TI + G::TI * (TB ? 2 : 1);
   // MFMAs [i0, i1) of the step, i-major (A tile i, B tile j).
   auto mma = [&](const bf16x8 *fa, const bf16x8 *fb, int i0, int i1) {
 #pragma unroll
@@ -433,20 +500,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     rd(nxt, na, nb);
     issue(kt + 3, fut, 1);
     mma(fa, fb, Q, G::TI);
-    if constexpr (BMT == 256) {  // 48 MFMAs, 16 fragment reads, 4 loads
+    if constexpr (BMT == 256) {  // 48 MFMAs, 16-32 LDS reads, 4 loads
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        if (NRD == 24 && (i & 1))
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-    } else {  // 12 MFMAs, 8 fragment reads, 2 loads
+    } else {  // 12 MFMAs, 8-16 LDS reads, 2 loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (NRD == 16)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (NRD >= 12)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
@@ -507,7 +583,7 @@ __device__ __forceinline__ void tail_coords(const GemmArgs &g, int bid, int &tm,
 // tiles [0, n_full) of the 256-grid), or the 128-tiles (BMT = 128: the four
 // quarters of every 256-tile from n_full on, or -- when n_full == 0 -- the
 // whole 128-grid).
-template <int MODE, int ACT, int BMT, bool GA>
+template <int MODE, int ACT, int BMT, bool GA, bool TB>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   using G = Geo<BMT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -520,8 +596,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
     tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   else
     tail_coords(g, blockIdx.x, tm, tn);
-  gemm_tile<MODE, ACT, BMT, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, g.K / BK,
-                                nullptr);
+  gemm_tile<MODE, ACT, BMT, GA, TB>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, g.K / BK,
+                                    nullptr);
 }
 
 // Both parts in one launch: workgroups [0, n_full) take the 256-tiles, the
@@ -529,7 +605,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
 // whose last whole tile is done starts a quarter tile at once instead of
 // waiting for the slowest whole tile of the launch.  n_full is a multiple of
 // 256, so workgroup n_full + q still runs on XCD q % 8.
-template <int MODE, int ACT, bool GA>
+template <int MODE, int ACT, bool GA, bool TB>
 __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   using G = Geo<256>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[G::STAGE];
@@ -552,12 +628,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
     part = g.split_part + static_cast<int64_t>(u) * (256 * 256);
   } else {
     tail_coords(g, bid - g.n_full, tm, tn);
-    gemm_tile<MODE, ACT, 128, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, ksn,
-                                  nullptr);
+    gemm_tile<MODE, ACT, 128, GA, TB>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, ksn,
+                                      nullptr);
     return;
   }
-  gemm_tile<MODE, ACT, 256, GA>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, ks0, ksn,
-                                part);
+  gemm_tile<MODE, ACT, 256, GA, TB>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, ks0, ksn,
+                                    part);
 }
 
 // out rows of the split tail tiles: tile q's k_splits partial tiles added in
@@ -581,22 +657,22 @@ __global__ __launch_bounds__(256) void k_split_sum(GemmArgs g) {
       acc;
 }
 
-template <int MODE, int ACT, bool GA = false>
+template <int MODE, int ACT, bool GA = false, bool TB = false>
 void launch_bf16(const GemmArgs &g, int blocks256, int blocks128, hipStream_t s) {
   // Whole tiles and the quarter-tile tail in one launch while the quarter
   // tiles fit one round at one per CU; beyond that the quarter-tile kernel of
   // its own (two per CU: a third of the registers and half the LDS) is faster
   // (dW1 of workload 1, 272 quarter tiles: 340 against 367 us).
   if (blocks256 > 0 && blocks128 > 0 && blocks128 <= kPlanCUs)
-    hipLaunchKernelGGL((k_gemm_bf16_mixed<MODE, ACT, GA>), dim3(blocks256 + blocks128),
+    hipLaunchKernelGGL((k_gemm_bf16_mixed<MODE, ACT, GA, TB>), dim3(blocks256 + blocks128),
                        dim3(NTHREADS), 0, s, g);
   else {
     if (blocks256 > 0)
-      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256, GA>), dim3(blocks256), dim3(NTHREADS), 0, s,
-                         g);
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 256, GA, TB>), dim3(blocks256), dim3(NTHREADS), 0,
+                         s, g);
     if (blocks128 > 0)
-      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128, GA>), dim3(blocks128), dim3(NTHREADS), 0, s,
-                         g);
+      hipLaunchKernelGGL((k_gemm_bf16<MODE, ACT, 128, GA, TB>), dim3(blocks128), dim3(NTHREADS), 0,
+                         s, g);
   }
 }
 
@@ -619,19 +695,32 @@ hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
   g.tiles_m = tp.tiles_m;
   g.tiles_n = tp.tiles_n;
   g.n_full = tp.n_full;
+  // Token-major B: the saved activations in the weight-gradient products, a
+  // packed weight read transposed in the products with a weight.
+  if (g.b_tmaj && g.tb_w % BK) return hipErrorInvalidValue;
   switch (mode) {
-    case kGemmBlocked: launch_act<kGemmBlocked>(g, tp, s); break;
+    case kGemmBlocked:
+      if (g.b_tmaj && g.act == 2)
+        launch_bf16<kGemmBlocked, 2, false, true>(g, tp.n_full, tp.blocks128, s);
+      else if (!g.b_tmaj)
+        launch_act<kGemmBlocked>(g, tp, s);
+      else
+        return hipErrorInvalidValue;
+      break;
     case kGemmGatherBlocked:  // A gathered from the grid through g.desc
-      if (!g.desc || g.C % BK || g.k < 1 || g.k > 3) return hipErrorInvalidValue;
+      if (!g.desc || g.C % BK || g.k < 1 || g.k > 3 || g.b_tmaj) return hipErrorInvalidValue;
       launch_act<kGemmBlocked, true>(g, tp, s);
       break;
     case kGemmBlockedSave:
-      if (!g.out2) return hipErrorInvalidValue;
+      if (!g.out2 || g.b_tmaj) return hipErrorInvalidValue;
       launch_act<kGemmBlockedSave>(g, tp, s);
       break;
     case kGemmRows:  // no activation
       if (g.act != 2) return hipErrorInvalidValue;
-      launch_bf16<kGemmRows, 2>(g, tp.n_full, tp.blocks128, s);
+      if (g.b_tmaj)
+        launch_bf16<kGemmRows, 2, false, true>(g, tp.n_full, tp.blocks128, s);
+      else
+        launch_bf16<kGemmRows, 2>(g, tp.n_full, tp.blocks128, s);
       break;
     case kGemmF32: {  // no bias, no activation
       if (g.act != 2 || g.N % 4 || g.ldo % 4) return hipErrorInvalidValue;
@@ -639,9 +728,15 @@ hipError_t launch_gemm_bf16(int mode, GemmArgs g, hipStream_t s) {
       g.k_splits = S;
       if (S > 1) {  // whole tiles and the split tail in one launch, then the sums
         const int rem = tp.tiles_m * tp.tiles_n - tp.n_full;
-        hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2, false>), dim3(tp.n_full + rem * S),
-                           dim3(NTHREADS), 0, s, g);
+        if (g.b_tmaj)
+          hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2, false, true>),
+                             dim3(tp.n_full + rem * S), dim3(NTHREADS), 0, s, g);
+        else
+          hipLaunchKernelGGL((k_gemm_bf16_mixed<kGemmF32, 2, false, false>),
+                             dim3(tp.n_full + rem * S), dim3(NTHREADS), 0, s, g);
         hipLaunchKernelGGL(k_split_sum, dim3(64, rem), dim3(256), 0, s, g);
+      } else if (g.b_tmaj) {
+        launch_bf16<kGemmF32, 2, false, true>(g, tp.n_full, tp.blocks128, s);
       } else {
         launch_bf16<kGemmF32, 2>(g, tp.n_full, tp.blocks128, s);
       }

@@ -85,6 +85,15 @@ struct GemmArgs {
   // tile are added in order into out by a second kernel.  Set by the launcher.
   float *split_part;
   int32_t k_splits;
+  // bf16 path, b_tmaj: B is token-major, stored tile-blocked with the
+  // contraction index as its row -- [K][W] with element (k, n) at
+  // ((k/256 * W/32 + n/32) * 256 + k%256) * 32 + n%32 -- so a product that
+  // contracts over tokens reads it as the producing kernel wrote it, and a
+  // packed weight [N][K] serves as the B of the product with its transpose.
+  // tb_w: the stored width W (a multiple of 32); contraction indices at or
+  // past k_valid read zero.
+  int32_t b_tmaj;
+  int32_t tb_w, k_valid;
 };
 
 // Epilogues of the bf16 GEMM.
@@ -239,20 +248,13 @@ int bwd_unmerge_grid(int64_t items);   // workgroups for items (token row, posit
 hipError_t launch_bwd_gather_dy(const void *G, const int32_t *dst_row, int32_t T, int32_t O,
                                 int32_t Op, int32_t Tk, void *dy, void *dyt, float *part,
                                 hipStream_t s);
-// act(Z1)^T [H][Tk] from the blocked pre-activation Z1 [T][H].
-hipError_t launch_bwd_act_t(int act, const void *z1, int32_t T, int32_t H, int32_t Tk, void *a1t,
-                            hipStream_t s);
-// dZ1 = dA1 * act'(Z1) -> dZ1 [T][H], dZ1^T [H][Tk], part [Tk/32][H].
-hipError_t launch_bwd_dact(int act, const void *da1, const void *z1, int32_t T, int32_t H,
-                           int32_t Tk, void *dz1, void *dz1t, float *part, hipStream_t s);
 // Merged tokens Xm [T][C*k*k] (K position-major) -> Xm^T [C*k*k][Tk], rows in
 // the pages' feature order.
 hipError_t launch_bwd_xm_t(const void *xm, int32_t T, int32_t C, int32_t k, int32_t Tk, void *xmt,
                            hipStream_t s);
-// Row-major W [R][Cs] -> blocked W^T [Cs][Rk] (zeros past R); k > 1: W is
-// W1 and output rows are position-major.
-hipError_t launch_bwd_weight_t(const void *w, int32_t R, int32_t Cs, int32_t C, int32_t k,
-                               int32_t Rk, void *out, hipStream_t s);
+// dZ1 = dA1 * act'(Z1) -> dZ1 [T][H], dZ1^T [H][Tk], part [Tk/32][H].
+hipError_t launch_bwd_dact(int act, const void *da1, const void *z1, int32_t T, int32_t H,
+                           int32_t Tk, void *dz1, void *dz1t, float *part, hipStream_t s);
 // Feature gradient of one chunk of views from dXm (row-major [T][C*k*k], K
 // position-major) through the LayerNorm (gamma non-null) or not; grid rows of
 // part_g / part_b ([grid][C]) take the per-workgroup dgamma / dbeta sums.

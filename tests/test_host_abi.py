@@ -202,13 +202,17 @@ def test_training_entry_points_validate():
     b = v.Batch([(4, 4)], [1])
     T = v.vlb_num_tokens(p, b)
     K1 = p.C * p.k * p.k
-    assert v.vlb_saved_bytes(p, b) == 256 * K1 * 2 + 256 * p.hidden * 2
+    # bf16: blocked merged rows, then Z1 and act(Z1), 256-row blocks each
+    assert v.vlb_saved_bytes(p, b) == 256 * K1 * 2 + 2 * 256 * p.hidden * 2
     # fp32: row-major merged rows (4 x 256) and Z1 (4 x 128), 256-byte aligned
     assert v.vlb_saved_bytes(_proj(dtype=v.F32), b) == 4 * K1 * 4 + 4 * p.hidden * 4
     need = v.vlb_backward_workspace_bytes(p, b, 32)
     assert need > 0
     assert v.vlb_backward_workspace_bytes(_proj(dtype=v.F32), b, 32) > 0
     assert v.vlb_backward_workspace_bytes(_proj(packed=True), b, 32) > 0
+    # unpacked weights are packed into the backward workspace
+    assert v.vlb_backward_workspace_bytes(_proj(), b, 32) > v.vlb_backward_workspace_bytes(
+        _proj(packed=True), b, 32)
     assert v.vlb_backward_workspace_bytes(_proj(has_ln=True, C=2112), b, 32) == 0
     w = v.vlb_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     fneed = v.vlb_workspace_bytes(p, b, 32)
@@ -259,8 +263,9 @@ def test_depth_validation():
     n2, n3 = v.vlb_workspace_bytes(_proj(), b, 32), v.vlb_workspace_bytes(p3, b, 32)
     # a second hidden buffer (256 x 128 bf16) and one packed middle weight (256 x 128)
     assert n3 - n2 == 2 * 256 * 128 * 2
-    # saved: merged tokens and the pre-activations of Linear1 and the middle Linear
-    assert v.vlb_saved_bytes(p3, b) == 256 * 256 * 2 + 2 * 256 * 128 * 2
+    # saved: merged tokens, then the pre-activations and the activations of
+    # Linear1 and the middle Linear
+    assert v.vlb_saved_bytes(p3, b) == 256 * 256 * 2 + 4 * 256 * 128 * 2
     assert v.vlb_backward_workspace_bytes(p3, b, 32) > v.vlb_backward_workspace_bytes(_proj(), b, 32)
 
     def fused(w, proj=p3):
