@@ -10,7 +10,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <type_traits>
 
 #include "vlb_common.h"
 #include "vlb_internal.h"
@@ -410,11 +409,10 @@ __global__ __launch_bounds__(256) void k_layernorm(const T *x, int64_t npix, int
 //
 // One launch covers the token rows of a chunk of up to 64 views; lane v of
 // every wave keeps view v's table entry, so a row's view is found with one
-// ballot.  An item is 16 consecutive rows (aligned to 16, so they share a
-// 256-row block) at one position; a workgroup of 16 waves takes items in
-// turn (two persistent workgroups per CU).  Wave r loads row r's pixel (NCH
-// 16-byte chunks per lane, or with DW NCH dwords), normalises it and stages
-// it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
+// ballot.  A workgroup of 16 waves takes one item: 16 consecutive rows
+// (aligned to 16, so they share a 256-row block) at one position.  Wave r
+// loads row r's pixel (NCH 16-byte chunks per lane, or with DW NCH dwords),
+// normalises it and stages it in LDS; then, per 32-wide K slice, the 16 rows' 64-byte pieces -- one
 // contiguous KiB of the output -- go out as one store instruction of a wave.
 // gamma and beta are staged once per workgroup in LDS.  With a ScanArgs job,
 // workgroup 0 of the launch runs the placeholder scan instead (scan_body),
@@ -427,60 +425,73 @@ constexpr int kMbRows = 16;  // rows per item = waves per workgroup
 constexpr bool mb_gb32(int nch_per_lane) { return nch_per_lane <= 6; }
 static_assert(kPlanViews >= 64, "each lane reads one view-table entry");
 
-// Two workgroups per CU (8 waves per SIMD, so at most 64 VGPRs) where a lane
-// holds little of a pixel; the 16-byte LayerNorm form past 2 chunks per lane
-// keeps its registers and runs one.
-constexpr int mb_waves_per_simd(bool ln, int nch, bool dw) { return (dw || !ln || nch <= 2) ? 8 : 4; }
-
 template <bool LN, int NCH, bool DW>
-__global__ __launch_bounds__(64 * kMbRows, mb_waves_per_simd(LN, NCH, DW)) void k_merge_blocked(const uint16_t *x, PlanChunk c,
+__global__ __launch_bounds__(64 * kMbRows) void k_merge_blocked(const uint16_t *x, PlanChunk c,
                                                                 int C, const uint16_t *gamma,
                                                                 const uint16_t *beta, float eps,
-                                                                uint16_t *out, ScanArgs scan,
-                                                                int n_items) {
+                                                                uint16_t *out, ScanArgs scan) {
   extern __shared__ uint4 mb_lds[];
   static_assert(64 * kMbRows == kScanThreads, "the scan workgroup has the merge's shape");
   static_assert(LN || !DW, "the dword layout is for the LayerNorm path");
-  int first = blockIdx.x, stride = gridDim.x;
+  int item = blockIdx.x;
   if (scan.on) {  // workgroup 0 runs the placeholder scan (LDS >= kScanChunk positions)
-    if (first == 0) {
+    if (item == 0) {
       scan_body(scan, reinterpret_cast<int32_t *>(mb_lds));
       return;
     }
-    --first;
-    --stride;
+    --item;
   }
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int k = c.k, kk = k * k, nch = C / 8;
   const int rs = nch + 1;  // LDS row stride in 16-byte chunks (odd: rows hit distinct banks)
   const int64_t KB = static_cast<int64_t>(C) * kk / 32;
   const int32_t t_begin = c.tok0[0], t_end = c.tok0[c.n];
   const int g0 = t_begin / kMbRows;
+  const int grp = g0 + item / kk, p = item % kk;
+  const int dy = p / k, dx = p - dy * k;
 
-  // The view table, lane v holding view v's entry (every lane loads: the
-  // tables hold kPlanViews = 64 entries; entries past n are masked).  A row's
-  // view is the number of views starting at or before it, less one, found
-  // with a ballot and picked with shuffles; the table is never indexed with a
-  // wave-uniform value (a scalar load from a computed kernel-argument address
-  // must be dword-aligned at its base, which the 16-bit entries do not
-  // guarantee).
-  const bool have = lane < c.n;
-  const int32_t e_tok0 = c.tok0[lane], e_pix0 = c.pix0[lane];
-  const int32_t e_gh = c.gh[lane], e_gw = c.gw[lane];
-  const int32_t l_tok0 = have ? e_tok0 : INT32_MAX;
-  const int32_t l_pix0 = have ? e_pix0 : 0;
-  const int32_t l_gh = have ? e_gh : 0, l_gw = have ? e_gw : 1;
-
-  // gamma and beta (LN) are staged once in LDS after the rows, widened to
-  // fp32 (no conversion per element later) while that fits: up to 6 chunks
-  // per lane (C <= 3072); for C up to 4096 they stay bf16.
+  // This wave's row and its pixel (wave-uniform): the view is the number of
+  // views starting at or before the row, less one.  Lane l reads view l's
+  // entry with a vector load and the wave picks entry v with a shuffle; the
+  // table is never indexed with the uniform v directly (a scalar load from a
+  // computed kernel-argument address must be dword-aligned at its base, which
+  // the 16-bit entries do not guarantee).
+  const int m = grp * kMbRows + wid;
+  bool inside = false;
+  int64_t off = 0;
+  if (m >= t_begin && m < t_end) {
+    // Every lane loads (the tables hold kPlanViews = 64 entries), so the four
+    // loads go out together; entries past n are then masked.
+    const bool have = lane < c.n;
+    const int32_t e_tok0 = c.tok0[lane], e_pix0 = c.pix0[lane];
+    const int32_t e_gh = c.gh[lane], e_gw = c.gw[lane];
+    const int32_t l_tok0 = have ? e_tok0 : INT32_MAX;
+    const int32_t l_pix0 = have ? e_pix0 : 0;
+    const int32_t l_gh = have ? e_gh : 0, l_gw = have ? e_gw : 1;
+    const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
+    const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
+    const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
+    const int wp = (gw + k - 1) / k, t = m - tok0;
+    const int y = (t / wp) * k + dy, xx = (t % wp) * k + dx;
+    inside = y < gh && xx < gw;
+    off = static_cast<int64_t>(pix0 + y * gw + xx) * C;
+  }
+  // gamma and beta (LN) are staged once per workgroup in LDS after the rows,
+  // widened to fp32 (no conversion per element later) while that fits: up to
+  // 6 chunks per lane (C <= 3072); for C up to 4096 they stay bf16.  Their
+  // loads go out before the pixel's, so waiting for them (loads return in
+  // order) never waits on the pixel.
   constexpr bool GB32 = DW || mb_gb32(NCH);
   float4 *s_gb = reinterpret_cast<float4 *>(mb_lds + kMbRows * rs);  // GB32: [2][C] fp32
   uint4 *s_gb16 = mb_lds + kMbRows * rs;                              // else [2][C] bf16
-  if (LN) {
+  const int tid = threadIdx.x;
+  uint4 gb = make_uint4(0, 0, 0, 0);
+  if (LN && tid < 2 * nch)
+    gb = tid < nch ? reinterpret_cast<const uint4 *>(gamma)[tid]
+                   : reinterpret_cast<const uint4 *>(beta)[tid - nch];
+  // Stage gamma and beta in LDS; every thread of the workgroup reaches it.
+  auto stage_gb = [&]() {
     if (tid < 2 * nch) {  // chunk tid: 8 values (GB32: two float4 entries)
-      const uint4 gb = tid < nch ? reinterpret_cast<const uint4 *>(gamma)[tid]
-                                 : reinterpret_cast<const uint4 *>(beta)[tid - nch];
       if (GB32) {
         s_gb[2 * tid] = make_float4(bf2f(gb.x & 0xffff), bf2f(gb.x >> 16), bf2f(gb.y & 0xffff),
                                     bf2f(gb.y >> 16));
@@ -490,77 +501,50 @@ __global__ __launch_bounds__(64 * kMbRows, mb_waves_per_simd(LN, NCH, DW)) void 
         s_gb16[tid] = gb;
       }
     }
-  }
-
-  // Item: 16 consecutive rows (aligned to 16, so they share a 256-row block)
-  // at block position p; wave r handles row grp*16 + r, pixel off (elements)
-  // -- or nothing when the position lies outside the grid (zero padding).
-  struct Loc {
-    int grp, p;
-    bool inside;
-    int64_t off;
+    __syncthreads();
   };
-  auto locate = [&](int item) {
-    Loc L{g0 + item / kk, item % kk, false, 0};
-    const int dy = L.p / k, dx = L.p - dy * k;
-    const int m = L.grp * kMbRows + wid;
-    if (m >= t_begin && m < t_end) {
-      const int v = __popcll(__ballot(l_tok0 <= m)) - 1;
-      const int tok0 = __shfl(l_tok0, v), pix0 = __shfl(l_pix0, v);
-      const int gh = __shfl(l_gh, v), gw = __shfl(l_gw, v);
-      const int wp = (gw + k - 1) / k, t = m - tok0;
-      const int y = (t / wp) * k + dy, xx = (t % wp) * k + dx;
-      L.inside = y < gh && xx < gw;
-      L.off = static_cast<int64_t>(pix0 + y * gw + xx) * C;
-    }
-    return L;
-  };
+  uint4 *row = mb_lds + wid * rs;
   // The features are read once: non-temporal loads keep them from displacing
-  // the GEMMs' operands in the caches.  DW: one dword (two channels) per lane
-  // and step -- at C = 1152 a pixel is 9 dwords on every lane, where 16-byte
-  // chunks leave 48 lanes idle in the third step; the launcher takes this
-  // form only for C = 128 * NCH.  inside is the same on all lanes of the
-  // wave (one row per wave): made scalar, it branches the wave.
-  // The loads go out unconditionally, with no branch around them (a branch
-  // would make every later wait count as if no younger loads were in flight):
-  // a position outside the grid reads pixel 0 and a lane past the pixel's
-  // chunks re-reads its last one, both inside the features, and the row is
-  // zeroed where it is used.
-  typedef typename std::conditional<DW, uint32_t, uint4>::type Piece;
-  auto load = [&](const Loc &L, Piece (&d)[NCH]) {
-    if constexpr (DW) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(x + (L.inside ? L.off : 0));
+  // the GEMMs' operands in the caches (interleaved A/B, workload 1: step
+  // 0.5291 -> 0.5232 ms, the GEMMs faster, this kernel 0.6 us slower).
+  if constexpr (DW) {
+    // One dword (two channels) per lane and step: at C = 1152 a pixel is 9
+    // dwords on every lane, where 16-byte chunks leave 48 lanes idle in the
+    // third step.  x - mean is kept for the normalisation, the mean and
+    // variance scale by 1/C, and 1/sqrt is the hardware reciprocal root.
+    // The launcher takes this form only for C = 128 * NCH, so every lane of
+    // every step holds a dword of the pixel.  inside is the same on all lanes
+    // of the wave (one row per wave): made scalar, it branches the wave.
+    constexpr int ndw = 64 * NCH;  // dwords per pixel (C / 2)
+    const bool in_w = __builtin_amdgcn_readfirstlane(inside ? 1 : 0) != 0;
+    uint32_t d[NCH];
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(x + off);
+    if (in_w) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) d[i] = load_nt(src + lane + 64 * i);
     } else {
-      const uint4 *src = reinterpret_cast<const uint4 *>(x + (L.inside ? L.off : 0));
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) d[i] = load_nt(src + min(lane + 64 * i, nch - 1));
+      for (int i = 0; i < NCH; ++i) d[i] = 0u;
     }
-  };
-  // LayerNorm of one pixel in place (rows outside the grid stay zero: the
-  // padding comes after the norm).  DW: x - mean is kept for the
-  // normalisation, the mean and variance scale by 1/C, and 1/sqrt is the
-  // hardware reciprocal root.
-  auto normalise = [&](const Loc &L, Piece (&d)[NCH]) {
-    if constexpr (DW) {
-      constexpr int ndw = 64 * NCH;  // dwords per pixel (C / 2)
-      if (!__builtin_amdgcn_readfirstlane(L.inside ? 1 : 0)) return;
-      // the two channels of a dword, widened again in each pass (a shift and
-      // a mask) rather than kept: two pixels per lane already sit in registers
-      auto lo = [&](int i) { return __uint_as_float(d[i] << 16); };
-      auto hi = [&](int i) { return __uint_as_float(d[i] & 0xffff0000u); };
+    stage_gb();
+    if (in_w) {  // rows outside the grid stay zero (padding comes after the norm)
+      float lo[NCH], hi[NCH];
       float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) sum += lo(i) + hi(i);
+      for (int i = 0; i < NCH; ++i) {
+        lo[i] = __uint_as_float(d[i] << 16);
+        hi[i] = __uint_as_float(d[i] & 0xffff0000u);
+        sum += lo[i] + hi[i];
+      }
       constexpr float inv_c = 1.0f / static_cast<float>(2 * ndw);
       const float mean = wave_sum(sum) * inv_c;
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const float a = lo(i) - mean, b = hi(i) - mean;
-        ss = fmaf(a, a, ss);
-        ss = fmaf(b, b, ss);
+        lo[i] -= mean;
+        hi[i] -= mean;
+        ss = fmaf(lo[i], lo[i], ss);
+        ss = fmaf(hi[i], hi[i], ss);
       }
       const float rstd = rsqrtf(wave_sum(ss) * inv_c + eps);
       const float2 *g2 = reinterpret_cast<const float2 *>(s_gb);  // [C] gamma, then [C] beta
@@ -568,25 +552,35 @@ __global__ __launch_bounds__(64 * kMbRows, mb_waves_per_simd(LN, NCH, DW)) void 
       for (int i = 0; i < NCH; ++i) {
         const int q = lane + 64 * i;
         const float2 g = g2[q], be = g2[ndw + q];
-        d[i] = f2bf2(fmaf((lo(i) - mean) * rstd, g.x, be.x), fmaf((hi(i) - mean) * rstd, g.y, be.y));
+        d[i] = f2bf2(fmaf(lo[i] * rstd, g.x, be.x), fmaf(hi[i] * rstd, g.y, be.y));
       }
-    } else {
-      if (!L.inside) return;
+    }
+    uint32_t *row32 = reinterpret_cast<uint32_t *>(row);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) row32[lane + 64 * i] = d[i];
+  } else {
+    uint4 v[NCH];
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + off);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = lane + 64 * i;
+      v[i] = (inside && q < nch) ? load_nt(src + q) : make_uint4(0, 0, 0, 0);
+    }
+    if (LN) stage_gb();
+    if (LN && inside) {  // rows outside the grid stay zero (padding comes after the norm)
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        if (lane + 64 * i < nch) {  // lanes past the pixel hold a re-read chunk (see load)
-          const uint16_t *e = reinterpret_cast<const uint16_t *>(&d[i]);
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
-        }
+        for (int j = 0; j < 8; ++j) sum += bf2f(e[j]);
       }
       const float mean = wave_sum(sum) / C;
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
         if (lane + 64 * i < nch) {
-          const uint16_t *e = reinterpret_cast<const uint16_t *>(&d[i]);
+          const uint16_t *e = reinterpret_cast<const uint16_t *>(&v[i]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float dlt = bf2f(e[j]) - mean;
@@ -601,10 +595,10 @@ __global__ __launch_bounds__(64 * kMbRows, mb_waves_per_simd(LN, NCH, DW)) void 
         if (q < nch) {
           float gf[8], bfv[8];
           if (GB32) {
-            const float4 g0v = s_gb[2 * q], g1v = s_gb[2 * q + 1];
+            const float4 g0 = s_gb[2 * q], g1 = s_gb[2 * q + 1];
             const float4 b0 = s_gb[2 * (nch + q)], b1 = s_gb[2 * (nch + q) + 1];
-            gf[0] = g0v.x; gf[1] = g0v.y; gf[2] = g0v.z; gf[3] = g0v.w;
-            gf[4] = g1v.x; gf[5] = g1v.y; gf[6] = g1v.z; gf[7] = g1v.w;
+            gf[0] = g0.x; gf[1] = g0.y; gf[2] = g0.z; gf[3] = g0.w;
+            gf[4] = g1.x; gf[5] = g1.y; gf[6] = g1.z; gf[7] = g1.w;
             bfv[0] = b0.x; bfv[1] = b0.y; bfv[2] = b0.z; bfv[3] = b0.w;
             bfv[4] = b1.x; bfv[5] = b1.y; bfv[6] = b1.z; bfv[7] = b1.w;
           } else {
@@ -617,87 +611,26 @@ __global__ __launch_bounds__(64 * kMbRows, mb_waves_per_simd(LN, NCH, DW)) void 
               bfv[j] = bf2f(be[j]);
             }
           }
-          uint16_t *e = reinterpret_cast<uint16_t *>(&d[i]);
+          uint16_t *e = reinterpret_cast<uint16_t *>(&v[i]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) e[j] = f2bf(fmaf((bf2f(e[j]) - mean) * rstd, gf[j], bfv[j]));
         }
       }
     }
-  };
-
-  // Persistent: this workgroup takes items first, first + stride, ...  With
-  // PREF each item's pixel loads go out before the previous item is
-  // normalised and stored, so their latency hides under that work; PREF holds
-  // two pixels per lane and is taken where that stays within the 64 VGPRs of
-  // two 1024-thread workgroups per CU (the dword LayerNorm form, and the plain
-  // merge up to 4 chunks per lane).  Two barriers per item: the LDS rows are
-  // rewritten only after every wave has stored the last item's (and, on the
-  // first item, gamma and beta are visible).
-  constexpr bool PREF = DW || (!LN && NCH <= 4);
-  uint4 *row = mb_lds + wid * rs;
-  const int r = lane >> 2, c4 = lane & 3;  // store: lane -> (row lane/4, chunk lane%4)
-  const int slices = C / 32;
-  auto body = [&](const Loc &L, Piece (&d)[NCH]) {
-    __syncthreads();
-    if (LN) normalise(L, d);
-    if constexpr (DW) {  // positions outside the grid are zero (the padding comes after the norm)
-      const bool in_w = __builtin_amdgcn_readfirstlane(L.inside ? 1 : 0) != 0;
-      uint32_t *row32 = reinterpret_cast<uint32_t *>(row);
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) row32[lane + 64 * i] = in_w ? d[i] : 0u;
-    } else {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i)
-        if (lane + 64 * i < nch) row[lane + 64 * i] = L.inside ? d[i] : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
-    // per K slice: the 16 rows' 64-byte pieces, one contiguous KiB, in one
-    // store instruction of a wave; only this item's rows are written
-    const int mr = L.grp * kMbRows + r;
-    if (mr >= t_begin && mr < t_end) {
-      uint16_t *dst = out + (static_cast<int64_t>(mr >> 8) * KB * 256 + (mr & 255)) * 32 + c4 * 8;
-      const int sl0 = L.p * slices;
-      for (int sl = wid; sl < slices; sl += kMbRows)
-        *reinterpret_cast<uint4 *>(dst + static_cast<int64_t>(sl0 + sl) * (256 * 32)) =
-            mb_lds[r * rs + sl * 4 + c4];
-    }
-  };
-  // Two pixel buffers used in turn (the loop is unrolled by two), so a
-  // prefetched pixel is never copied -- a copy would wait for its loads.
-  // After a prefetch the wave waits until only those NCH loads are in flight:
-  // the pixel about to be used and the last item's stores (counted by vmcnt
-  // too, their number known only at run time) are then done, and the
-  // compiler's own waits need not drain the prefetch.
-  constexpr int kWaitPrefetched = (NCH & 15) | ((NCH >> 4) << 14) | 0x70 | 0xF00;  // vmcnt(NCH)
-  Loc L0 = locate(first < n_items ? first : 0), L1 = L0;
-  Piece d0[NCH], d1[NCH];
-  if (PREF) load(L0, d0);
-  int item = first;
-  while (item < n_items) {
-    const int i1 = item + stride;
-    if (!PREF) {
-      L0 = locate(item);
-      load(L0, d0);
-    } else {  // past the last item locate() gives a position outside every grid
-      L1 = locate(i1);
-      load(L1, d1);
-      __builtin_amdgcn_s_waitcnt(kWaitPrefetched);
-    }
-    body(L0, d0);
-    item = i1;
-    if (item >= n_items) break;
-    const int i2 = item + stride;
-    if (!PREF) {
-      L1 = locate(item);
-      load(L1, d1);
-    } else {
-      L0 = locate(i2);
-      load(L0, d0);
-      __builtin_amdgcn_s_waitcnt(kWaitPrefetched);
-    }
-    body(L1, d1);
-    item = i2;
+    for (int i = 0; i < NCH; ++i)
+      if (lane + 64 * i < nch) row[lane + 64 * i] = v[i];
   }
+  __syncthreads();
+  // Per K slice: lane -> (row lane/4, chunk lane%4); only this chunk's rows are written.
+  const int r = lane >> 2, c4 = lane & 3;
+  const int mr = grp * kMbRows + r;
+  if (mr < t_begin || mr >= t_end) return;
+  uint16_t *dst = out + (static_cast<int64_t>(mr >> 8) * KB * 256 + (mr & 255)) * 32 + c4 * 8;
+  const int slices = C / 32, sl0 = p * slices;
+  for (int sl = wid; sl < slices; sl += kMbRows)
+    *reinterpret_cast<uint4 *>(dst + static_cast<int64_t>(sl0 + sl) * (256 * 32)) =
+        mb_lds[r * rs + sl * 4 + c4];
 }
 
 // ---------------------------------------------------------------------------
@@ -970,10 +903,8 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
                             const void *beta, float eps, void *out, hipStream_t s,
                             const ScanArgs &scan) {
   const int64_t items =
-      ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k;
-  // persistent workgroups: two per CU (the thread limit for 1024-thread
-  // workgroups), plus the scan's
-  const int64_t grid = std::min<int64_t>(items, 2 * kPlanCUs) + (scan.on ? 1 : 0);
+      ((c.tok0[c.n] + kMbRows - 1) / kMbRows - c.tok0[0] / kMbRows) * int64_t{c.k} * c.k +
+      (scan.on ? 1 : 0);
   // staged rows, then (LN) gamma and beta (fp32 or bf16, see mb_gb32):
   // <= 160 KiB for every C the dispatch takes
   size_t lds = static_cast<size_t>(kMbRows) * (C / 8 + 1) * 16 +
@@ -988,10 +919,10 @@ static hipError_t mb_launch(const void *x, const PlanChunk &c, int C, const void
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_merge_blocked<LN, NCH, DW>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((k_merge_blocked<LN, NCH, DW>), dim3(static_cast<uint32_t>(items)),
                      dim3(64 * kMbRows), lds, s, static_cast<const uint16_t *>(x), c, C,
                      static_cast<const uint16_t *>(gamma), static_cast<const uint16_t *>(beta),
-                     eps, static_cast<uint16_t *>(out), scan, static_cast<int>(items));
+                     eps, static_cast<uint16_t *>(out), scan);
   return hipGetLastError();
 }
 
