@@ -33,7 +33,7 @@ struct Plan {
   std::vector<int32_t> img_view0;      // [n_images]
   // workspace carving (bytes)
   size_t off_status = 0, off_dst = 0, off_desc = 0, off_xn = 0, off_h = 0, off_h2 = 0,
-         off_w1p = 0, off_w2p = 0, off_wmp = 0, off_slot = 0, total = 0;
+         off_w1p = 0, off_w2p = 0, off_wmp = 0, off_slot = 0, off_text = 0, total = 0;
 };
 
 constexpr int kMaxDepth = 16;
@@ -194,6 +194,9 @@ vlb_status make_plan(const vlb_projector *p, const vlb_batch *b, int64_t seq_len
   }
   pl->off_slot = off;
   off = align256(off + static_cast<size_t>(seq_len) * 4);
+  // the token-id form's text positions and ids (vlb_bridge_embed)
+  pl->off_text = off;
+  off = align256(off + static_cast<size_t>(seq_len) * 8);
   pl->total = off;
   return VLB_OK;
 }
@@ -411,7 +414,7 @@ vlb_status run_project(const vlb_projector *p, const vlb_batch *b, const Plan &p
   if (scan && (p->dtype != VLB_BF16 || b->n_views < 1)) {  // no merge launch to carry it
     VLB_LAUNCH(VLB_K_SCAN, s,
                vlb::launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
-                                scan->P, scan->slot_pos, scan->status, scan->direct, s));
+                                scan->P, scan->slot_pos, scan->status, scan->direct, s, scan->text));
     scan = nullptr;
   }
   // Gather mode (the projector's gather flag; bf16 without LayerNorm, and no
@@ -604,15 +607,17 @@ vlb_status run_place(const vlb_projector *p, const vlb_batch *b, const Plan &pl,
   int32_t *status = reinterpret_cast<int32_t *>(ws + pl.off_status);
   int32_t *slot_pos = reinterpret_cast<int32_t *>(ws + pl.off_slot);
   int32_t *dst_row = reinterpret_cast<int32_t *>(ws + pl.off_dst);
+  // the token-id form also lists the text positions and their ids
+  int32_t *text = src.ids ? reinterpret_cast<int32_t *>(ws + pl.off_text) : nullptr;
   if (b->layout == VLB_LAYOUT_PLAIN) {  // token row r -> the r-th placeholder: the scan writes dst_row
     VLB_LAUNCH(VLB_K_SCAN, s,
                vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, dst_row,
-                                status, true, s));
+                                status, true, s, text));
     return VLB_OK;
   }
   VLB_LAUNCH(VLB_K_SCAN, s,
              vlb::launch_scan(src.mask, src.ids, src.image_id, src.vocab, seq_len, pl.P, slot_pos,
-                              status, false, s));
+                              status, false, s, text));
   return run_place_tiled(p, b, pl, newline, separator, seq, ws, s);
 }
 
@@ -630,7 +635,8 @@ vlb::ScanJob merge_scan(const vlb_batch *b, const Plan &pl, const uint8_t *mask,
   const bool plain = b->layout == VLB_LAYOUT_PLAIN;
   return vlb::ScanJob{mask, ids, image_id, vocab, seq_len, pl.P,
                       reinterpret_cast<int32_t *>(ws + (plain ? pl.off_dst : pl.off_slot)),
-                      reinterpret_cast<int32_t *>(ws + pl.off_status), plain};
+                      reinterpret_cast<int32_t *>(ws + pl.off_status), plain,
+                      ids ? reinterpret_cast<int32_t *>(ws + pl.off_text) : nullptr};
 }
 
 vlb_status check_weights(const vlb_projector *p, const vlb_weights *w) {
@@ -1353,6 +1359,8 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
   uint8_t *w8 = static_cast<uint8_t *>(ws);
   const int32_t *status = reinterpret_cast<const int32_t *>(w8 + pl.off_status);
   const int32_t *dst_row = reinterpret_cast<const int32_t *>(w8 + pl.off_dst);
+  // (position, id) of every text position, written by the token-id scan
+  const int32_t *text = reinterpret_cast<const int32_t *>(w8 + pl.off_text);
   if (pl.T > 0 && scan_in_merge(p)) {
     // The token-id scan rides in the first merge launch (the tiled slot map
     // follows the merge); the text rows, which wait for its verdict, follow
@@ -1363,16 +1371,16 @@ vlb_status vlb_bridge_embed(const vlb_projector *p, const vlb_batch *b, const vo
                      b->layout == VLB_LAYOUT_TILED_2D ? &tp : nullptr);
     if (st != VLB_OK) return st;
     VLB_LAUNCH(VLB_K_EMBED, s,
-               vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
-                                      status, seq, s));
+               vlb::launch_embed_rows(p->dtype, text, seq_len - pl.P, embed, p->out_dim, status,
+                                      seq, s));
     return VLB_OK;
   }
   st = run_place(p, b, pl, newline, separator, PlaceSrc{nullptr, ids, image_token_id, vocab},
                  seq_len, seq, w8, s);
   if (st != VLB_OK) return st;
   VLB_LAUNCH(VLB_K_EMBED, s,
-             vlb::launch_embed_rows(p->dtype, ids, seq_len, image_token_id, embed, p->out_dim,
-                                    status, seq, s));
+             vlb::launch_embed_rows(p->dtype, text, seq_len - pl.P, embed, p->out_dim, status, seq,
+                                    s));
   if (pl.T == 0) return VLB_OK;
   return run_project(p, b, pl, features, w, seq, dst_row, w8, s);
 }

@@ -94,6 +94,7 @@ struct ScanArgs {
   int32_t *status;
   int32_t direct;
   int32_t on;
+  int2 *text;  // token-id form: (position, id) of every text position, in order (may be null)
 };
 
 ScanArgs scan_args(const ScanJob *j) {
@@ -106,6 +107,7 @@ ScanArgs scan_args(const ScanJob *j) {
     a.status = j->status;
     a.direct = j->direct ? 1 : 0;
     a.on = 1;
+    a.text = reinterpret_cast<int2 *>(j->text);
   }
   return a;
 }
@@ -144,6 +146,19 @@ __device__ __forceinline__ void scan_body(const ScanArgs &a, int32_t *s_pos) {
     }
     __syncthreads();
     int pos = (x - cnt) + (wid > 0 ? wsum[wid - 1] : 0);  // inside this pass
+    if (a.text) {  // text position q is the (q - placeholders before it)-th text position
+      int64_t img = carry + pos;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t q = off + i;
+        if (q < S) {
+          if (b[i])
+            ++img;
+          else  // the id is read again (from the cache) rather than kept in registers
+            a.text[q - img] = make_int2(static_cast<int32_t>(q), src.ids[q]);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (b[i]) s_pos[pos++] = static_cast<int32_t>(off + i);
@@ -209,25 +224,24 @@ __global__ __launch_bounds__(kScanThreads) void k_plan(PlanChunk c, RowDesc *des
 }
 
 // ---------------------------------------------------------------------------
-// Token-embedding rows: seq[s] = embed[ids[s]] for every position whose id is
-// not the image token, nothing when the scan reported an error.  One wave per
-// position, 16-byte copies.
+// Token-embedding rows: seq[q] = embed[id] for every text position q, from
+// the (position, id) list the token-id scan writes -- nothing when the scan
+// reported an error.  One wave per text row (the pair and the status word are
+// loaded together, then the row), 16-byte copies.
 template <typename T>
-__global__ __launch_bounds__(256) void k_embed_rows(const int32_t *ids, int64_t S, int32_t image_id,
-                                                    const T *embed, int D, const int32_t *status,
-                                                    T *seq) {
+__global__ __launch_bounds__(256) void k_embed_rows(const int2 *text, int64_t n, const T *embed,
+                                                    int D, const int32_t *status, T *seq) {
   constexpr int V = 8;  // 16-byte chunks per lane per pass: up to 8 KiB of a row in flight
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  const int32_t st = status[kStatusWord];  // read together with the first id
+  const int32_t st = status[kStatusWord];  // read together with the first pair
   const int n16 = D * static_cast<int>(sizeof(T)) / 16;
-  for (int64_t s = wave; s < S; s += nwaves) {
-    const int32_t id = ids[s];
+  for (int64_t j = wave; j < n; j += nwaves) {
+    const int2 e = text[j];
     if (st != 0) return;
-    if (id == image_id) continue;
-    const uint4 *from = reinterpret_cast<const uint4 *>(embed + static_cast<int64_t>(id) * D);
-    uint4 *to = reinterpret_cast<uint4 *>(seq + s * D);
+    const uint4 *from = reinterpret_cast<const uint4 *>(embed + static_cast<int64_t>(e.y) * D);
+    uint4 *to = reinterpret_cast<uint4 *>(seq + static_cast<int64_t>(e.x) * D);
     // All of a pass's loads are issued before its stores (the table and the
     // sequence may not be assumed apart, so a plain copy loop would wait on
     // every load in turn).
@@ -791,7 +805,7 @@ hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s, const S
   const int64_t n = c.tok0[c.n] - c.tok0[0];
   if (n <= 0)  // no rows: the scan (if any) runs on its own
     return scan ? launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
-                              scan->P, scan->slot_pos, scan->status, scan->direct, s)
+                              scan->P, scan->slot_pos, scan->status, scan->direct, s, scan->text)
                 : hipSuccess;
   const ScanArgs sa = scan_args(scan);
   const int grid = grid_for(n, kScanThreads, 1 << 30) + (sa.on ? 1 : 0);
@@ -814,22 +828,22 @@ hipError_t launch_copy_status(const int32_t *src, int32_t *dst, hipStream_t s) {
 
 hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
                        int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
-                       hipStream_t s) {
-  const ScanJob j{mask, ids, image_id, vocab, S, P, slot_pos, status, direct};
+                       hipStream_t s, int32_t *text) {
+  const ScanJob j{mask, ids, image_id, vocab, S, P, slot_pos, status, direct, text};
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, scan_args(&j));
   return hipGetLastError();
 }
 
-hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
-                             const void *embed, int D, const int32_t *status, void *seq,
-                             hipStream_t s) {
-  if (S <= 0) return hipSuccess;
-  const int grid = grid_for(S, 4, 16384);
+hipError_t launch_embed_rows(int dtype, const int32_t *text, int64_t n, const void *embed, int D,
+                             const int32_t *status, void *seq, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int grid = grid_for(n, 4, 16384);
+  const int2 *t = reinterpret_cast<const int2 *>(text);
   if (dtype == 0)
-    hipLaunchKernelGGL(k_embed_rows<float>, dim3(grid), dim3(256), 0, s, ids, S, image_id,
+    hipLaunchKernelGGL(k_embed_rows<float>, dim3(grid), dim3(256), 0, s, t, n,
                        static_cast<const float *>(embed), D, status, static_cast<float *>(seq));
   else
-    hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(grid), dim3(256), 0, s, ids, S, image_id,
+    hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(grid), dim3(256), 0, s, t, n,
                        static_cast<const uint16_t *>(embed), D, status,
                        static_cast<uint16_t *>(seq));
   return hipGetLastError();
@@ -957,7 +971,7 @@ hipError_t launch_merge_blocked(const void *x, const PlanChunk &c, int C, const 
                                 const ScanJob *scan) {
   if (c.n <= 0 || c.tok0[c.n] <= c.tok0[0])  // no rows: the scan (if any) runs on its own
     return scan ? launch_scan(scan->mask, scan->ids, scan->image_id, scan->vocab, scan->S,
-                              scan->P, scan->slot_pos, scan->status, scan->direct, s)
+                              scan->P, scan->slot_pos, scan->status, scan->direct, s, scan->text)
                 : hipSuccess;
   const ScanArgs sa = scan_args(scan);
   return gamma ? mb_dispatch<true>(x, c, C, gamma, beta, eps, out, s, sa)

@@ -170,7 +170,7 @@ inline size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
 // themselves, or -1 everywhere when the input is invalid.
 hipError_t launch_scan(const uint8_t *mask, const int32_t *ids, int32_t image_id, int64_t vocab,
                        int64_t S, int64_t P, int32_t *slot_pos, int32_t *status, bool direct,
-                       hipStream_t s);
+                       hipStream_t s, int32_t *text = nullptr);
 // The same scan, carried by a merge launch (launch_merge_blocked) as one extra
 // workgroup that runs beside the merge: it reads neither the features nor
 // the merged rows, so the two need no ordering.
@@ -183,6 +183,9 @@ struct ScanJob {
   int32_t *slot_pos;
   int32_t *status;
   bool direct;
+  // token-id form, optional: the (position, id) pairs of the text positions,
+  // in order ([S][2] int32 of room: a count mismatch may leave more than S - P)
+  int32_t *text = nullptr;
 };
 // dst[0..3] = src[0..3] (the status words), or zeros when src is null.
 hipError_t launch_copy_status(const int32_t *src, int32_t *dst, hipStream_t s);
@@ -190,10 +193,10 @@ hipError_t launch_copy_status(const int32_t *src, int32_t *dst, hipStream_t s);
 // non-null, the launch also runs that placeholder scan (one extra workgroup).
 hipError_t launch_plan(const PlanChunk &c, RowDesc *desc, hipStream_t s,
                        const ScanJob *scan = nullptr);
-// seq[s] = embed[ids[s]] where ids[s] != image_id (nothing if the scan failed).
-hipError_t launch_embed_rows(int dtype, const int32_t *ids, int64_t S, int32_t image_id,
-                             const void *embed, int D, const int32_t *status, void *seq,
-                             hipStream_t s);
+// seq[q] = embed[id] for the first n (q, id) pairs of text, the list the
+// token-id scan writes (nothing if the scan failed).
+hipError_t launch_embed_rows(int dtype, const int32_t *text, int64_t n, const void *embed, int D,
+                             const int32_t *status, void *seq, hipStream_t s);
 hipError_t launch_place_tiled(int dtype, const PlaceChunk &c, const int32_t *slot_pos,
                               const int32_t *status, int32_t *dst_row, const void *newline,
                               const void *separator, void *seq, int D, hipStream_t s);
