@@ -70,10 +70,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // Byte offset of 16-byte chunk `chunk` (0..3) of row `row` inside a stage
-// half: 64-byte rows, the chunk XOR-ed with ((row >> 1) ^ (row >> 3)) & 3 so
-// that any 8 or 16 consecutive rows reading the same logical chunk fall on
-// distinct LDS banks.
-__device__ __forceinline__ int swz_xor(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// half: 64-byte rows, the chunk XOR-ed with (row >> 1) & 3.  A fragment read
+// (16 consecutive rows from a multiple of 16, one logical chunk per group of
+// 16 lanes) then takes 4 LDS cycles per ds_read_b128, the rate of a linear
+// read; ((row >> 1) ^ (row >> 3)) & 3, or no swizzle, takes 8 (measured with
+// the LDS bank-conflict counters on gfx950).
+__device__ __forceinline__ int swz_xor(int row) { return (row >> 1) & 3; }
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 64 + ((chunk ^ swz_xor(row)) << 4);
 }
