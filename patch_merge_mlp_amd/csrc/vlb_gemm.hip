@@ -502,7 +502,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
     rd(nxt, na, nb);
     issue(kt + 3, fut, 1);
     mma(fa, fb, Q, G::TI);
-    if constexpr (BMT == 256) {  // 48 MFMAs, 16-32 LDS reads, 4 loads
+    if constexpr (BMT == 256) {  // 48 MFMAs, 16 or 24 LDS reads, 4 loads
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
@@ -512,16 +512,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-    } else {  // 12 MFMAs, 8-16 LDS reads, 2 loads
+    } else {  // 12 MFMAs, 8 or 12 LDS reads, 2 loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (NRD == 16)
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (NRD >= 12)
+        if (NRD == 12)
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         else
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
