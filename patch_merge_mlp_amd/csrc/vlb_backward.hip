@@ -548,8 +548,19 @@ __global__ __launch_bounds__(256) void k_colsum(const float *part, int32_t R, in
   const int n = blockIdx.x * 32 + c;
   float acc = 0.f;
   if (n < N) {
-#pragma unroll 4
-    for (int r = rg; r < R; r += 8) acc += part[static_cast<int64_t>(r) * N + n];
+    // rows rg, rg + 8, ...: 16 loads in flight at a time, then added in row
+    // order (the same order on every run)
+    constexpr int B = 16;
+    for (int r0 = rg; r0 < R; r0 += 8 * B) {
+      float v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int r = r0 + 8 * i;
+        v[i] = r < R ? part[static_cast<int64_t>(r) * N + n] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) acc += v[i];
+    }
   }
   red[rg][c] = acc;
   __syncthreads();
