@@ -69,6 +69,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Whole tiles: workgroups are dealt round-robin to the 8 XCDs (workgroup b
+// runs on XCD b % 8) and each XCD starts its workgroups in order, so its j-th
+// group of 32 (one per CU) runs at about the same time as every other XCD's
+// j-th.  Group j of XCD x takes the 32 logical tiles of block 8j + x: in every
+// round the eight XCDs work on 256 consecutive logical tiles, so the A panels
+// of those tile rows are read by several XCDs at once and the B panels stay
+// in use from round to round.  A last round that is not full keeps launch
+// order.
+__device__ __forceinline__ int whole_tile_order(int bid, int n) {
+  const int full = n & ~255;
+  if (bid >= full) return bid;
+  const int xcd = bid & 7, local = bid >> 3;
+  return ((((local >> 5) << 3) + xcd) << 5) + (local & 31);
+}
+
 // Byte offset of 16-byte chunk `chunk` (0..3) of row `row` inside a stage
 // half: 64-byte rows, the chunk XOR-ed with (row >> 1) & 3.  A fragment read
 // (16 consecutive rows from a multiple of 16, one logical chunk per group of
@@ -592,7 +607,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16(GemmArgs g) {
   __shared__ int32_t s_dst[BMT];  // destination row per tile row
   int tm, tn;
   if (BMT == 256)
-    tile_coords(xcd_remap(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+    tile_coords(whole_tile_order(blockIdx.x, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   else
     tail_coords(g, blockIdx.x, tm, tn);
   gemm_tile<MODE, ACT, BMT, GA, TB>(g, tm, tn, smem0, smem1, smem2, smem3, s_dst, 0, g.K / BK,
@@ -616,7 +631,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k_gemm_bf16_mixed(GemmArgs g) {
   float *part = nullptr;
   const int bid = static_cast<int>(blockIdx.x);
   if (bid < g.n_full) {
-    tile_coords(xcd_remap(bid, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
+    tile_coords(whole_tile_order(bid, g.n_full), g.tiles_m, g.tiles_n, tm, tn);
   } else if (!GA && MODE == kGemmF32 && g.k_splits > 1) {
     // K range r of tail tile q, as a whole tile: workgroup n_full + q*S + r
     // (S = k_splits), its partial tile at split_part + (q*S + r) tiles.
