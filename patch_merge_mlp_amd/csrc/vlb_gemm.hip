@@ -484,11 +484,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
       for (int j = 0; j < G::TI; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
-  // One K step of 32 (NM MFMAs): the loads of step kt+3 are issued into the
+  // One K step of 32 (TI x TI MFMAs): the loads of step kt+3 are issued into the
   // stage freed by step kt-1; after the first quarter of the MFMAs the barrier
   // (step kt+1 landed everywhere, step kt's fragments all read) lets the next
   // step's fragments be read under the remaining MFMAs.
-  constexpr int NM = G::TI * G::TI;
   constexpr int Q = G::TI / 4;  // A tiles per quarter
   auto step = [&](const uint8_t *nxt, uint8_t *fut, int kt, const bf16x8 *fa, const bf16x8 *fb,
                   bf16x8 *na, bf16x8 *nb) {
