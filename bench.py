@@ -62,6 +62,8 @@ def parse():
                     help="skip timing the standalone merge and scatter entry points")
     ap.add_argument("--no-sclk", action="store_true",
                     help="skip sampling the GFX clock under load (amd-smi, after the timed region)")
+    ap.add_argument("--no-power-probe", action="store_true",
+                    help="skip timing Linear1 on the headline workload with all-zero features")
     ap.add_argument("--no-train", action="store_true",
                     help="skip timing the training step (forward + backward)")
     ap.add_argument("--no-depth", action="store_true",
@@ -310,6 +312,8 @@ def measure_config(args, v, wl, torch, i, headline, extras):
 
     if not args.no_sclk and headline:
         line["sclk"] = sclk_under_load(args.sampler, step, torch, sec)
+    if not args.no_power_probe and headline and bf16:
+        line["power_probe"] = power_probe(v, torch, args.sampler, step, feats, sec)
 
     if not args.no_hbm_kernels:
         summary["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
@@ -570,6 +574,48 @@ def sclk_under_load(sampler, step, torch, sec_per_step, seconds=2.5):
     return {"median_mhz": q(0.5), "p10_mhz": q(0.1), "p90_mhz": q(0.9), "samples": len(samples),
             "how": "amd-smi metric -c (per-XCD GFX clocks) in a child process, samples taken "
                    "during an untimed burst of steps"}
+
+
+def power_probe(v, torch, sampler, step, feats, sec_per_step, seconds=1.5):
+    """Linear1 with the workload's features and with all-zero features (the
+    merged operand, and with it half of every MFMA's input, is then zero):
+    the same instructions and memory traffic, but the MFMA's power depends on
+    the data, so on a power-capped board a loop bound by power runs the zero
+    operand faster, at a higher clock, while a loop bound by its instruction
+    stream would not change.  For each: Linear1's mean time (HIP events on
+    every PROF_EVERY-th step of a burst of steps) and the GFX clock during the
+    burst (None without the sampler).  The features are restored afterwards."""
+    saved = feats.clone()
+    n = max(PROF_EVERY, int(seconds / max(sec_per_step, 1e-6)))
+    out = {}
+    for name in ("workload_features", "zero_features"):
+        if name == "zero_features":
+            feats.zero_()
+        for _ in range(10):
+            step()
+        v.vlb_prof_enable(1 << v.K_GEMM1)
+        v.vlb_prof_resume(0)
+        torch.cuda.synchronize()
+        t0 = time.monotonic()
+        for i in range(n):
+            if i % PROF_EVERY == 0:
+                v.vlb_prof_resume(1 << v.K_GEMM1)
+                step()
+                v.vlb_prof_resume(0)
+            else:
+                step()
+        torch.cuda.synchronize()
+        t1 = time.monotonic()
+        v.vlb_prof_enable(False)
+        k, ms = v.vlb_prof_read(v.K_GEMM1)
+        mhz = None
+        if sampler is not None and sampler.proc is not None:
+            smp = sorted(sampler.window(t0, t1))
+            mhz = smp[len(smp) // 2] if smp else None
+        out[name] = {"gemm1_us": round(1000.0 * ms / k, 2) if k else None, "sclk_median_mhz": mhz}
+    feats.copy_(saved)
+    torch.cuda.synchronize()
+    return out
 
 
 def train_step(v, torch, wl, w, p, b, t, d, T, K1, steps):
