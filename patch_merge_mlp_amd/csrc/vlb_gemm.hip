@@ -476,13 +476,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   };
   // LDS read instructions per step: one per fragment, two for a token-major one
   constexpr int NRD = G::TI + G::TI * (TB ? 2 : 1);
-  // MFMAs [i0, i1) of the step, i-major (A tile i, B tile j).
+  // MFMAs [i0, i1) of the step, i-major (A tile i, B tile j), the j order
+  // reversed on odd i, so that every MFMA shares an operand with the one
+  // before it (the MFMA's power depends on its data, and this loop is bound
+  // by power: interleaved A/B, ragged-3x3 step 2.055 -> 2.047 ms).
   auto mma = [&](const bf16x8 *fa, const bf16x8 *fb, int i0, int i1) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
 #pragma unroll
-      for (int j = 0; j < G::TI; ++j)
+      for (int jj = 0; jj < G::TI; ++jj) {
+        const int j = (i & 1) ? G::TI - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      }
   };
   // One K step of 32 (TI x TI MFMAs): the loads of step kt+3 are issued into the
   // stage freed by step kt-1; after the first quarter of the MFMAs the barrier
