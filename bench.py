@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -76,10 +77,16 @@ def parse():
 
 
 def kernel_sha() -> str:
+    """Hash of the GEMM's code (vlb_gemm.hip and vlb_common.h) with comments
+    and whitespace removed, so that a comment edit keeps the counters valid
+    and any change to the code does not."""
     h = hashlib.sha256()
     for name in ("vlb_gemm.hip", "vlb_common.h"):
-        with open(os.path.join(ROOT, "patch_merge_mlp_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "patch_merge_mlp_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -57,8 +57,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // load instruction instead of one contiguous KiB), which grows with its
 // hidden width, while the merge pass it saves moves a fixed T * C * k * k * 4
 // bytes.  Measured: hidden 2560 (the tiled 2x2 workload) runs 3% faster per
-// call with the gather, hidden 5120 (both 3x3 workloads) 1.7% slower; the
-// automatic choice takes the gather up to hidden 4096.
+// call with the gather, hidden 5120 (both 3x3 workloads) from 1% faster to
+// 1.7% slower, depending on the run; the automatic choice takes the gather up
+// to hidden 4096.
 constexpr int kGatherMaxHidden = 4096;
 bool gathers(const vlb_projector *p) {
   if (p->dtype != VLB_BF16 || p->has_ln || p->gather == VLB_GATHER_OFF) return false;

@@ -337,9 +337,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, uin
   // past every buffer, so the load returns zeros.  Each load instruction then
   // moves 16 separate 64-byte pieces (half lines, the other half read one step
   // later) instead of one contiguous KiB, and this loop is sensitive to that:
-  // Linear1 runs 18-25% slower than on the blocked operand, which costs more
-  // than the merge pass it saves (so this is the memory-lean mode, not the
-  // default).
+  // Linear1 runs 8-11% slower than on the blocked operand.  The merge pass it
+  // saves costs the same per token whatever the hidden width, so the gather
+  // pays for narrow hidden widths only (the automatic choice in vlb_api.hip).
   // Token-major B (TB; see GemmArgs::tb_w).  Instruction i of wave wid fills
   // KiB gi = wid*LPW + i of the half: the 16 contraction indices k = 16 (gi &
   // 1) + lane/4 of tile rows n0 + 32 (gi >> 1) + [0, 32), lane slot lane%4
