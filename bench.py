@@ -63,6 +63,8 @@ def parse():
                     help="skip timing the standalone merge and scatter entry points")
     ap.add_argument("--no-sclk", action="store_true",
                     help="skip sampling the GFX clock under load (amd-smi, after the timed region)")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing the vendor GEMM (torch.matmul) on the headline's two products")
     ap.add_argument("--no-power-probe", action="store_true",
                     help="skip timing Linear1 on the headline workload with all-zero features")
     ap.add_argument("--no-train", action="store_true",
@@ -321,6 +323,9 @@ def measure_config(args, v, wl, torch, i, headline, extras):
         line["sclk"] = sclk_under_load(args.sampler, step, torch, sec)
     if not args.no_power_probe and headline and bf16:
         line["power_probe"] = power_probe(v, torch, args.sampler, step, feats, sec)
+    if not args.no_vendor_gemm and headline and bf16:
+        line["vendor_gemm"] = vendor_gemm(torch, T, K1, w.hidden, w.out_dim,
+                                          gemm1_us, g2 * 1e6)
 
     if not args.no_hbm_kernels:
         summary["hbm_kernels"] = hbm_kernels(v, torch, w, p, b, t, d, T, K1, args.steps)
@@ -581,6 +586,37 @@ def sclk_under_load(sampler, step, torch, sec_per_step, seconds=2.5):
     return {"median_mhz": q(0.5), "p10_mhz": q(0.1), "p90_mhz": q(0.9), "samples": len(samples),
             "how": "amd-smi metric -c (per-XCD GFX clocks) in a child process, samples taken "
                    "during an untimed burst of steps"}
+
+
+def vendor_gemm(torch, T, K1, H, O, gemm1_us, gemm2_us, reps=30):
+    """The two products of the step through torch.matmul in bf16 (hipBLASLt on
+    ROCm), on seeded operands of the same shapes, for comparison: the plain
+    products only -- no bias, activation, tile-blocked output or scatter --
+    with the weight passed transposed and contiguous.  Mean over `reps` calls
+    between two events, after warm-up; next to it the library's own Linear1
+    and Linear2 means from this run."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    out = {}
+    for name, K, N, ours in (("linear1", K1, H, gemm1_us), ("linear2", H, O, gemm2_us)):
+        a = torch.randn(T, K, device="cuda", generator=g).to(torch.bfloat16)
+        wt = (torch.randn(N, K, device="cuda", generator=g) * K ** -0.5).to(torch.bfloat16)
+        wt = wt.t().contiguous()
+        for _ in range(5):
+            c = a @ wt
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = a @ wt
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        flop = 2.0 * T * K * N
+        out[name] = {"shape_MxKxN": [T, K, N], "torch_matmul_us": round(us, 1),
+                     "torch_matmul_TFLOP/s": round(flop / us / 1e6, 1),
+                     "library_us": round(ours, 1), "library_TFLOP/s": round(flop / ours / 1e6, 1)}
+        del a, wt, c
+    return out
 
 
 def power_probe(v, torch, sampler, step, feats, sec_per_step, seconds=1.5):
